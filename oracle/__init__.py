@@ -1,0 +1,16 @@
+"""fp64 CPU oracle of the SPLA decode step -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import this package.  See ``spla_oracle`` for the definitions, the
+passages they follow and the readings taken where the pages are silent.
+"""
+from .spla_oracle import (  # noqa: F401
+    SplaOracle,
+    block_stats,
+    group_log_score,
+    linear_attention_numerator,
+    phi,
+    select_blocks,
+    softmax_attention,
+    taylor_log_score,
+)
