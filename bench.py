@@ -1,0 +1,281 @@
+"""SPLA decode benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama_gqa_128k]
+
+A step is one pass of the whole decode hot path for one SPLA attention layer:
+spla_append_kv of the step's token for every sequence (page write, S_all /
+z_all update, statistics of a completed block), then spla_decode (Taylor
+block score, top-k, attend + residual linear attention, combine).  Inputs
+(the prefilled state and every step's q, k, v) are resident in HBM before
+the timed region starts.
+
+The per-step footprint of the 128K workload (~26 MB) fits the 256 MB
+Infinity Cache, so the state is replicated into L_rot independent layer
+instances (device copies, L_rot = max(2, ceil(512 MB / bytes per step))) and
+each timed step runs every instance in turn on one stream; t_step = timed
+time / (K * L_rot).  Every instance sees identical inputs, so their outputs
+must be bitwise equal (checked after the run).
+
+Prints one JSON line (rank 0) with the throughput, a roofline entry for the
+dominant kernel (the block scorer: its launch duration measured with HIP
+events recorded on the launch stream around that kernel) and a CPU baseline
+(the fp64 oracle timed on a bounded sample of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def step_bytes(w, lens, s_kv: int) -> dict:
+    """Algorithmic bytes of one decode step (after the step's append) for
+    sequence lengths ``lens``: candidate statistics, selected K/V rows,
+    S_all / z_all read + write, q in, o out, gate, new k/v."""
+    d, G, H, B, bk, k = w.head_dim, w.n_kv_heads, w.n_q_heads, w.batch, w.block_size, w.top_k
+    stats = kv = state = 0
+    for T in lens:
+        nb = -(-T // bk)
+        if nb > k:
+            stats += G * (nb - 2) * 2 * d * 4
+            ntok = (k - 1) * bk + (T - (nb - 1) * bk)
+        else:
+            ntok = T
+        kv += G * ntok * 2 * d * s_kv
+        state += G * 2 * (d * d * 4 + d * 4)
+    io = B * H * d * (s_kv + 4) + H * 4 + B * G * d * 2 * s_kv
+    return {"stats": stats, "kv": kv, "state": state, "io": io, "total": stats + kv + state + io}
+
+
+def score_bytes(w, lens, s_kv: int) -> int:
+    """Algorithmic bytes of one scorer launch: mean and variance of every
+    candidate block plus the queries."""
+    d, G, bk, k = w.head_dim, w.n_kv_heads, w.block_size, w.top_k
+    tot = 0
+    for T in lens:
+        nb = -(-T // bk)
+        if nb > k:
+            tot += G * (nb - 2) * 2 * d * 4
+    return tot + w.batch * w.n_q_heads * d * s_kv
+
+
+def cpu_baseline(w, n_steps: int, budget_s: float) -> dict:
+    """Time the fp64 oracle's append + decode per step on the host cores."""
+    import numpy as np
+    from oracle import SplaOracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    o = SplaOracle(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k,
+                   w.max_tokens(n_steps))
+    t0 = time.time()
+    for b in range(w.batch):
+        for _, k, v in w.prefill_chunks(b):
+            o.append([b], [k.shape[0]], k, v)
+    log(f"oracle prefill {time.time() - t0:.1f}s")
+    gate = w.gate()
+    mix = w.mixture_state()
+    done = 0
+    spent = 0.0
+    for s in range(n_steps):
+        st = w.step(s, mix)
+        t = time.perf_counter()
+        cs = [int(x) for x in st["chunk_seqs"]]
+        if cs:
+            o.append(cs, [w.chunk_len] * len(cs), st["chunk_k"], st["chunk_v"])
+        o.append(list(range(w.batch)), [1] * w.batch, st["k"], st["v"])
+        o.decode(st["q"], gate)
+        spent += time.perf_counter() - t
+        done += 1
+        if spent >= budget_s:
+            break
+    t_step = spent / done
+    return {"value": w.batch / t_step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{w.name}: fp64 NumPy oracle append+decode of the first {done} decode steps after an "
+                      f"untimed prefill ({spent:.1f}s timed, {t_step * 1e3:.1f} ms/step)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="llama_gqa_128k")
+    ap.add_argument("--lrot", type=int, default=0, help="layer instances (0 = auto)")
+    ap.add_argument("--prof-steps", type=int, default=16, help="steps of the per-kernel event pass")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        log("multi-GPU runs are not part of this build (one GPU per process, no collectives)")
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        log("WORLD_SIZE > 1 is not supported")
+        return 2
+
+    import numpy as np
+    import torch
+
+    from block_sparse_linear_amd import SplaLayer
+    from workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    K, W, P = args.steps, args.warmup, args.prof_steps
+    total_steps = W + K + P
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s_kv = 2 if w.kv_dtype == "bf16" else 4
+    tdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    mb = w.max_blocks_per_seq(total_steps)
+
+    def new_layer():
+        return SplaLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k, mb,
+                         kv_dtype=w.kv_dtype, device="cuda:0")
+
+    t0 = time.time()
+    base = new_layer()
+    for b in range(w.batch):
+        for _, k, v in w.prefill_chunks(b):
+            base.append([b], [k.shape[0]], torch.from_numpy(k).to(dev).to(tdt),
+                        torch.from_numpy(v).to(dev).to(tdt))
+    torch.cuda.synchronize()
+    log(f"prefill {time.time() - t0:.1f}s lens={base.lens[:4]}")
+
+    # per-step inputs, resident on the device
+    mix = w.mixture_state()
+    steps_in = []
+    for s in range(total_steps):
+        st = w.step(s, mix)
+        steps_in.append({
+            "q": torch.from_numpy(st["q"]).to(dev).to(tdt),
+            "k": torch.from_numpy(st["k"]).to(dev).to(tdt),
+            "v": torch.from_numpy(st["v"]).to(dev).to(tdt),
+            "cs": [int(x) for x in st["chunk_seqs"]],
+            "ck": torch.from_numpy(st["chunk_k"]).to(dev).to(tdt),
+            "cv": torch.from_numpy(st["chunk_v"]).to(dev).to(tdt),
+        })
+    gate = torch.from_numpy(w.gate()).to(dev)
+
+    lens0 = [t + 1 for t in base.lens]
+    sb = step_bytes(w, lens0, s_kv)
+    L = args.lrot or max(2, math.ceil(512e6 / sb["total"]))
+    layers = [base]
+    for _ in range(L - 1):
+        x = new_layer()
+        for dst, src in zip(x.state_tensors(), base.state_tensors()):
+            dst.copy_(src)
+        x._bind(base.lens)
+        layers.append(x)
+    torch.cuda.synchronize()
+    log(f"L_rot={L} step_bytes={sb}")
+    outs = [torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev) for _ in layers]
+    allb = list(range(w.batch))
+    ones = [1] * w.batch
+
+    def run_step(s, layer, out, kernel_events=None):
+        x = steps_in[s]
+        if x["cs"]:
+            layer.append(x["cs"], [w.chunk_len] * len(x["cs"]), x["ck"], x["cv"])
+        layer.append(allb, ones, x["k"], x["v"])
+        layer.decode(x["q"], gate, out=out, kernel_events=kernel_events)
+
+    for s in range(W):
+        for layer, out in zip(layers, outs):
+            run_step(s, layer, out)
+    torch.cuda.synchronize()
+    lens_t = [t + 1 for t in layers[0].lens]
+    bytes_first = step_bytes(w, lens_t, s_kv)["total"]
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(W, W + K):
+        for layer, out in zip(layers, outs):
+            run_step(s, layer, out)
+    end.record()
+    torch.cuda.synchronize()
+    elapsed_ms = start.elapsed_time(end)
+    t_step = elapsed_ms / 1e3 / (K * L)
+    lens_end = layers[0].lens
+    bytes_last = step_bytes(w, lens_end, s_kv)["total"]
+    bytes_avg = 0.5 * (bytes_first + bytes_last)
+    for o in outs[1:]:
+        if not torch.equal(o, outs[0]):
+            log("WARNING: layer instances disagree bitwise")
+    log(f"timed {K} steps x {L} instances: {elapsed_ms:.2f} ms, t_step {t_step * 1e6:.2f} us")
+
+    # per-kernel durations: HIP events recorded on the launch stream around
+    # each kernel of spla_decode (order: score, select, attend, combine)
+    names = ["score", "select", "attend", "combine"]
+    durs = {n: [] for n in names}
+    import ctypes
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
+    for e in evs:
+        e.record(stream)  # materialise the event handles
+    torch.cuda.synchronize()
+    handles = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+    score_launch_bytes = []
+    for s in range(W + K, W + K + P):
+        for layer, out in zip(layers, outs):
+            run_step(s, layer, out, kernel_events=handles)
+            torch.cuda.synchronize()
+            for i, n in enumerate(names):
+                durs[n].append(evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e-3)
+        score_launch_bytes.append(score_bytes(w, layers[0].lens, s_kv))
+    avg = {n: float(np.mean(v)) for n, v in durs.items()}
+    sc_bytes = float(np.mean(score_launch_bytes))
+    achieved = sc_bytes / avg["score"] / 1e9
+    log("kernel us: " + ", ".join(f"{n}={avg[n] * 1e6:.2f}" for n in names))
+
+    result = {
+        "metric": "SPLA decode tokens/s at 128K ctx GQA 32/8x128; achieved HBM GB/s vs peak",
+        "value": w.batch / t_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic (seeded; see workloads/)",
+        "config": {"workload": w.name, "batch": w.batch, "context": max(w.t0), "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "top_k": w.top_k, "l_rot": L},
+        "step_bytes": bytes_avg,
+        "step_GBps": bytes_avg / t_step / 1e9,
+        "step_frac_of_peak": bytes_avg / t_step / 1e9 / HBM_PEAK_GBS,
+        "kernel_us": {n: avg[n] * 1e6 for n in names},
+        "roofline": {"kernel": "k_score", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": sc_bytes},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, K + W, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

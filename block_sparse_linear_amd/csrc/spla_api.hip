@@ -1,0 +1,306 @@
+// Host side of the C ABI declared in include/spla.h: configuration checks,
+// the host mirror of sequence lengths, workspace layout and kernel launches.
+#include <math.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/spla.h"
+#include "spla_common.h"
+
+using namespace spla;
+
+struct spla_handle {
+  spla_config cfg{};
+  int r = 0;
+  int n_tiles = 0;
+  bool bound = false;
+  spla_buffers buf{};
+  std::vector<int32_t> lens;
+  // workspace layout (bytes)
+  size_t off_lg = 0, off_sel = 0, off_part = 0, ws_bytes = 0;
+};
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+void layout(spla_handle* h) {
+  const spla_config& c = h->cfg;
+  const size_t B = c.batch, H = c.n_q_heads, G = c.n_kv_heads, d = c.head_dim, k = c.top_k;
+  size_t off = 256;  // error word + spare
+  h->off_lg = off;
+  off = align256(off + B * G * (size_t)h->n_tiles * kTile * sizeof(float));
+  h->off_sel = off;
+  off = align256(off + B * G * k * sizeof(int32_t));
+  h->off_part = off;
+  off = align256(off + B * H * k * (2 * d + kPartHdr) * sizeof(float));
+  h->ws_bytes = off;
+}
+
+template <typename T>
+T* ws_ptr(const spla_handle* h, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(h->buf.workspace) + off);
+}
+
+spla_status fill_decode_args(const spla_handle* h, const void* q, const float* gate, float* out,
+                             const spla_decode_aux* aux, DecodeArgs* a) {
+  const spla_config& c = h->cfg;
+  memset(a, 0, sizeof(*a));
+  a->q = q;
+  a->gate = gate;
+  a->out = out;
+  a->k_pages = h->buf.k_pages;
+  a->v_pages = h->buf.v_pages;
+  a->block_table = h->buf.block_table;
+  a->blk_mean = h->buf.blk_mean;
+  a->blk_var = h->buf.blk_var;
+  a->s_all = h->buf.s_all;
+  a->z_all = h->buf.z_all;
+  a->lg = ws_ptr<float>(h, h->off_lg);
+  a->sel = ws_ptr<int32_t>(h, h->off_sel);
+  a->part = ws_ptr<float>(h, h->off_part);
+  a->err = ws_ptr<uint32_t>(h, 0);
+  if (aux) {
+    a->sel_in = aux->sel_in;
+    a->sel_out = aux->sel_idx;
+    a->lg_out = aux->lg;
+    a->o_sparse_out = aux->o_sparse;
+    a->o_rla_out = aux->o_rla;
+    a->d_rla_out = aux->d_rla;
+  }
+  a->B = c.batch;
+  a->H = c.n_q_heads;
+  a->G = c.n_kv_heads;
+  a->d = c.head_dim;
+  a->r = h->r;
+  a->bk = c.block_size;
+  a->top_k = c.top_k;
+  a->max_blocks = c.max_blocks_per_seq;
+  a->num_pages = c.num_pages;
+  a->n_tiles = h->n_tiles;
+  a->inv_sqrt_d = (float)(1.0 / sqrt((double)c.head_dim));
+  int max_tiles = 0;
+  for (int b = 0; b < c.batch; ++b) {
+    a->lens[b] = h->lens[b];
+    const int nb = (h->lens[b] + c.block_size - 1) / c.block_size;
+    if (nb > c.top_k) {
+      const int tiles = (nb - 2) / kTile + 1;  // tiles holding candidates 1..nb-2
+      if (tiles > max_tiles) max_tiles = tiles;
+    }
+  }
+  a->score_tiles = max_tiles;
+  return SPLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spla_status_str(spla_status st) {
+  switch (st) {
+    case SPLA_OK: return "ok";
+    case SPLA_ERR_INVALID_ARG: return "invalid argument";
+    case SPLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SPLA_ERR_CAPACITY: return "capacity exceeded";
+    case SPLA_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+    case SPLA_ERR_HIP: return "HIP launch failed";
+    case SPLA_ERR_STATE: return "handle not bound";
+  }
+  return "unknown status";
+}
+
+int32_t spla_abi_version(void) { return SPLA_ABI_VERSION; }
+
+spla_status spla_create(const spla_config* cfg, spla_handle** out) {
+  if (!cfg || !out) return SPLA_ERR_INVALID_ARG;
+  *out = nullptr;
+  const spla_config& c = *cfg;
+  if (c.batch < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 || c.head_dim < 1 || c.block_size < 1 ||
+      c.top_k < 1 || c.max_blocks_per_seq < 1 || c.num_pages < 1)
+    return SPLA_ERR_INVALID_ARG;
+  if (c.batch > kMaxBatch) return SPLA_ERR_UNSUPPORTED;
+  if (c.head_dim != 64 && c.head_dim != 128) return SPLA_ERR_UNSUPPORTED;
+  if (c.block_size != 64 && c.block_size != 128) return SPLA_ERR_UNSUPPORTED;
+  if (c.n_q_heads % c.n_kv_heads) return SPLA_ERR_UNSUPPORTED;
+  const int r = c.n_q_heads / c.n_kv_heads;
+  if (r != 1 && r != 2 && r != 4 && r != 8) return SPLA_ERR_UNSUPPORTED;
+  if (c.top_k < 2 || c.top_k > 256) return SPLA_ERR_UNSUPPORTED;
+  if (c.max_blocks_per_seq > 131072) return SPLA_ERR_UNSUPPORTED;
+  if (c.kv_dtype != SPLA_F32 && c.kv_dtype != SPLA_BF16) return SPLA_ERR_UNSUPPORTED;
+  spla_handle* h = new (std::nothrow) spla_handle();
+  if (!h) return SPLA_ERR_INVALID_ARG;
+  h->cfg = c;
+  h->r = r;
+  h->n_tiles = (c.max_blocks_per_seq + kTile - 1) / kTile;
+  h->lens.assign(c.batch, 0);
+  layout(h);
+  *out = h;
+  return SPLA_OK;
+}
+
+void spla_destroy(spla_handle* h) { delete h; }
+
+size_t spla_workspace_bytes(const spla_handle* h) { return h ? h->ws_bytes : 0; }
+
+size_t spla_stats_floats(const spla_handle* h) {
+  if (!h) return 0;
+  const spla_config& c = h->cfg;
+  return (size_t)c.batch * c.n_kv_heads * h->n_tiles * kTile * c.head_dim;
+}
+
+spla_status spla_bind(spla_handle* h, const spla_buffers* b, const int32_t* lens_host) {
+  if (!h || !b) return SPLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {b->k_pages, b->v_pages, b->block_table, b->blk_mean, b->blk_var,
+                        b->s_all, b->z_all, b->workspace};
+  for (const void* p : ptrs)
+    if (!p) return SPLA_ERR_INVALID_ARG;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPLA_ERR_ALIGNMENT;
+  if (b->workspace_bytes < h->ws_bytes) return SPLA_ERR_INVALID_ARG;
+  const spla_config& c = h->cfg;
+  const int64_t cap = (int64_t)c.max_blocks_per_seq * c.block_size;
+  if (lens_host) {
+    for (int i = 0; i < c.batch; ++i)
+      if (lens_host[i] < 0 || lens_host[i] > cap) return SPLA_ERR_INVALID_ARG;
+  }
+  h->buf = *b;
+  for (int i = 0; i < c.batch; ++i) h->lens[i] = lens_host ? lens_host[i] : 0;
+  h->bound = true;
+  return SPLA_OK;
+}
+
+spla_status spla_get_lens(const spla_handle* h, int32_t* lens_host) {
+  if (!h || !lens_host) return SPLA_ERR_INVALID_ARG;
+  for (int i = 0; i < h->cfg.batch; ++i) lens_host[i] = h->lens[i];
+  return SPLA_OK;
+}
+
+spla_status spla_append_kv(spla_handle* h, int32_t n_seqs, const int32_t* seq_ids_host,
+                           const int32_t* n_new_host, const void* k_new, const void* v_new,
+                           void* stream) {
+  if (!h) return SPLA_ERR_INVALID_ARG;
+  if (!h->bound) return SPLA_ERR_STATE;
+  const spla_config& c = h->cfg;
+  if (n_seqs < 0 || n_seqs > c.batch) return SPLA_ERR_INVALID_ARG;
+  if (n_seqs == 0) return SPLA_OK;
+  if (!seq_ids_host || !n_new_host) return SPLA_ERR_INVALID_ARG;
+  const int64_t cap = (int64_t)c.max_blocks_per_seq * c.block_size;
+  std::vector<char> seen(c.batch, 0);
+  int64_t total = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int s = seq_ids_host[i];
+    if (s < 0 || s >= c.batch || seen[s]) return SPLA_ERR_INVALID_ARG;
+    seen[s] = 1;
+    if (n_new_host[i] < 0) return SPLA_ERR_INVALID_ARG;
+    total += n_new_host[i];
+  }
+  for (int i = 0; i < n_seqs; ++i)
+    if ((int64_t)h->lens[seq_ids_host[i]] + n_new_host[i] > cap) return SPLA_ERR_CAPACITY;
+  if (total == 0) return SPLA_OK;
+  if (total > (int64_t)INT32_MAX / (c.n_kv_heads * c.head_dim)) return SPLA_ERR_INVALID_ARG;
+  if (!k_new || !v_new) return SPLA_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return SPLA_ERR_ALIGNMENT;
+
+  const bool bf16 = c.kv_dtype == SPLA_BF16;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int chunks = c.head_dim / (1024 / c.head_dim);
+  AppendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k_pages = h->buf.k_pages;
+  a.v_pages = h->buf.v_pages;
+  a.block_table = h->buf.block_table;
+  a.blk_mean = h->buf.blk_mean;
+  a.blk_var = h->buf.blk_var;
+  a.s_all = h->buf.s_all;
+  a.z_all = h->buf.z_all;
+  a.err = ws_ptr<uint32_t>(h, 0);
+  a.G = c.n_kv_heads;
+  a.d = c.head_dim;
+  a.bk = c.block_size;
+  a.max_blocks = c.max_blocks_per_seq;
+  a.num_pages = c.num_pages;
+  a.n_tiles = h->n_tiles;
+  const size_t es = bf16 ? 2 : 4;
+  const size_t row_bytes = (size_t)c.n_kv_heads * c.head_dim * es;
+  int64_t row = 0;
+  // launches of at most kMaxAppendEntries entries; the rows of one launch
+  // start at its first entry's row
+  for (int i0 = 0; i0 < n_seqs; i0 += kMaxAppendEntries) {
+    const int ne = n_seqs - i0 < kMaxAppendEntries ? n_seqs - i0 : kMaxAppendEntries;
+    a.k_new = static_cast<const char*>(k_new) + row * row_bytes;
+    a.v_new = static_cast<const char*>(v_new) + row * row_bytes;
+    a.n_entries = ne;
+    int lrow = 0, pp = 0, sp = 0;
+    for (int e = 0; e < ne; ++e) {
+      const int s = seq_ids_host[i0 + e];
+      const int n = n_new_host[i0 + e];
+      const int t0 = h->lens[s];
+      a.e[e].seq = s;
+      a.e[e].n = n;
+      a.e[e].t0 = t0;
+      a.e[e].row = lrow;
+      a.page_prefix[e] = pp;
+      a.stat_prefix[e] = sp;
+      pp += (n + 63) / 64;
+      sp += ((t0 + n) / c.block_size - t0 / c.block_size) * c.n_kv_heads;
+      lrow += n;
+    }
+    a.page_prefix[ne] = pp;
+    a.stat_prefix[ne] = sp;
+    a.s_items = ne * c.n_kv_heads * chunks;
+    a.page_items = pp;
+    a.stat_items = sp;
+    if (launch_append(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
+    row += lrow;
+  }
+  for (int i = 0; i < n_seqs; ++i) h->lens[seq_ids_host[i]] += n_new_host[i];
+  return SPLA_OK;
+}
+
+spla_status spla_decode(spla_handle* h, const void* q, const float* gate, float* out,
+                        const spla_decode_aux* aux, void* stream) {
+  if (!h) return SPLA_ERR_INVALID_ARG;
+  if (!h->bound) return SPLA_ERR_STATE;
+  if (!q || !gate || !out) return SPLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(gate) || !aligned16(out)) return SPLA_ERR_ALIGNMENT;
+  if (aux) {
+    const void* ap[] = {aux->sel_idx, aux->lg, aux->o_sparse, aux->o_rla, aux->d_rla, aux->sel_in};
+    for (const void* p : ap)
+      if (p && !aligned16(p)) return SPLA_ERR_ALIGNMENT;
+  }
+  const spla_config& c = h->cfg;
+  for (int b = 0; b < c.batch; ++b)
+    if (h->lens[b] <= 0) return SPLA_ERR_INVALID_ARG;
+  DecodeArgs a;
+  fill_decode_args(h, q, gate, out, aux, &a);
+  const bool bf16 = c.kv_dtype == SPLA_BF16;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  void* const* ev = aux ? aux->kernel_events : nullptr;
+  const int nev = (aux && ev) ? aux->n_kernel_events : 0;
+  int kidx = 0;
+  auto mark = [&](int which) {
+    if (kidx < nev && ev[2 * kidx + which]) hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * kidx + which]), st);
+    if (which == 1) ++kidx;
+  };
+  if (!a.sel_in) {
+    mark(0);
+    if (launch_score(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
+    mark(1);
+    mark(0);
+    if (launch_select(a, st) != hipSuccess) return SPLA_ERR_HIP;
+    mark(1);
+  }
+  mark(0);
+  if (launch_attend(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
+  mark(1);
+  mark(0);
+  if (launch_combine(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
+  mark(1);
+  return SPLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+/*
+ * spla.h -- C ABI of the SPLA (Block Sparse Plus Linear Attention) decode
+ * step on one AMD Instinct MI355X (gfx950).
+ *
+ * Method (arXiv 2601.22379, "SPLA: Block Sparse Plus Linear Attention for
+ * Long Context Modeling"; gist.science Technical Summary):
+ *   - every KV block keeps first/second order key statistics (mean and the
+ *     diagonal of the covariance), Technical Summary section 2.1;
+ *   - a decode query scores each block with the second-order Taylor
+ *     estimate exp(q_hat.mean) (1 + 1/2 q_hat^T diag(var) q_hat) of the
+ *     block's attention mass, q_hat = q / sqrt(d) (section 2.1, score);
+ *   - the top_k blocks (sink block 0 and the current block always among
+ *     them) get exact softmax attention (sections 1 and 2);
+ *   - the rest ("long tail") enters through Residual Linear Attention in its
+ *     subtraction form o_rla = o_bar - o_tilde: o_bar = phi(q)^T S_all from a
+ *     running state over all tokens, o_tilde = phi(q)^T sum_sel phi(k) v^T
+ *     from the K/V tiles already loaded for exact attention, so unselected
+ *     blocks are never read (section 2.2, IO-efficient formulation);
+ *   - o = o_sparse + g_h * o_rla with a per-query-head gate g_h; phi(x) =
+ *     elu(x) + 1 (section 2.3 leaves both open; they are fixed parameters of
+ *     this library).
+ *
+ * Two calls do the work: spla_append_kv (update K/V pages, block statistics
+ * and S_all / z_all) and spla_decode (score -> top-k -> attend + correct ->
+ * combine).  A decode step is spla_append_kv of the step's token for every
+ * sequence followed by spla_decode (the token attends to itself).
+ *
+ * Conventions
+ *   - Every device buffer is allocated and owned by the caller.  The library
+ *     owns only the host handle (a copy of the configuration, the buffer
+ *     pointers and a host mirror of the sequence lengths).  It never
+ *     allocates or frees device memory and never synchronises a stream.
+ *   - Work is enqueued on the caller's stream (a hipStream_t passed as
+ *     void*; NULL = the null stream).  Outputs are valid when the stream
+ *     reaches that point.  Kernel launch parameters (grid sizes, lengths)
+ *     come from the host mirror, so a captured HIP graph replays exactly the
+ *     step it recorded.
+ *   - Validation happens on the host before anything is enqueued.  On any
+ *     error status nothing is enqueued and nothing (the mirror included)
+ *     changes, except SPLA_ERR_HIP, which reports a failed launch.
+ *   - Device pointers must be 16-byte aligned.
+ *   - One handle must not be used from two host threads at once; distinct
+ *     handles are independent.  Calls on one handle are ordered by the
+ *     caller's stream(s): use one stream per handle or order them yourself.
+ *   - Layouts are row-major, index order as written.
+ *
+ * Buffer layouts (B = batch, H = n_q_heads, G = n_kv_heads, d = head_dim,
+ * Bk = block_size, MB = max_blocks_per_seq, NT = ceil(MB / 64)):
+ *   k_pages, v_pages  [num_pages][G][Bk][d] kv_dtype.  One page holds one
+ *                     block (Bk consecutive tokens) of one sequence, all KV
+ *                     heads.
+ *   block_table       [B][MB] int32: page id of block j of sequence b.
+ *                     Filled by the caller for every block a sequence will
+ *                     reach; an id outside [0, num_pages) is never
+ *                     dereferenced: the access is skipped and bit 0 of the
+ *                     workspace error word is set.
+ *   blk_mean, blk_var [B][G][NT][d/4][64][4] float32: statistics of block j,
+ *                     channel c of (b, g) live at
+ *                     ((((b*G + g)*NT + j/64)*(d/4) + c/4)*64 + j%64)*4 + c%4.
+ *                     (64 blocks side by side per channel quartet, so the
+ *                     scorer reads them with whole-wavefront vector loads.)
+ *                     Only blocks completed by an append are written.
+ *   s_all             [B][G][d][d] float32: S[b][g][x][y] = sum_t phi(k_t[x]) v_t[y].
+ *   z_all             [B][G][d] float32:    z[b][g][x]    = sum_t phi(k_t[x]).
+ *   workspace         spla_workspace_bytes() bytes, zero-filled by the
+ *                     caller once before the first call.  Bytes [0, 4) hold
+ *                     a sticky uint32 error word (bit 0: out-of-range page
+ *                     id, bit 1: a selected block id outside the sequence);
+ *                     the rest is scratch that the library clears itself.
+ *                     A fresh state needs s_all, z_all zero-filled.
+ */
+#ifndef SPLA_H
+#define SPLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPLA_ABI_VERSION 1
+
+typedef enum {
+    SPLA_OK = 0,
+    SPLA_ERR_INVALID_ARG = 1,  /* null/out-of-range argument, empty sequence at decode */
+    SPLA_ERR_UNSUPPORTED = 2,  /* configuration outside the supported set */
+    SPLA_ERR_CAPACITY = 3,     /* append would exceed max_blocks_per_seq * block_size */
+    SPLA_ERR_ALIGNMENT = 4,    /* a device pointer is not 16-byte aligned */
+    SPLA_ERR_HIP = 5,          /* a kernel launch failed (hipGetLastError) */
+    SPLA_ERR_STATE = 6         /* call before spla_bind */
+} spla_status;
+
+typedef enum { SPLA_F32 = 0, SPLA_BF16 = 1 } spla_dtype;
+
+/* Supported: 1 <= batch <= 256; head_dim in {64, 128}; block_size in {64,
+ * 128}; n_q_heads = r * n_kv_heads with r in {1, 2, 4, 8}; 2 <= top_k <= 256;
+ * 1 <= max_blocks_per_seq <= 131072; num_pages >= 1; kv_dtype F32 or BF16
+ * (K, V and q share it).  Anything else returns SPLA_ERR_UNSUPPORTED. */
+typedef struct {
+    int32_t batch;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t top_k;              /* blocks kept per (sequence, KV head), sink and current included */
+    int32_t max_blocks_per_seq;
+    int32_t num_pages;
+    int32_t kv_dtype;           /* spla_dtype */
+} spla_config;
+
+typedef struct {               /* device pointers, all caller-owned */
+    void *k_pages;
+    void *v_pages;
+    const int32_t *block_table;
+    float *blk_mean;
+    float *blk_var;
+    float *s_all;
+    float *z_all;
+    void *workspace;
+    size_t workspace_bytes;
+} spla_buffers;
+
+typedef struct {               /* optional outputs / test hook of spla_decode; NULL = unused */
+    int32_t *sel_idx;          /* out [B][G][top_k] selected block ids, ascending, -1 padded */
+    float *lg;                 /* out [B][G][MB] group log score LG(j) of candidate blocks
+                                  1..nb-2 (other entries untouched); written only when
+                                  nb > top_k, the case where a choice is made */
+    float *o_sparse;           /* out [B][H][d] exact attention over the selected blocks */
+    float *o_rla;              /* out [B][H][d] o_bar - o_tilde (0 when every block is selected) */
+    float *d_rla;              /* out [B][H] phi(q).(z_all - z_sel) (0 when every block is selected) */
+    const int32_t *sel_in;     /* in  [B][G][top_k]: use these block ids (ascending, -1 padded,
+                                  each < nb) instead of scoring + top-k */
+    void *const *kernel_events;  /* in: hipEvent_t[2 * n]; when set, kernel_events[2i] is recorded on
+                                  the stream right before the i-th kernel this call launches and
+                                  kernel_events[2i+1] right after it (NULL entries skipped), for
+                                  per-kernel timing.  Launch order: score, select, attend, combine
+                                  (score and select are skipped when sel_in is set). */
+    int32_t n_kernel_events;   /* n: entries of kernel_events / 2 */
+} spla_decode_aux;
+
+typedef struct spla_handle spla_handle;
+
+/* Validate cfg and create a handle (host only, no HIP call). */
+spla_status spla_create(const spla_config *cfg, spla_handle **out);
+void spla_destroy(spla_handle *h);
+
+/* Sizes the caller allocates: workspace bytes; floats of blk_mean (= of
+ * blk_var). */
+size_t spla_workspace_bytes(const spla_handle *h);
+size_t spla_stats_floats(const spla_handle *h);
+
+/* Attach the caller's buffers and the current sequence lengths (host array
+ * of batch entries; NULL = all zero).  The buffers must already hold the
+ * state of those lengths (all zero for an empty state).  Host only. */
+spla_status spla_bind(spla_handle *h, const spla_buffers *b, const int32_t *lens_host);
+
+/* Append n_new_host[i] tokens to sequence seq_ids_host[i] for i < n_seqs
+ * (distinct ids).  k_new, v_new: device [sum n_new][G][d] kv_dtype, the
+ * rows of entry i following those of entry i-1.  Writes the rows into the
+ * pages (via block_table), adds phi(k) v^T and phi(k) to s_all and z_all,
+ * and writes blk_mean / blk_var of every block the append completes
+ * (population variance, two passes).  Technical Summary 2.1 (statistics)
+ * and 2.2 (global linear-attention state). */
+spla_status spla_append_kv(spla_handle *h, int32_t n_seqs, const int32_t *seq_ids_host,
+                           const int32_t *n_new_host, const void *k_new, const void *v_new,
+                           void *stream);
+
+/* Decode one query token per sequence.  q: device [B][H][d] kv_dtype;
+ * gate: device [H] float32; out: device [B][H][d] float32 receives
+ * o = o_sparse + gate[h] * o_rla.  Query head h uses KV head h / (H/G).
+ * Every sequence must be non-empty (SPLA_ERR_INVALID_ARG otherwise).
+ * Selection per (b, g): nb = ceil(T/Bk); if nb <= top_k every block;
+ * otherwise blocks 0 and nb-1 plus the top_k-2 candidates 1..nb-2 with the
+ * largest LG(j) = log sum_h exp(q_hat_h.mean_j + log1p(1/2 sum_c
+ * q_hat_hc^2 var_jc)), ties to the smaller id.  aux may be NULL. */
+spla_status spla_decode(spla_handle *h, const void *q, const float *gate, float *out,
+                        const spla_decode_aux *aux, void *stream);
+
+/* Copy the host mirror of the sequence lengths (batch entries). */
+spla_status spla_get_lens(const spla_handle *h, int32_t *lens_host);
+
+const char *spla_status_str(spla_status st);
+int32_t spla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLA_H */

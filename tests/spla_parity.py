@@ -1,0 +1,228 @@
+"""Parity machinery shared by the GPU tests, smoke() and bench.py: drive the
+HIP library (through its C ABI binding) and the fp64 oracle with the same
+seeded inputs and compare them with the acceptance rules of the decode
+specification:
+
+  sets     every (b, g) selection holds the sink, the current block and
+           |P| = top_k - 2 scored candidates (or every block when nb <= top_k),
+           and no excluded candidate beats an included one by more than 1e-5
+           relative in the oracle's fp64 score: min_in LG >= max_out LG +
+           log(1 - 1e-5).  Outputs are then compared with the oracle re-run on
+           the GPU's selection, because a legal near-tie swap moves o_sparse
+           far more than the output tolerance.
+  outputs  o, o_sparse and o_rla each: max|gpu - ref| <= 2e-3 * max|ref|
+           (o_rla ~ 1e5 dwarfs o_sparse ~ 1 at long context, so each is
+           checked on its own); D: <= 1e-4 relative.
+  state    S_all, z_all per (b, g): max|gpu - ref| <= 1e-4 * max|ref|;
+           block mean / variance: <= 1e-5 relative (+1e-6 absolute).
+"""
+from __future__ import annotations
+
+import math
+import time
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+
+from oracle import SplaOracle
+from workloads import Workload
+
+OUT_REL = 2e-3
+D_REL = 1e-4
+S_REL = 1e-4
+STAT_REL = 1e-5
+TIE_REL = 1e-5
+
+
+def check_selection(sel_row, lg: Dict[int, float], nb: int, top_k: int) -> Optional[str]:
+    """None if the GPU selection of one (b, g) is acceptable, else a message."""
+    sel = [int(x) for x in sel_row]
+    valid = [x for x in sel if x >= 0]
+    if valid != sorted(valid) or len(set(valid)) != len(valid):
+        return f"not ascending/distinct: {sel}"
+    if sel[:len(valid)] != valid or any(x != -1 for x in sel[len(valid):]):
+        return f"-1 padding not at the end: {sel}"
+    if nb <= top_k:
+        return None if valid == list(range(nb)) else f"expected all {nb} blocks, got {valid}"
+    if 0 not in valid or (nb - 1) not in valid:
+        return f"sink/current missing: {valid}"
+    if len(valid) != top_k:
+        return f"expected {top_k} blocks, got {len(valid)}"
+    P = [j for j in valid if 0 < j < nb - 1]
+    out = [j for j in range(1, nb - 1) if j not in set(P)]
+    if not out:
+        return None
+    lo = min(lg[j] for j in P)
+    hi = max(lg[j] for j in out)
+    if lo < hi + math.log1p(-TIE_REL):
+        return f"selection beaten beyond the tie tolerance: min in {lo}, max out {hi}"
+    return None
+
+
+def rel_err(x, ref) -> float:
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = np.abs(ref).max()
+    diff = np.abs(x - ref).max() if x.size else 0.0
+    if scale == 0:
+        return float(diff)
+    return float(diff / scale)
+
+
+@dataclass
+class StepReport:
+    step: int
+    errors: Dict[str, float] = field(default_factory=dict)
+    sel_equal: bool = True
+    near_ties: int = 0
+    failures: List[str] = field(default_factory=list)
+
+
+class ParityRun:
+    """A SplaLayer and a SplaOracle fed from one Workload."""
+
+    def __init__(self, w: Workload, page_order: str = "identity", steps: Optional[int] = None,
+                 device: str = "cuda", prefill_chunk: int = 4096):
+        import torch
+        from block_sparse_linear_amd import SplaLayer
+
+        self.torch = torch
+        self.w = w
+        self.steps = w.steps if steps is None else steps
+        self.device = device
+        self.prefill_chunk = prefill_chunk
+        mb = w.max_blocks_per_seq(self.steps)
+        self.layer = SplaLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k, mb,
+                               kv_dtype=w.kv_dtype, device=device, page_order=page_order, seed=w.seed)
+        self.oracle = SplaOracle(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k,
+                                 w.max_tokens(self.steps))
+        self.gate_np = w.gate()
+        self.gate = torch.from_numpy(self.gate_np).to(device)
+        self.mix = w.mixture_state()
+
+    def dev(self, x: np.ndarray):
+        return self.torch.from_numpy(np.ascontiguousarray(x)).to(self.device).to(self.layer.dtype)
+
+    def prefill(self) -> None:
+        for b in range(self.w.batch):
+            for _, k, v in self.w.prefill_chunks(b, self.prefill_chunk):
+                self.layer.append([b], [k.shape[0]], self.dev(k), self.dev(v))
+                self.oracle.append([b], [k.shape[0]], k, v)
+
+    def append_step(self, s: int) -> Dict[str, np.ndarray]:
+        st = self.w.step(s, self.mix)
+        cs = [int(x) for x in st["chunk_seqs"]]
+        if cs:
+            n = [self.w.chunk_len] * len(cs)
+            self.layer.append(cs, n, self.dev(st["chunk_k"]), self.dev(st["chunk_v"]))
+            self.oracle.append(cs, n, st["chunk_k"], st["chunk_v"])
+        allb = list(range(self.w.batch))
+        self.layer.append(allb, [1] * self.w.batch, self.dev(st["k"]), self.dev(st["v"]))
+        self.oracle.append(allb, [1] * self.w.batch, st["k"], st["v"])
+        return st
+
+    def gpu_decode(self, q_np: np.ndarray, sel_in=None):
+        t = self.torch
+        w = self.w
+        B, H, G, d = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
+        aux = {
+            "sel_idx": t.empty((B, G, w.top_k), dtype=t.int32, device=self.device),
+            "lg": t.zeros((B, G, self.layer.mb), dtype=t.float32, device=self.device),
+            "o_sparse": t.empty((B, H, d), dtype=t.float32, device=self.device),
+            "o_rla": t.empty((B, H, d), dtype=t.float32, device=self.device),
+            "d_rla": t.empty((B, H), dtype=t.float32, device=self.device),
+        }
+        if sel_in is not None:
+            aux["sel_in"] = t.from_numpy(np.ascontiguousarray(sel_in, np.int32)).to(self.device)
+        out = self.layer.decode(self.dev(q_np), self.gate, aux=aux)
+        t.cuda.synchronize()
+        res = {k: v.cpu().numpy() for k, v in aux.items() if k != "sel_in"}
+        res["o"] = out.cpu().numpy()
+        return res
+
+    def check_decode(self, s: int, q_np: np.ndarray, sel_in=None) -> StepReport:
+        w = self.w
+        rep = StepReport(step=s)
+        g = self.gpu_decode(q_np, sel_in)
+        ref = self.oracle.decode(q_np, self.gate_np, sel_override=sel_in)
+        sel_gpu = g["sel_idx"]
+        if sel_in is None:
+            for b in range(w.batch):
+                nb = -(-int(self.oracle.lens[b]) // w.block_size)
+                for gg in range(w.n_kv_heads):
+                    msg = check_selection(sel_gpu[b, gg], ref["lg"][b][gg], nb, w.top_k)
+                    if msg:
+                        rep.failures.append(f"step {s} b {b} g {gg}: {msg}")
+                    if not np.array_equal(sel_gpu[b, gg], ref["sel"][b, gg]):
+                        rep.sel_equal = False
+                        rep.near_ties += 1
+                    # group log scores (diagnostic, absolute in the log domain)
+                    if nb > w.top_k:
+                        js = np.arange(1, nb - 1)
+                        lg_ref = np.array([ref["lg"][b][gg][int(j)] for j in js])
+                        rep.errors["lg_abs"] = max(rep.errors.get("lg_abs", 0.0),
+                                                   float(np.abs(g["lg"][b, gg, js] - lg_ref).max()))
+            if not rep.sel_equal:
+                ref = self.oracle.decode(q_np, self.gate_np, sel_override=sel_gpu)
+        else:
+            if not np.array_equal(sel_gpu, np.asarray(sel_in)):
+                rep.failures.append("sel_idx output != sel_in")
+        for k, tol in (("o", OUT_REL), ("o_sparse", OUT_REL), ("o_rla", OUT_REL), ("d_rla", D_REL)):
+            e = rel_err(g[k], ref[k])
+            rep.errors[k] = e
+            if e > tol:
+                rep.failures.append(f"step {s}: {k} rel err {e:.3g} > {tol}")
+        return rep
+
+    def check_state(self) -> Dict[str, float]:
+        w = self.w
+        S = self.layer.s_all.cpu().numpy()
+        z = self.layer.z_all.cpu().numpy()
+        mean, var = (x.cpu().numpy() for x in self.layer.stats())
+        errs = {"S": 0.0, "z": 0.0, "mean": 0.0, "var": 0.0}
+        for b in range(w.batch):
+            nfull = int(self.oracle.lens[b]) // w.block_size
+            for g in range(w.n_kv_heads):
+                errs["S"] = max(errs["S"], rel_err(S[b, g], self.oracle.S[b, g]))
+                errs["z"] = max(errs["z"], rel_err(z[b, g], self.oracle.z[b, g]))
+                if nfull:
+                    for name, gv, ov in (("mean", mean, self.oracle.mean), ("var", var, self.oracle.var)):
+                        d = np.abs(gv[b, g, :nfull].astype(np.float64) - ov[b, g, :nfull])
+                        scale = np.abs(ov[b, g, :nfull])
+                        errs[name] = max(errs[name], float((d / (scale + 1e-6 / STAT_REL)).max()))
+        return errs
+
+    def state_failures(self, errs: Dict[str, float]) -> List[str]:
+        f = []
+        if errs["S"] > S_REL:
+            f.append(f"S_all rel err {errs['S']:.3g}")
+        if errs["z"] > S_REL:
+            f.append(f"z_all rel err {errs['z']:.3g}")
+        if errs["mean"] > STAT_REL:
+            f.append(f"block mean rel err {errs['mean']:.3g}")
+        if errs["var"] > STAT_REL:
+            f.append(f"block var rel err {errs['var']:.3g}")
+        return f
+
+    def run(self, steps: Optional[int] = None, verbose: bool = False) -> List[str]:
+        steps = self.steps if steps is None else steps
+        t0 = time.time()
+        self.prefill()
+        failures = self.state_failures(self.check_state())
+        worst: Dict[str, float] = {}
+        ties = 0
+        for s in range(steps):
+            st = self.append_step(s)
+            rep = self.check_decode(s, st["q"])
+            failures += rep.failures
+            ties += rep.near_ties
+            for k, v in rep.errors.items():
+                worst[k] = max(worst.get(k, 0.0), v)
+        errs = self.check_state()
+        failures += self.state_failures(errs)
+        failures += ([f"error word {self.layer.error_word():#x}"] if self.layer.error_word() else [])
+        if verbose:
+            print(f"[parity] {self.w.name} steps={steps} worst={worst} state={errs} near_tie_sets={ties} "
+                  f"({time.time() - t0:.1f}s)", flush=True)
+        return failures

@@ -1,0 +1,94 @@
+"""GPU parity of the HIP decode path against the fp64 oracle (through the C ABI).
+
+Small shapes that still span several score tiles, a ragged tail, both block
+sizes, both head dims, every GQA ratio, shuffled pages, chunked appends that
+are not block aligned, a ragged batch, the degenerate lengths (one partial
+block, exactly one block, every block selected) and the selection hook.
+"""
+import numpy as np
+import pytest
+
+from workloads import Workload, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _needs_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(w, steps=None, page_order="identity", verbose=True):
+    _needs_gpu()
+    from tests.spla_parity import ParityRun
+    print(f"[case] {w.name} B={w.batch} H={w.n_q_heads} G={w.n_kv_heads} d={w.head_dim} "
+          f"Bk={w.block_size} k={w.top_k} t0={w.t0[:4]} pages={page_order}", flush=True)
+    run = ParityRun(w, page_order=page_order, steps=steps, prefill_chunk=1000)
+    failures = run.run(verbose=verbose)
+    assert not failures, "\n".join(failures[:20])
+
+
+def small(name="small", **kw):
+    base = dict(name=name, batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=64, top_k=8,
+                kv_dtype="bf16", t0=(64 * 150 + 37,), steps=4, kind="normal", seed=77)
+    base.update(kw)
+    return Workload(**base)
+
+
+def test_tiny_fp32_config():
+    _run(make_workload("tiny_fp32"))
+
+
+def test_small_gqa4_bf16_ragged_tail():
+    _run(small(steps=6), page_order="shuffled")
+
+
+@pytest.mark.parametrize("r", [1, 2, 8])
+def test_group_ratios(r):
+    _run(small(name=f"r{r}", n_q_heads=2 * r, t0=(64 * 70 + 5,), steps=3))
+
+
+def test_block128_d64():
+    _run(small(name="bk128_d64", head_dim=64, block_size=128, t0=(128 * 90 + 100,), top_k=12, steps=3))
+
+
+def test_fp32_d128_outliers():
+    _run(small(name="f32_outlier", kv_dtype="f32", kind="outlier", n_outlier=8, t0=(64 * 80,), steps=3))
+
+
+@pytest.mark.parametrize("t0", [1, 30, 63, 64, 65, 64 * 7, 64 * 7 + 1])
+def test_short_sequences_all_selected(t0):
+    # nb <= top_k: every block selected, o_rla == 0, output = dense attention
+    _run(small(name=f"short{t0}", t0=(t0,), steps=2))
+
+
+def test_ragged_batch_with_chunks():
+    w = small(name="ragged", batch=5, t0=(1, 700, 64 * 40 + 13, 64 * 9, 3000), steps=3, chunk_seqs=2,
+              chunk_len=100, top_k=6)
+    _run(w, page_order="shuffled")
+
+
+def test_planted_batched_small():
+    _run(make_workload("batched_32k", batch=3, t0=(4096,) * 3, steps=3))
+
+
+def test_mixture_block128_small():
+    _run(make_workload("million_1m", t0=(128 * 200 + 77,), steps=3))
+
+
+def test_selection_hook():
+    _needs_gpu()
+    from tests.spla_parity import ParityRun
+    w = small(name="hook", t0=(64 * 40 + 9,), steps=1)
+    run = ParityRun(w, steps=1, prefill_chunk=512)
+    run.prefill()
+    st = run.append_step(0)
+    nb = -(-int(run.oracle.lens[0]) // 64)
+    rng = np.random.default_rng(3)
+    sel = np.full((1, 2, w.top_k), -1, np.int32)
+    for g in range(2):
+        ids = sorted(set([0, nb - 1]) | set(rng.choice(np.arange(1, nb - 1), 4, replace=False).tolist()))
+        sel[0, g, :len(ids)] = ids
+    rep = run.check_decode(0, st["q"], sel_in=sel)
+    assert not rep.failures, rep.failures
