@@ -204,13 +204,21 @@ def main() -> int:
     lens_t = [t + 1 for t in layers[0].lens]
     bytes_first = step_bytes(w, lens_t, s_kv)["total"]
 
+    # one HIP graph per timed step holding every instance's append + decode
+    # (captured ahead of the timed region; replay order = step order)
+    graphs = []
+    for s in range(W, W + K):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for layer, out in zip(layers, outs):
+                run_step(s, layer, out)
+        graphs.append(gr)
+    torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
-    for s in range(W, W + K):
-        for layer, out in zip(layers, outs):
-            run_step(s, layer, out)
+    for gr in graphs:
+        gr.replay()
     end.record()
     torch.cuda.synchronize()
     elapsed_ms = start.elapsed_time(end)
@@ -222,30 +230,47 @@ def main() -> int:
         if not torch.equal(o, outs[0]):
             log("WARNING: layer instances disagree bitwise")
     log(f"timed {K} steps x {L} instances: {elapsed_ms:.2f} ms, t_step {t_step * 1e6:.2f} us")
+    del graphs
 
-    # per-kernel durations: HIP events recorded on the launch stream around
-    # each kernel of spla_decode (order: score, select, attend, combine)
+    # per-kernel durations: HIP events recorded on the launch stream right
+    # before and after each kernel of spla_decode (order: score, select,
+    # attend, combine), captured into the same kind of per-step graph
     names = ["score", "select", "attend", "combine"]
-    durs = {n: [] for n in names}
     import ctypes
-    stream = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
-    for e in evs:
-        e.record(stream)  # materialise the event handles
-    torch.cuda.synchronize()
-    handles = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
-    score_launch_bytes = []
+    ev_sets = []
+    pgraphs = []
     for s in range(W + K, W + K + P):
-        for layer, out in zip(layers, outs):
-            run_step(s, layer, out, kernel_events=handles)
-            torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        sets = []
+        for _ in layers:
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
+            for e in evs:
+                e.record()  # materialise the handles
+            sets.append(evs)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr):
+            for layer, out, evs in zip(layers, outs, sets):
+                handles = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+                run_step(s, layer, out, kernel_events=handles)
+        pgraphs.append(gr)
+        ev_sets.append(sets)
+    torch.cuda.synchronize()
+    durs = {n: [] for n in names}
+    score_launch_bytes = []
+    for gr, sets in zip(pgraphs, ev_sets):
+        gr.replay()
+    torch.cuda.synchronize()
+    lens_p = list(lens_end)
+    for sets in ev_sets:
+        lens_p = [t + 1 for t in lens_p]
+        for evs in sets:
             for i, n in enumerate(names):
                 durs[n].append(evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e-3)
-        score_launch_bytes.append(score_bytes(w, layers[0].lens, s_kv))
+        score_launch_bytes.append(score_bytes(w, lens_p, s_kv))
     avg = {n: float(np.mean(v)) for n, v in durs.items()}
     sc_bytes = float(np.mean(score_launch_bytes))
     achieved = sc_bytes / avg["score"] / 1e9
-    log("kernel us: " + ", ".join(f"{n}={avg[n] * 1e6:.2f}" for n in names))
+    log("kernel us (graph, HIP events): " + ", ".join(f"{n}={avg[n] * 1e6:.2f}" for n in names))
 
     result = {
         "metric": "SPLA decode tokens/s at 128K ctx GQA 32/8x128; achieved HBM GB/s vs peak",

@@ -181,7 +181,10 @@ class SplaLayer:
         self.bk, self.top_k, self.mb = block_size, top_k, max_blocks_per_seq
         self.kv_dtype = kv_dtype
         self.dtype = torch.bfloat16 if kv_dtype == "bf16" else torch.float32
-        self.device = torch.device(device)
+        dv = torch.device(device)
+        if dv.type == "cuda" and dv.index is None:
+            dv = torch.device("cuda", torch.cuda.current_device())
+        self.device = dv
         npages = num_pages or batch * max_blocks_per_seq
         self.num_pages = npages
         self.handle = SplaHandle(batch, n_q_heads, n_kv_heads, head_dim, block_size, top_k,

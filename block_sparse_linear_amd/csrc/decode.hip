@@ -22,75 +22,92 @@ __device__ __forceinline__ int n_blocks(const DecodeArgs& a, int b) { return (a.
 
 // ============================================================== score
 // grid (score_tiles, G, B); lane = block within a 64-block tile, the four
-// wavefronts split the channels and meet in LDS.
+// wavefronts split the channels and meet in LDS.  Every wavefront issues its
+// query loads and then all of its statistics loads before the first wait.
 template <bool BF16, int R, int D>
 __global__ __launch_bounds__(kThreads) void k_score(const DecodeArgs a) {
-  __shared__ float qs[R][D];
-  __shared__ float q2s[R][D];
+  constexpr int NC4 = D / 16;  // channel quartets per wavefront
+  constexpr int CW = D / 4;    // channels per wavefront
+  constexpr int QPL = (R * CW + 63) / 64;  // query elements per lane
+  __shared__ float4 qs[4][R][CW / 4];
+  __shared__ float4 q2s[4][R][CW / 4];
   __shared__ float red[4][2 * R][kTile];
   const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int nb = n_blocks(a, b);
   if (nb <= a.top_k) return;  // every block is selected, nothing to rank
   const int j0 = t * kTile;
   if (j0 > nb - 2) return;
-  constexpr int d = D;
-  for (int i = threadIdx.x; i < R * d; i += kThreads) {
-    const int h = i / d, c = i - h * d;
-    const float v = load_elem<BF16>(a.q, ((size_t)b * a.H + g * R + h) * d + c);
-    qs[h][c] = v;
-    q2s[h][c] = v * v;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64;
+  // queries of this wavefront's channel quarter
+  float qv[QPL];
+#pragma unroll
+  for (int i = 0; i < QPL; ++i) {
+    const int e = lane + 64 * i;
+    qv[i] = 0.f;
+    if (e < R * CW) {
+      const int h = e / CW, c = e - h * CW;
+      qv[i] = load_elem<BF16>(a.q, ((size_t)b * a.H + g * R + h) * D + w * CW + c);
+    }
   }
-  __syncthreads();
-  const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
-  constexpr int nc4 = d / 16;  // channel quartets per wavefront
+  // statistics of the tile: 64 blocks x this wavefront's channels
   const float4* mean4 = reinterpret_cast<const float4*>(a.blk_mean);
   const float4* var4 = reinterpret_cast<const float4*>(a.blk_var);
-  const size_t base = (((size_t)b * a.G + g) * a.n_tiles + t) * (size_t)(d / 4) * kTile;
-  float dot[R], qv[R];
+  const size_t base = (((size_t)b * a.G + g) * a.n_tiles + t) * (size_t)(D / 4) * kTile + (size_t)(w * NC4) * kTile + lane;
+  float4 m[NC4], v[NC4];
 #pragma unroll
-  for (int h = 0; h < R; ++h) dot[h] = qv[h] = 0.f;
-  float4 m[nc4], v[nc4];
+  for (int i = 0; i < NC4; ++i) m[i] = mean4[base + (size_t)i * kTile];
 #pragma unroll
-  for (int i = 0; i < nc4; ++i) {
-    const size_t o = base + (size_t)(w * nc4 + i) * kTile + lane;
-    m[i] = mean4[o];
-    v[i] = var4[o];
+  for (int i = 0; i < NC4; ++i) v[i] = var4[base + (size_t)i * kTile];
+  // keep every load above this point: the whole tile is in flight before the
+  // first use
+  __builtin_amdgcn_sched_barrier(0);
+  // wavefront-private staging of q and q^2 (LDS operations of one wavefront
+  // complete in order, so no barrier is needed)
+  float* qf = reinterpret_cast<float*>(&qs[w][0][0]);
+  float* q2f = reinterpret_cast<float*>(&q2s[w][0][0]);
+#pragma unroll
+  for (int i = 0; i < QPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < R * CW) {
+      qf[e] = qv[i];
+      q2f[e] = qv[i] * qv[i];
+    }
   }
+  float dot[R], qq[R];
 #pragma unroll
-  for (int i = 0; i < nc4; ++i) {
-    {
-      const int c = (w * nc4 + i) * 4;
+  for (int h = 0; h < R; ++h) dot[h] = qq[h] = 0.f;
 #pragma unroll
-      for (int h = 0; h < R; ++h) {
-        const float4 q = *reinterpret_cast<const float4*>(&qs[h][c]);
-        const float4 q2 = *reinterpret_cast<const float4*>(&q2s[h][c]);
-        dot[h] = fmaf(q.x, m[i].x, dot[h]);
-        dot[h] = fmaf(q.y, m[i].y, dot[h]);
-        dot[h] = fmaf(q.z, m[i].z, dot[h]);
-        dot[h] = fmaf(q.w, m[i].w, dot[h]);
-        qv[h] = fmaf(q2.x, v[i].x, qv[h]);
-        qv[h] = fmaf(q2.y, v[i].y, qv[h]);
-        qv[h] = fmaf(q2.z, v[i].z, qv[h]);
-        qv[h] = fmaf(q2.w, v[i].w, qv[h]);
-      }
+  for (int i = 0; i < NC4; ++i) {
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      const float4 q = qs[w][h][i];
+      const float4 q2 = q2s[w][h][i];
+      dot[h] = fmaf(q.x, m[i].x, dot[h]);
+      dot[h] = fmaf(q.y, m[i].y, dot[h]);
+      dot[h] = fmaf(q.z, m[i].z, dot[h]);
+      dot[h] = fmaf(q.w, m[i].w, dot[h]);
+      qq[h] = fmaf(q2.x, v[i].x, qq[h]);
+      qq[h] = fmaf(q2.y, v[i].y, qq[h]);
+      qq[h] = fmaf(q2.z, v[i].z, qq[h]);
+      qq[h] = fmaf(q2.w, v[i].w, qq[h]);
     }
   }
 #pragma unroll
   for (int h = 0; h < R; ++h) {
     red[w][h][lane] = dot[h];
-    red[w][R + h][lane] = qv[h];
+    red[w][R + h][lane] = qq[h];
   }
   __syncthreads();
   if (w != 0) return;
   const int j = j0 + lane;
-  if (j < 1 || j > nb - 2) return;
-  const float half_inv_d = 0.5f / (float)d;
+  const float half_inv_d = 0.5f / (float)D;
   float ls[R];
   float mx = -INFINITY;
 #pragma unroll
   for (int h = 0; h < R; ++h) {
-    const float dd = red[0][h][lane] + red[1][h][lane] + red[2][h][lane] + red[3][h][lane];
-    const float vv = red[0][R + h][lane] + red[1][R + h][lane] + red[2][R + h][lane] + red[3][R + h][lane];
+    const float dd = (red[0][h][lane] + red[1][h][lane]) + (red[2][h][lane] + red[3][h][lane]);
+    const float vv = (red[0][R + h][lane] + red[1][R + h][lane]) + (red[2][R + h][lane] + red[3][R + h][lane]);
     ls[h] = dd * a.inv_sqrt_d + log1pf(fmaxf(vv, 0.f) * half_inv_d);
     mx = fmaxf(mx, ls[h]);
   }
@@ -101,130 +118,225 @@ __global__ __launch_bounds__(kThreads) void k_score(const DecodeArgs a) {
     for (int h = 0; h < R; ++h) s += expf(ls[h] - mx);
     lg = mx + logf(s);
   }
+  if (j < 1 || j > nb - 2) lg = -INFINITY;  // not a candidate
   a.lg[((size_t)b * a.G + g) * (size_t)(a.n_tiles * kTile) + j] = lg;
-  if (a.lg_out) a.lg_out[((size_t)b * a.G + g) * a.max_blocks + j] = lg;
+  if (a.lg_out && j >= 1 && j <= nb - 2) a.lg_out[((size_t)b * a.G + g) * a.max_blocks + j] = lg;
 }
 
 // ============================================================== select
-__device__ __forceinline__ int block_excl_scan(int v, int* tmp) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) tmp[w] = x;
-  __syncthreads();
-  int add = 0;
-  for (int i = 0; i < w; ++i) add += tmp[i];
-  __syncthreads();
-  return x - v + add;
+constexpr int kSelMax = kMaxBlocksPerSeq - 2;  // candidates per (b, g) the selector handles
+constexpr int kSelLevels = 12;   // bucket refinement levels
+constexpr int kSelRank = 256;    // threshold-bucket size ranked exactly
+
+// bucket of x at one refinement level: monotone non-decreasing in x
+__device__ __forceinline__ int sel_bucket(float x, float lo, float scale) {
+  const float f = (x - lo) * scale;
+  return f >= 255.f ? 255 : (f <= 0.f ? 0 : (int)f);
 }
 
-// grid (G, B).  Finds the exact key tau of the k'-th largest LG by four 8-bit
-// radix passes (LDS histograms), then keeps every candidate with key > tau and
-// the lowest-id candidates with key == tau.
+// append the flagged entries of a wavefront to an LDS list (one atomic per
+// wavefront); returns this lane's slot or -1
+__device__ __forceinline__ int wave_append(bool flag, int* counter) {
+  const uint64_t m = __ballot(flag);
+  if (m == 0) return -1;
+  const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+  int base = 0;
+  if ((threadIdx.x & 63) == 0) base = atomicAdd(counter, __popcll(m));
+  base = __builtin_amdgcn_readfirstlane(base);
+  return flag ? base + below : -1;
+}
+
+// grid (G, B).  Bucket select over the scores held in registers (KPT per
+// thread, candidate i = thread + 256 u): the scores are binned into 256
+// buckets spread over [min, max] of the remaining candidates; every
+// candidate in a bucket above the one holding the k'-th largest is taken, and
+// that bucket is refined the same way until it holds at most kSelRank
+// candidates (then ranked exactly by (score desc, id asc)) or only equal
+// scores (then taken by ascending id).  The bucket index is a monotone function
+// of the score, so the result is the exact top k'.  The chosen ids are sorted
+// by a rank count and written ascending with their page ids.
+template <int KPT>
 __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ int s_digit, s_gt;
-  __shared__ int tmp[4];
+  __shared__ int hist[256];
+  __shared__ float s_mn[4], s_mx[4];
+  __shared__ int s_cnt[4];
+  __shared__ int s_bt, s_above, s_n, s_nm;
+  __shared__ float mkey[kSelRank];
+  __shared__ int midx[kSelRank];
+  __shared__ int slist[256];
   const int g = blockIdx.x, b = blockIdx.y;
   const int nb = n_blocks(a, b);
   int32_t* out = a.sel + ((size_t)b * a.G + g) * a.top_k;
   int32_t* out2 = a.sel_out ? a.sel_out + ((size_t)b * a.G + g) * a.top_k : nullptr;
+  int32_t* pages = a.sel_page + ((size_t)b * a.G + g) * a.top_k;
+  const int32_t* btab = a.block_table + (size_t)b * a.max_blocks;
   if (nb <= a.top_k) {
     for (int s = threadIdx.x; s < a.top_k; s += kThreads) {
       out[s] = s < nb ? s : -1;
       if (out2) out2[s] = s < nb ? s : -1;
+      pages[s] = s < nb ? btab[s] : -1;
     }
     return;
   }
   const int nc = nb - 2;
   const int kp = a.top_k - 2;
-  const float* L = a.lg + ((size_t)b * a.G + g) * (size_t)(a.n_tiles * kTile) + 1;  // L[i] = LG(i + 1)
-  const int per = (nc + kThreads - 1) / kThreads;
-  const int i0 = min(nc, (int)threadIdx.x * per), i1 = min(nc, i0 + per);
-  uint32_t prefix = 0, mask = 0;
-  int krem = kp;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const float* row = a.lg + ((size_t)b * a.G + g) * (size_t)(a.n_tiles * kTile) + 1;  // row[i] = LG(i + 1)
+  float x[KPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int i = threadIdx.x + u * kThreads;
+    x[u] = i < nc ? row[i] : 0.f;
+  }
+  uint64_t memb = 0, above = 0;  // bit u: key u still in the threshold bucket / already taken
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if ((int)threadIdx.x + u * kThreads < nc) memb |= 1ull << u;
+  if (threadIdx.x == 0) {
+    s_n = 0;
+    s_nm = 0;
+  }
+  int need = kp;
+  bool equal_mode = false;
+  for (int lev = 0;; ++lev) {
+    float mn = INFINITY, mx = -INFINITY;
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      if (memb >> u & 1) {
+        mn = fminf(mn, x[u]);
+        mx = fmaxf(mx, x[u]);
+        ++cnt;
+      }
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    cnt = wave_sum_i(cnt);
     hist[threadIdx.x] = 0;
-    __syncthreads();
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t key = float_key(L[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    if (lane == 0) {
+      s_mn[wv] = mn;
+      s_mx[wv] = mx;
+      s_cnt[wv] = cnt;
     }
     __syncthreads();
-    if (threadIdx.x < 64) {
-      const int lane = threadIdx.x;
-      uint32_t c[4];
-      int sum = 0;
+    mn = fminf(fminf(s_mn[0], s_mn[1]), fminf(s_mn[2], s_mn[3]));
+    mx = fmaxf(fmaxf(s_mx[0], s_mx[1]), fmaxf(s_mx[2], s_mx[3]));
+    cnt = (s_cnt[0] + s_cnt[1]) + (s_cnt[2] + s_cnt[3]);
+    if (cnt <= kSelRank) break;
+    const float range = mx - mn;
+    if (!(range > 0.f) || !(range < INFINITY) || lev == kSelLevels) {
+      equal_mode = true;  // equal scores (or a degenerate range): take by id
+      if (range > 0.f && threadIdx.x == 0) atomicOr(a.err, kErrSel);
+      break;
+    }
+    const float scale = 256.f / range;
+    int bkt[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      bkt[u] = sel_bucket(x[u], mn, scale);
+      if (memb >> u & 1) atomicAdd(&hist[bkt[u]], 1);
+    }
+    __syncthreads();
+    if (wv == 0) {
+      int c[4], sum = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         c[q] = hist[255 - 4 * lane - q];
-        sum += (int)c[q];
+        sum += c[q];
       }
-      int incl = sum;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-      }
-      int run = incl - sum;  // keys in higher bins than this lane's
+      int run = wave_incl_scan_i(sum) - sum;  // keys in buckets above this lane's
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (run < krem && run + (int)c[q] >= krem) {
-          s_digit = 255 - 4 * lane - q;
-          s_gt = run;
+        if (run < need && run + c[q] >= need) {
+          s_bt = 255 - 4 * lane - q;
+          s_above = run;
         }
-        run += (int)c[q];
+        run += c[q];
       }
     }
     __syncthreads();
-    prefix |= (uint32_t)s_digit << shift;
-    mask |= 255u << shift;
-    krem -= s_gt;
+    const int bt = s_bt;
+    need -= s_above;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      if (memb >> u & 1) {
+        if (bkt[u] > bt) above |= 1ull << u;
+        if (bkt[u] != bt) memb &= ~(1ull << u);
+      }
+    }
+  }
+  // taken so far: every key above a threshold bucket
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int slot = wave_append(above >> u & 1, &s_n);
+    if (slot >= 0) slist[slot] = threadIdx.x + u * kThreads;
+  }
+  if (!equal_mode) {
+    // the final bucket (<= kSelRank candidates): exact rank by (score desc, id asc)
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int slot = wave_append(memb >> u & 1, &s_nm);
+      if (slot >= 0) {
+        mkey[slot] = x[u];
+        midx[slot] = threadIdx.x + u * kThreads;
+      }
+    }
     __syncthreads();
-  }
-  const uint32_t tau = prefix;
-  int my_eq = 0;
-  for (int i = i0; i < i1; ++i) my_eq += float_key(L[i]) == tau;
-  const int eq_before = block_excl_scan(my_eq, tmp);
-  int my_sel = 0, seen = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = float_key(L[i]);
-    if (key > tau) {
-      ++my_sel;
-    } else if (key == tau) {
-      if (eq_before + seen < krem) ++my_sel;
-      ++seen;
-    }
-  }
-  int pos = 1 + block_excl_scan(my_sel, tmp);
-  seen = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = float_key(L[i]);
+    const int nm = s_nm;
     bool take = false;
-    if (key > tau) {
-      take = true;
-    } else if (key == tau) {
-      take = eq_before + seen < krem;
-      ++seen;
+    int my = 0;
+    if ((int)threadIdx.x < nm) {
+      const float xv = mkey[threadIdx.x];
+      my = midx[threadIdx.x];
+      int rank = 0;
+      for (int v = 0; v < nm; ++v) {
+        const float y = mkey[v];
+        rank += (y > xv) || (y == xv && midx[v] < my);
+      }
+      take = rank < need;
     }
-    if (take) {
-      out[pos] = i + 1;
-      if (out2) out2[pos] = i + 1;
-      ++pos;
+    const int slot = wave_append(take, &s_n);
+    if (slot >= 0) slist[slot] = my;
+  } else {
+    // equal scores: the `need` smallest ids among the members; find the id
+    // bound by bisection on counts
+    int lo = 0, hi = nc;  // smallest X with #members(id < X) >= need
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      int c = 0;
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) c += (memb >> u & 1) && ((int)threadIdx.x + u * kThreads < mid);
+      c = wave_sum_i(c);
+      __syncthreads();
+      if (lane == 0) s_cnt[wv] = c;
+      __syncthreads();
+      c = (s_cnt[0] + s_cnt[1]) + (s_cnt[2] + s_cnt[3]);
+      if (c >= need) hi = mid; else lo = mid + 1;
+    }
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int i = threadIdx.x + u * kThreads;
+      const int slot = wave_append((memb >> u & 1) && i < lo, &s_n);
+      if (slot >= 0) slist[slot] = i;
     }
   }
-  if (threadIdx.x == 0) {
+  __syncthreads();
+  // ascending order by a rank count over the kp chosen ids
+  if ((int)threadIdx.x < kp) {
+    const int v = slist[threadIdx.x];
+    int pos = 0;
+    for (int u = 0; u < kp; ++u) pos += slist[u] < v;
+    out[1 + pos] = v + 1;
+    if (out2) out2[1 + pos] = v + 1;
+    pages[1 + pos] = btab[v + 1];
+  } else if ((int)threadIdx.x == kp) {
     out[0] = 0;
+    if (out2) out2[0] = 0;
+    pages[0] = btab[0];
+  } else if ((int)threadIdx.x == kp + 1) {
     out[kp + 1] = nb - 1;
-    if (out2) {
-      out2[0] = 0;
-      out2[kp + 1] = nb - 1;
-    }
+    if (out2) out2[kp + 1] = nb - 1;
+    pages[kp + 1] = btab[nb - 1];
   }
 }
 
@@ -377,108 +489,486 @@ __global__ __launch_bounds__(kThreads) void k_attend(const DecodeArgs a) {
   }
 }
 
+// ============================================================== attend (MFMA)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                  c, 0, 0, 0);
+}
+
+// phi(x) of 8 packed bf16 values, split into bf16 hi + lo parts (hi + lo
+// carries phi to ~2^-16 relative)
+__device__ __forceinline__ void phi_hilo(const uint4& raw, uint4& hi, uint4& lo) {
+  const uint32_t in[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float x0 = __uint_as_float(in[k] << 16);
+    const float x1 = __uint_as_float(in[k] & 0xffff0000u);
+    const float f0 = x0 > 0.f ? x0 + 1.f : __expf(x0);
+    const float f1 = x1 > 0.f ? x1 + 1.f : __expf(x1);
+    const uint32_t h0 = bf16_rne_bits(f0), h1 = bf16_rne_bits(f1);
+    const uint32_t l0 = bf16_rne_bits(f0 - __uint_as_float(h0 << 16));
+    const uint32_t l1 = bf16_rne_bits(f1 - __uint_as_float(h1 << 16));
+    h[k] = h0 | (h1 << 16);
+    l[k] = l0 | (l1 << 16);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// grid (top_k, G, B): one selected block of one (b, g) per workgroup, all R
+// query heads of the group, bf16 K/V.  Matrix cores do both contractions:
+//   (1) logits s = q.k and linear weights w = phi(q).phi(k) of the block's
+//       tokens: rows of the 16-row A operand are the R queries and the R
+//       phi(q) (bf16 hi/lo split), B is the K tile read straight from the
+//       page plus phi(K) hi/lo computed in registers; wavefront w takes 16
+//       (Bk = 64) or 32 (Bk = 128) tokens;
+//   (2) sum_t p_t v_t and sum_t w_t v_t: rows of A are p and w (hi/lo split,
+//       from LDS), B is the V tile staged transposed in LDS; wavefront w
+//       takes a quarter of the value channels.
+// Softmax max / sums cross the wavefronts through LDS (two barriers).
+template <int R, int D, int BK>
+__global__ __launch_bounds__(kThreads) void k_attend_mfma(const DecodeArgs a) {
+  constexpr int NKS = D / 32;              // k-steps per channel block
+  constexpr int NT1W = BK / 64;            // 16-token tiles per wavefront
+  constexpr int WB = R <= 4 ? 4 : 8;       // first linear-weight row of product (1)
+  constexpr int NT2W = D / 64;             // 16-channel tiles per wavefront
+  constexpr int MT2 = (4 * R + 15) / 16;   // row tiles of product (2): hi/lo rows of p and w
+  constexpr int KS2 = BK / 32;             // token k-steps of product (2)
+  constexpr int VS = BK + 8;               // row stride (elements) of the transposed V tile
+  constexpr int PS = BK + 8;               // row stride of the p / w rows
+  constexpr int NV = BK * D / (16 * kThreads);  // token-pair x 8-channel pieces per thread
+  __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t pw[MT2 * 16 * PS];
+  __shared__ float s_max[4][R], s_l[4][R], s_sw[4][R];
+
+  const int slot = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64, l16 = lane % 16, lg4 = lane / 16;
+  // queries first: they do not depend on the selection
+  const int m = l16;  // A-operand row of this lane in product (1)
+  const int hq = m < R ? m : ((m >= WB && m < WB + R) ? m - WB : -1);
+  uint4 qraw[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    qraw[ks] = make_uint4(0, 0, 0, 0);
+    if (hq >= 0)
+      qraw[ks] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                                 ((size_t)b * a.H + g * R + hq) * D + 32 * ks + 8 * lg4);
+  }
+  const size_t srow = ((size_t)b * a.G + g) * a.top_k + slot;
+  int j, page;
+  if (a.sel_in) {
+    j = a.sel_in[srow];
+    page = (j >= 0 && j < a.max_blocks) ? a.block_table[(size_t)b * a.max_blocks + j] : -1;
+  } else {
+    j = a.sel[srow];
+    page = a.sel_page[srow];
+  }
+  if (j < 0) return;
+  const int T = a.lens[b];
+  const int nb = n_blocks(a, b);
+  if (j >= nb) {
+    if (threadIdx.x == 0) atomicOr(a.err, kErrSel);
+    return;
+  }
+  if (page < 0 || page >= a.num_pages) {
+    if (threadIdx.x == 0) atomicOr(a.err, kErrPage);
+    return;
+  }
+  const int ntok = min(BK, T - j * BK);
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k_pages) + ((size_t)page * a.G + g) * BK * D;
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v_pages) + ((size_t)page * a.G + g) * BK * D;
+
+  // ---- issue every global load first: K operands, V pieces, queries
+  uint4 kraw[NT1W][NKS];
+#pragma unroll
+  for (int nt = 0; nt < NT1W; ++nt) {
+    const int tok = (w * NT1W + nt) * 16 + l16;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      kraw[nt][ks] = *reinterpret_cast<const uint4*>(kp + (size_t)tok * D + 32 * ks + 8 * lg4);
+  }
+  uint4 vr[NV][2];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = threadIdx.x + kThreads * i;
+    const int tp = idx % (BK / 2), cg = idx / (BK / 2);
+    vr[i][0] = *reinterpret_cast<const uint4*>(vp + (size_t)(2 * tp) * D + 8 * cg);
+    vr[i][1] = *reinterpret_cast<const uint4*>(vp + (size_t)(2 * tp + 1) * D + 8 * cg);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (R < 4) {
+    for (int i = threadIdx.x; i < MT2 * 16 * PS / 2; i += kThreads) reinterpret_cast<uint32_t*>(pw)[i] = 0u;
+  }
+
+  // ---- A operands of product (1)
+  const bool is_q = m < R, is_w = m >= WB && m < WB + R;
+  // rows that are not queries / phi(q) rows are zero (bit masks keep this
+  // plain VALU work)
+  const uint32_t mq = is_q ? 0xffffffffu : 0u, mw = is_w ? 0xffffffffu : 0u;
+  uint4 aq[NKS], afh[NKS], afl[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    uint4 hi, lo;
+    phi_hilo(qraw[ks], hi, lo);
+    aq[ks] = make_uint4(qraw[ks].x & mq, qraw[ks].y & mq, qraw[ks].z & mq, qraw[ks].w & mq);
+    afh[ks] = make_uint4(hi.x & mw, hi.y & mw, hi.z & mw, hi.w & mw);
+    afl[ks] = make_uint4(lo.x & mw, lo.y & mw, lo.z & mw, lo.w & mw);
+  }
+
+  // ---- product (1): logits and linear weights of this wavefront's tokens
+  f32x4_t c1[NT1W];
+#pragma unroll
+  for (int nt = 0; nt < NT1W; ++nt) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 fh, fl;
+      phi_hilo(kraw[nt][ks], fh, fl);
+      c = mfma_bf16(aq[ks], kraw[nt][ks], c);
+      c = mfma_bf16(afh[ks], fh, c);
+      c = mfma_bf16(afh[ks], fl, c);
+      c = mfma_bf16(afl[ks], fh, c);
+    }
+    c1[nt] = c;
+  }
+  // lane (lg4, reg i) holds row 4*lg4 + i of the 16 x 16 result, token l16
+  const float inv_sqrt_d = a.inv_sqrt_d;
+  float mloc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int nt = 0; nt < NT1W; ++nt) {
+    const int tok = (w * NT1W + nt) * 16 + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * lg4 + i;
+      if (row < R && tok < ntok) mloc[i] = fmaxf(mloc[i], c1[nt][i] * inv_sqrt_d);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mloc[i] = row16_max(mloc[i]);
+  if (l16 == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * lg4 + i;
+      if (row < R) s_max[w][row] = mloc[i];
+    }
+  }
+  __syncthreads();
+  // ---- p = exp(s - m) and w, split hi/lo, into the rows of product (2)
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f}, wsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int nt = 0; nt < NT1W; ++nt) {
+    const int tok = (w * NT1W + nt) * 16 + l16;
+    const bool valid = tok < ntok;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * lg4 + i;
+      int kind = -1, h = 0;
+      float x = 0.f;
+      if (row < R) {
+        h = row;
+        const float mh = fmaxf(fmaxf(s_max[0][h], s_max[1][h]), fmaxf(s_max[2][h], s_max[3][h]));
+        x = valid ? __expf(c1[nt][i] * inv_sqrt_d - mh) : 0.f;
+        lsum[i] += x;
+        kind = 0;
+      } else if (row >= WB && row < WB + R) {
+        h = row - WB;
+        x = valid ? c1[nt][i] : 0.f;
+        wsum[i] += x;
+        kind = 1;
+      }
+      if (kind >= 0) {
+        // product (2) rows: pair pi = kind * R + h owns rows 2 pi (hi) and
+        // 2 pi + 1 (lo), so one lane of the result holds both halves
+        const uint32_t hb = bf16_rne_bits(x);
+        const uint32_t lb = bf16_rne_bits(x - __uint_as_float(hb << 16));
+        const int rh = 2 * (kind * R + h);
+        pw[rh * PS + tok] = (uint16_t)hb;
+        pw[(rh + 1) * PS + tok] = (uint16_t)lb;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lsum[i] = row16_sum(lsum[i]);
+    wsum[i] = row16_sum(wsum[i]);
+  }
+  if (l16 == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * lg4 + i;
+      if (row < R) s_l[w][row] = lsum[i];
+      if (row >= WB && row < WB + R) s_sw[w][row - WB] = wsum[i];
+    }
+  }
+  // ---- V tile, transposed into LDS (rows past the block's end are zero)
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = threadIdx.x + kThreads * i;
+    const int tp = idx % (BK / 2), cg = idx / (BK / 2);
+    const bool v0 = 2 * tp < ntok, v1 = 2 * tp + 1 < ntok;
+    const uint32_t r0[4] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w};
+    const uint32_t r1[4] = {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
+    uint32_t* dst = reinterpret_cast<uint32_t*>(vt) + (size_t)(8 * cg) * (VS / 2) + tp;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t a0 = v0 ? r0[k] : 0u, a1 = v1 ? r1[k] : 0u;
+      dst[(2 * k) * (VS / 2)] = (a0 & 0xffffu) | (a1 << 16);
+      dst[(2 * k + 1) * (VS / 2)] = (a0 >> 16) | (a1 & 0xffff0000u);
+    }
+  }
+  __syncthreads();
+  // ---- product (2)
+  const int rec = 2 * D + kPartHdr;
+  float* part0 = a.part + (((size_t)b * a.H + g * R) * a.top_k + slot) * rec;
+#pragma unroll
+  for (int nt2 = 0; nt2 < NT2W; ++nt2) {
+    const int ch = (w * NT2W + nt2) * 16 + l16;
+#pragma unroll
+    for (int mt = 0; mt < MT2; ++mt) {
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS2; ++ks) {
+        const uint4 av = *reinterpret_cast<const uint4*>(&pw[(mt * 16 + l16) * PS + 32 * ks + 8 * lg4]);
+        const uint4 bv = *reinterpret_cast<const uint4*>(&vt[ch * VS + 32 * ks + 8 * lg4]);
+        c = mfma_bf16(av, bv, c);
+      }
+      // lane group lg4 holds rows 4 lg4 .. 4 lg4 + 3 of tile mt: pairs
+      // pi0 = 8 mt + 2 lg4 (hi + lo in c[0], c[1]) and pi0 + 1 (c[2], c[3])
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int pi = 8 * mt + 2 * lg4 + e;
+        if (pi < 2 * R) {
+          const int kind = pi / R, h = pi % R;
+          part0[(size_t)h * a.top_k * rec + kPartHdr + (kind ? D : 0) + ch] = c[2 * e] + c[2 * e + 1];
+        }
+      }
+    }
+  }
+  if (threadIdx.x < R) {
+    const int h = threadIdx.x;
+    float* dst = part0 + (size_t)h * a.top_k * rec;
+    dst[0] = fmaxf(fmaxf(s_max[0][h], s_max[1][h]), fmaxf(s_max[2][h], s_max[3][h])) ;
+    dst[1] = (s_l[0][h] + s_l[1][h]) + (s_l[2][h] + s_l[3][h]);
+    dst[2] = (s_sw[0][h] + s_sw[1][h]) + (s_sw[2][h] + s_sw[3][h]);
+    dst[3] = 0.f;
+  }
+}
+
 // ============================================================== combine
-// grid (G, B): merge the slot partials of the R heads of (b, g), contract
-// phi(q) with S_all and z_all, write o (and the optional outputs).
+// grid (D/32, G, B): one 32-channel slice of the R heads of (b, g).  Merges
+// the per-block partials (softmax rescaling by exp(m_s - m) / L), contracts
+// phi(q) with the slice's S_all columns (o_bar) and, in slice 0, with z_all
+// (the normaliser D), and writes o = o_sparse + g_h (o_bar - o_tilde).
+// Every global load is issued before the first wait (slots in batches of 32).
 template <bool BF16, int R, int D>
 __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
-  constexpr int ngrp = kThreads / D;
+  constexpr int CS = 32;               // channels per workgroup
+  constexpr int RG = kThreads / CS;    // row groups of the S contraction
+  constexpr int RPG = D / RG;          // rows per group
+  constexpr int NP = (2 * R * CS + kThreads - 1) / kThreads;  // (kind, head, channel) items per thread
+  constexpr int SB = 32;               // slots per load batch
   __shared__ float fq[R][D];
-  __shared__ float wsl[R][256];  // per-slot softmax weight exp(m_s - m) / L
-  __shared__ float s_sw[R];
-  __shared__ float obr[ngrp][R][D];
-  __shared__ float s_dz[R];
+  __shared__ float wsl[R][256];        // exp(m_s - m) / L per head and slot (0 for unused slots)
+  __shared__ float obr[RG][R][CS];
+  __shared__ float osp[R][CS];
+  __shared__ float s_sw[R], s_dz[R];
   __shared__ int valid[256];
-  const int g = blockIdx.x, b = blockIdx.y;
-  constexpr int d = D;
+  const int cc = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int nb = n_blocks(a, b);
   const bool covers_all = nb <= a.top_k;
   const int32_t* selp = a.sel_in ? a.sel_in : a.sel;
   const int32_t* srow = selp + ((size_t)b * a.G + g) * a.top_k;
-  for (int s = threadIdx.x; s < a.top_k; s += kThreads) {
-    const int j = srow[s];
-    valid[s] = (j >= 0 && j < nb) ? 1 : 0;
-    if (a.sel_out) a.sel_out[((size_t)b * a.G + g) * a.top_k + s] = j;
+  const int rec = 2 * D + kPartHdr;
+  const float* P0 = a.part + ((size_t)b * a.H + g * R) * a.top_k * (size_t)rec;
+  const int c0 = cc * CS;
+  const int top_k = a.top_k;
+  const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
+  // ---- loads: S slice, queries, z, slot headers, first batch of slot data
+  const int sc = threadIdx.x % CS, rg = threadIdx.x / CS;
+  const float* S = a.s_all + ((size_t)b * a.G + g) * D * (size_t)D + (size_t)(rg * RPG) * D + c0 + sc;
+  float sv[RPG];
+#pragma unroll
+  for (int x = 0; x < RPG; ++x) sv[x] = S[(size_t)x * D];
+  float qv[(R * D + kThreads - 1) / kThreads];
+#pragma unroll
+  for (int k = 0; k < (R * D + kThreads - 1) / kThreads; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    qv[k] = i < R * D ? load_elem<BF16>(a.q, ((size_t)b * a.H + g * R) * D + i) : 0.f;
   }
-  for (int i = threadIdx.x; i < R * d; i += kThreads) {
-    const int h = i / d, c = i - h * d;
-    fq[h][c] = phi_f(load_elem<BF16>(a.q, ((size_t)b * a.H + g * R + h) * d + c));
+  float zv[(D + 63) / 64];
+#pragma unroll
+  for (int k = 0; k < (D + 63) / 64; ++k) zv[k] = a.z_all[((size_t)b * a.G + g) * D + lane + 64 * k];
+  // headers: wavefront w handles heads w, w + 4; lane = slot (strided by 64)
+  constexpr int HPW = (R + 3) / 4;
+  constexpr int SPL = 4;  // slots per lane: top_k <= 256
+  float hm[HPW][SPL], hl[HPW][SPL], hs[HPW][SPL];
+  int vs[SPL];
+#pragma unroll
+  for (int u = 0; u < SPL; ++u) {
+    const int s = lane + 64 * u;
+    vs[u] = s < top_k ? srow[s] : -1;
+  }
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int h = w + 4 * hh;
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      const int s = lane + 64 * u;
+      hm[hh][u] = hl[hh][u] = hs[hh][u] = 0.f;
+      if (h < R && s < top_k) {
+        const float* P = P0 + ((size_t)h * top_k + s) * rec;
+        hm[hh][u] = P[0];
+        hl[hh][u] = P[1];
+        hs[hh][u] = P[2];
+      }
+    }
+  }
+  // slot data of this thread's items, first batch
+  float dv[NP][SB];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int it = threadIdx.x + k * kThreads;
+    const int kind = it / (R * CS), h = (it / CS) % R, c = it % CS;
+    const float* P = P0 + (size_t)h * top_k * rec + kPartHdr + (kind ? D : 0) + c0 + c;
+#pragma unroll
+    for (int u = 0; u < SB; ++u) dv[k][u] = (it < 2 * R * CS && u < top_k) ? P[(size_t)u * rec] : 0.f;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- phi(q), softmax merge weights, phi(q).z
+#pragma unroll
+  for (int k = 0; k < (R * D + kThreads - 1) / kThreads; ++k) {
+    const int i = threadIdx.x + k * kThreads;
+    if (i < R * D) fq[i / D][i % D] = phi_f(qv[k]);
+  }
+  if (w == 0) {
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      const int s = lane + 64 * u;
+      if (s < top_k) valid[s] = (vs[u] >= 0 && vs[u] < nb) ? 1 : 0;
+    }
   }
   __syncthreads();
-  const int rec = 2 * d + kPartHdr;
-  const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
-  for (int h = w; h < R; h += 4) {
-    const float* P = a.part + ((size_t)b * a.H + g * R + h) * a.top_k * (size_t)rec;
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int h = w + 4 * hh;
+    if (h >= R) continue;
+    bool ok[SPL];
     float m = -INFINITY;
-    for (int s = lane; s < a.top_k; s += 64)
-      if (valid[s]) m = fmaxf(m, P[(size_t)s * rec]);
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      ok[u] = vs[u] >= 0 && vs[u] < nb;
+      if (ok[u]) m = fmaxf(m, hm[hh][u]);
+    }
     m = wave_max(m);
-    float l = 0.f, sw = 0.f;
-    for (int s = lane; s < a.top_k; s += 64) {
-      if (valid[s]) {
-        const float e = expf(P[(size_t)s * rec] - m);
-        wsl[h][s] = e;
-        l += e * P[(size_t)s * rec + 1];
-        sw += P[(size_t)s * rec + 2];
-      } else {
-        wsl[h][s] = 0.f;
-      }
+    float l = 0.f, sw = 0.f, e[SPL];
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      e[u] = ok[u] ? expf(hm[hh][u] - m) : 0.f;
+      l = fmaf(e[u], ok[u] ? hl[hh][u] : 0.f, l);
+      sw += ok[u] ? hs[hh][u] : 0.f;
     }
     l = wave_sum(l);
     sw = wave_sum(sw);
     const float inv_l = 1.f / l;
-    for (int s = lane; s < a.top_k; s += 64) wsl[h][s] *= inv_l;
-    // phi(q) . z_all
+#pragma unroll
+    for (int u = 0; u < SPL; ++u) {
+      const int s = lane + 64 * u;
+      if (s < top_k) wsl[h][s] = e[u] * inv_l;
+    }
     float dz = 0.f;
-    const float* z = a.z_all + ((size_t)b * a.G + g) * d;
-    for (int c = lane; c < d; c += 64) dz = fmaf(fq[h][c], z[c], dz);
+#pragma unroll
+    for (int k = 0; k < (D + 63) / 64; ++k) dz = fmaf(fq[h][lane + 64 * k], zv[k], dz);
     dz = wave_sum(dz);
     if (lane == 0) {
       s_sw[h] = sw;
       s_dz[h] = dz;
     }
   }
-  // o_bar = phi(q)^T S: thread = column, rows split over ngrp thread groups
+  // ---- o_bar partial sums over this thread's rows
   {
-    const int c = threadIdx.x % d, grp = threadIdx.x / d;
-    const float* S = a.s_all + ((size_t)b * a.G + g) * d * (size_t)d;
-    constexpr int rows = d / ngrp;
     float ob[R];
 #pragma unroll
     for (int h = 0; h < R; ++h) ob[h] = 0.f;
-    for (int x = grp * rows; x < (grp + 1) * rows; ++x) {
-      const float sv = S[(size_t)x * d + c];
 #pragma unroll
-      for (int h = 0; h < R; ++h) ob[h] = fmaf(fq[h][x], sv, ob[h]);
+    for (int x = 0; x < RPG; ++x) {
+#pragma unroll
+      for (int h = 0; h < R; ++h) ob[h] = fmaf(fq[h][rg * RPG + x], sv[x], ob[h]);
     }
 #pragma unroll
-    for (int h = 0; h < R; ++h) obr[grp][h][c] = ob[h];
+    for (int h = 0; h < R; ++h) obr[rg][h][sc] = ob[h];
   }
   __syncthreads();
-  // finalize: thread -> (h, c)
-  for (int i = threadIdx.x; i < R * d; i += kThreads) {
-    const int h = i / d, c = i - h * d;
-    const float* P = a.part + ((size_t)b * a.H + g * R + h) * a.top_k * (size_t)rec;
-    float os = 0.f, ot = 0.f;
-    for (int s = 0; s < a.top_k; ++s) {
-      if (!valid[s]) continue;
-      const float* ps = P + (size_t)s * rec + kPartHdr;
-      os = fmaf(wsl[h][s], ps[c], os);
-      ot += ps[d + c];
+  // ---- merge of the slot partials: item = (kind, head, channel)
+  float acc[NP];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) acc[k] = 0.f;
+  for (int s0 = 0; s0 < top_k; s0 += SB) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int k = 0; k < NP; ++k) {
+        const int it = threadIdx.x + k * kThreads;
+        const int kind = it / (R * CS), h = (it / CS) % R, c = it % CS;
+        const float* P = P0 + (size_t)h * top_k * rec + kPartHdr + (kind ? D : 0) + c0 + c;
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+          dv[k][u] = (it < 2 * R * CS && s0 + u < top_k) ? P[(size_t)(s0 + u) * rec] : 0.f;
+      }
     }
-    float orla = 0.f, drla = 0.f;
-    if (!covers_all) {
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int it = threadIdx.x + k * kThreads;
+      if (it >= 2 * R * CS) continue;
+      const int kind = it / (R * CS), h = (it / CS) % R;
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int s = s0 + u;
+        if (s >= top_k) break;
+        // wsl is 0 for unused slots
+        if (kind == 0) {
+          acc[k] = fmaf(wsl[h][s], dv[k][u], acc[k]);
+        } else if (valid[s]) {
+          acc[k] += dv[k][u];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int it = threadIdx.x + k * kThreads;
+    if (it >= 2 * R * CS) continue;
+    const int kind = it / (R * CS), h = (it / CS) % R, c = it % CS;
+    if (kind == 0) {
+      osp[h][c] = acc[k];
+    } else {
       float obar = 0.f;
 #pragma unroll
-      for (int q = 0; q < ngrp; ++q) obar += obr[q][h][c];
-      orla = obar - ot;
-      drla = s_dz[h] - s_sw[h];
+      for (int q = 0; q < RG; ++q) obar += obr[q][h][c];
+      obr[0][h][c] = covers_all ? 0.f : obar - acc[k];  // o_rla of this slice
     }
-    const size_t oi = ((size_t)b * a.H + g * R + h) * d + c;
-    a.out[oi] = os + a.gate[g * R + h] * orla;
-    if (a.o_sparse_out) a.o_sparse_out[oi] = os;
+  }
+  __syncthreads();
+  for (int it = threadIdx.x; it < R * CS; it += kThreads) {
+    const int h = it / CS, c = it % CS;
+    const size_t oi = ((size_t)b * a.H + g * R + h) * D + c0 + c;
+    const float orla = obr[0][h][c];
+    a.out[oi] = osp[h][c] + a.gate[g * R + h] * orla;
+    if (a.o_sparse_out) a.o_sparse_out[oi] = osp[h][c];
     if (a.o_rla_out) a.o_rla_out[oi] = orla;
-    if (a.d_rla_out && c == 0) a.d_rla_out[(size_t)b * a.H + g * R + h] = drla;
+  }
+  if (cc == 0 && threadIdx.x < a.top_k && a.sel_out) a.sel_out[((size_t)b * a.G + g) * a.top_k + threadIdx.x] = srow[threadIdx.x];
+  if (cc == 0 && threadIdx.x < R && a.d_rla_out) {
+    const int h = threadIdx.x;
+    a.d_rla_out[(size_t)b * a.H + g * R + h] = covers_all ? 0.f : s_dz[h] - s_sw[h];
   }
 }
 
@@ -511,14 +1001,35 @@ hipError_t launch_score(const DecodeArgs& a, bool bf16, hipStream_t s) {
 }
 
 hipError_t launch_select(const DecodeArgs& a, hipStream_t s) {
-  k_select<<<dim3(a.G, a.B), kThreads, 0, s>>>(a);
+  // keys per thread: enough for the longest sequence of the batch
+  const int nc = a.score_tiles * kTile;
+  const dim3 grid(a.G, a.B);
+  if (nc <= 1 * kThreads) {
+    k_select<1><<<grid, kThreads, 0, s>>>(a);
+  } else if (nc <= 2 * kThreads) {
+    k_select<2><<<grid, kThreads, 0, s>>>(a);
+  } else if (nc <= 4 * kThreads) {
+    k_select<4><<<grid, kThreads, 0, s>>>(a);
+  } else if (nc <= 8 * kThreads) {
+    k_select<8><<<grid, kThreads, 0, s>>>(a);
+  } else if (nc <= 16 * kThreads) {
+    k_select<16><<<grid, kThreads, 0, s>>>(a);
+  } else if (nc <= 32 * kThreads) {
+    k_select<32><<<grid, kThreads, 0, s>>>(a);
+  } else {
+    k_select<64><<<grid, kThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_attend(const DecodeArgs& a, bool bf16, hipStream_t s) {
   dim3 grid(a.top_k, a.G, a.B);
   if (bf16) {
-    SPLA_DISPATCH_RD(a.r, a.d, (k_attend<true, RR, DD><<<grid, kThreads, 0, s>>>(a)))
+    if (a.bk == 64) {
+      SPLA_DISPATCH_RD(a.r, a.d, (k_attend_mfma<RR, DD, 64><<<grid, kThreads, 0, s>>>(a)))
+    } else {
+      SPLA_DISPATCH_RD(a.r, a.d, (k_attend_mfma<RR, DD, 128><<<grid, kThreads, 0, s>>>(a)))
+    }
   } else {
     SPLA_DISPATCH_RD(a.r, a.d, (k_attend<false, RR, DD><<<grid, kThreads, 0, s>>>(a)))
   }
@@ -526,7 +1037,7 @@ hipError_t launch_attend(const DecodeArgs& a, bool bf16, hipStream_t s) {
 }
 
 hipError_t launch_combine(const DecodeArgs& a, bool bf16, hipStream_t s) {
-  dim3 grid(a.G, a.B);
+  dim3 grid(a.d / 32, a.G, a.B);
   if (bf16) {
     SPLA_DISPATCH_RD(a.r, a.d, (k_combine<true, RR, DD><<<grid, kThreads, 0, s>>>(a)))
   } else {

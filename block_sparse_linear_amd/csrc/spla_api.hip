@@ -19,7 +19,7 @@ struct spla_handle {
   spla_buffers buf{};
   std::vector<int32_t> lens;
   // workspace layout (bytes)
-  size_t off_lg = 0, off_sel = 0, off_part = 0, ws_bytes = 0;
+  size_t off_lg = 0, off_sel = 0, off_page = 0, off_part = 0, ws_bytes = 0;
 };
 
 namespace {
@@ -35,6 +35,8 @@ void layout(spla_handle* h) {
   h->off_lg = off;
   off = align256(off + B * G * (size_t)h->n_tiles * kTile * sizeof(float));
   h->off_sel = off;
+  off = align256(off + B * G * k * sizeof(int32_t));
+  h->off_page = off;
   off = align256(off + B * G * k * sizeof(int32_t));
   h->off_part = off;
   off = align256(off + B * H * k * (2 * d + kPartHdr) * sizeof(float));
@@ -62,6 +64,7 @@ spla_status fill_decode_args(const spla_handle* h, const void* q, const float* g
   a->z_all = h->buf.z_all;
   a->lg = ws_ptr<float>(h, h->off_lg);
   a->sel = ws_ptr<int32_t>(h, h->off_sel);
+  a->sel_page = ws_ptr<int32_t>(h, h->off_page);
   a->part = ws_ptr<float>(h, h->off_part);
   a->err = ws_ptr<uint32_t>(h, 0);
   if (aux) {
@@ -129,7 +132,7 @@ spla_status spla_create(const spla_config* cfg, spla_handle** out) {
   const int r = c.n_q_heads / c.n_kv_heads;
   if (r != 1 && r != 2 && r != 4 && r != 8) return SPLA_ERR_UNSUPPORTED;
   if (c.top_k < 2 || c.top_k > 256) return SPLA_ERR_UNSUPPORTED;
-  if (c.max_blocks_per_seq > 131072) return SPLA_ERR_UNSUPPORTED;
+  if (c.max_blocks_per_seq > kMaxBlocksPerSeq) return SPLA_ERR_UNSUPPORTED;
   if (c.kv_dtype != SPLA_F32 && c.kv_dtype != SPLA_BF16) return SPLA_ERR_UNSUPPORTED;
   spla_handle* h = new (std::nothrow) spla_handle();
   if (!h) return SPLA_ERR_INVALID_ARG;

@@ -8,6 +8,7 @@
 namespace spla {
 
 constexpr int kMaxBatch = 256;
+constexpr int kMaxBlocksPerSeq = 16386;  // the selector ranks at most 16384 candidates in LDS
 constexpr int kMaxAppendEntries = 64;  // entries per append launch (host splits larger calls)
 constexpr int kTile = 64;              // blocks per statistics tile (= wavefront width)
 constexpr int kThreads = 256;          // threads per workgroup of every kernel
@@ -57,7 +58,8 @@ struct DecodeArgs {
   const float* s_all;
   const float* z_all;
   float* lg;        // workspace [B][G][NT*64]
-  int32_t* sel;     // workspace [B][G][top_k]
+  int32_t* sel;     // workspace [B][G][top_k] selected block ids
+  int32_t* sel_page;  // workspace [B][G][top_k] their page ids
   float* part;      // workspace [B][H][top_k][2d + kPartHdr]
   uint32_t* err;    // workspace error word
   const int32_t* sel_in;
@@ -107,16 +109,84 @@ __device__ __forceinline__ float4 load4(const void* p, size_t i) {
   }
 }
 
-// 64-wide wavefront reductions
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+// ----------------------------------------------------- cross-lane (DPP) ops
+// DPP moves run on the VALU with a few cycles of latency, unlike the LDS
+// crossbar behind __shfl_*.  Controls (GFX9 encoding): quad_perm, row_shr:n,
+// row_mirror, row_half_mirror, row_bcast:15, row_bcast:31.
+constexpr int kDppXor1 = 0xb1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4e;         // quad_perm [2,3,0,1]
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr3 = 0x113;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf, bool BOUND_CTRL = false>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, BANK_MASK, BOUND_CTRL));
+}
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf, bool BOUND_CTRL = false>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, BANK_MASK, BOUND_CTRL);
+}
+
+// reductions over each 16-lane row; every lane of the row gets the result
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v, v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v, v));
+  v = fmaxf(v, dpp_f<kDppRowHalfMirror>(v, v));
+  v = fmaxf(v, dpp_f<kDppRowMirror>(v, v));
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<kDppXor1>(0.f, v);
+  v += dpp_f<kDppXor2>(0.f, v);
+  v += dpp_f<kDppRowHalfMirror>(0.f, v);
+  v += dpp_f<kDppRowMirror>(0.f, v);
   return v;
+}
+
+// full 64-lane reductions, result returned in every lane
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  v = fmaxf(v, dpp_f<kDppRowBcast15, 0xa>(-INFINITY, v));
+  v = fmaxf(v, dpp_f<kDppRowBcast31, 0xc>(-INFINITY, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_min(float v) {
+  v = -v;
+  return -wave_max(v);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += dpp_f<kDppRowBcast15, 0xa>(0.f, v);
+  v += dpp_f<kDppRowBcast31, 0xc>(0.f, v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_i<kDppXor1>(0, v);
+  v += dpp_i<kDppXor2>(0, v);
+  v += dpp_i<kDppRowHalfMirror>(0, v);
+  v += dpp_i<kDppRowMirror>(0, v);
+  v += dpp_i<kDppRowBcast15, 0xa>(0, v);
+  v += dpp_i<kDppRowBcast31, 0xc>(0, v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ int wave_incl_scan_i(int v) {
+  int t = v + dpp_i<kDppRowShr1, 0xf, 0xf, true>(0, v);
+  t += dpp_i<kDppRowShr2, 0xf, 0xf, true>(0, v);
+  t += dpp_i<kDppRowShr3, 0xf, 0xf, true>(0, v);
+  t += dpp_i<kDppRowShr4, 0xf, 0xe>(0, t);
+  t += dpp_i<kDppRowShr8, 0xf, 0xc>(0, t);
+  t += dpp_i<kDppRowBcast15, 0xa>(0, t);
+  t += dpp_i<kDppRowBcast31, 0xc>(0, t);
+  return t;
 }
 
 // order-preserving map float -> uint32 (larger float -> larger key)

@@ -95,7 +95,7 @@ typedef enum { SPLA_F32 = 0, SPLA_BF16 = 1 } spla_dtype;
 
 /* Supported: 1 <= batch <= 256; head_dim in {64, 128}; block_size in {64,
  * 128}; n_q_heads = r * n_kv_heads with r in {1, 2, 4, 8}; 2 <= top_k <= 256;
- * 1 <= max_blocks_per_seq <= 131072; num_pages >= 1; kv_dtype F32 or BF16
+ * 1 <= max_blocks_per_seq <= 16386 (1M tokens at block 64, 2M at 128); num_pages >= 1; kv_dtype F32 or BF16
  * (K, V and q share it).  Anything else returns SPLA_ERR_UNSUPPORTED. */
 typedef struct {
     int32_t batch;
