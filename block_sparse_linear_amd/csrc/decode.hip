@@ -99,28 +99,35 @@ __global__ __launch_bounds__(kThreads) void k_score(const DecodeArgs a) {
     red[w][R + h][lane] = qq[h];
   }
   __syncthreads();
-  if (w != 0) return;
-  const int j = j0 + lane;
+  // finalisation spread over the four wavefronts: lane = (block, head), the
+  // R lanes of a block combine their log scores with DPP (max, exp-sum)
+  constexpr int BPW = 64 / R;  // blocks per wavefront pass
   const float half_inv_d = 0.5f / (float)D;
-  float ls[R];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int h = 0; h < R; ++h) {
-    const float dd = (red[0][h][lane] + red[1][h][lane]) + (red[2][h][lane] + red[3][h][lane]);
-    const float vv = (red[0][R + h][lane] + red[1][R + h][lane]) + (red[2][R + h][lane] + red[3][R + h][lane]);
-    ls[h] = dd * a.inv_sqrt_d + log1pf(fmaxf(vv, 0.f) * half_inv_d);
-    mx = fmaxf(mx, ls[h]);
+  const int h = lane % R;
+  for (int blk0 = w * BPW; blk0 < kTile; blk0 += 4 * BPW) {
+    const int blk = blk0 + lane / R;
+    const float dd = (red[0][h][blk] + red[1][h][blk]) + (red[2][h][blk] + red[3][h][blk]);
+    const float vv = (red[0][R + h][blk] + red[1][R + h][blk]) + (red[2][R + h][blk] + red[3][R + h][blk]);
+    const float ls = dd * a.inv_sqrt_d + __logf(1.f + fmaxf(vv, 0.f) * half_inv_d);
+    float lg = ls;
+    if constexpr (R > 1) {
+      float mx = ls;
+      mx = fmaxf(mx, dpp_f<kDppXor1>(mx, mx));
+      if constexpr (R > 2) mx = fmaxf(mx, dpp_f<kDppXor2>(mx, mx));
+      if constexpr (R > 4) mx = fmaxf(mx, dpp_f<kDppRowHalfMirror>(mx, mx));
+      float e = __expf(ls - mx);
+      e += dpp_f<kDppXor1>(0.f, e);
+      if constexpr (R > 2) e += dpp_f<kDppXor2>(0.f, e);
+      if constexpr (R > 4) e += dpp_f<kDppRowHalfMirror>(0.f, e);
+      lg = mx + __logf(e);
+    }
+    const int j = j0 + blk;
+    if (h == 0) {
+      const bool cand = j >= 1 && j <= nb - 2;
+      a.lg[((size_t)b * a.G + g) * (size_t)(a.n_tiles * kTile) + j] = cand ? lg : -INFINITY;
+      if (a.lg_out && cand) a.lg_out[((size_t)b * a.G + g) * a.max_blocks + j] = lg;
+    }
   }
-  float lg = ls[0];
-  if (R > 1) {
-    float s = 0.f;
-#pragma unroll
-    for (int h = 0; h < R; ++h) s += expf(ls[h] - mx);
-    lg = mx + logf(s);
-  }
-  if (j < 1 || j > nb - 2) lg = -INFINITY;  // not a candidate
-  a.lg[((size_t)b * a.G + g) * (size_t)(a.n_tiles * kTile) + j] = lg;
-  if (a.lg_out && j >= 1 && j <= nb - 2) a.lg_out[((size_t)b * a.G + g) * a.max_blocks + j] = lg;
 }
 
 // ============================================================== select
@@ -134,16 +141,33 @@ __device__ __forceinline__ int sel_bucket(float x, float lo, float scale) {
   return f >= 255.f ? 255 : (f <= 0.f ? 0 : (int)f);
 }
 
-// append the flagged entries of a wavefront to an LDS list (one atomic per
-// wavefront); returns this lane's slot or -1
-__device__ __forceinline__ int wave_append(bool flag, int* counter) {
-  const uint64_t m = __ballot(flag);
-  if (m == 0) return -1;
-  const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// append the entries flagged in bit u of `flags` (u < KPT) of every lane of a
+// wavefront to an LDS list with one atomic per wavefront; slot[u] receives the
+// entry's position (or -1)
+template <int KPT>
+__device__ __forceinline__ void wave_append(uint64_t flags, int* counter, int (&slot)[KPT]) {
+  int total = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) total += __popcll(__ballot((flags >> u) & 1));
+  if (total == 0) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) slot[u] = -1;
+    return;
+  }
   int base = 0;
-  if ((threadIdx.x & 63) == 0) base = atomicAdd(counter, __popcll(m));
+  if ((threadIdx.x & 63) == 0) base = atomicAdd(counter, total);
   base = __builtin_amdgcn_readfirstlane(base);
-  return flag ? base + below : -1;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const bool f = (flags >> u) & 1;
+    const uint64_t m = __ballot(f);
+    slot[u] = f ? base + lanes_below(m) : -1;
+    base += __popcll(m);
+  }
 }
 
 // grid (G, B).  Bucket select over the scores held in registers (KPT per
@@ -157,7 +181,7 @@ __device__ __forceinline__ int wave_append(bool flag, int* counter) {
 // by a rank count and written ascending with their page ids.
 template <int KPT>
 __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
-  __shared__ int hist[256];
+  __shared__ int hist[4][256];  // one histogram per wavefront
   __shared__ float s_mn[4], s_mx[4];
   __shared__ int s_cnt[4];
   __shared__ int s_bt, s_above, s_n, s_nm;
@@ -212,7 +236,8 @@ __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
     mn = wave_min(mn);
     mx = wave_max(mx);
     cnt = wave_sum_i(cnt);
-    hist[threadIdx.x] = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hist[q][threadIdx.x] = 0;
     if (lane == 0) {
       s_mn[wv] = mn;
       s_mx[wv] = mx;
@@ -234,14 +259,15 @@ __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
       bkt[u] = sel_bucket(x[u], mn, scale);
-      if (memb >> u & 1) atomicAdd(&hist[bkt[u]], 1);
+      if (memb >> u & 1) atomicAdd(&hist[wv][bkt[u]], 1);
     }
     __syncthreads();
     if (wv == 0) {
       int c[4], sum = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        c[q] = hist[255 - 4 * lane - q];
+        const int bin = 255 - 4 * lane - q;
+        c[q] = (hist[0][bin] + hist[1][bin]) + (hist[2][bin] + hist[3][bin]);
         sum += c[q];
       }
       int run = wave_incl_scan_i(sum) - sum;  // keys in buckets above this lane's
@@ -266,19 +292,24 @@ __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
     }
   }
   // taken so far: every key above a threshold bucket
+  {
+    int slot[KPT];
+    wave_append<KPT>(above, &s_n, slot);
 #pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const int slot = wave_append(above >> u & 1, &s_n);
-    if (slot >= 0) slist[slot] = threadIdx.x + u * kThreads;
+    for (int u = 0; u < KPT; ++u)
+      if (slot[u] >= 0) slist[slot[u]] = threadIdx.x + u * kThreads;
   }
   if (!equal_mode) {
     // the final bucket (<= kSelRank candidates): exact rank by (score desc, id asc)
+    {
+      int slot[KPT];
+      wave_append<KPT>(memb, &s_nm, slot);
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int slot = wave_append(memb >> u & 1, &s_nm);
-      if (slot >= 0) {
-        mkey[slot] = x[u];
-        midx[slot] = threadIdx.x + u * kThreads;
+      for (int u = 0; u < KPT; ++u) {
+        if (slot[u] >= 0) {
+          mkey[slot[u]] = x[u];
+          midx[slot[u]] = threadIdx.x + u * kThreads;
+        }
       }
     }
     __syncthreads();
@@ -295,8 +326,9 @@ __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
       }
       take = rank < need;
     }
-    const int slot = wave_append(take, &s_n);
-    if (slot >= 0) slist[slot] = my;
+    int slot1[1];
+    wave_append<1>(take ? 1ull : 0ull, &s_n, slot1);
+    if (slot1[0] >= 0) slist[slot1[0]] = my;
   } else {
     // equal scores: the `need` smallest ids among the members; find the id
     // bound by bisection on counts
@@ -313,12 +345,15 @@ __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
       c = (s_cnt[0] + s_cnt[1]) + (s_cnt[2] + s_cnt[3]);
       if (c >= need) hi = mid; else lo = mid + 1;
     }
+    uint64_t low = 0;
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int i = threadIdx.x + u * kThreads;
-      const int slot = wave_append((memb >> u & 1) && i < lo, &s_n);
-      if (slot >= 0) slist[slot] = i;
-    }
+    for (int u = 0; u < KPT; ++u)
+      if ((memb >> u & 1) && (int)threadIdx.x + u * kThreads < lo) low |= 1ull << u;
+    int slot[KPT];
+    wave_append<KPT>(low, &s_n, slot);
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      if (slot[u] >= 0) slist[slot[u]] = threadIdx.x + u * kThreads;
   }
   __syncthreads();
   // ascending order by a rank count over the kp chosen ids
@@ -493,32 +528,42 @@ __global__ __launch_bounds__(kThreads) void k_attend(const DecodeArgs a) {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair (round to nearest even, hardware conversion)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ float bf16_lo_f(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi_f(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                   c, 0, 0, 0);
 }
 
-// phi(x) of 8 packed bf16 values, split into bf16 hi + lo parts (hi + lo
-// carries phi to ~2^-16 relative)
+__device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+// phi of 8 packed bf16 values rounded to bf16
+__device__ __forceinline__ uint4 phi_bf16(const uint4& raw) {
+  const uint32_t in[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = pack_bf16(phi_fast(bf16_lo_f(in[k])), phi_fast(bf16_hi_f(in[k])));
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// phi of 8 packed bf16 values split into bf16 hi + lo parts (hi + lo carries
+// phi to ~2^-16 relative)
 __device__ __forceinline__ void phi_hilo(const uint4& raw, uint4& hi, uint4& lo) {
   const uint32_t in[4] = {raw.x, raw.y, raw.z, raw.w};
   uint32_t h[4], l[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float x0 = __uint_as_float(in[k] << 16);
-    const float x1 = __uint_as_float(in[k] & 0xffff0000u);
-    const float f0 = x0 > 0.f ? x0 + 1.f : __expf(x0);
-    const float f1 = x1 > 0.f ? x1 + 1.f : __expf(x1);
-    const uint32_t h0 = bf16_rne_bits(f0), h1 = bf16_rne_bits(f1);
-    const uint32_t l0 = bf16_rne_bits(f0 - __uint_as_float(h0 << 16));
-    const uint32_t l1 = bf16_rne_bits(f1 - __uint_as_float(h1 << 16));
-    h[k] = h0 | (h1 << 16);
-    l[k] = l0 | (l1 << 16);
+    const float f0 = phi_fast(bf16_lo_f(in[k])), f1 = phi_fast(bf16_hi_f(in[k]));
+    h[k] = pack_bf16(f0, f1);
+    l[k] = pack_bf16(f0 - bf16_lo_f(h[k]), f1 - bf16_hi_f(h[k]));
   }
   hi = make_uint4(h[0], h[1], h[2], h[3]);
   lo = make_uint4(l[0], l[1], l[2], l[3]);
@@ -632,12 +677,12 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(const DecodeArgs a) {
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      uint4 fh, fl;
-      phi_hilo(kraw[nt][ks], fh, fl);
+      // phi(k) in bf16 (its rounding is independent per token and averages
+      // out of o_tilde); phi(q) keeps hi + lo (shared by every token)
+      const uint4 fk = phi_bf16(kraw[nt][ks]);
       c = mfma_bf16(aq[ks], kraw[nt][ks], c);
-      c = mfma_bf16(afh[ks], fh, c);
-      c = mfma_bf16(afh[ks], fl, c);
-      c = mfma_bf16(afl[ks], fh, c);
+      c = mfma_bf16(afh[ks], fk, c);
+      c = mfma_bf16(afl[ks], fk, c);
     }
     c1[nt] = c;
   }
@@ -689,8 +734,8 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(const DecodeArgs a) {
       if (kind >= 0) {
         // product (2) rows: pair pi = kind * R + h owns rows 2 pi (hi) and
         // 2 pi + 1 (lo), so one lane of the result holds both halves
-        const uint32_t hb = bf16_rne_bits(x);
-        const uint32_t lb = bf16_rne_bits(x - __uint_as_float(hb << 16));
+        const uint32_t hb = pack_bf16(x, 0.f) & 0xffffu;
+        const uint32_t lb = pack_bf16(x - bf16_lo_f(hb), 0.f) & 0xffffu;
         const int rh = 2 * (kind * R + h);
         pw[rh * PS + tok] = (uint16_t)hb;
         pw[(rh + 1) * PS + tok] = (uint16_t)lb;
@@ -769,55 +814,57 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(const DecodeArgs a) {
 // the per-block partials (softmax rescaling by exp(m_s - m) / L), contracts
 // phi(q) with the slice's S_all columns (o_bar) and, in slice 0, with z_all
 // (the normaliser D), and writes o = o_sparse + g_h (o_bar - o_tilde).
-// Every global load is issued before the first wait (slots in batches of 32).
+// Item = (kind, head, channel quartet) of the slice; the slots are split over
+// SG thread groups whose float4 sums meet in LDS.  Every global load is
+// issued before the first wait.
 template <bool BF16, int R, int D>
 __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
-  constexpr int CS = 32;               // channels per workgroup
-  constexpr int RG = kThreads / CS;    // row groups of the S contraction
-  constexpr int RPG = D / RG;          // rows per group
-  constexpr int NP = (2 * R * CS + kThreads - 1) / kThreads;  // (kind, head, channel) items per thread
-  constexpr int SB = 32;               // slots per load batch
+  constexpr int CS = 32;                 // channels per workgroup
+  constexpr int RG = kThreads / CS;      // row groups of the S contraction
+  constexpr int RPG = D / RG;            // rows per group
+  constexpr int NIT = 2 * R * (CS / 4);  // float4 items
+  constexpr int SG = kThreads / NIT;     // slot groups
+  constexpr int SPT = 16;                // slots per thread per load batch
+  constexpr int HPW = (R + 3) / 4;       // heads per wavefront (header pass)
+  constexpr int SPL = 4;                 // slots per lane in the header pass (top_k <= 256)
+  constexpr int QPT = (R * D + kThreads - 1) / kThreads;
   __shared__ float fq[R][D];
-  __shared__ float wsl[R][256];        // exp(m_s - m) / L per head and slot (0 for unused slots)
-  __shared__ float obr[RG][R][CS];
-  __shared__ float osp[R][CS];
-  __shared__ float s_sw[R], s_dz[R];
+  __shared__ float wsl[R][256];          // exp(m_s - m) / L per head and slot (0 for unused slots)
   __shared__ int valid[256];
+  __shared__ float obr[RG][R][CS];
+  __shared__ float4 red4[SG][NIT];
+  __shared__ float s_sw[R], s_dz[R];
   const int cc = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int nb = n_blocks(a, b);
   const bool covers_all = nb <= a.top_k;
-  const int32_t* selp = a.sel_in ? a.sel_in : a.sel;
-  const int32_t* srow = selp + ((size_t)b * a.G + g) * a.top_k;
-  const int rec = 2 * D + kPartHdr;
-  const float* P0 = a.part + ((size_t)b * a.H + g * R) * a.top_k * (size_t)rec;
-  const int c0 = cc * CS;
   const int top_k = a.top_k;
+  const int32_t* srow = (a.sel_in ? a.sel_in : a.sel) + ((size_t)b * a.G + g) * top_k;
+  const int rec = 2 * D + kPartHdr;
+  const float* P0 = a.part + ((size_t)b * a.H + g * R) * top_k * (size_t)rec;
+  const int c0 = cc * CS;
   const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
-  // ---- loads: S slice, queries, z, slot headers, first batch of slot data
+  // ---- loads
   const int sc = threadIdx.x % CS, rg = threadIdx.x / CS;
   const float* S = a.s_all + ((size_t)b * a.G + g) * D * (size_t)D + (size_t)(rg * RPG) * D + c0 + sc;
   float sv[RPG];
 #pragma unroll
   for (int x = 0; x < RPG; ++x) sv[x] = S[(size_t)x * D];
-  float qv[(R * D + kThreads - 1) / kThreads];
+  float qv[QPT];
 #pragma unroll
-  for (int k = 0; k < (R * D + kThreads - 1) / kThreads; ++k) {
+  for (int k = 0; k < QPT; ++k) {
     const int i = threadIdx.x + k * kThreads;
     qv[k] = i < R * D ? load_elem<BF16>(a.q, ((size_t)b * a.H + g * R) * D + i) : 0.f;
   }
   float zv[(D + 63) / 64];
 #pragma unroll
   for (int k = 0; k < (D + 63) / 64; ++k) zv[k] = a.z_all[((size_t)b * a.G + g) * D + lane + 64 * k];
-  // headers: wavefront w handles heads w, w + 4; lane = slot (strided by 64)
-  constexpr int HPW = (R + 3) / 4;
-  constexpr int SPL = 4;  // slots per lane: top_k <= 256
-  float hm[HPW][SPL], hl[HPW][SPL], hs[HPW][SPL];
   int vs[SPL];
 #pragma unroll
   for (int u = 0; u < SPL; ++u) {
     const int s = lane + 64 * u;
     vs[u] = s < top_k ? srow[s] : -1;
   }
+  float hm[HPW][SPL], hl[HPW][SPL], hs[HPW][SPL];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     const int h = w + 4 * hh;
@@ -833,20 +880,19 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
       }
     }
   }
-  // slot data of this thread's items, first batch
-  float dv[NP][SB];
+  const int it = threadIdx.x % NIT, sg = threadIdx.x / NIT;
+  const int kind = it / (R * CS / 4), ih = (it / (CS / 4)) % R, c4 = it % (CS / 4);
+  const float* PD = P0 + (size_t)ih * top_k * rec + kPartHdr + (kind ? D : 0) + c0 + 4 * c4;
+  float4 dv[SPT];
 #pragma unroll
-  for (int k = 0; k < NP; ++k) {
-    const int it = threadIdx.x + k * kThreads;
-    const int kind = it / (R * CS), h = (it / CS) % R, c = it % CS;
-    const float* P = P0 + (size_t)h * top_k * rec + kPartHdr + (kind ? D : 0) + c0 + c;
-#pragma unroll
-    for (int u = 0; u < SB; ++u) dv[k][u] = (it < 2 * R * CS && u < top_k) ? P[(size_t)u * rec] : 0.f;
+  for (int u = 0; u < SPT; ++u) {
+    const int s = sg + SG * u;
+    dv[u] = s < top_k ? *reinterpret_cast<const float4*>(PD + (size_t)s * rec) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // ---- phi(q), softmax merge weights, phi(q).z
+  // ---- phi(q), validity, merge weights and phi(q).z per head
 #pragma unroll
-  for (int k = 0; k < (R * D + kThreads - 1) / kThreads; ++k) {
+  for (int k = 0; k < QPT; ++k) {
     const int i = threadIdx.x + k * kThreads;
     if (i < R * D) fq[i / D][i % D] = phi_f(qv[k]);
   }
@@ -886,15 +932,17 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
       if (s < top_k) wsl[h][s] = e[u] * inv_l;
     }
     float dz = 0.f;
+    if (cc == 0) {
 #pragma unroll
-    for (int k = 0; k < (D + 63) / 64; ++k) dz = fmaf(fq[h][lane + 64 * k], zv[k], dz);
-    dz = wave_sum(dz);
+      for (int k = 0; k < (D + 63) / 64; ++k) dz = fmaf(fq[h][lane + 64 * k], zv[k], dz);
+      dz = wave_sum(dz);
+    }
     if (lane == 0) {
       s_sw[h] = sw;
       s_dz[h] = dz;
     }
   }
-  // ---- o_bar partial sums over this thread's rows
+  // o_bar partial sums over this thread's rows
   {
     float ob[R];
 #pragma unroll
@@ -908,65 +956,61 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
     for (int h = 0; h < R; ++h) obr[rg][h][sc] = ob[h];
   }
   __syncthreads();
-  // ---- merge of the slot partials: item = (kind, head, channel)
-  float acc[NP];
+  // ---- this thread's slots of its item
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int u0 = 0; sg + SG * u0 < top_k; u0 += SPT) {
+    if (u0 > 0) {
 #pragma unroll
-  for (int k = 0; k < NP; ++k) acc[k] = 0.f;
-  for (int s0 = 0; s0 < top_k; s0 += SB) {
-    if (s0 > 0) {
-#pragma unroll
-      for (int k = 0; k < NP; ++k) {
-        const int it = threadIdx.x + k * kThreads;
-        const int kind = it / (R * CS), h = (it / CS) % R, c = it % CS;
-        const float* P = P0 + (size_t)h * top_k * rec + kPartHdr + (kind ? D : 0) + c0 + c;
-#pragma unroll
-        for (int u = 0; u < SB; ++u)
-          dv[k][u] = (it < 2 * R * CS && s0 + u < top_k) ? P[(size_t)(s0 + u) * rec] : 0.f;
+      for (int u = 0; u < SPT; ++u) {
+        const int s = sg + SG * (u0 + u);
+        dv[u] = s < top_k ? *reinterpret_cast<const float4*>(PD + (size_t)s * rec) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
 #pragma unroll
-    for (int k = 0; k < NP; ++k) {
-      const int it = threadIdx.x + k * kThreads;
-      if (it >= 2 * R * CS) continue;
-      const int kind = it / (R * CS), h = (it / CS) % R;
-#pragma unroll
-      for (int u = 0; u < SB; ++u) {
-        const int s = s0 + u;
-        if (s >= top_k) break;
-        // wsl is 0 for unused slots
-        if (kind == 0) {
-          acc[k] = fmaf(wsl[h][s], dv[k][u], acc[k]);
-        } else if (valid[s]) {
-          acc[k] += dv[k][u];
-        }
-      }
+    for (int u = 0; u < SPT; ++u) {
+      const int s = sg + SG * (u0 + u);
+      if (s >= top_k || !valid[s]) continue;  // unused slot: its record holds stale data
+      const float wt = kind == 0 ? wsl[ih][s] : 1.f;
+      acc.x = fmaf(wt, dv[u].x, acc.x);
+      acc.y = fmaf(wt, dv[u].y, acc.y);
+      acc.z = fmaf(wt, dv[u].z, acc.z);
+      acc.w = fmaf(wt, dv[u].w, acc.w);
     }
   }
-#pragma unroll
-  for (int k = 0; k < NP; ++k) {
-    const int it = threadIdx.x + k * kThreads;
-    if (it >= 2 * R * CS) continue;
-    const int kind = it / (R * CS), h = (it / CS) % R, c = it % CS;
-    if (kind == 0) {
-      osp[h][c] = acc[k];
-    } else {
-      float obar = 0.f;
-#pragma unroll
-      for (int q = 0; q < RG; ++q) obar += obr[q][h][c];
-      obr[0][h][c] = covers_all ? 0.f : obar - acc[k];  // o_rla of this slice
-    }
-  }
+  red4[sg][it] = acc;
   __syncthreads();
-  for (int it = threadIdx.x; it < R * CS; it += kThreads) {
-    const int h = it / CS, c = it % CS;
-    const size_t oi = ((size_t)b * a.H + g * R + h) * D + c0 + c;
-    const float orla = obr[0][h][c];
-    a.out[oi] = osp[h][c] + a.gate[g * R + h] * orla;
-    if (a.o_sparse_out) a.o_sparse_out[oi] = osp[h][c];
-    if (a.o_rla_out) a.o_rla_out[oi] = orla;
+  // ---- finalise: thread = (head, channel quartet), both kinds from LDS
+  if ((int)threadIdx.x < R * CS / 4) {
+    const int h = threadIdx.x / (CS / 4), q4 = threadIdx.x % (CS / 4);
+    float4 os = make_float4(0.f, 0.f, 0.f, 0.f), ot = os;
+#pragma unroll
+    for (int k = 0; k < SG; ++k) {
+      const float4 x0 = red4[k][h * (CS / 4) + q4];
+      const float4 x1 = red4[k][R * CS / 4 + h * (CS / 4) + q4];
+      os.x += x0.x; os.y += x0.y; os.z += x0.z; os.w += x0.w;
+      ot.x += x1.x; ot.y += x1.y; ot.z += x1.z; ot.w += x1.w;
+    }
+    float orl[4] = {0.f, 0.f, 0.f, 0.f};
+    if (!covers_all) {
+      const float otv[4] = {ot.x, ot.y, ot.z, ot.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float obar = 0.f;
+#pragma unroll
+        for (int q = 0; q < RG; ++q) obar += obr[q][h][4 * q4 + e];
+        orl[e] = obar - otv[e];
+      }
+    }
+    const size_t oi = ((size_t)b * a.H + g * R + h) * D + c0 + 4 * q4;
+    const float gh = a.gate[g * R + h];
+    *reinterpret_cast<float4*>(a.out + oi) =
+        make_float4(fmaf(gh, orl[0], os.x), fmaf(gh, orl[1], os.y), fmaf(gh, orl[2], os.z), fmaf(gh, orl[3], os.w));
+    if (a.o_sparse_out) *reinterpret_cast<float4*>(a.o_sparse_out + oi) = os;
+    if (a.o_rla_out) *reinterpret_cast<float4*>(a.o_rla_out + oi) = make_float4(orl[0], orl[1], orl[2], orl[3]);
   }
-  if (cc == 0 && threadIdx.x < a.top_k && a.sel_out) a.sel_out[((size_t)b * a.G + g) * a.top_k + threadIdx.x] = srow[threadIdx.x];
-  if (cc == 0 && threadIdx.x < R && a.d_rla_out) {
+  if (cc == 0 && (int)threadIdx.x < top_k && a.sel_out)
+    a.sel_out[((size_t)b * a.G + g) * top_k + threadIdx.x] = srow[threadIdx.x];
+  if (cc == 0 && (int)threadIdx.x < R && a.d_rla_out) {
     const int h = threadIdx.x;
     a.d_rla_out[(size_t)b * a.H + g * R + h] = covers_all ? 0.f : s_dz[h] - s_sw[h];
   }
