@@ -30,7 +30,7 @@ SPLA_F32, SPLA_BF16 = 0, 1
 
 EXPORTED = [
     "spla_create", "spla_destroy", "spla_workspace_bytes", "spla_stats_floats", "spla_bind",
-    "spla_append_kv", "spla_decode", "spla_get_lens", "spla_status_str", "spla_abi_version",
+    "spla_append_kv", "spla_decode", "spla_decode_step", "spla_get_lens", "spla_status_str", "spla_abi_version",
 ]
 
 
@@ -88,6 +88,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spla_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.POINTER(SplaDecodeAux), ctypes.c_void_p]
     lib.spla_decode.restype = ctypes.c_int
+    lib.spla_decode_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(SplaDecodeAux),
+                                     ctypes.c_void_p]
+    lib.spla_decode_step.restype = ctypes.c_int
     lib.spla_get_lens.argtypes = [ctypes.c_void_p, I32P]
     lib.spla_get_lens.restype = ctypes.c_int
     lib.spla_status_str.argtypes = [ctypes.c_int]
@@ -162,6 +166,13 @@ class SplaHandle:
                                     ctypes.c_void_p(out_ptr), ctypes.byref(aux) if aux is not None else None,
                                     ctypes.c_void_p(stream))
 
+    def decode_step_raw(self, k_ptr: int, v_ptr: int, q_ptr: int, gate_ptr: int, out_ptr: int,
+                        aux: Optional[SplaDecodeAux], stream: int) -> int:
+        return self.lib.spla_decode_step(self.h, ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
+                                         ctypes.c_void_p(q_ptr), ctypes.c_void_p(gate_ptr),
+                                         ctypes.c_void_p(out_ptr), ctypes.byref(aux) if aux is not None else None,
+                                         ctypes.c_void_p(stream))
+
 
 class SplaLayer:
     """One SPLA attention layer's decode state in torch-allocated device memory.
@@ -224,22 +235,18 @@ class SplaLayer:
 
     def append(self, seq_ids: Sequence[int], n_new: Sequence[int], k_new, v_new) -> None:
         """k_new, v_new: device tensors [sum n_new][G][d] of the layer's dtype."""
-        t = self.torch
-        for x in (k_new, v_new):
-            if x.dtype != self.dtype or x.device != self.device or not x.is_contiguous():
-                raise ValueError("k_new / v_new must be contiguous device tensors of the layer dtype")
-            if x.dim() != 3 or x.shape[1:] != (self.G, self.d) or x.shape[0] < sum(int(n) for n in n_new):
-                raise ValueError(f"k_new / v_new must be [sum n][{self.G}][{self.d}]")
-        del t
+        self._check_kv(k_new, v_new, sum(int(n) for n in n_new))
         st = self.handle.append_raw(list(seq_ids), list(n_new), k_new.data_ptr(), v_new.data_ptr(), self._stream())
         _check(st, "spla_append_kv")
 
-    def decode(self, q, gate, out=None, aux: Optional[Dict[str, object]] = None, kernel_events=None):
-        """q: device [B][H][d] layer dtype; gate: device [H] float32.  aux may
-        hold tensors under 'sel_idx', 'lg', 'o_sparse', 'o_rla', 'd_rla'
-        (outputs) and 'sel_in' (input).  kernel_events: optional ctypes array
-        of hipEvent_t handles (2 per launched kernel, see include/spla.h).
-        Returns out [B][H][d] float32."""
+    def _check_kv(self, k_new, v_new, rows: int) -> None:
+        for x in (k_new, v_new):
+            if x.dtype != self.dtype or x.device != self.device or not x.is_contiguous():
+                raise ValueError("k_new / v_new must be contiguous device tensors of the layer dtype")
+            if x.dim() != 3 or x.shape[1:] != (self.G, self.d) or x.shape[0] < rows:
+                raise ValueError(f"k_new / v_new must be [rows][{self.G}][{self.d}]")
+
+    def _decode_inputs(self, q, gate, out, aux, kernel_events):
         t = self.torch
         if q.dtype != self.dtype or tuple(q.shape) != (self.B, self.H, self.d) or not q.is_contiguous():
             raise ValueError("q must be a contiguous [B][H][d] tensor of the layer dtype")
@@ -267,6 +274,26 @@ class SplaLayer:
                 n_ev = len(kernel_events) // 2
             ax = SplaDecodeAux(ptrs.get("sel_idx"), ptrs.get("lg"), ptrs.get("o_sparse"), ptrs.get("o_rla"),
                                ptrs.get("d_rla"), ptrs.get("sel_in"), ev_ptr, n_ev)
+        return out, ax
+
+    def decode_step(self, k_new, v_new, q, gate, out=None, aux: Optional[Dict[str, object]] = None,
+                    kernel_events=None):
+        """append one token to every sequence (k_new, v_new: device [B][G][d])
+        and decode (spla_decode_step).  Same results as append + decode."""
+        self._check_kv(k_new, v_new, self.B)
+        out, ax = self._decode_inputs(q, gate, out, aux, kernel_events)
+        st = self.handle.decode_step_raw(k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), gate.data_ptr(),
+                                         out.data_ptr(), ax, self._stream())
+        _check(st, "spla_decode_step")
+        return out
+
+    def decode(self, q, gate, out=None, aux: Optional[Dict[str, object]] = None, kernel_events=None):
+        """q: device [B][H][d] layer dtype; gate: device [H] float32.  aux may
+        hold tensors under 'sel_idx', 'lg', 'o_sparse', 'o_rla', 'd_rla'
+        (outputs) and 'sel_in' (input).  kernel_events: optional ctypes array
+        of hipEvent_t handles (2 per launched kernel, see include/spla.h).
+        Returns out [B][H][d] float32."""
+        out, ax = self._decode_inputs(q, gate, out, aux, kernel_events)
         st = self.handle.decode_raw(q.data_ptr(), gate.data_ptr(), out.data_ptr(), ax, self._stream())
         _check(st, "spla_decode")
         return out

@@ -1,4 +1,4 @@
-// spla_append_kv kernels: page write, global linear-attention state update and
+// spla_append_kv kernel: page write, global linear-attention state update and
 // block statistics of completed blocks (SPLA Technical Summary 2.1 and 2.2).
 //
 // One launch covers up to kMaxAppendEntries (sequence, rows) entries.  The
@@ -11,70 +11,11 @@
 // The three kinds touch disjoint memory: statistics read tokens older than the
 // append from the pages (written by earlier launches) and the new tokens from
 // k_new, never the page rows this launch writes.
-#include "spla_common.h"
+#include "append_items.h"
 
 namespace spla {
 
 namespace {
-
-// ---------------------------------------------------------------- state
-// 256 threads cover rows_per_item = 1024/d rows of S, d/4 float4 columns each.
-template <bool BF16>
-__device__ void state_update(const AppendArgs& a, int item) {
-  const int d = a.d, G = a.G;
-  const int rows = 1024 / d;
-  const int chunks = d / rows;
-  const int e = item / (G * chunks);
-  const int rem = item - e * G * chunks;
-  const int g = rem / chunks;
-  const int rc = rem - g * chunks;
-  const AppendEntry E = a.e[e];
-  if (E.n <= 0) return;
-  const int c4n = d / 4;
-  const int x = rc * rows + threadIdx.x / c4n;   // row of S (key channel)
-  const int c4 = threadIdx.x % c4n;              // column quartet (value channels)
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float zacc = 0.f;
-  const size_t row_stride = (size_t)G * d;
-  size_t base = ((size_t)E.row * G + g) * d;
-  int t = 0;
-  for (; t + 4 <= E.n; t += 4) {
-    float f[4];
-    float4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      f[u] = phi_f(load_elem<BF16>(a.k_new, base + u * row_stride + x));
-      v[u] = load4<BF16>(a.v_new, base + u * row_stride + c4 * 4);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc.x = fmaf(f[u], v[u].x, acc.x);
-      acc.y = fmaf(f[u], v[u].y, acc.y);
-      acc.z = fmaf(f[u], v[u].z, acc.z);
-      acc.w = fmaf(f[u], v[u].w, acc.w);
-      zacc += f[u];
-    }
-    base += 4 * row_stride;
-  }
-  for (; t < E.n; ++t) {
-    float f = phi_f(load_elem<BF16>(a.k_new, base + x));
-    float4 v = load4<BF16>(a.v_new, base + c4 * 4);
-    acc.x = fmaf(f, v.x, acc.x);
-    acc.y = fmaf(f, v.y, acc.y);
-    acc.z = fmaf(f, v.z, acc.z);
-    acc.w = fmaf(f, v.w, acc.w);
-    zacc += f;
-    base += row_stride;
-  }
-  float4* S = reinterpret_cast<float4*>(a.s_all + (((size_t)E.seq * G + g) * d + x) * d) + c4;
-  float4 s = *S;
-  s.x += acc.x;
-  s.y += acc.y;
-  s.z += acc.z;
-  s.w += acc.w;
-  *S = s;
-  if (c4 == 0) a.z_all[((size_t)E.seq * G + g) * d + x] += zacc;
-}
 
 __device__ __forceinline__ int find_entry(const int32_t* prefix, int n, int item) {
   int e = 0;
@@ -82,107 +23,29 @@ __device__ __forceinline__ int find_entry(const int32_t* prefix, int n, int item
   return e;
 }
 
-// ---------------------------------------------------------------- pages
-template <bool BF16>
-__device__ void page_copy(const AppendArgs& a, int item) {
-  const int e = find_entry(a.page_prefix, a.n_entries, item);
-  const AppendEntry E = a.e[e];
-  const int tile = item - a.page_prefix[e];
-  const int i0 = tile * 64;
-  const int ntok = min(64, E.n - i0);
-  const int es = BF16 ? 2 : 4;
-  const int vec_per_row = a.d * es / 16;
-  const int per_tok = a.G * vec_per_row;
-  const int total = ntok * per_tok;
-  const uint4* kn = reinterpret_cast<const uint4*>(a.k_new);
-  const uint4* vn = reinterpret_cast<const uint4*>(a.v_new);
-  uint4* kp = reinterpret_cast<uint4*>(a.k_pages);
-  uint4* vp = reinterpret_cast<uint4*>(a.v_pages);
-  for (int idx = threadIdx.x; idx < total; idx += kThreads) {
-    const int i = idx / per_tok;
-    const int rem = idx - i * per_tok;
-    const int g = rem / vec_per_row;
-    const int v = rem - g * vec_per_row;
-    const int p = E.t0 + i0 + i;
-    const int j = p / a.bk;
-    const int page = a.block_table[(size_t)E.seq * a.max_blocks + j];
-    if (page < 0 || page >= a.num_pages) {
-      atomicOr(a.err, kErrPage);
-      continue;
-    }
-    const size_t src = (((size_t)(E.row + i0 + i)) * a.G + g) * vec_per_row + v;
-    const size_t dst = (((size_t)page * a.G + g) * a.bk + (p % a.bk)) * vec_per_row + v;
-    kp[dst] = kn[src];
-    vp[dst] = vn[src];
-  }
-}
-
-// ---------------------------------------------------------------- stats
-template <bool BF16>
-__device__ void block_statistics(const AppendArgs& a, int item) {
-  __shared__ float red[kThreads];
-  const int e = find_entry(a.stat_prefix, a.n_entries, item);
-  const AppendEntry E = a.e[e];
-  const int local = item - a.stat_prefix[e];
-  const int g = local % a.G;
-  const int j = E.t0 / a.bk + local / a.G;
-  const int d = a.d, bk = a.bk;
-  const int groups = kThreads / d;
-  const int c = threadIdx.x % d;
-  const int grp = threadIdx.x / d;
-  const int tpg = bk / groups;
-  const int page = a.block_table[(size_t)E.seq * a.max_blocks + j];
-  const bool page_ok = page >= 0 && page < a.num_pages;
-  if (!page_ok && j * bk < E.t0) {
-    if (threadIdx.x == 0) atomicOr(a.err, kErrPage);
-    return;
-  }
-  auto key = [&](int p) -> float {
-    if (p < E.t0) {
-      return load_elem<BF16>(a.k_pages, (((size_t)page * a.G + g) * bk + (p % bk)) * d + c);
-    }
-    return load_elem<BF16>(a.k_new, ((size_t)(E.row + p - E.t0) * a.G + g) * d + c);
-  };
-  const int p0 = j * bk + grp * tpg;
-  float s = 0.f;
-  for (int i = 0; i < tpg; ++i) s += key(p0 + i);
-  red[threadIdx.x] = s;
-  __syncthreads();
-  float tot = 0.f;
-  for (int q = 0; q < groups; ++q) tot += red[q * d + c];
-  const float mean = tot / (float)bk;
-  __syncthreads();
-  float s2 = 0.f;
-  for (int i = 0; i < tpg; ++i) {
-    const float dv = key(p0 + i) - mean;
-    s2 = fmaf(dv, dv, s2);
-  }
-  red[threadIdx.x] = s2;
-  __syncthreads();
-  if (grp == 0) {
-    float t2 = 0.f;
-    for (int q = 0; q < groups; ++q) t2 += red[q * d + c];
-    const size_t idx = ((((size_t)E.seq * a.G + g) * a.n_tiles + j / kTile) * (d / 4) + c / 4) * (kTile * 4) +
-                       (j % kTile) * 4 + (c % 4);
-    a.blk_mean[idx] = mean;
-    a.blk_var[idx] = t2 / (float)bk;
-  }
-}
-
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_append(const AppendArgs a) {
   int item = blockIdx.x;
+  const int chunks = a.st.d / (1024 / a.st.d);
   if (item < a.s_items) {
-    state_update<BF16>(a, item);
+    const int per = a.st.G * chunks;
+    const int e = item / per;
+    const int rem = item - e * per;
+    append_state_rows<BF16>(a.st, a.e[e], rem / chunks, rem % chunks);
     return;
   }
   item -= a.s_items;
   if (item < a.page_items) {
-    page_copy<BF16>(a, item);
+    const int e = find_entry(a.page_prefix, a.n_entries, item);
+    append_page_rows<BF16>(a.st, a.e[e], (item - a.page_prefix[e]) * 64);
     return;
   }
   item -= a.page_items;
-  if (item < a.stat_items) block_statistics<BF16>(a, item);
+  if (item < a.stat_items) {
+    const int e = find_entry(a.stat_prefix, a.n_entries, item);
+    const int local = item - a.stat_prefix[e];
+    append_block_stats<BF16>(a.st, a.e[e], a.e[e].t0 / a.st.bk + local / a.st.G, local % a.st.G);
+  }
 }
 
 }  // namespace

@@ -12,7 +12,7 @@
 //              (Technical Summary 2.2: o_tilde from the blocks already loaded)
 //   k_combine  merge of the partials, o_bar = phi(q)^T S_all, o_rla = o_bar -
 //              o_tilde, D = phi(q).z_all - sum w, o = o_sparse + g_h o_rla
-#include "spla_common.h"
+#include "append_items.h"
 
 namespace spla {
 
@@ -25,14 +25,13 @@ __device__ __forceinline__ int n_blocks(const DecodeArgs& a, int b) { return (a.
 // wavefronts split the channels and meet in LDS.  Every wavefront issues its
 // query loads and then all of its statistics loads before the first wait.
 template <bool BF16, int R, int D>
-__global__ __launch_bounds__(kThreads) void k_score(const DecodeArgs a) {
+__device__ void score_tile(const DecodeArgs& a, const int t, const int g, const int b) {
   constexpr int NC4 = D / 16;  // channel quartets per wavefront
   constexpr int CW = D / 4;    // channels per wavefront
   constexpr int QPL = (R * CW + 63) / 64;  // query elements per lane
   __shared__ float4 qs[4][R][CW / 4];
   __shared__ float4 q2s[4][R][CW / 4];
   __shared__ float red[4][2 * R][kTile];
-  const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int nb = n_blocks(a, b);
   if (nb <= a.top_k) return;  // every block is selected, nothing to rank
   const int j0 = t * kTile;
@@ -40,15 +39,14 @@ __global__ __launch_bounds__(kThreads) void k_score(const DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int lane = threadIdx.x % 64;
   // queries of this wavefront's channel quarter
+  // (loads are unconditional, from clamped in-range addresses, and masked
+  // afterwards: a load under a branch makes the compiler wait for it there)
   float qv[QPL];
 #pragma unroll
   for (int i = 0; i < QPL; ++i) {
-    const int e = lane + 64 * i;
-    qv[i] = 0.f;
-    if (e < R * CW) {
-      const int h = e / CW, c = e - h * CW;
-      qv[i] = load_elem<BF16>(a.q, ((size_t)b * a.H + g * R + h) * D + w * CW + c);
-    }
+    const int e = min(lane + 64 * i, R * CW - 1);
+    const int h = e / CW, c = e - h * CW;
+    qv[i] = load_elem<BF16>(a.q, ((size_t)b * a.H + g * R + h) * D + w * CW + c);
   }
   // statistics of the tile: 64 blocks x this wavefront's channels
   const float4* mean4 = reinterpret_cast<const float4*>(a.blk_mean);
@@ -130,6 +128,51 @@ __global__ __launch_bounds__(kThreads) void k_score(const DecodeArgs a) {
   }
 }
 
+template <bool BF16, int R, int D>
+__global__ __launch_bounds__(kThreads) void k_score(const DecodeArgs a) {
+  score_tile<BF16, R, D>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Fused decode step, first launch: the scorer's tiles (flat, first) and the
+// append of this step's token for every sequence.  The two are independent:
+// the scorer reads statistics of candidate blocks 1..nb-2 only, all completed
+// by earlier appends, and neither pages nor S_all.
+template <bool BF16, int R, int D>
+__global__ __launch_bounds__(kThreads) void k_step_score(const StepArgs a) {
+  const DecodeArgs& dc = a.dec;
+  const int nsc = dc.score_tiles * dc.G * dc.B;
+  int item = blockIdx.x;
+  if (item < nsc) {
+    const int t = item % dc.score_tiles;
+    const int g = (item / dc.score_tiles) % dc.G;
+    const int b = item / (dc.score_tiles * dc.G);
+    score_tile<BF16, R, D>(dc, t, g, b);
+    return;
+  }
+  item -= nsc;
+  const int chunks = D / (1024 / D);
+  if (item < a.s_items) {
+    const int per = dc.G * chunks;
+    const int b = item / per;
+    const int rem = item - b * per;
+    const AppendEntry E{b, 1, dc.lens[b] - 1, b};
+    append_state_rows<BF16>(a.st, E, rem / chunks, rem % chunks);
+    return;
+  }
+  item -= a.s_items;
+  if (item < dc.B) {
+    const AppendEntry E{item, 1, dc.lens[item] - 1, item};
+    append_page_rows<BF16>(a.st, E, 0);
+    return;
+  }
+  item -= dc.B;
+  if (item < a.n_stat * dc.G) {
+    const int b = a.stat_seq[item / dc.G];
+    const AppendEntry E{b, 1, dc.lens[b] - 1, b};
+    append_block_stats<BF16>(a.st, E, dc.lens[b] / dc.bk - 1, item % dc.G);
+  }
+}
+
 // ============================================================== select
 constexpr int kSelMax = kMaxBlocksPerSeq - 2;  // candidates per (b, g) the selector handles
 constexpr int kSelLevels = 12;   // bucket refinement levels
@@ -185,9 +228,12 @@ __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
   __shared__ float s_mn[4], s_mx[4];
   __shared__ int s_cnt[4];
   __shared__ int s_bt, s_above, s_n, s_nm;
-  __shared__ float mkey[kSelRank];
-  __shared__ int midx[kSelRank];
-  __shared__ int slist[256];
+  // lists padded with sentinels so the rank counts read them four at a time
+  __shared__ __attribute__((aligned(16))) float mkey[kSelRank];
+  __shared__ __attribute__((aligned(16))) int midx[kSelRank];
+  __shared__ __attribute__((aligned(16))) int slist[256];
+  __shared__ int spage[256];      // page of slist[i]
+  __shared__ int mpage[kSelRank];  // page of midx[i]
   const int g = blockIdx.x, b = blockIdx.y;
   const int nb = n_blocks(a, b);
   int32_t* out = a.sel + ((size_t)b * a.G + g) * a.top_k;
@@ -206,12 +252,17 @@ __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
   const int kp = a.top_k - 2;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const float* row = a.lg + ((size_t)b * a.G + g) * (size_t)(a.n_tiles * kTile) + 1;  // row[i] = LG(i + 1)
+  // scores and page ids of this thread's candidates (the pages ride along so
+  // the output needs no dependent lookup), plus the sink's and current's pages
   float x[KPT];
+  int pg[KPT];
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
-    const int i = threadIdx.x + u * kThreads;
-    x[u] = i < nc ? row[i] : 0.f;
+    const int i = min((int)threadIdx.x + u * kThreads, nc - 1);  // clamped, masked by memb below
+    x[u] = row[i];
+    pg[u] = btab[i + 1];
   }
+  const int pg_sink = btab[0], pg_cur = btab[nb - 1];
   uint64_t memb = 0, above = 0;  // bit u: key u still in the threshold bucket / already taken
 #pragma unroll
   for (int u = 0; u < KPT; ++u)
@@ -220,6 +271,9 @@ __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
     s_n = 0;
     s_nm = 0;
   }
+  mkey[threadIdx.x] = -INFINITY;
+  midx[threadIdx.x] = 0x7fffffff;
+  slist[threadIdx.x] = 0x7fffffff;
   int need = kp;
   bool equal_mode = false;
   for (int lev = 0;; ++lev) {
@@ -296,8 +350,12 @@ __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
     int slot[KPT];
     wave_append<KPT>(above, &s_n, slot);
 #pragma unroll
-    for (int u = 0; u < KPT; ++u)
-      if (slot[u] >= 0) slist[slot[u]] = threadIdx.x + u * kThreads;
+    for (int u = 0; u < KPT; ++u) {
+      if (slot[u] >= 0) {
+        slist[slot[u]] = threadIdx.x + u * kThreads;
+        spage[slot[u]] = pg[u];
+      }
+    }
   }
   if (!equal_mode) {
     // the final bucket (<= kSelRank candidates): exact rank by (score desc, id asc)
@@ -309,26 +367,36 @@ __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
         if (slot[u] >= 0) {
           mkey[slot[u]] = x[u];
           midx[slot[u]] = threadIdx.x + u * kThreads;
+          mpage[slot[u]] = pg[u];
         }
       }
     }
     __syncthreads();
     const int nm = s_nm;
     bool take = false;
-    int my = 0;
+    int my = 0, mypg = 0;
     if ((int)threadIdx.x < nm) {
       const float xv = mkey[threadIdx.x];
       my = midx[threadIdx.x];
+      mypg = mpage[threadIdx.x];
       int rank = 0;
-      for (int v = 0; v < nm; ++v) {
-        const float y = mkey[v];
-        rank += (y > xv) || (y == xv && midx[v] < my);
+#pragma unroll 4
+      for (int v = 0; v < nm; v += 4) {
+        const float4 y = *reinterpret_cast<const float4*>(&mkey[v]);
+        const int4 iy = *reinterpret_cast<const int4*>(&midx[v]);
+        rank += (y.x > xv) || (y.x == xv && iy.x < my);
+        rank += (y.y > xv) || (y.y == xv && iy.y < my);
+        rank += (y.z > xv) || (y.z == xv && iy.z < my);
+        rank += (y.w > xv) || (y.w == xv && iy.w < my);
       }
       take = rank < need;
     }
     int slot1[1];
     wave_append<1>(take ? 1ull : 0ull, &s_n, slot1);
-    if (slot1[0] >= 0) slist[slot1[0]] = my;
+    if (slot1[0] >= 0) {
+      slist[slot1[0]] = my;
+      spage[slot1[0]] = mypg;
+    }
   } else {
     // equal scores: the `need` smallest ids among the members; find the id
     // bound by bisection on counts
@@ -352,26 +420,34 @@ __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
     int slot[KPT];
     wave_append<KPT>(low, &s_n, slot);
 #pragma unroll
-    for (int u = 0; u < KPT; ++u)
-      if (slot[u] >= 0) slist[slot[u]] = threadIdx.x + u * kThreads;
+    for (int u = 0; u < KPT; ++u) {
+      if (slot[u] >= 0) {
+        slist[slot[u]] = threadIdx.x + u * kThreads;
+        spage[slot[u]] = pg[u];
+      }
+    }
   }
   __syncthreads();
   // ascending order by a rank count over the kp chosen ids
   if ((int)threadIdx.x < kp) {
     const int v = slist[threadIdx.x];
     int pos = 0;
-    for (int u = 0; u < kp; ++u) pos += slist[u] < v;
+#pragma unroll 4
+    for (int u = 0; u < kp; u += 4) {
+      const int4 y = *reinterpret_cast<const int4*>(&slist[u]);
+      pos += (y.x < v) + (y.y < v) + (y.z < v) + (y.w < v);
+    }
     out[1 + pos] = v + 1;
     if (out2) out2[1 + pos] = v + 1;
-    pages[1 + pos] = btab[v + 1];
+    pages[1 + pos] = spage[threadIdx.x];
   } else if ((int)threadIdx.x == kp) {
     out[0] = 0;
     if (out2) out2[0] = 0;
-    pages[0] = btab[0];
+    pages[0] = pg_sink;
   } else if ((int)threadIdx.x == kp + 1) {
     out[kp + 1] = nb - 1;
     if (out2) out2[kp + 1] = nb - 1;
-    pages[kp + 1] = btab[nb - 1];
+    pages[kp + 1] = pg_cur;
   }
 }
 
@@ -604,10 +680,10 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(const DecodeArgs a) {
   uint4 qraw[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    qraw[ks] = make_uint4(0, 0, 0, 0);
-    if (hq >= 0)
-      qraw[ks] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
-                                                 ((size_t)b * a.H + g * R + hq) * D + 32 * ks + 8 * lg4);
+    // unconditional load of a valid row; rows that hold no query are masked
+    // when the A operands are formed
+    qraw[ks] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                               ((size_t)b * a.H + g * R + max(hq, 0)) * D + 32 * ks + 8 * lg4);
   }
   const size_t srow = ((size_t)b * a.G + g) * a.top_k + slot;
   int j, page;
@@ -853,7 +929,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
     const int i = threadIdx.x + k * kThreads;
-    qv[k] = i < R * D ? load_elem<BF16>(a.q, ((size_t)b * a.H + g * R) * D + i) : 0.f;
+    qv[k] = load_elem<BF16>(a.q, ((size_t)b * a.H + g * R) * D + min(i, R * D - 1));
   }
   float zv[(D + 63) / 64];
 #pragma unroll
@@ -862,22 +938,20 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
 #pragma unroll
   for (int u = 0; u < SPL; ++u) {
     const int s = lane + 64 * u;
-    vs[u] = s < top_k ? srow[s] : -1;
+    const int v = srow[min(s, top_k - 1)];
+    vs[u] = s < top_k ? v : -1;
   }
   float hm[HPW][SPL], hl[HPW][SPL], hs[HPW][SPL];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    const int h = w + 4 * hh;
+    const int h = min(w + 4 * hh, R - 1);
 #pragma unroll
     for (int u = 0; u < SPL; ++u) {
-      const int s = lane + 64 * u;
-      hm[hh][u] = hl[hh][u] = hs[hh][u] = 0.f;
-      if (h < R && s < top_k) {
-        const float* P = P0 + ((size_t)h * top_k + s) * rec;
-        hm[hh][u] = P[0];
-        hl[hh][u] = P[1];
-        hs[hh][u] = P[2];
-      }
+      const int s = min(lane + 64 * u, top_k - 1);
+      const float* P = P0 + ((size_t)h * top_k + s) * rec;
+      hm[hh][u] = P[0];
+      hl[hh][u] = P[1];
+      hs[hh][u] = P[2];
     }
   }
   const int it = threadIdx.x % NIT, sg = threadIdx.x / NIT;
@@ -887,7 +961,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
 #pragma unroll
   for (int u = 0; u < SPT; ++u) {
     const int s = sg + SG * u;
-    dv[u] = s < top_k ? *reinterpret_cast<const float4*>(PD + (size_t)s * rec) : make_float4(0.f, 0.f, 0.f, 0.f);
+    dv[u] = *reinterpret_cast<const float4*>(PD + (size_t)min(s, top_k - 1) * rec);
   }
   __builtin_amdgcn_sched_barrier(0);
   // ---- phi(q), validity, merge weights and phi(q).z per head
@@ -963,7 +1037,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
 #pragma unroll
       for (int u = 0; u < SPT; ++u) {
         const int s = sg + SG * (u0 + u);
-        dv[u] = s < top_k ? *reinterpret_cast<const float4*>(PD + (size_t)s * rec) : make_float4(0.f, 0.f, 0.f, 0.f);
+        dv[u] = *reinterpret_cast<const float4*>(PD + (size_t)min(s, top_k - 1) * rec);
       }
     }
 #pragma unroll
@@ -1040,6 +1114,16 @@ hipError_t launch_score(const DecodeArgs& a, bool bf16, hipStream_t s) {
     SPLA_DISPATCH_RD(a.r, a.d, (k_score<true, RR, DD><<<grid, kThreads, 0, s>>>(a)))
   } else {
     SPLA_DISPATCH_RD(a.r, a.d, (k_score<false, RR, DD><<<grid, kThreads, 0, s>>>(a)))
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_step_score(const StepArgs& a, bool bf16, hipStream_t s) {
+  const int grid = a.dec.score_tiles * a.dec.G * a.dec.B + a.s_items + a.dec.B + a.n_stat * a.dec.G;
+  if (bf16) {
+    SPLA_DISPATCH_RD(a.dec.r, a.dec.d, (k_step_score<true, RR, DD><<<grid, kThreads, 0, s>>>(a)))
+  } else {
+    SPLA_DISPATCH_RD(a.dec.r, a.dec.d, (k_step_score<false, RR, DD><<<grid, kThreads, 0, s>>>(a)))
   }
   return hipGetLastError();
 }

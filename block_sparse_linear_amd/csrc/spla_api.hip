@@ -99,6 +99,65 @@ spla_status fill_decode_args(const spla_handle* h, const void* q, const float* g
   return SPLA_OK;
 }
 
+void fill_state_refs(const spla_handle* h, const void* k_new, const void* v_new, StateRefs* st) {
+  const spla_config& c = h->cfg;
+  st->k_new = k_new;
+  st->v_new = v_new;
+  st->k_pages = h->buf.k_pages;
+  st->v_pages = h->buf.v_pages;
+  st->block_table = h->buf.block_table;
+  st->blk_mean = h->buf.blk_mean;
+  st->blk_var = h->buf.blk_var;
+  st->s_all = h->buf.s_all;
+  st->z_all = h->buf.z_all;
+  st->err = ws_ptr<uint32_t>(h, 0);
+  st->G = c.n_kv_heads;
+  st->d = c.head_dim;
+  st->bk = c.block_size;
+  st->max_blocks = c.max_blocks_per_seq;
+  st->num_pages = c.num_pages;
+  st->n_tiles = h->n_tiles;
+}
+
+// validation shared by spla_decode and spla_decode_step
+spla_status check_decode_args(const spla_handle* h, const void* q, const float* gate, float* out,
+                              const spla_decode_aux* aux) {
+  if (!q || !gate || !out) return SPLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(gate) || !aligned16(out)) return SPLA_ERR_ALIGNMENT;
+  if (aux) {
+    const void* ap[] = {aux->sel_idx, aux->lg, aux->o_sparse, aux->o_rla, aux->d_rla, aux->sel_in};
+    for (const void* p : ap)
+      if (p && !aligned16(p)) return SPLA_ERR_ALIGNMENT;
+    if (aux->kernel_events && aux->n_kernel_events < 0) return SPLA_ERR_INVALID_ARG;
+  }
+  (void)h;
+  return SPLA_OK;
+}
+
+// per-kernel event recording (spla_decode_aux.kernel_events)
+struct EventMarks {
+  void* const* ev = nullptr;
+  int nev = 0, k = 0;
+  hipStream_t st = nullptr;
+  void mark(int which) {
+    if (k < nev && ev[2 * k + which]) hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * k + which]), st);
+    if (which == 1) ++k;
+  }
+};
+
+spla_status launch_decode_tail(const DecodeArgs& a, bool bf16, hipStream_t st, EventMarks& em) {
+  em.mark(0);
+  if (launch_select(a, st) != hipSuccess) return SPLA_ERR_HIP;
+  em.mark(1);
+  em.mark(0);
+  if (launch_attend(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
+  em.mark(1);
+  em.mark(0);
+  if (launch_combine(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
+  em.mark(1);
+  return SPLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -213,20 +272,7 @@ spla_status spla_append_kv(spla_handle* h, int32_t n_seqs, const int32_t* seq_id
   const int chunks = c.head_dim / (1024 / c.head_dim);
   AppendArgs a;
   memset(&a, 0, sizeof(a));
-  a.k_pages = h->buf.k_pages;
-  a.v_pages = h->buf.v_pages;
-  a.block_table = h->buf.block_table;
-  a.blk_mean = h->buf.blk_mean;
-  a.blk_var = h->buf.blk_var;
-  a.s_all = h->buf.s_all;
-  a.z_all = h->buf.z_all;
-  a.err = ws_ptr<uint32_t>(h, 0);
-  a.G = c.n_kv_heads;
-  a.d = c.head_dim;
-  a.bk = c.block_size;
-  a.max_blocks = c.max_blocks_per_seq;
-  a.num_pages = c.num_pages;
-  a.n_tiles = h->n_tiles;
+  fill_state_refs(h, k_new, v_new, &a.st);
   const size_t es = bf16 ? 2 : 4;
   const size_t row_bytes = (size_t)c.n_kv_heads * c.head_dim * es;
   int64_t row = 0;
@@ -234,8 +280,8 @@ spla_status spla_append_kv(spla_handle* h, int32_t n_seqs, const int32_t* seq_id
   // start at its first entry's row
   for (int i0 = 0; i0 < n_seqs; i0 += kMaxAppendEntries) {
     const int ne = n_seqs - i0 < kMaxAppendEntries ? n_seqs - i0 : kMaxAppendEntries;
-    a.k_new = static_cast<const char*>(k_new) + row * row_bytes;
-    a.v_new = static_cast<const char*>(v_new) + row * row_bytes;
+    a.st.k_new = static_cast<const char*>(k_new) + row * row_bytes;
+    a.st.v_new = static_cast<const char*>(v_new) + row * row_bytes;
     a.n_entries = ne;
     int lrow = 0, pp = 0, sp = 0;
     for (int e = 0; e < ne; ++e) {
@@ -268,13 +314,8 @@ spla_status spla_decode(spla_handle* h, const void* q, const float* gate, float*
                         const spla_decode_aux* aux, void* stream) {
   if (!h) return SPLA_ERR_INVALID_ARG;
   if (!h->bound) return SPLA_ERR_STATE;
-  if (!q || !gate || !out) return SPLA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(gate) || !aligned16(out)) return SPLA_ERR_ALIGNMENT;
-  if (aux) {
-    const void* ap[] = {aux->sel_idx, aux->lg, aux->o_sparse, aux->o_rla, aux->d_rla, aux->sel_in};
-    for (const void* p : ap)
-      if (p && !aligned16(p)) return SPLA_ERR_ALIGNMENT;
-  }
+  const spla_status vs = check_decode_args(h, q, gate, out, aux);
+  if (vs != SPLA_OK) return vs;
   const spla_config& c = h->cfg;
   for (int b = 0; b < c.batch; ++b)
     if (h->lens[b] <= 0) return SPLA_ERR_INVALID_ARG;
@@ -282,28 +323,61 @@ spla_status spla_decode(spla_handle* h, const void* q, const float* gate, float*
   fill_decode_args(h, q, gate, out, aux, &a);
   const bool bf16 = c.kv_dtype == SPLA_BF16;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  void* const* ev = aux ? aux->kernel_events : nullptr;
-  const int nev = (aux && ev) ? aux->n_kernel_events : 0;
-  int kidx = 0;
-  auto mark = [&](int which) {
-    if (kidx < nev && ev[2 * kidx + which]) hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * kidx + which]), st);
-    if (which == 1) ++kidx;
-  };
+  EventMarks em;
+  em.ev = aux ? aux->kernel_events : nullptr;
+  em.nev = em.ev ? aux->n_kernel_events : 0;
+  em.st = st;
   if (!a.sel_in) {
-    mark(0);
+    em.mark(0);
     if (launch_score(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
-    mark(1);
-    mark(0);
-    if (launch_select(a, st) != hipSuccess) return SPLA_ERR_HIP;
-    mark(1);
+    em.mark(1);
+    return launch_decode_tail(a, bf16, st, em);
   }
-  mark(0);
+  em.mark(0);
   if (launch_attend(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
-  mark(1);
-  mark(0);
+  em.mark(1);
+  em.mark(0);
   if (launch_combine(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
-  mark(1);
+  em.mark(1);
   return SPLA_OK;
+}
+
+spla_status spla_decode_step(spla_handle* h, const void* k_new, const void* v_new, const void* q, const float* gate,
+                             float* out, const spla_decode_aux* aux, void* stream) {
+  if (!h) return SPLA_ERR_INVALID_ARG;
+  if (!h->bound) return SPLA_ERR_STATE;
+  const spla_status vs = check_decode_args(h, q, gate, out, aux);
+  if (vs != SPLA_OK) return vs;
+  if (aux && aux->sel_in) return SPLA_ERR_INVALID_ARG;
+  if (!k_new || !v_new) return SPLA_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return SPLA_ERR_ALIGNMENT;
+  const spla_config& c = h->cfg;
+  const int64_t cap = (int64_t)c.max_blocks_per_seq * c.block_size;
+  for (int b = 0; b < c.batch; ++b)
+    if ((int64_t)h->lens[b] + 1 > cap) return SPLA_ERR_CAPACITY;
+  StepArgs a;
+  memset(&a, 0, sizeof(a));
+  // the decode part sees the lengths after the append
+  std::vector<int32_t> saved = h->lens;
+  for (int b = 0; b < c.batch; ++b) h->lens[b] += 1;
+  fill_decode_args(h, q, gate, out, aux, &a.dec);
+  fill_state_refs(h, k_new, v_new, &a.st);
+  a.s_items = c.batch * c.n_kv_heads * (c.head_dim / (1024 / c.head_dim));
+  for (int b = 0; b < c.batch; ++b)
+    if (h->lens[b] % c.block_size == 0) a.stat_seq[a.n_stat++] = (int16_t)b;
+  const bool bf16 = c.kv_dtype == SPLA_BF16;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  EventMarks em;
+  em.ev = aux ? aux->kernel_events : nullptr;
+  em.nev = em.ev ? aux->n_kernel_events : 0;
+  em.st = st;
+  em.mark(0);
+  if (launch_step_score(a, bf16, st) != hipSuccess) {
+    h->lens = saved;
+    return SPLA_ERR_HIP;
+  }
+  em.mark(1);
+  return launch_decode_tail(a.dec, bf16, st, em);
 }
 
 }  // extern "C"

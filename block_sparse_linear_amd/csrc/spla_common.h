@@ -25,27 +25,6 @@ struct AppendEntry {
   int32_t row;  // first row of this entry in k_new / v_new
 };
 
-struct AppendArgs {
-  const void* k_new;
-  const void* v_new;
-  void* k_pages;
-  void* v_pages;
-  const int32_t* block_table;
-  float* blk_mean;
-  float* blk_var;
-  float* s_all;
-  float* z_all;
-  uint32_t* err;
-  int32_t G, d, bk, max_blocks, num_pages, n_tiles;
-  int32_t n_entries;
-  int32_t s_items;     // state-update workgroups (n_entries * G * d / rows_per_item)
-  int32_t page_items;  // page-copy workgroups
-  int32_t stat_items;  // block-statistics workgroups
-  int32_t page_prefix[kMaxAppendEntries + 1];
-  int32_t stat_prefix[kMaxAppendEntries + 1];
-  AppendEntry e[kMaxAppendEntries];
-};
-
 struct DecodeArgs {
   const void* q;
   const float* gate;
@@ -74,12 +53,49 @@ struct DecodeArgs {
   int32_t lens[kMaxBatch];
 };
 
+// where the state lives (device pointers) and its dimensions
+struct StateRefs {
+  const void* k_new;
+  const void* v_new;
+  void* k_pages;
+  void* v_pages;
+  const int32_t* block_table;
+  float* blk_mean;
+  float* blk_var;
+  float* s_all;
+  float* z_all;
+  uint32_t* err;
+  int32_t G, d, bk, max_blocks, num_pages, n_tiles;
+};
+
+struct AppendArgs {
+  StateRefs st;
+  int32_t n_entries;
+  int32_t s_items;     // state-update workgroups (n_entries * G * d / rows_per_item)
+  int32_t page_items;  // page-copy workgroups
+  int32_t stat_items;  // block-statistics workgroups
+  int32_t page_prefix[kMaxAppendEntries + 1];
+  int32_t stat_prefix[kMaxAppendEntries + 1];
+  AppendEntry e[kMaxAppendEntries];
+};
+
+// fused decode step: append one token to every sequence (row b of k_new /
+// v_new is sequence b) inside the scorer's launch, then the usual decode
+struct StepArgs {
+  DecodeArgs dec;      // lens: after the append
+  StateRefs st;
+  int32_t s_items;     // B * G * d / rows_per_item state-update workgroups
+  int32_t n_stat;      // sequences whose current block this token completes
+  int16_t stat_seq[kMaxBatch];
+};
+
 // host-side launchers (defined next to their kernels)
 hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_score(const DecodeArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_select(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_attend(const DecodeArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_step_score(const StepArgs& a, bool bf16, hipStream_t s);
 
 // ------------------------------------------------------------ device helpers
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }

@@ -177,6 +177,16 @@ spla_status spla_append_kv(spla_handle *h, int32_t n_seqs, const int32_t *seq_id
 spla_status spla_decode(spla_handle *h, const void *q, const float *gate, float *out,
                         const spla_decode_aux *aux, void *stream);
 
+/* One decode step as a single call: spla_append_kv of one token for every
+ * sequence (k_new, v_new: device [B][G][d] kv_dtype, row b = sequence b)
+ * followed by spla_decode, with the same results.  The append runs inside
+ * the scorer's launch (the scorer reads statistics of blocks completed by
+ * earlier appends only), so the step takes one kernel launch less.
+ * aux->sel_in is not accepted here (SPLA_ERR_INVALID_ARG); kernel_events
+ * order: append+score, select, attend, combine. */
+spla_status spla_decode_step(spla_handle *h, const void *k_new, const void *v_new, const void *q,
+                             const float *gate, float *out, const spla_decode_aux *aux, void *stream);
+
 /* Copy the host mirror of the sequence lengths (batch entries). */
 spla_status spla_get_lens(const spla_handle *h, int32_t *lens_host);
 

@@ -83,7 +83,7 @@ class ParityRun:
     """A SplaLayer and a SplaOracle fed from one Workload."""
 
     def __init__(self, w: Workload, page_order: str = "identity", steps: Optional[int] = None,
-                 device: str = "cuda", prefill_chunk: int = 4096):
+                 device: str = "cuda", prefill_chunk: int = 4096, use_step: bool = False):
         import torch
         from block_sparse_linear_amd import SplaLayer
 
@@ -92,6 +92,7 @@ class ParityRun:
         self.steps = w.steps if steps is None else steps
         self.device = device
         self.prefill_chunk = prefill_chunk
+        self.use_step = use_step  # spla_decode_step instead of spla_append_kv + spla_decode
         mb = w.max_blocks_per_seq(self.steps)
         self.layer = SplaLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k, mb,
                                kv_dtype=w.kv_dtype, device=device, page_order=page_order, seed=w.seed)
@@ -110,7 +111,9 @@ class ParityRun:
                 self.layer.append([b], [k.shape[0]], self.dev(k), self.dev(v))
                 self.oracle.append([b], [k.shape[0]], k, v)
 
-    def append_step(self, s: int) -> Dict[str, np.ndarray]:
+    def append_step(self, s: int, token: bool = True) -> Dict[str, np.ndarray]:
+        """The step's chunk appends and (token=True) its one-token append, on
+        both sides."""
         st = self.w.step(s, self.mix)
         cs = [int(x) for x in st["chunk_seqs"]]
         if cs:
@@ -118,11 +121,12 @@ class ParityRun:
             self.layer.append(cs, n, self.dev(st["chunk_k"]), self.dev(st["chunk_v"]))
             self.oracle.append(cs, n, st["chunk_k"], st["chunk_v"])
         allb = list(range(self.w.batch))
-        self.layer.append(allb, [1] * self.w.batch, self.dev(st["k"]), self.dev(st["v"]))
+        if token:
+            self.layer.append(allb, [1] * self.w.batch, self.dev(st["k"]), self.dev(st["v"]))
         self.oracle.append(allb, [1] * self.w.batch, st["k"], st["v"])
         return st
 
-    def gpu_decode(self, q_np: np.ndarray, sel_in=None):
+    def gpu_decode(self, q_np: np.ndarray, sel_in=None, kv=None):
         t = self.torch
         w = self.w
         B, H, G, d = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim
@@ -135,16 +139,19 @@ class ParityRun:
         }
         if sel_in is not None:
             aux["sel_in"] = t.from_numpy(np.ascontiguousarray(sel_in, np.int32)).to(self.device)
-        out = self.layer.decode(self.dev(q_np), self.gate, aux=aux)
+        if kv is not None:
+            out = self.layer.decode_step(self.dev(kv[0]), self.dev(kv[1]), self.dev(q_np), self.gate, aux=aux)
+        else:
+            out = self.layer.decode(self.dev(q_np), self.gate, aux=aux)
         t.cuda.synchronize()
         res = {k: v.cpu().numpy() for k, v in aux.items() if k != "sel_in"}
         res["o"] = out.cpu().numpy()
         return res
 
-    def check_decode(self, s: int, q_np: np.ndarray, sel_in=None) -> StepReport:
+    def check_decode(self, s: int, q_np: np.ndarray, sel_in=None, kv=None) -> StepReport:
         w = self.w
         rep = StepReport(step=s)
-        g = self.gpu_decode(q_np, sel_in)
+        g = self.gpu_decode(q_np, sel_in, kv)
         ref = self.oracle.decode(q_np, self.gate_np, sel_override=sel_in)
         sel_gpu = g["sel_idx"]
         if sel_in is None:
@@ -213,8 +220,8 @@ class ParityRun:
         worst: Dict[str, float] = {}
         ties = 0
         for s in range(steps):
-            st = self.append_step(s)
-            rep = self.check_decode(s, st["q"])
+            st = self.append_step(s, token=not self.use_step)
+            rep = self.check_decode(s, st["q"], kv=(st["k"], st["v"]) if self.use_step else None)
             failures += rep.failures
             ties += rep.near_ties
             for k, v in rep.errors.items():

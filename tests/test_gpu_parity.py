@@ -19,12 +19,12 @@ def _needs_gpu():
         pytest.skip("no GPU")
 
 
-def _run(w, steps=None, page_order="identity", verbose=True):
+def _run(w, steps=None, page_order="identity", verbose=True, use_step=False):
     _needs_gpu()
     from tests.spla_parity import ParityRun
     print(f"[case] {w.name} B={w.batch} H={w.n_q_heads} G={w.n_kv_heads} d={w.head_dim} "
-          f"Bk={w.block_size} k={w.top_k} t0={w.t0[:4]} pages={page_order}", flush=True)
-    run = ParityRun(w, page_order=page_order, steps=steps, prefill_chunk=1000)
+          f"Bk={w.block_size} k={w.top_k} t0={w.t0[:4]} pages={page_order} step={use_step}", flush=True)
+    run = ParityRun(w, page_order=page_order, steps=steps, prefill_chunk=1000, use_step=use_step)
     failures = run.run(verbose=verbose)
     assert not failures, "\n".join(failures[:20])
 
@@ -92,3 +92,43 @@ def test_selection_hook():
         sel[0, g, :len(ids)] = ids
     rep = run.check_decode(0, st["q"], sel_in=sel)
     assert not rep.failures, rep.failures
+
+
+# ---- fused decode step (spla_decode_step) -------------------------------------
+def test_step_small_gqa4_crossing_block_boundaries():
+    # 70 steps from t0 = 64 * 150 - 3: the appends complete blocks along the way
+    _run(small(name="step", t0=(64 * 150 - 3,), steps=70), page_order="shuffled", use_step=True)
+
+
+def test_step_ragged_batch_with_chunks():
+    w = small(name="step_ragged", batch=5, t0=(1, 700, 64 * 40 + 13, 64 * 9 - 1, 3000), steps=4, chunk_seqs=2,
+              chunk_len=100, top_k=6)
+    _run(w, page_order="shuffled", use_step=True)
+
+
+def test_step_fp32_and_block128():
+    _run(make_workload("tiny_fp32", steps=4), use_step=True)
+    _run(small(name="step_bk128", head_dim=64, block_size=128, t0=(128 * 40 + 126,), top_k=12, steps=4),
+         use_step=True)
+
+
+def test_step_matches_two_calls_bitwise():
+    """spla_decode_step == spla_append_kv + spla_decode, bit for bit."""
+    _needs_gpu()
+    import torch
+    from tests.spla_parity import ParityRun
+    w = small(name="bitwise", batch=3, t0=(64 * 30 - 2, 500, 64 * 12), steps=5, kind="outlier", n_outlier=8)
+    a = ParityRun(w, steps=5, prefill_chunk=700)
+    b = ParityRun(w, steps=5, prefill_chunk=700)
+    a.prefill()
+    b.prefill()
+    for s in range(5):
+        st = w.step(s)
+        k, v, q = a.dev(st["k"]), a.dev(st["v"]), a.dev(st["q"])
+        a.layer.append(list(range(3)), [1] * 3, k, v)
+        oa = a.layer.decode(q, a.gate)
+        ob = b.layer.decode_step(k, v, q, b.gate)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), f"step {s}"
+    for x, y in zip(a.layer.state_tensors(), b.layer.state_tensors()):
+        assert torch.equal(x, y)
