@@ -238,10 +238,11 @@ def main() -> int:
     log(f"timed {K} steps x {L} instances: {elapsed_ms:.2f} ms, t_step {t_step * 1e6:.2f} us")
     del graphs
 
-    # per-kernel durations: HIP events recorded on the launch stream right
-    # before and after each kernel of the step (append+score, select, attend,
-    # combine).  The steps are enqueued while a spin kernel holds the GPU, so
-    # the GPU then runs them back to back (the host never starves it).
+    # per-kernel durations: every kernel of the step (append+score, select,
+    # attend, combine) is launched through hipExtLaunchKernel with a pair of
+    # HIP events, which take that kernel's begin and end timestamps on its
+    # launch stream.  The steps are enqueued while a spin kernel holds the
+    # GPU, so that the GPU then runs them back to back as in the graphs.
     names = ["step_score", "select", "attend", "combine"]
     import ctypes
     ev_sets = []

@@ -31,6 +31,7 @@ SPLA_F32, SPLA_BF16 = 0, 1
 EXPORTED = [
     "spla_create", "spla_destroy", "spla_workspace_bytes", "spla_stats_floats", "spla_bind",
     "spla_append_kv", "spla_decode", "spla_decode_step", "spla_get_lens", "spla_status_str", "spla_abi_version",
+    "spla_last_hip_error",
 ]
 
 
@@ -98,21 +99,29 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spla_status_str.restype = ctypes.c_char_p
     lib.spla_abi_version.argtypes = []
     lib.spla_abi_version.restype = ctypes.c_int32
+    lib.spla_last_hip_error.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_char_p)]
+    lib.spla_last_hip_error.restype = ctypes.c_int32
     if path is None:
         _lib = lib
     return lib
 
 
 class SplaError(RuntimeError):
-    def __init__(self, status: int, where: str):
+    def __init__(self, status: int, where: str, hip_error: Optional[str] = None):
         self.status = status
         self.name = STATUS.get(status, str(status))
-        super().__init__(f"{where}: {self.name}")
+        self.hip_error = hip_error
+        super().__init__(f"{where}: {self.name}" + (f" ({hip_error})" if hip_error else ""))
 
 
-def _check(st: int, where: str) -> None:
+def _check(st: int, where: str, lib=None, h=None) -> None:
     if st != 0:
-        raise SplaError(st, where)
+        hip = None
+        if st == 5 and lib is not None and h is not None:
+            name = ctypes.c_char_p()
+            code = lib.spla_last_hip_error(h, ctypes.byref(name))
+            hip = f"hip error {code}: {name.value.decode() if name.value else '?'}"
+        raise SplaError(st, where, hip)
 
 
 def _i32_array(vals: Sequence[int]):
@@ -237,7 +246,7 @@ class SplaLayer:
         """k_new, v_new: device tensors [sum n_new][G][d] of the layer's dtype."""
         self._check_kv(k_new, v_new, sum(int(n) for n in n_new))
         st = self.handle.append_raw(list(seq_ids), list(n_new), k_new.data_ptr(), v_new.data_ptr(), self._stream())
-        _check(st, "spla_append_kv")
+        _check(st, "spla_append_kv", self.handle.lib, self.handle.h)
 
     def _check_kv(self, k_new, v_new, rows: int) -> None:
         for x in (k_new, v_new):
@@ -284,7 +293,7 @@ class SplaLayer:
         out, ax = self._decode_inputs(q, gate, out, aux, kernel_events)
         st = self.handle.decode_step_raw(k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), gate.data_ptr(),
                                          out.data_ptr(), ax, self._stream())
-        _check(st, "spla_decode_step")
+        _check(st, "spla_decode_step", self.handle.lib, self.handle.h)
         return out
 
     def decode(self, q, gate, out=None, aux: Optional[Dict[str, object]] = None, kernel_events=None):
@@ -295,7 +304,7 @@ class SplaLayer:
         Returns out [B][H][d] float32."""
         out, ax = self._decode_inputs(q, gate, out, aux, kernel_events)
         st = self.handle.decode_raw(q.data_ptr(), gate.data_ptr(), out.data_ptr(), ax, self._stream())
-        _check(st, "spla_decode")
+        _check(st, "spla_decode", self.handle.lib, self.handle.h)
         return out
 
     # ----------------------------------------------------------- helpers

@@ -50,15 +50,10 @@ __global__ __launch_bounds__(kThreads) void k_append(const AppendArgs a) {
 
 }  // namespace
 
-hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s) {
-  const int grid = a.s_items + a.page_items + a.stat_items;
-  if (grid == 0) return hipSuccess;
-  if (bf16) {
-    k_append<true><<<grid, kThreads, 0, s>>>(a);
-  } else {
-    k_append<false><<<grid, kThreads, 0, s>>>(a);
-  }
-  return hipGetLastError();
+hipError_t launch_append(const AppendArgs& a, bool bf16, const Launch& l) {
+  const int n = a.s_items + a.page_items + a.stat_items;
+  if (n == 0) return hipSuccess;
+  return bf16 ? launch_kernel(k_append<true>, dim3(n), l, a) : launch_kernel(k_append<false>, dim3(n), l, a);
 }
 
 }  // namespace spla

@@ -1092,86 +1092,72 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
 
 }  // namespace
 
-#define SPLA_DISPATCH_D(D_, ...)                                 \
-  switch (D_) {                                                 \
-    case 64: { constexpr int DD = 64; __VA_ARGS__; } break;     \
-    case 128: { constexpr int DD = 128; __VA_ARGS__; } break;   \
-    default: return hipErrorInvalidValue;                       \
+// each launcher returns the status of its own launch (hipLaunchKernel /
+// hipExtLaunchKernel report it directly, so an error left behind by an
+// unrelated earlier HIP call is never attributed to it)
+#define SPLA_DISPATCH_D(D_, ...)                                     \
+  switch (D_) {                                                     \
+    case 64: { constexpr int DD = 64; return __VA_ARGS__; }         \
+    case 128: { constexpr int DD = 128; return __VA_ARGS__; }       \
+    default: return hipErrorInvalidValue;                           \
   }
-#define SPLA_DISPATCH_RD(R_, D_, ...)                                        \
-  switch (R_) {                                                             \
-    case 1: { constexpr int RR = 1; SPLA_DISPATCH_D(D_, __VA_ARGS__) } break; \
-    case 2: { constexpr int RR = 2; SPLA_DISPATCH_D(D_, __VA_ARGS__) } break; \
-    case 4: { constexpr int RR = 4; SPLA_DISPATCH_D(D_, __VA_ARGS__) } break; \
-    case 8: { constexpr int RR = 8; SPLA_DISPATCH_D(D_, __VA_ARGS__) } break; \
-    default: return hipErrorInvalidValue;                                   \
+#define SPLA_DISPATCH_RD(R_, D_, ...)                                         \
+  switch (R_) {                                                              \
+    case 1: { constexpr int RR = 1; SPLA_DISPATCH_D(D_, __VA_ARGS__) }       \
+    case 2: { constexpr int RR = 2; SPLA_DISPATCH_D(D_, __VA_ARGS__) }       \
+    case 4: { constexpr int RR = 4; SPLA_DISPATCH_D(D_, __VA_ARGS__) }       \
+    case 8: { constexpr int RR = 8; SPLA_DISPATCH_D(D_, __VA_ARGS__) }       \
+    default: return hipErrorInvalidValue;                                    \
   }
 
-hipError_t launch_score(const DecodeArgs& a, bool bf16, hipStream_t s) {
-  dim3 grid(a.score_tiles, a.G, a.B);
+hipError_t launch_score(const DecodeArgs& a, bool bf16, const Launch& l) {
+  const dim3 grid(a.score_tiles, a.G, a.B);
   if (a.score_tiles == 0) return hipSuccess;
-  if (bf16) {
-    SPLA_DISPATCH_RD(a.r, a.d, (k_score<true, RR, DD><<<grid, kThreads, 0, s>>>(a)))
-  } else {
-    SPLA_DISPATCH_RD(a.r, a.d, (k_score<false, RR, DD><<<grid, kThreads, 0, s>>>(a)))
-  }
-  return hipGetLastError();
+  if (bf16) SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_score<true, RR, DD>, grid, l, a))
+  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_score<false, RR, DD>, grid, l, a))
 }
 
-hipError_t launch_step_score(const StepArgs& a, bool bf16, hipStream_t s) {
-  const int grid = a.dec.score_tiles * a.dec.G * a.dec.B + a.s_items + a.dec.B + a.n_stat * a.dec.G;
-  if (bf16) {
-    SPLA_DISPATCH_RD(a.dec.r, a.dec.d, (k_step_score<true, RR, DD><<<grid, kThreads, 0, s>>>(a)))
-  } else {
-    SPLA_DISPATCH_RD(a.dec.r, a.dec.d, (k_step_score<false, RR, DD><<<grid, kThreads, 0, s>>>(a)))
-  }
-  return hipGetLastError();
+hipError_t launch_step_score(const StepArgs& a, bool bf16, const Launch& l) {
+  const dim3 grid(a.dec.score_tiles * a.dec.G * a.dec.B + a.s_items + a.dec.B + a.n_stat * a.dec.G);
+  if (bf16) SPLA_DISPATCH_RD(a.dec.r, a.dec.d, launch_kernel(k_step_score<true, RR, DD>, grid, l, a))
+  SPLA_DISPATCH_RD(a.dec.r, a.dec.d, launch_kernel(k_step_score<false, RR, DD>, grid, l, a))
 }
 
-hipError_t launch_select(const DecodeArgs& a, hipStream_t s) {
-  // keys per thread: enough for the longest sequence of the batch
-  const int nc = a.score_tiles * kTile;
-  const dim3 grid(a.G, a.B);
-  if (nc <= 1 * kThreads) {
-    k_select<1><<<grid, kThreads, 0, s>>>(a);
-  } else if (nc <= 2 * kThreads) {
-    k_select<2><<<grid, kThreads, 0, s>>>(a);
-  } else if (nc <= 4 * kThreads) {
-    k_select<4><<<grid, kThreads, 0, s>>>(a);
-  } else if (nc <= 8 * kThreads) {
-    k_select<8><<<grid, kThreads, 0, s>>>(a);
-  } else if (nc <= 16 * kThreads) {
-    k_select<16><<<grid, kThreads, 0, s>>>(a);
-  } else if (nc <= 32 * kThreads) {
-    k_select<32><<<grid, kThreads, 0, s>>>(a);
+// keys-per-thread sizes compiled for the selector: the smallest one that
+// holds the longest sequence's candidates is launched
+template <int... Ks>
+struct SelectSizes {};
+
+template <int K, int... Ks>
+hipError_t launch_select_sized(const DecodeArgs& a, const Launch& l, int nc, SelectSizes<K, Ks...>) {
+  if (nc <= K * kThreads) return launch_kernel(k_select<K>, dim3(a.G, a.B), l, a);
+  if constexpr (sizeof...(Ks) == 0) {
+    return hipErrorInvalidValue;
   } else {
-    k_select<64><<<grid, kThreads, 0, s>>>(a);
+    return launch_select_sized(a, l, nc, SelectSizes<Ks...>{});
   }
-  return hipGetLastError();
 }
 
-hipError_t launch_attend(const DecodeArgs& a, bool bf16, hipStream_t s) {
-  dim3 grid(a.top_k, a.G, a.B);
-  if (bf16) {
-    if (a.bk == 64) {
-      SPLA_DISPATCH_RD(a.r, a.d, (k_attend_mfma<RR, DD, 64><<<grid, kThreads, 0, s>>>(a)))
-    } else {
-      SPLA_DISPATCH_RD(a.r, a.d, (k_attend_mfma<RR, DD, 128><<<grid, kThreads, 0, s>>>(a)))
-    }
-  } else {
-    SPLA_DISPATCH_RD(a.r, a.d, (k_attend<false, RR, DD><<<grid, kThreads, 0, s>>>(a)))
+hipError_t launch_select(const DecodeArgs& a, const Launch& l) {
+  int nc = 0;  // candidates of the longest sequence that has more blocks than top_k
+  for (int b = 0; b < a.B; ++b) {
+    const int nb = (a.lens[b] + a.bk - 1) / a.bk;
+    if (nb > a.top_k) nc = max(nc, nb - 2);
   }
-  return hipGetLastError();
+  return launch_select_sized(a, l, nc, SelectSizes<1, 2, 3, 4, 6, 8, 9, 10, 12, 16, 20, 24, 32, 40, 48, 64>{});
 }
 
-hipError_t launch_combine(const DecodeArgs& a, bool bf16, hipStream_t s) {
-  dim3 grid(a.d / 32, a.G, a.B);
-  if (bf16) {
-    SPLA_DISPATCH_RD(a.r, a.d, (k_combine<true, RR, DD><<<grid, kThreads, 0, s>>>(a)))
-  } else {
-    SPLA_DISPATCH_RD(a.r, a.d, (k_combine<false, RR, DD><<<grid, kThreads, 0, s>>>(a)))
-  }
-  return hipGetLastError();
+hipError_t launch_attend(const DecodeArgs& a, bool bf16, const Launch& l) {
+  const dim3 grid(a.top_k, a.G, a.B);
+  if (!bf16) SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_attend<false, RR, DD>, grid, l, a))
+  if (a.bk == 64) SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_attend_mfma<RR, DD, 64>, grid, l, a))
+  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_attend_mfma<RR, DD, 128>, grid, l, a))
+}
+
+hipError_t launch_combine(const DecodeArgs& a, bool bf16, const Launch& l) {
+  const dim3 grid(a.d / 32, a.G, a.B);
+  if (bf16) SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<true, RR, DD>, grid, l, a))
+  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<false, RR, DD>, grid, l, a))
 }
 
 }  // namespace spla

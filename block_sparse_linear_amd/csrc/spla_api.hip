@@ -18,6 +18,7 @@ struct spla_handle {
   bool bound = false;
   spla_buffers buf{};
   std::vector<int32_t> lens;
+  hipError_t last_hip = hipSuccess;  // status of the last launch that failed
   // workspace layout (bytes)
   size_t off_lg = 0, off_sel = 0, off_page = 0, off_part = 0, ws_bytes = 0;
 };
@@ -134,27 +135,41 @@ spla_status check_decode_args(const spla_handle* h, const void* q, const float* 
   return SPLA_OK;
 }
 
-// per-kernel event recording (spla_decode_aux.kernel_events)
-struct EventMarks {
+// launch descriptors of the kernels of one call, in launch order: the i-th
+// kernel carries kernel_events[2i] / [2i+1] as its begin / end events
+struct LaunchSeq {
+  hipStream_t st = nullptr;
   void* const* ev = nullptr;
   int nev = 0, k = 0;
-  hipStream_t st = nullptr;
-  void mark(int which) {
-    if (k < nev && ev[2 * k + which]) hipEventRecord(reinterpret_cast<hipEvent_t>(ev[2 * k + which]), st);
-    if (which == 1) ++k;
+  LaunchSeq(hipStream_t s, const spla_decode_aux* aux) : st(s) {
+    if (aux && aux->kernel_events) {
+      ev = aux->kernel_events;
+      nev = aux->n_kernel_events;
+    }
+  }
+  Launch next() {
+    Launch l;
+    l.s = st;
+    if (k < nev) {
+      l.start = reinterpret_cast<hipEvent_t>(ev[2 * k]);
+      l.stop = reinterpret_cast<hipEvent_t>(ev[2 * k + 1]);
+    }
+    ++k;
+    return l;
   }
 };
 
-spla_status launch_decode_tail(const DecodeArgs& a, bool bf16, hipStream_t st, EventMarks& em) {
-  em.mark(0);
-  if (launch_select(a, st) != hipSuccess) return SPLA_ERR_HIP;
-  em.mark(1);
-  em.mark(0);
-  if (launch_attend(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
-  em.mark(1);
-  em.mark(0);
-  if (launch_combine(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
-  em.mark(1);
+// record a failed launch on the handle
+spla_status hip_fail(spla_handle* h, hipError_t e) {
+  h->last_hip = e;
+  return SPLA_ERR_HIP;
+}
+
+spla_status launch_decode_tail(spla_handle* h, const DecodeArgs& a, bool bf16, LaunchSeq& ls) {
+  hipError_t e;
+  if ((e = launch_select(a, ls.next())) != hipSuccess) return hip_fail(h, e);
+  if ((e = launch_attend(a, bf16, ls.next())) != hipSuccess) return hip_fail(h, e);
+  if ((e = launch_combine(a, bf16, ls.next())) != hipSuccess) return hip_fail(h, e);
   return SPLA_OK;
 }
 
@@ -176,6 +191,12 @@ const char* spla_status_str(spla_status st) {
 }
 
 int32_t spla_abi_version(void) { return SPLA_ABI_VERSION; }
+
+int32_t spla_last_hip_error(const spla_handle* h, const char** name) {
+  const hipError_t e = h ? h->last_hip : hipSuccess;
+  if (name) *name = hipGetErrorName(e);
+  return (int32_t)e;
+}
 
 spla_status spla_create(const spla_config* cfg, spla_handle** out) {
   if (!cfg || !out) return SPLA_ERR_INVALID_ARG;
@@ -303,7 +324,8 @@ spla_status spla_append_kv(spla_handle* h, int32_t n_seqs, const int32_t* seq_id
     a.s_items = ne * c.n_kv_heads * chunks;
     a.page_items = pp;
     a.stat_items = sp;
-    if (launch_append(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
+    const hipError_t e = launch_append(a, bf16, Launch{st, nullptr, nullptr});
+    if (e != hipSuccess) return hip_fail(h, e);
     row += lrow;
   }
   for (int i = 0; i < n_seqs; ++i) h->lens[seq_ids_host[i]] += n_new_host[i];
@@ -323,22 +345,14 @@ spla_status spla_decode(spla_handle* h, const void* q, const float* gate, float*
   fill_decode_args(h, q, gate, out, aux, &a);
   const bool bf16 = c.kv_dtype == SPLA_BF16;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  EventMarks em;
-  em.ev = aux ? aux->kernel_events : nullptr;
-  em.nev = em.ev ? aux->n_kernel_events : 0;
-  em.st = st;
+  LaunchSeq ls(st, aux);
+  hipError_t e;
   if (!a.sel_in) {
-    em.mark(0);
-    if (launch_score(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
-    em.mark(1);
-    return launch_decode_tail(a, bf16, st, em);
+    if ((e = launch_score(a, bf16, ls.next())) != hipSuccess) return hip_fail(h, e);
+    return launch_decode_tail(h, a, bf16, ls);
   }
-  em.mark(0);
-  if (launch_attend(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
-  em.mark(1);
-  em.mark(0);
-  if (launch_combine(a, bf16, st) != hipSuccess) return SPLA_ERR_HIP;
-  em.mark(1);
+  if ((e = launch_attend(a, bf16, ls.next())) != hipSuccess) return hip_fail(h, e);
+  if ((e = launch_combine(a, bf16, ls.next())) != hipSuccess) return hip_fail(h, e);
   return SPLA_OK;
 }
 
@@ -367,17 +381,13 @@ spla_status spla_decode_step(spla_handle* h, const void* k_new, const void* v_ne
     if (h->lens[b] % c.block_size == 0) a.stat_seq[a.n_stat++] = (int16_t)b;
   const bool bf16 = c.kv_dtype == SPLA_BF16;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  EventMarks em;
-  em.ev = aux ? aux->kernel_events : nullptr;
-  em.nev = em.ev ? aux->n_kernel_events : 0;
-  em.st = st;
-  em.mark(0);
-  if (launch_step_score(a, bf16, st) != hipSuccess) {
+  LaunchSeq ls(st, aux);
+  const hipError_t e = launch_step_score(a, bf16, ls.next());
+  if (e != hipSuccess) {
     h->lens = saved;
-    return SPLA_ERR_HIP;
+    return hip_fail(h, e);
   }
-  em.mark(1);
-  return launch_decode_tail(a.dec, bf16, st, em);
+  return launch_decode_tail(h, a.dec, bf16, ls);
 }
 
 }  // extern "C"

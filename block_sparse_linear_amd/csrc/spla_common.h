@@ -1,6 +1,7 @@
 // Internal definitions shared by the SPLA HIP kernels and the host ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -89,13 +90,31 @@ struct StepArgs {
   int16_t stat_seq[kMaxBatch];
 };
 
+// where a kernel is launched; with start / stop set, the launch goes through
+// hipExtLaunchKernel, which stamps the two events with the kernel's own begin
+// and end times (the dispatch packet's timestamps)
+struct Launch {
+  hipStream_t s = nullptr;
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+// launch a kernel that takes one argument struct; returns this launch's status
+template <typename Args>
+inline hipError_t launch_kernel(void (*kernel)(Args), dim3 grid, const Launch& l, const Args& a) {
+  void* args[] = {const_cast<Args*>(&a)};
+  const void* f = reinterpret_cast<const void*>(kernel);
+  if (l.start || l.stop) return hipExtLaunchKernel(f, grid, dim3(kThreads), args, 0, l.s, l.start, l.stop, 0);
+  return hipLaunchKernel(f, grid, dim3(kThreads), args, 0, l.s);
+}
+
 // host-side launchers (defined next to their kernels)
-hipError_t launch_append(const AppendArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_score(const DecodeArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_select(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_attend(const DecodeArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_combine(const DecodeArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_step_score(const StepArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, bool bf16, const Launch& l);
+hipError_t launch_score(const DecodeArgs& a, bool bf16, const Launch& l);
+hipError_t launch_select(const DecodeArgs& a, const Launch& l);
+hipError_t launch_attend(const DecodeArgs& a, bool bf16, const Launch& l);
+hipError_t launch_combine(const DecodeArgs& a, bool bf16, const Launch& l);
+hipError_t launch_step_score(const StepArgs& a, bool bf16, const Launch& l);
 
 // ------------------------------------------------------------ device helpers
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }

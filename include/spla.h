@@ -87,7 +87,7 @@ typedef enum {
     SPLA_ERR_UNSUPPORTED = 2,  /* configuration outside the supported set */
     SPLA_ERR_CAPACITY = 3,     /* append would exceed max_blocks_per_seq * block_size */
     SPLA_ERR_ALIGNMENT = 4,    /* a device pointer is not 16-byte aligned */
-    SPLA_ERR_HIP = 5,          /* a kernel launch failed (hipGetLastError) */
+    SPLA_ERR_HIP = 5,          /* a kernel launch failed (see spla_last_hip_error) */
     SPLA_ERR_STATE = 6         /* call before spla_bind */
 } spla_status;
 
@@ -131,11 +131,13 @@ typedef struct {               /* optional outputs / test hook of spla_decode; N
     float *d_rla;              /* out [B][H] phi(q).(z_all - z_sel) (0 when every block is selected) */
     const int32_t *sel_in;     /* in  [B][G][top_k]: use these block ids (ascending, -1 padded,
                                   each < nb) instead of scoring + top-k */
-    void *const *kernel_events;  /* in: hipEvent_t[2 * n]; when set, kernel_events[2i] is recorded on
-                                  the stream right before the i-th kernel this call launches and
-                                  kernel_events[2i+1] right after it (NULL entries skipped), for
-                                  per-kernel timing.  Launch order: score, select, attend, combine
-                                  (score and select are skipped when sel_in is set). */
+    void *const *kernel_events;  /* in: hipEvent_t[2 * n], created by the caller; when set, the i-th
+                                  kernel this call launches (i < n) is launched with
+                                  hipExtLaunchKernel and kernel_events[2i] / [2i+1] take the
+                                  kernel's own begin / end timestamps (either may be NULL), for
+                                  per-kernel timing.  Not for use under stream capture.  Launch
+                                  order: score, select, attend, combine (score and select are
+                                  skipped when sel_in is set). */
     int32_t n_kernel_events;   /* n: entries of kernel_events / 2 */
 } spla_decode_aux;
 
@@ -191,6 +193,11 @@ spla_status spla_decode_step(spla_handle *h, const void *k_new, const void *v_ne
 spla_status spla_get_lens(const spla_handle *h, int32_t *lens_host);
 
 const char *spla_status_str(spla_status st);
+
+/* The hipError_t of the last launch on this handle that failed (0 = none)
+ * and, if name is non-NULL, its name (hipGetErrorName; static storage).  A
+ * call that returned SPLA_ERR_HIP leaves its launch's code here. */
+int32_t spla_last_hip_error(const spla_handle *h, const char **name);
 int32_t spla_abi_version(void);
 
 #ifdef __cplusplus

@@ -15,6 +15,11 @@ specification:
            checked on its own); D: <= 1e-4 relative.
   state    S_all, z_all per (b, g): max|gpu - ref| <= 1e-4 * max|ref|;
            block mean / variance: <= 1e-5 relative (+1e-6 absolute).
+
+Sampled checks: the method treats every (sequence, KV head) pair on its own,
+so at full sizes the oracle is run on a subset of sequences and KV heads (their
+slices of the same inputs, with their query heads and gates) and compared with
+the matching slices of the GPU's results; the GPU still runs the whole batch.
 """
 from __future__ import annotations
 
@@ -83,7 +88,8 @@ class ParityRun:
     """A SplaLayer and a SplaOracle fed from one Workload."""
 
     def __init__(self, w: Workload, page_order: str = "identity", steps: Optional[int] = None,
-                 device: str = "cuda", prefill_chunk: int = 4096, use_step: bool = False):
+                 device: str = "cuda", prefill_chunk: int = 4096, use_step: bool = False,
+                 seqs: Optional[List[int]] = None, kv_heads: Optional[List[int]] = None):
         import torch
         from block_sparse_linear_amd import SplaLayer
 
@@ -96,8 +102,13 @@ class ParityRun:
         mb = w.max_blocks_per_seq(self.steps)
         self.layer = SplaLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k, mb,
                                kv_dtype=w.kv_dtype, device=device, page_order=page_order, seed=w.seed)
-        self.oracle = SplaOracle(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k,
-                                 w.max_tokens(self.steps))
+        # sequences / KV heads the oracle checks (all by default)
+        self.bs = list(range(w.batch)) if seqs is None else [int(b) for b in seqs]
+        self.gs = list(range(w.n_kv_heads)) if kv_heads is None else [int(g) for g in kv_heads]
+        r = w.group
+        self.hs = [g * r + i for g in self.gs for i in range(r)]
+        self.oracle = SplaOracle(len(self.bs), r * len(self.gs), len(self.gs), w.head_dim, w.block_size,
+                                 w.top_k, w.max_tokens(self.steps))
         self.gate_np = w.gate()
         self.gate = torch.from_numpy(self.gate_np).to(device)
         self.mix = w.mixture_state()
@@ -105,25 +116,38 @@ class ParityRun:
     def dev(self, x: np.ndarray):
         return self.torch.from_numpy(np.ascontiguousarray(x)).to(self.device).to(self.layer.dtype)
 
+    def _ob(self, b: int) -> int:
+        """oracle index of sequence b (-1 if not checked)"""
+        return self.bs.index(b) if b in self.bs else -1
+
     def prefill(self) -> None:
+        gs = self.gs
         for b in range(self.w.batch):
+            ob = self._ob(b)
             for _, k, v in self.w.prefill_chunks(b, self.prefill_chunk):
                 self.layer.append([b], [k.shape[0]], self.dev(k), self.dev(v))
-                self.oracle.append([b], [k.shape[0]], k, v)
+                if ob >= 0:
+                    self.oracle.append([ob], [k.shape[0]], k[:, gs], v[:, gs])
 
     def append_step(self, s: int, token: bool = True) -> Dict[str, np.ndarray]:
         """The step's chunk appends and (token=True) its one-token append, on
         both sides."""
         st = self.w.step(s, self.mix)
         cs = [int(x) for x in st["chunk_seqs"]]
+        gs, L = self.gs, self.w.chunk_len
         if cs:
-            n = [self.w.chunk_len] * len(cs)
+            n = [L] * len(cs)
             self.layer.append(cs, n, self.dev(st["chunk_k"]), self.dev(st["chunk_v"]))
-            self.oracle.append(cs, n, st["chunk_k"], st["chunk_v"])
+            picks = [i for i, b in enumerate(cs) if self._ob(b) >= 0]
+            if picks:
+                rows = np.concatenate([np.arange(i * L, (i + 1) * L) for i in picks])
+                self.oracle.append([self._ob(cs[i]) for i in picks], [L] * len(picks),
+                                   st["chunk_k"][rows][:, gs], st["chunk_v"][rows][:, gs])
         allb = list(range(self.w.batch))
         if token:
             self.layer.append(allb, [1] * self.w.batch, self.dev(st["k"]), self.dev(st["v"]))
-        self.oracle.append(allb, [1] * self.w.batch, st["k"], st["v"])
+        bs = self.bs
+        self.oracle.append(list(range(len(bs))), [1] * len(bs), st["k"][bs][:, gs], st["v"][bs][:, gs])
         return st
 
     def gpu_decode(self, q_np: np.ndarray, sel_in=None, kv=None):
@@ -151,16 +175,23 @@ class ParityRun:
     def check_decode(self, s: int, q_np: np.ndarray, sel_in=None, kv=None) -> StepReport:
         w = self.w
         rep = StepReport(step=s)
+        bs, gs, hs = self.bs, self.gs, self.hs
         g = self.gpu_decode(q_np, sel_in, kv)
-        ref = self.oracle.decode(q_np, self.gate_np, sel_override=sel_in)
+        # the checked slices of the GPU's results
+        g = {"o": g["o"][bs][:, hs], "o_sparse": g["o_sparse"][bs][:, hs], "o_rla": g["o_rla"][bs][:, hs],
+             "d_rla": g["d_rla"][bs][:, hs], "sel_idx": g["sel_idx"][bs][:, gs], "lg": g["lg"][bs][:, gs]}
+        q_o = q_np[bs][:, hs]
+        gate_o = self.gate_np[hs]
+        sel_o = None if sel_in is None else np.asarray(sel_in)[bs][:, gs]
+        ref = self.oracle.decode(q_o, gate_o, sel_override=sel_o)
         sel_gpu = g["sel_idx"]
         if sel_in is None:
-            for b in range(w.batch):
+            for b in range(len(bs)):
                 nb = -(-int(self.oracle.lens[b]) // w.block_size)
-                for gg in range(w.n_kv_heads):
+                for gg in range(len(gs)):
                     msg = check_selection(sel_gpu[b, gg], ref["lg"][b][gg], nb, w.top_k)
                     if msg:
-                        rep.failures.append(f"step {s} b {b} g {gg}: {msg}")
+                        rep.failures.append(f"step {s} b {bs[b]} g {gs[gg]}: {msg}")
                     if not np.array_equal(sel_gpu[b, gg], ref["sel"][b, gg]):
                         rep.sel_equal = False
                         rep.near_ties += 1
@@ -171,9 +202,9 @@ class ParityRun:
                         rep.errors["lg_abs"] = max(rep.errors.get("lg_abs", 0.0),
                                                    float(np.abs(g["lg"][b, gg, js] - lg_ref).max()))
             if not rep.sel_equal:
-                ref = self.oracle.decode(q_np, self.gate_np, sel_override=sel_gpu)
+                ref = self.oracle.decode(q_o, gate_o, sel_override=sel_gpu)
         else:
-            if not np.array_equal(sel_gpu, np.asarray(sel_in)):
+            if not np.array_equal(sel_gpu, sel_o):
                 rep.failures.append("sel_idx output != sel_in")
         for k, tol in (("o", OUT_REL), ("o_sparse", OUT_REL), ("o_rla", OUT_REL), ("d_rla", D_REL)):
             e = rel_err(g[k], ref[k])
@@ -184,13 +215,14 @@ class ParityRun:
 
     def check_state(self) -> Dict[str, float]:
         w = self.w
-        S = self.layer.s_all.cpu().numpy()
-        z = self.layer.z_all.cpu().numpy()
-        mean, var = (x.cpu().numpy() for x in self.layer.stats())
+        bs, gs = self.bs, self.gs
+        S = self.layer.s_all.cpu().numpy()[bs][:, gs]
+        z = self.layer.z_all.cpu().numpy()[bs][:, gs]
+        mean, var = (x.cpu().numpy()[bs][:, gs] for x in self.layer.stats())
         errs = {"S": 0.0, "z": 0.0, "mean": 0.0, "var": 0.0}
-        for b in range(w.batch):
+        for b in range(len(bs)):
             nfull = int(self.oracle.lens[b]) // w.block_size
-            for g in range(w.n_kv_heads):
+            for g in range(len(gs)):
                 errs["S"] = max(errs["S"], rel_err(S[b, g], self.oracle.S[b, g]))
                 errs["z"] = max(errs["z"], rel_err(z[b, g], self.oracle.z[b, g]))
                 if nfull:

@@ -1,0 +1,247 @@
+"""The C ABI without a GPU: libspla.so loads, exports every function that
+include/spla.h declares under its C name, and the host-side validation returns
+the documented status codes before anything is launched.  Device pointers
+here are never dereferenced: every call below is rejected (or completes) on
+the host, ahead of any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_linear_amd as bsl
+from block_sparse_linear_amd import SplaBuffers, SplaConfig, SplaDecodeAux, load_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spla.h")
+
+OK, INVALID, UNSUPPORTED, CAPACITY, ALIGN, HIPERR, STATE = range(7)
+FAKE = 0x7F0000000000  # 256-byte aligned stand-in for a device address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(spla_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return load_library()
+
+
+def cfg(**kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=64, top_k=16,
+                max_blocks_per_seq=40, num_pages=80, kv_dtype=1)
+    base.update(kw)
+    return SplaConfig(*[base[n] for n, _ in SplaConfig._fields_])
+
+
+def create(lib, c):
+    h = ctypes.c_void_p()
+    st = lib.spla_create(ctypes.byref(c), ctypes.byref(h))
+    return st, h
+
+
+def buffers(ws_bytes, **override):
+    b = SplaBuffers()
+    for i, (n, _) in enumerate(SplaBuffers._fields_[:-1]):
+        setattr(b, n, FAKE + i * (1 << 30))
+    b.workspace_bytes = ws_bytes
+    for k, v in override.items():
+        setattr(b, k, v)
+    return b
+
+
+def i32(vals):
+    return (ctypes.c_int32 * max(1, len(vals)))(*vals)
+
+
+def bound(lib, lens=(100, 2000), **kw):
+    c = cfg(**kw)
+    st, h = create(lib, c)
+    assert st == OK
+    ws = lib.spla_workspace_bytes(h)
+    assert lib.spla_bind(h, ctypes.byref(buffers(ws)), i32(list(lens))) == OK
+    return h, c
+
+
+def lens_of(lib, h, n):
+    out = i32([0] * n)
+    assert lib.spla_get_lens(h, out) == OK
+    return list(out)[:n]
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("spla_create", "spla_bind", "spla_append_kv", "spla_decode", "spla_decode_step", "spla_destroy"):
+        assert n in names
+    assert sorted(bsl.EXPORTED) == names
+
+
+def test_library_exports_every_declared_function(lib):
+    # a C++-mangled name would not be found under its plain C name
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define\s+SPLA_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert lib.spla_abi_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    strs = [lib.spla_status_str(i).decode() for i in range(7)]
+    assert all(strs) and len(set(strs)) == 7
+    assert lib.spla_status_str(99).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({}, OK),
+    (dict(kv_dtype=0, head_dim=64, block_size=128), OK),
+    (dict(n_q_heads=64, n_kv_heads=8), OK),                      # r = 8
+    (dict(batch=256), OK),
+    (dict(top_k=256), OK),
+    (dict(top_k=2), OK),
+    (dict(max_blocks_per_seq=16386), OK),
+    (dict(batch=0), INVALID),
+    (dict(num_pages=0), INVALID),
+    (dict(top_k=0), INVALID),
+    (dict(batch=257), UNSUPPORTED),
+    (dict(head_dim=96), UNSUPPORTED),
+    (dict(block_size=32), UNSUPPORTED),
+    (dict(n_q_heads=6, n_kv_heads=4), UNSUPPORTED),              # not a multiple
+    (dict(n_q_heads=48, n_kv_heads=2), UNSUPPORTED),             # r = 24
+    (dict(top_k=1), UNSUPPORTED),
+    (dict(top_k=257), UNSUPPORTED),
+    (dict(max_blocks_per_seq=16387), UNSUPPORTED),
+    (dict(kv_dtype=2), UNSUPPORTED),
+])
+def test_create_validation(lib, kw, expect):
+    st, h = create(lib, cfg(**kw))
+    assert st == expect
+    assert (h.value is not None) == (expect == OK)
+    if h.value:
+        lib.spla_destroy(h)
+
+
+def test_create_null_arguments(lib):
+    h = ctypes.c_void_p()
+    assert lib.spla_create(None, ctypes.byref(h)) == INVALID
+    assert lib.spla_create(ctypes.byref(cfg()), None) == INVALID
+    lib.spla_destroy(None)  # no-op
+
+
+def test_sizes(lib):
+    c = cfg(batch=3, n_kv_heads=2, n_q_heads=8, head_dim=64, max_blocks_per_seq=130, top_k=20)
+    st, h = create(lib, c)
+    assert st == OK
+    n_tiles = -(-130 // 64)
+    assert lib.spla_stats_floats(h) == 3 * 2 * n_tiles * 64 * 64
+    # error word + scores + two index lists + per-head partials, each part
+    # rounded up to 256 bytes
+    need = 256 + 3 * 2 * n_tiles * 64 * 4 + 2 * 3 * 2 * 20 * 4 + 3 * 8 * 20 * (2 * 64 + 4) * 4
+    ws = lib.spla_workspace_bytes(h)
+    assert need <= ws <= need + 4 * 256 and ws % 256 == 0
+    assert lib.spla_workspace_bytes(None) == 0 and lib.spla_stats_floats(None) == 0
+    lib.spla_destroy(h)
+
+
+def test_bind_validation(lib):
+    st, h = create(lib, cfg())
+    ws = lib.spla_workspace_bytes(h)
+    assert lib.spla_bind(h, None, None) == INVALID
+    assert lib.spla_bind(h, ctypes.byref(buffers(ws, s_all=None)), None) == INVALID
+    assert lib.spla_bind(h, ctypes.byref(buffers(ws, z_all=FAKE + 8)), None) == ALIGN
+    assert lib.spla_bind(h, ctypes.byref(buffers(ws - 1)), None) == INVALID
+    cap = 40 * 64
+    assert lib.spla_bind(h, ctypes.byref(buffers(ws)), i32([cap + 1, 0])) == INVALID
+    assert lib.spla_bind(h, ctypes.byref(buffers(ws)), i32([-1, 0])) == INVALID
+    assert lib.spla_bind(h, ctypes.byref(buffers(ws)), i32([cap, 7])) == OK
+    assert lens_of(lib, h, 2) == [cap, 7]
+    assert lib.spla_bind(h, ctypes.byref(buffers(ws)), None) == OK
+    assert lens_of(lib, h, 2) == [0, 0]
+    lib.spla_destroy(h)
+
+
+def test_unbound_handle_is_rejected(lib):
+    st, h = create(lib, cfg())
+    gate = q = out = ctypes.c_void_p(FAKE)
+    assert lib.spla_append_kv(h, 1, i32([0]), i32([1]), FAKE, FAKE, None) == STATE
+    assert lib.spla_decode(h, q, gate, out, None, None) == STATE
+    assert lib.spla_decode_step(h, FAKE, FAKE, q, gate, out, None, None) == STATE
+    lib.spla_destroy(h)
+
+
+def test_append_validation_leaves_mirror_unchanged(lib):
+    h, c = bound(lib)
+    cap = c.max_blocks_per_seq * c.block_size
+    cases = [
+        ((2, [0, 0], [1, 1]), INVALID),          # duplicate sequence
+        ((1, [2], [1]), INVALID),                # sequence out of range
+        ((1, [-1], [1]), INVALID),
+        ((1, [0], [-3]), INVALID),               # negative count
+        ((3, [0, 1, 0], [1, 1, 1]), INVALID),    # more entries than the batch
+        ((-1, [0], [1]), INVALID),
+        ((1, [1], [cap - 2000 + 1]), CAPACITY),
+        ((2, [0, 1], [1, cap]), CAPACITY),
+    ]
+    for (n, ids, cnt), expect in cases:
+        assert lib.spla_append_kv(h, n, i32(ids), i32(cnt), FAKE, FAKE, None) == expect, (n, ids, cnt)
+        assert lens_of(lib, h, 2) == [100, 2000]
+    # nothing to do: accepted without a launch
+    assert lib.spla_append_kv(h, 0, None, None, None, None, None) == OK
+    assert lib.spla_append_kv(h, 2, i32([0, 1]), i32([0, 0]), None, None, None) == OK
+    assert lens_of(lib, h, 2) == [100, 2000]
+    # rows present but no K/V pointer, or misaligned ones
+    assert lib.spla_append_kv(h, 1, i32([0]), i32([4]), None, FAKE, None) == INVALID
+    assert lib.spla_append_kv(h, 1, i32([0]), i32([4]), FAKE + 2, FAKE, None) == ALIGN
+    assert lens_of(lib, h, 2) == [100, 2000]
+    lib.spla_destroy(h)
+
+
+def test_decode_validation(lib):
+    h, c = bound(lib, lens=(0, 500))
+    P = ctypes.c_void_p
+    # an empty sequence cannot be decoded
+    assert lib.spla_decode(h, P(FAKE), P(FAKE), P(FAKE), None, None) == INVALID
+    lib.spla_destroy(h)
+
+    h, c = bound(lib, lens=(64, 500))
+    assert lib.spla_decode(h, None, P(FAKE), P(FAKE), None, None) == INVALID
+    assert lib.spla_decode(h, P(FAKE + 4), P(FAKE), P(FAKE), None, None) == ALIGN
+    aux = SplaDecodeAux()
+    aux.o_rla = FAKE + 8
+    assert lib.spla_decode(h, P(FAKE), P(FAKE), P(FAKE), ctypes.byref(aux), None) == ALIGN
+    aux = SplaDecodeAux()
+    aux.kernel_events = FAKE
+    aux.n_kernel_events = -1
+    assert lib.spla_decode(h, P(FAKE), P(FAKE), P(FAKE), ctypes.byref(aux), None) == INVALID
+    # the fused step takes no selection override, needs k / v, and checks capacity
+    aux = SplaDecodeAux()
+    aux.sel_in = FAKE
+    assert lib.spla_decode_step(h, FAKE, FAKE, P(FAKE), P(FAKE), P(FAKE), ctypes.byref(aux), None) == INVALID
+    assert lib.spla_decode_step(h, None, FAKE, P(FAKE), P(FAKE), P(FAKE), None, None) == INVALID
+    assert lib.spla_decode_step(h, FAKE, FAKE + 6, P(FAKE), P(FAKE), P(FAKE), None, None) == ALIGN
+    assert lens_of(lib, h, 2) == [64, 500]
+    lib.spla_destroy(h)
+
+    cap = 40 * 64
+    h, c = bound(lib, lens=(cap, 1))
+    assert lib.spla_decode_step(h, FAKE, FAKE, P(FAKE), P(FAKE), P(FAKE), None, None) == CAPACITY
+    assert lens_of(lib, h, 2) == [cap, 1]
+    lib.spla_destroy(h)
+
+
+def test_binding_raises_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        load_library(str(tmp_path / "libspla.so"))
+
+
+def test_last_hip_error_starts_clear(lib):
+    st, h = create(lib, cfg())
+    name = ctypes.c_char_p()
+    assert lib.spla_last_hip_error(h, ctypes.byref(name)) == 0
+    assert name.value == b"hipSuccess"
+    assert lib.spla_last_hip_error(None, None) == 0
+    lib.spla_destroy(h)

@@ -1,0 +1,81 @@
+"""Parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (spla_decode_step: the one-token append fused into the
+scorer's launch, then select / attend / combine; pages in shuffled order).
+
+The GPU runs the whole batch and every head; the oracle checks sampled
+(sequence, KV head) pairs: the method treats each pair on its own, so the
+oracle run on their slices of the same inputs gives exactly the values the
+full oracle would.  Each case prints its name, shapes and samples before the
+GPU work starts.
+"""
+import pytest
+
+from spla_parity import ParityRun
+from workloads import Workload, make_workload
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _run(w, steps, seqs=None, kv_heads=None, page_order="shuffled"):
+    print(f"[fullsize] {w.name}: B={w.batch} H={w.n_q_heads} G={w.n_kv_heads} d={w.head_dim} "
+          f"Bk={w.block_size} k={w.top_k} t0={w.t0[:4]}{'...' if w.batch > 4 else ''} steps={steps} "
+          f"seqs={seqs} kv_heads={kv_heads}", flush=True)
+    run = ParityRun(w, page_order=page_order, steps=steps, use_step=True, seqs=seqs, kv_heads=kv_heads)
+    failures = run.run(verbose=True)
+    assert not failures, "\n".join(failures[:20])
+
+
+@pytest.mark.timeout(600)
+def test_llama_gqa_128k_full():
+    # B=1, 128K context, GQA 32/8 x 128, Bk=64, k=32: every head checked
+    _run(make_workload("llama_gqa_128k"), steps=3)
+
+
+@pytest.mark.timeout(600)
+def test_batched_32k_full():
+    # B=16 x 32K, planted blocks: 3 sequences x 2 KV heads sampled
+    _run(make_workload("batched_32k"), steps=3, seqs=[0, 7, 15], kv_heads=[0, 5])
+
+
+@pytest.mark.timeout(900)
+def test_million_1m_full():
+    # B=1, 1M context, Bk=128, k=64 (8192 blocks): 2 KV heads sampled
+    _run(make_workload("million_1m"), steps=2, kv_heads=[2, 7])
+
+
+@pytest.mark.timeout(900)
+def test_ragged_chunked_full():
+    # B=64 ragged contexts with 8 x 256-token chunk appends per step: the
+    # shortest, the longest and sequences that get chunks, 1 KV head each
+    w = make_workload("ragged_chunked")
+    lens = list(w.t0)
+    chunked = sorted(set(int(b) for s in range(3) for b in w.chunk_plan(s)))
+    seqs = sorted({lens.index(min(lens)), lens.index(max(lens))} | set(chunked[:3]))
+    _run(w, steps=3, seqs=seqs, kv_heads=[3])
+
+
+# the selector holds KPT candidates per thread in registers, with one compiled
+# size per entry below; a sequence whose candidate count just exceeds the next
+# smaller size runs each of them (single KV head, d = 64 keeps the data small)
+SELECT_SIZES = [2, 3, 4, 6, 8, 9, 10, 12, 16, 20, 24, 32, 40, 48, 64]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("kpt", SELECT_SIZES)
+def test_selector_sizes(kpt):
+    prev = SELECT_SIZES[SELECT_SIZES.index(kpt) - 1] if kpt > 2 else 1
+    nb = prev * 256 + 2 + 37  # candidates = nb - 2 > prev * 256
+    w = Workload(name=f"sel_kpt{kpt}", batch=1, n_q_heads=2, n_kv_heads=1, head_dim=64, block_size=64,
+                 top_k=24, kv_dtype="bf16", t0=(nb * 64 - 9,), steps=2, kind="outlier", seed=500 + kpt,
+                 n_outlier=4, prefill_chunk=16384)
+    _run(w, steps=2, page_order="shuffled")
+
+
+@pytest.mark.timeout(300)
+def test_selector_max_blocks():
+    # the largest supported table: 16386 blocks per sequence, 16384 candidates
+    w = Workload(name="sel_max", batch=1, n_q_heads=2, n_kv_heads=1, head_dim=64, block_size=64,
+                 top_k=256, kv_dtype="bf16", t0=(16386 * 64 - 5,), steps=2, kind="normal", seed=599,
+                 prefill_chunk=16384)
+    assert w.max_blocks_per_seq(2) == 16386
+    _run(w, steps=2, page_order="shuffled")
