@@ -3,11 +3,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama_gqa_128k]
 
 A step is one pass of the whole decode hot path for one SPLA attention layer:
-spla_append_kv of the step's token for every sequence (page write, S_all /
-z_all update, statistics of a completed block), then spla_decode (Taylor
-block score, top-k, attend + residual linear attention, combine).  Inputs
-(the prefilled state and every step's q, k, v) are resident in HBM before
-the timed region starts.
+spla_decode_step, i.e. the append of the step's token for every sequence
+(page write, S_all / z_all update, statistics of a completed block) fused
+into the launch of the Taylor block scorer, then top-k, attend + residual
+linear attention and combine (plus the chunk appends of workloads that have
+them, through spla_append_kv).  Inputs (the prefilled state and every step's
+q, k, v) are resident in HBM before the timed region starts.
 
 The per-step footprint of the 128K workload (~26 MB) fits the 256 MB
 Infinity Cache, so the state is replicated into L_rot independent layer
@@ -17,13 +18,16 @@ time / (K * L_rot).  Every instance sees identical inputs, so their outputs
 must be bitwise equal (checked after the run).
 
 Prints one JSON line (rank 0) with the throughput, a roofline entry for the
-dominant kernel (the block scorer: its launch duration measured with HIP
-events recorded on the launch stream around that kernel) and a CPU baseline
-(the fp64 oracle timed on a bounded sample of the same workload).
+dominant kernel (the fused append + block scorer: its launch duration from
+HIP events that hipExtLaunchKernel stamps with the kernel's own begin / end
+on its launch stream; its HBM traffic from the committed rocprofv3 counter
+summary when that was taken on the current kernel sources) and a CPU
+baseline (the fp64 oracle timed on a bounded sample of the same workload).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -35,6 +39,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+# sources of the dominant kernel (k_step_score); the counter summary below is
+# only used while their hash matches the one it was taken on
+KERNEL_SOURCES = ["block_sparse_linear_amd/csrc/decode.hip", "block_sparse_linear_amd/csrc/append_items.h",
+                  "block_sparse_linear_amd/csrc/spla_common.h"]
+PMC_SUMMARY = "profiles/k_step_score_{workload}_pmc.txt"
+# plain copy of known size run by every bench (outside the timed region) so the
+# HBM byte counters can be scaled: reads and writes CALIB_BYTES each
+CALIB_BYTES = 512 << 20
 
 
 def log(msg: str) -> None:
@@ -75,6 +88,39 @@ def step_score_bytes(w, lens, s_kv: int) -> int:
     tot += w.batch * G * 2 * (d * d * 4 + d * 4)
     tot += w.batch * G * d * 2 * s_kv * 2
     return tot
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
+    counter reads for the calibration copy), or None when there is no summary
+    for this workload or the kernel sources changed since it was taken."""
+    p = os.path.join(ROOT, PMC_SUMMARY.format(workload=workload))
+    if not os.path.exists(p):
+        return None, "no counter summary"
+    kv = {}
+    with open(p) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#") and "=" in line:
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    fetch_scale = float(kv["copy_bytes"]) / (float(kv["copy_fetch_kib"]) * 1024.0)
+    write_scale = float(kv["copy_bytes"]) / (float(kv["copy_write_kib"]) * 1024.0)
+    fetch = float(kv["fetch_kib_per_dispatch"]) * 1024.0 * fetch_scale
+    write = float(kv["write_kib_per_dispatch"]) * 1024.0 * write_scale
+    return {"bytes": fetch + write, "fetch": fetch, "write": write,
+            "fetch_scale": fetch_scale, "write_scale": write_scale}, None
 
 
 def cpu_baseline(w, n_steps: int, budget_s: float) -> dict:
@@ -129,8 +175,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
-        log("multi-GPU runs are not part of this build (one GPU per process, no collectives)")
+        print(json.dumps({"error": "one GPU per process only; --gpus must be 1"}))
+        log("the SPLA decode library runs on one GPU per process and has no collectives")
         return 2
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         log("WORLD_SIZE > 1 is not supported")
@@ -192,8 +238,6 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"L_rot={L} step_bytes={sb}")
     outs = [torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev) for _ in layers]
-    allb = list(range(w.batch))
-    ones = [1] * w.batch
 
     def run_step(s, layer, out, kernel_events=None):
         # chunk appends (ragged serving preset), then the fused decode step:
@@ -269,6 +313,15 @@ def main() -> int:
                 durs[n].append(evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e-3)
         score_launch_bytes.append(step_score_bytes(w, lens_p, s_kv))
     avg = {n: float(np.mean(v)) for n, v in durs.items()}
+
+    # calibration copy for the HBM byte counters (see CALIB_BYTES)
+    calib = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    calib_out = torch.neg(calib)
+    torch.cuda.synchronize()
+    del calib, calib_out
+    traffic, why = read_traffic(w.name)
+    if traffic is None:
+        log(f"roofline traffic: null ({why})")
     sc_bytes = float(np.mean(score_launch_bytes))
     achieved = sc_bytes / avg["step_score"] / 1e9
     log("kernel us (HIP events): " + ", ".join(f"{n}={avg[n] * 1e6:.2f}" for n in names))
@@ -294,8 +347,8 @@ def main() -> int:
         "step_frac_of_peak": bytes_avg / t_step / 1e9 / HBM_PEAK_GBS,
         "kernel_us": {n: avg[n] * 1e6 for n in names},
         "roofline": {"kernel": "k_step_score", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "bytes_per_launch": sc_bytes},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic["bytes"] if traffic else None, "bytes_per_launch": sc_bytes},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, K + W, args.cpu_budget)
