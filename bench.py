@@ -316,8 +316,17 @@ def main() -> int:
 
     # calibration copy for the HBM byte counters (see CALIB_BYTES)
     calib = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
-    calib_out = torch.neg(calib)
+    calib_out = torch.empty_like(calib)
+    torch.neg(calib, out=calib_out)
     torch.cuda.synchronize()
+    # its time gives the copy bandwidth this machine reaches (read + write)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(4):
+        torch.neg(calib, out=calib_out)
+    c1.record()
+    torch.cuda.synchronize()
+    probe_gbs = 4 * 2 * CALIB_BYTES / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del calib, calib_out
     traffic, why = read_traffic(w.name)
     if traffic is None:
@@ -348,7 +357,8 @@ def main() -> int:
         "kernel_us": {n: avg[n] * 1e6 for n in names},
         "roofline": {"kernel": "k_step_score", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic["bytes"] if traffic else None, "bytes_per_launch": sc_bytes},
+                     "traffic": traffic["bytes"] if traffic else None, "bytes_per_launch": sc_bytes,
+                     "copy_probe_GBps": probe_gbs},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, K + W, args.cpu_budget)
