@@ -42,8 +42,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
 # sources of the dominant kernel (k_step_score); the counter summary below is
 # only used while their hash matches the one it was taken on
-KERNEL_SOURCES = ["block_sparse_linear_amd/csrc/decode.hip", "block_sparse_linear_amd/csrc/append_items.h",
-                  "block_sparse_linear_amd/csrc/spla_common.h"]
+KERNEL_SOURCES = ["block_sparse_linear_amd/csrc/score.hip", "block_sparse_linear_amd/csrc/append_items.h",
+                  "block_sparse_linear_amd/csrc/decode_common.h", "block_sparse_linear_amd/csrc/spla_common.h"]
 PMC_SUMMARY = "profiles/k_step_score_{workload}_pmc.txt"
 # plain copy of known size run by every bench (outside the timed region) so the
 # HBM byte counters can be scaled: reads and writes CALIB_BYTES each
@@ -172,6 +172,8 @@ def main() -> int:
     ap.add_argument("--prof-steps", type=int, default=16, help="steps of the per-kernel event pass")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused-select", type=int, default=-1, choices=(-1, 0, 1),
+                    help="selector placement: -1 automatic, 0 stand-alone kernel, 1 fused into attend")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -198,8 +200,10 @@ def main() -> int:
     mb = w.max_blocks_per_seq(total_steps)
 
     def new_layer():
-        return SplaLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k, mb,
-                         kv_dtype=w.kv_dtype, device="cuda:0")
+        layer = SplaLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k, mb,
+                          kv_dtype=w.kv_dtype, device="cuda:0")
+        layer.set_fused_select(args.fused_select)
+        return layer
 
     t0 = time.time()
     base = new_layer()
@@ -287,7 +291,7 @@ def main() -> int:
     # HIP events, which take that kernel's begin and end timestamps on its
     # launch stream.  The steps are enqueued while a spin kernel holds the
     # GPU, so that the GPU then runs them back to back as in the graphs.
-    names = ["step_score", "select", "attend", "combine"]
+    names = layers[0].launch_plan(step=True)  # e.g. step_score, select_attend, combine
     import ctypes
     ev_sets = []
     for s in range(W + K, W + K + P):
@@ -300,6 +304,8 @@ def main() -> int:
     torch.cuda._sleep(int(2.4e9 * 0.3))
     for s, sets in zip(range(W + K, W + K + P), ev_sets):
         for layer, out, evs in zip(layers, outs, sets):
+            if layer.launch_plan(step=True) != names:
+                raise RuntimeError("the launch plan changed during the per-kernel pass")
             handles = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
             run_step(s, layer, out, kernel_events=handles)
     torch.cuda.synchronize()
@@ -355,6 +361,7 @@ def main() -> int:
         "step_GBps": bytes_avg / t_step / 1e9,
         "step_frac_of_peak": bytes_avg / t_step / 1e9 / HBM_PEAK_GBS,
         "kernel_us": {n: avg[n] * 1e6 for n in names},
+        "kernels": names,
         "roofline": {"kernel": "k_step_score", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic["bytes"] if traffic else None, "bytes_per_launch": sc_bytes,

@@ -31,8 +31,13 @@ SPLA_F32, SPLA_BF16 = 0, 1
 EXPORTED = [
     "spla_create", "spla_destroy", "spla_workspace_bytes", "spla_stats_floats", "spla_bind",
     "spla_append_kv", "spla_decode", "spla_decode_step", "spla_get_lens", "spla_status_str", "spla_abi_version",
-    "spla_last_hip_error",
+    "spla_last_hip_error", "spla_set_tuning", "spla_launch_plan",
 ]
+
+# spla_kernel ids (include/spla.h) -> kernel names
+KERNELS = {1: "score", 2: "step_score", 3: "select", 4: "attend", 5: "select_attend", 6: "combine"}
+CALL_DECODE, CALL_DECODE_SEL_IN, CALL_DECODE_STEP = 0, 1, 2
+TUNE_FUSED_SELECT = 0
 
 
 class SplaConfig(ctypes.Structure):
@@ -101,6 +106,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spla_abi_version.restype = ctypes.c_int32
     lib.spla_last_hip_error.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_char_p)]
     lib.spla_last_hip_error.restype = ctypes.c_int32
+    lib.spla_set_tuning.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
+    lib.spla_set_tuning.restype = ctypes.c_int
+    lib.spla_launch_plan.argtypes = [ctypes.c_void_p, ctypes.c_int32, I32P, ctypes.c_int32]
+    lib.spla_launch_plan.restype = ctypes.c_int32
     if path is None:
         _lib = lib
     return lib
@@ -164,6 +173,17 @@ class SplaHandle:
         arr = (ctypes.c_int32 * self.cfg.batch)()
         _check(self.lib.spla_get_lens(self.h, arr), "spla_get_lens")
         return list(arr)
+
+    def set_tuning(self, key: int, value: int) -> None:
+        _check(self.lib.spla_set_tuning(self.h, key, value), "spla_set_tuning")
+
+    def launch_plan(self, call: int):
+        """Names of the kernels the next call of kind `call` launches, in order."""
+        arr = (ctypes.c_int32 * 8)()
+        n = self.lib.spla_launch_plan(self.h, call, arr, 8)
+        if n < 0:
+            raise ValueError(f"spla_launch_plan: bad call {call}")
+        return [KERNELS[int(arr[i])] for i in range(n)]
 
     def append_raw(self, seq_ids, n_new, k_ptr: int, v_ptr: int, stream: int) -> int:
         return self.lib.spla_append_kv(self.h, len(seq_ids), _i32_array(seq_ids), _i32_array(n_new),
@@ -238,6 +258,14 @@ class SplaLayer:
     @property
     def lens(self):
         return self.handle.lens()
+
+    def set_fused_select(self, mode: int) -> None:
+        """-1 automatic, 0 stand-alone selector, 1 fused select + attend where supported."""
+        self.handle.set_tuning(TUNE_FUSED_SELECT, mode)
+
+    def launch_plan(self, step: bool = True, sel_in: bool = False):
+        call = CALL_DECODE_STEP if step else (CALL_DECODE_SEL_IN if sel_in else CALL_DECODE)
+        return self.handle.launch_plan(call)
 
     def _stream(self) -> int:
         return self.torch.cuda.current_stream(self.device).cuda_stream

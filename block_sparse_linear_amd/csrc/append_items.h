@@ -88,6 +88,25 @@ __device__ void append_page_rows(const StateRefs& a, const AppendEntry& E, int i
   }
 }
 
+// the page row of entry E's first appended token, KV head g only (threads
+// 0 .. d * element size / 16 - 1 copy one 16-byte piece each of k and v)
+template <bool BF16>
+__device__ void append_page_row_head(const StateRefs& a, const AppendEntry& E, int g) {
+  const int vec_per_row = a.d * (BF16 ? 2 : 4) / 16;
+  const int v = threadIdx.x;
+  if (v >= vec_per_row) return;
+  const int p = E.t0;
+  const int page = a.block_table[(size_t)E.seq * a.max_blocks + p / a.bk];
+  if (page < 0 || page >= a.num_pages) {
+    if (v == 0) atomicOr(a.err, kErrPage);
+    return;
+  }
+  const size_t src = ((size_t)E.row * a.G + g) * vec_per_row + v;
+  const size_t dst = (((size_t)page * a.G + g) * a.bk + (p % a.bk)) * vec_per_row + v;
+  reinterpret_cast<uint4*>(a.k_pages)[dst] = reinterpret_cast<const uint4*>(a.k_new)[src];
+  reinterpret_cast<uint4*>(a.v_pages)[dst] = reinterpret_cast<const uint4*>(a.v_new)[src];
+}
+
 // mean and population variance (two passes) of block j of entry E's
 // sequence, KV head g, completed by this append: tokens older than the
 // append come from the pages, the new ones from k_new

@@ -1,0 +1,172 @@
+// Block scorer: log-domain second-order Taylor score of every candidate block,
+// summed over the query heads of a KV group (SPLA Technical Summary 2.1, score
+// formula with the diagonal covariance of its implementation paragraph), and
+// the fused decode-step kernel that also carries the one-token append.
+#include "decode_common.h"
+
+namespace spla {
+
+namespace {
+
+// ============================================================== score
+// grid (score_tiles, G, B); lane = block within a 64-block tile, the four
+// wavefronts split the channels and meet in LDS.  Every wavefront issues its
+// query loads and then all of its statistics loads before the first wait.
+template <bool BF16, int R, int D>
+__device__ void score_tile(const DecodeArgs& a, const int t, const int g, const int b) {
+  constexpr int NC4 = D / 16;  // channel quartets per wavefront
+  constexpr int CW = D / 4;    // channels per wavefront
+  constexpr int QPL = (R * CW + 63) / 64;  // query elements per lane
+  __shared__ float4 qs[4][R][CW / 4];
+  __shared__ float4 q2s[4][R][CW / 4];
+  __shared__ float red[4][2 * R][kTile];
+  const int T = a.lens[b];
+  SPLA_SCALARS_READY("s"(T), "s"(a.bk), "s"(a.top_k), "s"(a.H), "s"(a.G), "s"(a.n_tiles), "s"(a.q),
+                     "s"(a.blk_mean), "s"(a.blk_var));
+  const int nb = (T + a.bk - 1) / a.bk;
+  if (nb <= a.top_k) return;  // every block is selected, nothing to rank
+  const int j0 = t * kTile;
+  if (j0 > nb - 2) return;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64;
+  // queries of this wavefront's channel quarter
+  // (loads are unconditional, from clamped in-range addresses, and masked
+  // afterwards: a load under a branch makes the compiler wait for it there)
+  float qv[QPL];
+#pragma unroll
+  for (int i = 0; i < QPL; ++i) {
+    const int e = min(lane + 64 * i, R * CW - 1);
+    const int h = e / CW, c = e - h * CW;
+    qv[i] = load_elem<BF16>(a.q, ((size_t)b * a.H + g * R + h) * D + w * CW + c);
+  }
+  // statistics of the tile: 64 blocks x this wavefront's channels
+  const float4* mean4 = reinterpret_cast<const float4*>(a.blk_mean);
+  const float4* var4 = reinterpret_cast<const float4*>(a.blk_var);
+  const size_t base = (((size_t)b * a.G + g) * a.n_tiles + t) * (size_t)(D / 4) * kTile + (size_t)(w * NC4) * kTile + lane;
+  float4 m[NC4], v[NC4];
+#pragma unroll
+  for (int i = 0; i < NC4; ++i) m[i] = mean4[base + (size_t)i * kTile];
+#pragma unroll
+  for (int i = 0; i < NC4; ++i) v[i] = var4[base + (size_t)i * kTile];
+  // keep every load above this point: the whole tile is in flight before the
+  // first use
+  __builtin_amdgcn_sched_barrier(0);
+  // wavefront-private staging of q and q^2 (LDS operations of one wavefront
+  // complete in order, so no barrier is needed)
+  float* qf = reinterpret_cast<float*>(&qs[w][0][0]);
+  float* q2f = reinterpret_cast<float*>(&q2s[w][0][0]);
+#pragma unroll
+  for (int i = 0; i < QPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < R * CW) {
+      qf[e] = qv[i];
+      q2f[e] = qv[i] * qv[i];
+    }
+  }
+  float dot[R], qq[R];
+#pragma unroll
+  for (int h = 0; h < R; ++h) dot[h] = qq[h] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC4; ++i) {
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      const float4 q = qs[w][h][i];
+      const float4 q2 = q2s[w][h][i];
+      dot[h] = fmaf(q.x, m[i].x, dot[h]);
+      dot[h] = fmaf(q.y, m[i].y, dot[h]);
+      dot[h] = fmaf(q.z, m[i].z, dot[h]);
+      dot[h] = fmaf(q.w, m[i].w, dot[h]);
+      qq[h] = fmaf(q2.x, v[i].x, qq[h]);
+      qq[h] = fmaf(q2.y, v[i].y, qq[h]);
+      qq[h] = fmaf(q2.z, v[i].z, qq[h]);
+      qq[h] = fmaf(q2.w, v[i].w, qq[h]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    red[w][h][lane] = dot[h];
+    red[w][R + h][lane] = qq[h];
+  }
+  __syncthreads();
+  // finalisation spread over the four wavefronts: lane = (block, head), the
+  // R lanes of a block combine their log scores with DPP (max, exp-sum)
+  constexpr int BPW = 64 / R;  // blocks per wavefront pass
+  const float half_inv_d = 0.5f / (float)D;
+  const int h = lane % R;
+  for (int blk0 = w * BPW; blk0 < kTile; blk0 += 4 * BPW) {
+    const int blk = blk0 + lane / R;
+    const float dd = (red[0][h][blk] + red[1][h][blk]) + (red[2][h][blk] + red[3][h][blk]);
+    const float vv = (red[0][R + h][blk] + red[1][R + h][blk]) + (red[2][R + h][blk] + red[3][R + h][blk]);
+    const float ls = dd * a.inv_sqrt_d + __logf(1.f + fmaxf(vv, 0.f) * half_inv_d);
+    float lg = ls;
+    if constexpr (R > 1) {
+      float mx = ls;
+      mx = fmaxf(mx, dpp_f<kDppXor1>(mx, mx));
+      if constexpr (R > 2) mx = fmaxf(mx, dpp_f<kDppXor2>(mx, mx));
+      if constexpr (R > 4) mx = fmaxf(mx, dpp_f<kDppRowHalfMirror>(mx, mx));
+      float e = __expf(ls - mx);
+      e += dpp_f<kDppXor1>(0.f, e);
+      if constexpr (R > 2) e += dpp_f<kDppXor2>(0.f, e);
+      if constexpr (R > 4) e += dpp_f<kDppRowHalfMirror>(0.f, e);
+      lg = mx + __logf(e);
+    }
+    const int j = j0 + blk;
+    if (h == 0) {
+      const bool cand = j >= 1 && j <= nb - 2;
+      a.lg[((size_t)b * a.G + g) * (size_t)(a.n_tiles * kTile) + j] = cand ? lg : -INFINITY;
+      if (a.lg_out && cand) a.lg_out[((size_t)b * a.G + g) * a.max_blocks + j] = lg;
+    }
+  }
+}
+
+template <bool BF16, int R, int D>
+__global__ __launch_bounds__(kThreads) void k_score(const DecodeArgs a) {
+  score_tile<BF16, R, D>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Fused decode step, first launch, grid (score_tiles + chunks + 1, G, B):
+// for each (b, g), the scorer's tiles, then the S_all / z_all update of this
+// step's token in row chunks, then the token's page row and the statistics
+// of the block it completes.  The two parts are independent: the scorer reads
+// statistics of candidate blocks 1..nb-2 only, all completed by earlier
+// appends, and neither pages nor S_all.
+template <bool BF16, int R, int D>
+__global__ __launch_bounds__(kThreads) void k_step_score(const StepArgs a) {
+  constexpr int kChunks = D / (1024 / D);  // S_all row chunks per (b, g)
+  const DecodeArgs& dc = a.dec;
+  const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tiles = dc.score_tiles;
+  const int T = dc.lens[b];  // after the append
+  SPLA_SCALARS_READY("s"(tiles), "s"(T), "s"(dc.bk), "s"(dc.top_k), "s"(dc.H), "s"(dc.G), "s"(dc.n_tiles),
+                     "s"(dc.q), "s"(dc.blk_mean), "s"(dc.blk_var), "s"(a.st.k_new), "s"(a.st.v_new),
+                     "s"(a.st.s_all), "s"(a.st.z_all));
+  if (x < tiles) {
+    score_tile<BF16, R, D>(dc, x, g, b);
+    return;
+  }
+  const AppendEntry E{b, 1, T - 1, b};
+  if (x < tiles + kChunks) {
+    append_state_rows<BF16>(a.st, E, g, x - tiles);
+    return;
+  }
+  append_page_row_head<BF16>(a.st, E, g);
+  if (T % dc.bk == 0) append_block_stats<BF16>(a.st, E, T / dc.bk - 1, g);
+}
+
+}  // namespace
+
+hipError_t launch_score(const DecodeArgs& a, bool bf16, const Launch& l) {
+  const dim3 grid(a.score_tiles, a.G, a.B);
+  if (a.score_tiles == 0) return hipSuccess;
+  if (bf16) SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_score<true, RR, DD>, grid, l, a))
+  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_score<false, RR, DD>, grid, l, a))
+}
+
+hipError_t launch_step_score(const StepArgs& a, bool bf16, const Launch& l) {
+  const int chunks = a.dec.d / (1024 / a.dec.d);
+  const dim3 grid(a.dec.score_tiles + chunks + 1, a.dec.G, a.dec.B);
+  if (bf16) SPLA_DISPATCH_RD(a.dec.r, a.dec.d, launch_kernel(k_step_score<true, RR, DD>, grid, l, a))
+  SPLA_DISPATCH_RD(a.dec.r, a.dec.d, launch_kernel(k_step_score<false, RR, DD>, grid, l, a))
+}
+
+}  // namespace spla

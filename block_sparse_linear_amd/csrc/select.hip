@@ -1,0 +1,55 @@
+// Stand-alone selector: grid (G, B), one (sequence, KV head) per workgroup;
+// writes the ascending selection and its page ids for the attend kernel.
+#include "select_core.h"
+
+namespace spla {
+
+namespace {
+
+template <int KPT>
+__global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
+  __shared__ SelectLds L;
+  const int g = blockIdx.x, b = blockIdx.y;
+  SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.top_k), "s"(a.max_blocks), "s"(a.block_table), "s"(a.lg),
+                     "s"(a.G), "s"(a.n_tiles));
+  const int nb = n_blocks(a, b);
+  SelectKeys<KPT> k;
+  select_load<KPT>(a, g, b, nb, k);  // first: nothing else waits on memory before it
+  const size_t row = ((size_t)b * a.G + g) * a.top_k;
+  int32_t* out = a.sel + row;
+  int32_t* out2 = a.sel_out ? a.sel_out + row : nullptr;
+  int32_t* pages = a.sel_page + row;
+  if (nb <= a.top_k) {
+    const int32_t* btab = a.block_table + (size_t)b * a.max_blocks;
+    for (int s = threadIdx.x; s < a.top_k; s += kThreads) {
+      out[s] = s < nb ? s : -1;
+      if (out2) out2[s] = s < nb ? s : -1;
+      pages[s] = s < nb ? btab[s] : -1;
+    }
+    return;
+  }
+  select_core<KPT>(a, nb, k, L, [&](int pos, int id, int page) {
+    out[pos] = id;
+    if (out2) out2[pos] = id;
+    pages[pos] = page;
+  });
+}
+
+template <int K, int... Ks>
+hipError_t launch_select_sized(const DecodeArgs& a, const Launch& l, int nc, SelectSizes<K, Ks...>) {
+  if (nc <= K * kThreads) return launch_kernel(k_select<K>, dim3(a.G, a.B), l, a);
+  if constexpr (sizeof...(Ks) == 0) {
+    return hipErrorInvalidValue;
+  } else {
+    return launch_select_sized(a, l, nc, SelectSizes<Ks...>{});
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select(const DecodeArgs& a, const Launch& l) {
+  return launch_select_sized(a, l, max_candidates(a),
+                             SelectSizes<1, 2, 3, 4, 6, 8, 9, 10, 12, 16, 20, 24, 32, 40, 48, 64>{});
+}
+
+}  // namespace spla

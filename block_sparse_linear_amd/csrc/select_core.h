@@ -1,0 +1,293 @@
+// Top-k block selection of one (sequence, KV head) by one 256-thread
+// workgroup: the sink (block 0), the current block (nb - 1) and the top_k - 2
+// candidates 1 .. nb - 2 with the largest group log score, ties to the
+// smaller block id (SPLA Technical Summary 1 and 2.1: only the most relevant
+// blocks are loaded; the Baidu Cloud sparse-attention article, section 5:
+// score, sort, keep the top K).  Shared by the stand-alone selector and the
+// fused select + attend kernel.
+#pragma once
+
+#include <type_traits>
+
+#include "decode_common.h"
+
+namespace spla {
+namespace {
+
+constexpr int kSelMax = kMaxBlocksPerSeq - 2;  // candidates per (b, g) the selector handles
+constexpr int kSelLevels = 12;                 // bucket refinement levels
+constexpr int kSelRank = 256;                  // threshold-bucket size ranked exactly
+
+// bucket of x at one refinement level: monotone non-decreasing in x
+__device__ __forceinline__ int sel_bucket(float x, float lo, float scale) {
+  const float f = (x - lo) * scale;
+  return f >= 255.f ? 255 : (f <= 0.f ? 0 : (int)f);
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// LDS of the selector (lists padded with sentinels so the rank counts read
+// them four at a time)
+struct __attribute__((aligned(16))) SelectLds {
+  int hist[4][256];  // one histogram per wavefront
+  float mkey[kSelRank];
+  int midx[kSelRank];
+  int slist[256];
+  int spage[256];          // page of slist[i]
+  int mpage[kSelRank];     // page of midx[i]
+  float s_mn[4], s_mx[4];
+  int s_cnt[4];
+  int s_bt, s_above, s_cbt, s_n, s_nm;
+};
+
+// one thread's candidates: scores and page ids (candidate i = thread + 256 u,
+// block id i + 1), plus the pages of the sink and the current block
+template <int KPT>
+struct SelectKeys {
+  float x[KPT];
+  int pg[KPT];
+  int pg_sink, pg_cur;
+};
+
+// Issue the loads of a selection.  Valid for any nb >= 1 (addresses are
+// clamped into the score row and the block table row), so a kernel can issue
+// them first, before it knows whether there is anything to rank.
+template <int KPT>
+__device__ __forceinline__ void select_load(const DecodeArgs& a, int g, int b, int nb, SelectKeys<KPT>& k) {
+  const int nc = max(nb - 2, 1);
+  const int last = a.max_blocks - 1;
+  const int32_t* btab = a.block_table + (size_t)b * a.max_blocks;
+  const float* row = a.lg + ((size_t)b * a.G + g) * (size_t)(a.n_tiles * kTile) + 1;  // row[i] = LG(i + 1)
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int i = min((int)threadIdx.x + u * kThreads, nc - 1);
+    k.x[u] = row[i];
+    k.pg[u] = btab[min(i + 1, last)];
+  }
+  k.pg_sink = btab[0];
+  k.pg_cur = btab[min(max(nb - 1, 0), last)];
+}
+
+// Append the keys flagged in `flags` (bit u: key u of this thread) to an LDS
+// list, one LDS atomic per wavefront; store(u, position) is called for each.
+// A key step where no lane of the wavefront has a flag costs one ballot and
+// a scalar branch.
+template <int KPT, typename Mask, typename Store>
+__device__ __forceinline__ void append_flagged(Mask flags, int* counter, Store&& store) {
+  int total = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) total += __popcll(__ballot((flags >> u) & 1));
+  if (total == 0) return;
+  int base = 0;
+  if ((threadIdx.x & 63) == 0) base = atomicAdd(counter, total);
+  base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const uint64_t m = __ballot((flags >> u) & 1);
+    if (m != 0) {
+      if ((flags >> u) & 1) store(u, base + lanes_below(m));
+      base += __popcll(m);
+    }
+  }
+}
+
+// Bucket select over the scores held in registers (KPT per thread,
+// KPT * 256 >= nb - 2): the scores are binned into 256 buckets spread over
+// [min, max] of the remaining candidates; every candidate in a bucket above
+// the one holding the k'-th largest is taken, and that bucket is refined the
+// same way until it holds at most kSelRank candidates (then ranked exactly by
+// (score desc, id asc)) or only equal scores (then taken by ascending id).
+// The bucket index is a monotone function of the score, so the result is the
+// exact top k'.  The chosen ids are put in ascending order by a rank count.
+//
+// Requires nb > top_k and the keys of select_load; every thread of the
+// workgroup must call it.  For each output position pos in [0, top_k),
+// exactly one thread calls emit(pos, block id, page id).
+template <int KPT, typename Emit>
+__device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const SelectKeys<KPT>& k, SelectLds& L,
+                                            Emit&& emit) {
+  using Mask = typename std::conditional<(KPT <= 32), uint32_t, uint64_t>::type;
+  const int nc = nb - 2;
+  const int kp = a.top_k - 2;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  Mask memb = 0, above = 0;  // bit u: key u still in the threshold bucket / already taken
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) memb |= (Mask)((int)threadIdx.x + u * kThreads < nc) << u;
+  if (threadIdx.x == 0) {
+    L.s_n = 0;
+    L.s_nm = 0;
+  }
+  L.mkey[threadIdx.x] = -INFINITY;
+  L.midx[threadIdx.x] = 0x7fffffff;
+  L.slist[threadIdx.x] = 0x7fffffff;
+  // the counters and sentinels above are used by every wavefront (the loop
+  // below may not run at all); this barrier waits on LDS only, not on the
+  // score loads in flight
+  __syncthreads();
+  int need = kp;
+  bool equal_mode = false;
+  // members of the threshold bucket: all candidates at first, then the count
+  // the histogram gives for the bucket picked (no extra pass to count them)
+  int cnt = nc;
+  for (int lev = 0; cnt > kSelRank; ++lev) {
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const bool in = (memb >> u) & 1;
+      mn = fminf(mn, in ? k.x[u] : INFINITY);
+      mx = fmaxf(mx, in ? k.x[u] : -INFINITY);
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) L.hist[q][threadIdx.x] = 0;
+    if (lane == 0) {
+      L.s_mn[wv] = mn;
+      L.s_mx[wv] = mx;
+    }
+    __syncthreads();
+    mn = fminf(fminf(L.s_mn[0], L.s_mn[1]), fminf(L.s_mn[2], L.s_mn[3]));
+    mx = fmaxf(fmaxf(L.s_mx[0], L.s_mx[1]), fmaxf(L.s_mx[2], L.s_mx[3]));
+    const float range = mx - mn;
+    if (!(range > 0.f) || !(range < INFINITY) || lev == kSelLevels) {
+      equal_mode = true;  // equal scores (or a degenerate range): take by id
+      if (range > 0.f && threadIdx.x == 0) atomicOr(a.err, kErrSel);
+      break;
+    }
+    const float scale = 256.f / range;
+    int bkt[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      bkt[u] = sel_bucket(k.x[u], mn, scale);
+      atomicAdd(&L.hist[wv][bkt[u]], (int)((memb >> u) & 1));  // non-members add 0: no branch
+    }
+    __syncthreads();
+    if (wv == 0) {
+      int c[4], sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int bin = 255 - 4 * lane - q;
+        c[q] = (L.hist[0][bin] + L.hist[1][bin]) + (L.hist[2][bin] + L.hist[3][bin]);
+        sum += c[q];
+      }
+      int run = wave_incl_scan_i(sum) - sum;  // keys in buckets above this lane's
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (run < need && run + c[q] >= need) {
+          L.s_bt = 255 - 4 * lane - q;
+          L.s_above = run;
+          L.s_cbt = c[q];
+        }
+        run += c[q];
+      }
+    }
+    __syncthreads();
+    const int bt = L.s_bt;
+    need -= L.s_above;
+    cnt = L.s_cbt;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const Mask bit = (Mask)1 << u;
+      const bool in = (memb & bit) != 0;
+      above |= (in && bkt[u] > bt) ? bit : (Mask)0;
+      memb &= (in && bkt[u] == bt) ? ~(Mask)0 : ~bit;
+    }
+  }
+  if (equal_mode) {
+    // equal scores: the `need` smallest ids among the members; find the id
+    // bound by bisection on counts
+    int lo = 0, hi = nc;  // smallest X with #members(id < X) >= need
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      int c = 0;
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) c += ((memb >> u) & 1) && ((int)threadIdx.x + u * kThreads < mid);
+      c = wave_sum_i(c);
+      __syncthreads();
+      if (lane == 0) L.s_cnt[wv] = c;
+      __syncthreads();
+      c = (L.s_cnt[0] + L.s_cnt[1]) + (L.s_cnt[2] + L.s_cnt[3]);
+      if (c >= need) hi = mid; else lo = mid + 1;
+    }
+    Mask low = 0;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      low |= (((memb >> u) & 1) && (int)threadIdx.x + u * kThreads < lo) ? ((Mask)1 << u) : (Mask)0;
+    above |= low;
+    memb = 0;
+  }
+  // every key above a threshold bucket (or taken by id) goes to the chosen
+  // list; the final bucket's keys go to the ranking list
+  append_flagged<KPT>(above, &L.s_n, [&](int u, int pos) {
+    L.slist[pos] = threadIdx.x + u * kThreads;
+    L.spage[pos] = k.pg[u];
+  });
+  append_flagged<KPT>(memb, &L.s_nm, [&](int u, int pos) {
+    L.mkey[pos] = k.x[u];
+    L.midx[pos] = threadIdx.x + u * kThreads;
+    L.mpage[pos] = k.pg[u];
+  });
+  __syncthreads();
+  // the final bucket (<= kSelRank candidates): exact rank by (score desc, id asc)
+  const int nm = L.s_nm;
+  if (nm > 0) {
+    bool take = false;
+    int my = 0, mypg = 0;
+    if ((int)threadIdx.x < nm) {
+      const float xv = L.mkey[threadIdx.x];
+      my = L.midx[threadIdx.x];
+      mypg = L.mpage[threadIdx.x];
+      int rank = 0;
+#pragma unroll 4
+      for (int v = 0; v < nm; v += 4) {
+        const float4 y = *reinterpret_cast<const float4*>(&L.mkey[v]);
+        const int4 iy = *reinterpret_cast<const int4*>(&L.midx[v]);
+        rank += (y.x > xv) || (y.x == xv && iy.x < my);
+        rank += (y.y > xv) || (y.y == xv && iy.y < my);
+        rank += (y.z > xv) || (y.z == xv && iy.z < my);
+        rank += (y.w > xv) || (y.w == xv && iy.w < my);
+      }
+      take = rank < need;
+    }
+    append_flagged<1>((uint32_t)take, &L.s_n, [&](int, int pos) {
+      L.slist[pos] = my;
+      L.spage[pos] = mypg;
+    });
+    __syncthreads();
+  }
+  // ascending order by a rank count over the kp chosen ids
+  if ((int)threadIdx.x < kp) {
+    const int v = L.slist[threadIdx.x];
+    int pos = 0;
+#pragma unroll 4
+    for (int u = 0; u < kp; u += 4) {
+      const int4 y = *reinterpret_cast<const int4*>(&L.slist[u]);
+      pos += (y.x < v) + (y.y < v) + (y.z < v) + (y.w < v);
+    }
+    emit(1 + pos, v + 1, L.spage[threadIdx.x]);
+  } else if ((int)threadIdx.x == kp) {
+    emit(0, 0, k.pg_sink);
+  } else if ((int)threadIdx.x == kp + 1) {
+    emit(kp + 1, nb - 1, k.pg_cur);
+  }
+}
+
+// keys-per-thread sizes compiled for a selector: the smallest one that holds
+// the longest sequence's candidates is launched
+template <int... Ks>
+struct SelectSizes {};
+
+// candidates of the longest sequence that has more blocks than top_k (0 if none)
+inline int max_candidates(const DecodeArgs& a) {
+  int nc = 0;
+  for (int b = 0; b < a.B; ++b) {
+    const int nb = (a.lens[b] + a.bk - 1) / a.bk;
+    if (nb > a.top_k) nc = nc > nb - 2 ? nc : nb - 2;
+  }
+  return nc;
+}
+
+}  // namespace
+}  // namespace spla

@@ -19,6 +19,7 @@ struct spla_handle {
   spla_buffers buf{};
   std::vector<int32_t> lens;
   hipError_t last_hip = hipSuccess;  // status of the last launch that failed
+  int32_t fused_select = -1;         // SPLA_TUNE_FUSED_SELECT
   // workspace layout (bytes)
   size_t off_lg = 0, off_sel = 0, off_page = 0, off_part = 0, ws_bytes = 0;
 };
@@ -165,12 +166,70 @@ spla_status hip_fail(spla_handle* h, hipError_t e) {
   return SPLA_ERR_HIP;
 }
 
-spla_status launch_decode_tail(spla_handle* h, const DecodeArgs& a, bool bf16, LaunchSeq& ls) {
-  hipError_t e;
-  if ((e = launch_select(a, ls.next())) != hipSuccess) return hip_fail(h, e);
-  if ((e = launch_attend(a, bf16, ls.next())) != hipSuccess) return hip_fail(h, e);
-  if ((e = launch_combine(a, bf16, ls.next())) != hipSuccess) return hip_fail(h, e);
-  return SPLA_OK;
+// (sequence, KV head) pairs up to which the automatic choice fuses the
+// selector into the attend kernel: there the decode is a chain of latency-
+// bound launches and removing one pays for the selection being recomputed
+// by every attend workgroup
+constexpr int kAutoFusedPairs = 64;
+
+bool use_fused_select(const spla_handle* h, const DecodeArgs& a, bool bf16) {
+  if (h->fused_select == 0 || !select_attend_supported(a, bf16)) return false;
+  return h->fused_select == 1 || a.B * a.G <= kAutoFusedPairs;
+}
+
+// the kernels one call launches, in order (SPLA_KERNEL_*); the single source
+// of truth for both the launches and spla_launch_plan
+int decode_plan(const spla_handle* h, const DecodeArgs& a, int32_t call, int32_t* k) {
+  const bool bf16 = h->cfg.kv_dtype == SPLA_BF16;
+  int n = 0;
+  if (call == SPLA_CALL_DECODE_STEP) {
+    k[n++] = SPLA_KERNEL_STEP_SCORE;
+  } else if (call == SPLA_CALL_DECODE && a.score_tiles > 0) {
+    k[n++] = SPLA_KERNEL_SCORE;
+  }
+  if (call == SPLA_CALL_DECODE_SEL_IN) {
+    k[n++] = SPLA_KERNEL_ATTEND;
+  } else if (use_fused_select(h, a, bf16)) {
+    k[n++] = SPLA_KERNEL_SELECT_ATTEND;
+  } else {
+    k[n++] = SPLA_KERNEL_SELECT;
+    k[n++] = SPLA_KERNEL_ATTEND;
+  }
+  k[n++] = SPLA_KERNEL_COMBINE;
+  return n;
+}
+
+constexpr int kMaxPlan = 4;
+
+// launch a plan; `step` carries the fused first kernel of spla_decode_step
+hipError_t run_plan(const spla_handle* h, const DecodeArgs& a, const StepArgs* step, const int32_t* plan, int n,
+                    LaunchSeq& ls) {
+  const bool bf16 = h->cfg.kv_dtype == SPLA_BF16;
+  for (int i = 0; i < n; ++i) {
+    const Launch l = ls.next();
+    hipError_t e = hipErrorInvalidValue;
+    switch (plan[i]) {
+      case SPLA_KERNEL_SCORE: e = launch_score(a, bf16, l); break;
+      case SPLA_KERNEL_STEP_SCORE: e = step ? launch_step_score(*step, bf16, l) : hipErrorInvalidValue; break;
+      case SPLA_KERNEL_SELECT: e = launch_select(a, l); break;
+      case SPLA_KERNEL_ATTEND: e = launch_attend(a, bf16, l); break;
+      case SPLA_KERNEL_SELECT_ATTEND: e = launch_select_attend(a, l); break;
+      case SPLA_KERNEL_COMBINE: e = launch_combine(a, bf16, l); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// the lengths the decode part of a step sees: after its one-token append
+void fill_step_args(spla_handle* h, const void* k_new, const void* v_new, const void* q, const float* gate,
+                    float* out, const spla_decode_aux* aux, StepArgs* a) {
+  const spla_config& c = h->cfg;
+  memset(a, 0, sizeof(*a));
+  for (int b = 0; b < c.batch; ++b) h->lens[b] += 1;
+  fill_decode_args(h, q, gate, out, aux, &a->dec);
+  fill_state_refs(h, k_new, v_new, &a->st);
+  for (int b = 0; b < c.batch; ++b) h->lens[b] -= 1;
 }
 
 }  // namespace
@@ -343,17 +402,11 @@ spla_status spla_decode(spla_handle* h, const void* q, const float* gate, float*
     if (h->lens[b] <= 0) return SPLA_ERR_INVALID_ARG;
   DecodeArgs a;
   fill_decode_args(h, q, gate, out, aux, &a);
-  const bool bf16 = c.kv_dtype == SPLA_BF16;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  LaunchSeq ls(st, aux);
-  hipError_t e;
-  if (!a.sel_in) {
-    if ((e = launch_score(a, bf16, ls.next())) != hipSuccess) return hip_fail(h, e);
-    return launch_decode_tail(h, a, bf16, ls);
-  }
-  if ((e = launch_attend(a, bf16, ls.next())) != hipSuccess) return hip_fail(h, e);
-  if ((e = launch_combine(a, bf16, ls.next())) != hipSuccess) return hip_fail(h, e);
-  return SPLA_OK;
+  int32_t plan[kMaxPlan];
+  const int n = decode_plan(h, a, a.sel_in ? SPLA_CALL_DECODE_SEL_IN : SPLA_CALL_DECODE, plan);
+  LaunchSeq ls(reinterpret_cast<hipStream_t>(stream), aux);
+  const hipError_t e = run_plan(h, a, nullptr, plan, n, ls);
+  return e == hipSuccess ? SPLA_OK : hip_fail(h, e);
 }
 
 spla_status spla_decode_step(spla_handle* h, const void* k_new, const void* v_new, const void* q, const float* gate,
@@ -370,24 +423,45 @@ spla_status spla_decode_step(spla_handle* h, const void* k_new, const void* v_ne
   for (int b = 0; b < c.batch; ++b)
     if ((int64_t)h->lens[b] + 1 > cap) return SPLA_ERR_CAPACITY;
   StepArgs a;
-  memset(&a, 0, sizeof(a));
-  // the decode part sees the lengths after the append
-  std::vector<int32_t> saved = h->lens;
+  fill_step_args(h, k_new, v_new, q, gate, out, aux, &a);
+  int32_t plan[kMaxPlan];
+  const int n = decode_plan(h, a.dec, SPLA_CALL_DECODE_STEP, plan);
+  LaunchSeq ls(reinterpret_cast<hipStream_t>(stream), aux);
+  const hipError_t e = run_plan(h, a.dec, &a, plan, n, ls);
+  // the mirror advances once the append is enqueued (the first kernel)
+  if (e != hipSuccess && ls.k <= 1) return hip_fail(h, e);
   for (int b = 0; b < c.batch; ++b) h->lens[b] += 1;
-  fill_decode_args(h, q, gate, out, aux, &a.dec);
-  fill_state_refs(h, k_new, v_new, &a.st);
-  a.s_items = c.batch * c.n_kv_heads * (c.head_dim / (1024 / c.head_dim));
-  for (int b = 0; b < c.batch; ++b)
-    if (h->lens[b] % c.block_size == 0) a.stat_seq[a.n_stat++] = (int16_t)b;
-  const bool bf16 = c.kv_dtype == SPLA_BF16;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  LaunchSeq ls(st, aux);
-  const hipError_t e = launch_step_score(a, bf16, ls.next());
-  if (e != hipSuccess) {
-    h->lens = saved;
-    return hip_fail(h, e);
+  return e == hipSuccess ? SPLA_OK : hip_fail(h, e);
+}
+
+spla_status spla_set_tuning(spla_handle* h, int32_t key, int32_t value) {
+  if (!h) return SPLA_ERR_INVALID_ARG;
+  switch (key) {
+    case SPLA_TUNE_FUSED_SELECT:
+      if (value < -1 || value > 1) return SPLA_ERR_INVALID_ARG;
+      h->fused_select = value;
+      return SPLA_OK;
   }
-  return launch_decode_tail(h, a.dec, bf16, ls);
+  return SPLA_ERR_INVALID_ARG;
+}
+
+int32_t spla_launch_plan(const spla_handle* h, int32_t call, int32_t* kernels, int32_t cap) {
+  if (!h || call < SPLA_CALL_DECODE || call > SPLA_CALL_DECODE_STEP) return -1;
+  spla_handle* hh = const_cast<spla_handle*>(h);  // lengths are restored before returning
+  int32_t plan[kMaxPlan];
+  int n;
+  if (call == SPLA_CALL_DECODE_STEP) {
+    StepArgs a;
+    fill_step_args(hh, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, &a);
+    n = decode_plan(h, a.dec, call, plan);
+  } else {
+    DecodeArgs a;
+    fill_decode_args(h, nullptr, nullptr, nullptr, nullptr, &a);
+    n = decode_plan(h, a, call, plan);
+  }
+  for (int i = 0; i < n && i < cap; ++i)
+    if (kernels) kernels[i] = plan[i];
+  return n;
 }
 
 }  // extern "C"

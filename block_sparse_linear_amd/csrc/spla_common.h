@@ -85,9 +85,6 @@ struct AppendArgs {
 struct StepArgs {
   DecodeArgs dec;      // lens: after the append
   StateRefs st;
-  int32_t s_items;     // B * G * d / rows_per_item state-update workgroups
-  int32_t n_stat;      // sequences whose current block this token completes
-  int16_t stat_seq[kMaxBatch];
 };
 
 // where a kernel is launched; with start / stop set, the launch goes through
@@ -115,6 +112,10 @@ hipError_t launch_select(const DecodeArgs& a, const Launch& l);
 hipError_t launch_attend(const DecodeArgs& a, bool bf16, const Launch& l);
 hipError_t launch_combine(const DecodeArgs& a, bool bf16, const Launch& l);
 hipError_t launch_step_score(const StepArgs& a, bool bf16, const Launch& l);
+// fused select + attend: supported for bf16 K/V, block size 64, no selection
+// override and at most 16 * 256 candidates per sequence
+bool select_attend_supported(const DecodeArgs& a, bool bf16);
+hipError_t launch_select_attend(const DecodeArgs& a, const Launch& l);
 
 // ------------------------------------------------------------ device helpers
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }

@@ -136,8 +136,7 @@ typedef struct {               /* optional outputs / test hook of spla_decode; N
                                   hipExtLaunchKernel and kernel_events[2i] / [2i+1] take the
                                   kernel's own begin / end timestamps (either may be NULL), for
                                   per-kernel timing.  Not for use under stream capture.  Launch
-                                  order: score, select, attend, combine (score and select are
-                                  skipped when sel_in is set). */
+                                  order: as spla_launch_plan reports it. */
     int32_t n_kernel_events;   /* n: entries of kernel_events / 2 */
 } spla_decode_aux;
 
@@ -184,8 +183,9 @@ spla_status spla_decode(spla_handle *h, const void *q, const float *gate, float 
  * followed by spla_decode, with the same results.  The append runs inside
  * the scorer's launch (the scorer reads statistics of blocks completed by
  * earlier appends only), so the step takes one kernel launch less.
- * aux->sel_in is not accepted here (SPLA_ERR_INVALID_ARG); kernel_events
- * order: append+score, select, attend, combine. */
+ * aux->sel_in is not accepted here (SPLA_ERR_INVALID_ARG).  If a launch
+ * after the first fails, the append has been enqueued and the mirror
+ * advances; if the first fails, nothing changes. */
 spla_status spla_decode_step(spla_handle *h, const void *k_new, const void *v_new, const void *q,
                              const float *gate, float *out, const spla_decode_aux *aux, void *stream);
 
@@ -193,6 +193,39 @@ spla_status spla_decode_step(spla_handle *h, const void *k_new, const void *v_ne
 spla_status spla_get_lens(const spla_handle *h, int32_t *lens_host);
 
 const char *spla_status_str(spla_status st);
+
+/* Tuning switches (host only, per handle; results are bitwise identical
+ * whatever the setting).
+ *   SPLA_TUNE_FUSED_SELECT: -1 automatic (default: fused for at most 64
+ *   (sequence, KV head) pairs), 0 = the stand-alone selector kernel, 1 = the
+ *   fused select + attend kernel whenever it supports the call (bf16 K/V,
+ *   block_size 64, no sel_in, at most 4096 candidate blocks per sequence).
+ *   The fused kernel recomputes the selection of a (sequence, KV head) in
+ *   every attend workgroup of that pair instead of handing it over through
+ *   memory, which saves one launch per decode.
+ * SPLA_ERR_INVALID_ARG for an unknown key or value. */
+typedef enum { SPLA_TUNE_FUSED_SELECT = 0 } spla_tune_key;
+spla_status spla_set_tuning(spla_handle *h, int32_t key, int32_t value);
+
+/* The kernels the next call of kind `call` on this handle would launch, in
+ * launch order (the order of spla_decode_aux.kernel_events), from the
+ * current lengths and tuning.  Writes min(n, cap) entries of kernels
+ * (SPLA_KERNEL_*) and returns n (at most 4), or -1 for a NULL handle or an
+ * unknown call. */
+typedef enum {
+    SPLA_KERNEL_SCORE = 1,         /* block scorer (spla_decode) */
+    SPLA_KERNEL_STEP_SCORE = 2,    /* one-token append + block scorer (spla_decode_step) */
+    SPLA_KERNEL_SELECT = 3,        /* stand-alone top-k selector */
+    SPLA_KERNEL_ATTEND = 4,        /* attend + correct over the selector's blocks */
+    SPLA_KERNEL_SELECT_ATTEND = 5, /* fused select + attend + correct */
+    SPLA_KERNEL_COMBINE = 6        /* merge, o_bar, o_rla, D, gate */
+} spla_kernel;
+typedef enum {
+    SPLA_CALL_DECODE = 0,          /* spla_decode without sel_in */
+    SPLA_CALL_DECODE_SEL_IN = 1,   /* spla_decode with sel_in */
+    SPLA_CALL_DECODE_STEP = 2      /* spla_decode_step */
+} spla_call;
+int32_t spla_launch_plan(const spla_handle *h, int32_t call, int32_t *kernels, int32_t cap);
 
 /* The hipError_t of the last launch on this handle that failed (0 = none)
  * and, if name is non-NULL, its name (hipGetErrorName; static storage).  A

@@ -89,7 +89,8 @@ class ParityRun:
 
     def __init__(self, w: Workload, page_order: str = "identity", steps: Optional[int] = None,
                  device: str = "cuda", prefill_chunk: int = 4096, use_step: bool = False,
-                 seqs: Optional[List[int]] = None, kv_heads: Optional[List[int]] = None):
+                 seqs: Optional[List[int]] = None, kv_heads: Optional[List[int]] = None,
+                 fused_select: int = -1):
         import torch
         from block_sparse_linear_amd import SplaLayer
 
@@ -102,6 +103,7 @@ class ParityRun:
         mb = w.max_blocks_per_seq(self.steps)
         self.layer = SplaLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k, mb,
                                kv_dtype=w.kv_dtype, device=device, page_order=page_order, seed=w.seed)
+        self.layer.set_fused_select(fused_select)
         # sequences / KV heads the oracle checks (all by default)
         self.bs = list(range(w.batch)) if seqs is None else [int(b) for b in seqs]
         self.gs = list(range(w.n_kv_heads)) if kv_heads is None else [int(g) for g in kv_heads]

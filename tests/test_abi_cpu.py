@@ -245,3 +245,55 @@ def test_last_hip_error_starts_clear(lib):
     assert name.value == b"hipSuccess"
     assert lib.spla_last_hip_error(None, None) == 0
     lib.spla_destroy(h)
+
+
+def test_tuning_validation(lib):
+    st, h = create(lib, cfg())
+    assert lib.spla_set_tuning(h, 0, -1) == OK
+    assert lib.spla_set_tuning(h, 0, 0) == OK
+    assert lib.spla_set_tuning(h, 0, 1) == OK
+    assert lib.spla_set_tuning(h, 0, 2) == INVALID
+    assert lib.spla_set_tuning(h, 7, 0) == INVALID
+    assert lib.spla_set_tuning(None, 0, 0) == INVALID
+    lib.spla_destroy(h)
+
+
+SCORE, STEP_SCORE, SELECT, ATTEND, SELECT_ATTEND, COMBINE = range(1, 7)
+
+
+def plan(lib, h, call):
+    out = i32([0] * 8)
+    n = lib.spla_launch_plan(h, call, out, 8)
+    return list(out)[:n] if n >= 0 else n
+
+
+def test_launch_plan(lib):
+    # bf16, Bk=64, top_k=16; lengths 100 (2 blocks) and 2000 (32 blocks > top_k)
+    h, c = bound(lib)
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]  # automatic: 4 (b, g) pairs -> fused
+    assert plan(lib, h, 0) == [SCORE, SELECT_ATTEND, COMBINE]
+    assert plan(lib, h, 1) == [ATTEND, COMBINE]                     # selection override
+    assert lib.spla_set_tuning(h, 0, 0) == OK
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT, ATTEND, COMBINE]
+    assert lib.spla_set_tuning(h, 0, 1) == OK
+    assert plan(lib, h, 0) == [SCORE, SELECT_ATTEND, COMBINE]
+    assert plan(lib, h, 3) == -1 and lib.spla_launch_plan(None, 0, None, 0) == -1
+    assert lib.spla_launch_plan(h, 2, None, 0) == 3                 # count only
+    assert lens_of(lib, h, 2) == [100, 2000]                       # the query changes nothing
+    lib.spla_destroy(h)
+    # every sequence short: no scorer launch for spla_decode
+    h, c = bound(lib, lens=(5, 64 * 16))
+    assert plan(lib, h, 0) == [SELECT_ATTEND, COMBINE]
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
+    lib.spla_destroy(h)
+    # the fused kernel needs bf16 and Bk = 64
+    for kw in (dict(kv_dtype=0), dict(block_size=128)):
+        h, c = bound(lib, lens=(100, 2000), **kw)
+        assert lib.spla_set_tuning(h, 0, 1) == OK
+        assert plan(lib, h, 2) == [STEP_SCORE, SELECT, ATTEND, COMBINE], kw
+        lib.spla_destroy(h)
+    # more than 4096 candidates: stand-alone selector
+    h, c = bound(lib, lens=(100, 64 * 4200), max_blocks_per_seq=4300)
+    assert lib.spla_set_tuning(h, 0, 1) == OK
+    assert plan(lib, h, 0) == [SCORE, SELECT, ATTEND, COMBINE]
+    lib.spla_destroy(h)

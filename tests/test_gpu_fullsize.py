@@ -16,11 +16,13 @@ from workloads import Workload, make_workload
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def _run(w, steps, seqs=None, kv_heads=None, page_order="shuffled"):
+def _run(w, steps, seqs=None, kv_heads=None, page_order="shuffled", fused_select=-1):
     print(f"[fullsize] {w.name}: B={w.batch} H={w.n_q_heads} G={w.n_kv_heads} d={w.head_dim} "
           f"Bk={w.block_size} k={w.top_k} t0={w.t0[:4]}{'...' if w.batch > 4 else ''} steps={steps} "
-          f"seqs={seqs} kv_heads={kv_heads}", flush=True)
-    run = ParityRun(w, page_order=page_order, steps=steps, use_step=True, seqs=seqs, kv_heads=kv_heads)
+          f"seqs={seqs} kv_heads={kv_heads} fused_select={fused_select}", flush=True)
+    run = ParityRun(w, page_order=page_order, steps=steps, use_step=True, seqs=seqs, kv_heads=kv_heads,
+                    fused_select=fused_select)
+    print(f"[fullsize] kernels: {run.layer.launch_plan()}", flush=True)
     failures = run.run(verbose=True)
     assert not failures, "\n".join(failures[:20])
 
@@ -56,19 +58,25 @@ def test_ragged_chunked_full():
 
 # the selector holds KPT candidates per thread in registers, with one compiled
 # size per entry below; a sequence whose candidate count just exceeds the next
-# smaller size runs each of them (single KV head, d = 64 keeps the data small)
+# smaller size runs each of them (single KV head, d = 64 keeps the data small).
+# Both placements: the stand-alone selector (fused_select = 0) and the fused
+# select + attend kernel (1; its sizes are 1, 2, 4, 6, 9, 12, 16 and it is not
+# used past 16).
 SELECT_SIZES = [2, 3, 4, 6, 8, 9, 10, 12, 16, 20, 24, 32, 40, 48, 64]
 
 
 @pytest.mark.timeout(300)
+@pytest.mark.parametrize("fused", [0, 1])
 @pytest.mark.parametrize("kpt", SELECT_SIZES)
-def test_selector_sizes(kpt):
+def test_selector_sizes(kpt, fused):
+    if fused and kpt > 16:
+        pytest.skip("the fused kernel is not used past 16 keys per thread")
     prev = SELECT_SIZES[SELECT_SIZES.index(kpt) - 1] if kpt > 2 else 1
     nb = prev * 256 + 2 + 37  # candidates = nb - 2 > prev * 256
     w = Workload(name=f"sel_kpt{kpt}", batch=1, n_q_heads=2, n_kv_heads=1, head_dim=64, block_size=64,
                  top_k=24, kv_dtype="bf16", t0=(nb * 64 - 9,), steps=2, kind="outlier", seed=500 + kpt,
                  n_outlier=4, prefill_chunk=16384)
-    _run(w, steps=2, page_order="shuffled")
+    _run(w, steps=2, page_order="shuffled", fused_select=fused)
 
 
 @pytest.mark.timeout(300)

@@ -132,3 +132,77 @@ def test_step_matches_two_calls_bitwise():
         assert torch.equal(oa, ob), f"step {s}"
     for x, y in zip(a.layer.state_tensors(), b.layer.state_tensors()):
         assert torch.equal(x, y)
+
+
+# ---- selector placement ---------------------------------------------------------
+def test_fused_select_matches_split_bitwise():
+    """The fused select + attend kernel and the stand-alone selector give the
+    same outputs and selections, bit for bit (both placements run the same
+    selection and the same attend arithmetic)."""
+    _needs_gpu()
+    import torch
+    from tests.spla_parity import ParityRun
+    # ragged: one sequence with every block selected, others crossing block ends
+    w = small(name="fused_vs_split", batch=4, t0=(64 * 300 - 3, 64 * 5, 64 * 40 + 1, 3000), steps=6,
+              kind="outlier", n_outlier=8, top_k=12)
+    runs = [ParityRun(w, steps=6, prefill_chunk=1000, page_order="shuffled", fused_select=m) for m in (0, 1)]
+    assert runs[0].layer.launch_plan() == ["step_score", "select", "attend", "combine"]
+    assert runs[1].layer.launch_plan() == ["step_score", "select_attend", "combine"]
+    for r in runs:
+        r.prefill()
+    for s in range(6):
+        st = w.step(s)
+        res = [r.gpu_decode(st["q"], kv=(st["k"], st["v"])) for r in runs]
+        for key in ("o", "sel_idx", "o_sparse", "o_rla", "d_rla", "lg"):
+            assert np.array_equal(res[0][key], res[1][key]), f"step {s}: {key}"
+    assert runs[0].layer.error_word() == 0 and runs[1].layer.error_word() == 0
+
+
+# ---- ties: equal group scores go to the smaller block id -------------------------
+def _tied(n_plant, fused, steps=2):
+    """Planted blocks with identical keys (noise 0): equal statistics, equal
+    scores, all above the random blocks.  The selection must be exactly the
+    oracle's: the smallest planted ids."""
+    from tests.spla_parity import ParityRun
+    w = Workload(name=f"tied{n_plant}", batch=1, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=64,
+                 top_k=32, kv_dtype="bf16", t0=(64 * 1500 + 17,), steps=steps, kind="planted", seed=91,
+                 n_plant=n_plant, plant_shared_heads=False, plant_noise=0.0)
+    print(f"[gpu-test] {w.name} fused={fused}", flush=True)
+    run = ParityRun(w, steps=steps, page_order="shuffled", fused_select=fused)
+    run.prefill()
+    for s in range(steps):
+        st = run.append_step(s)
+        rep = run.check_decode(s, st["q"])
+        assert not rep.failures, rep.failures[:5]
+        assert rep.sel_equal, "tied scores: the selection must be the smallest ids"
+    assert run.layer.error_word() == 0
+
+
+@pytest.mark.parametrize("fused", [0, 1])
+def test_tied_scores_ranked_exactly(fused):
+    # 100 tied blocks: fewer than the 256 ranked exactly in the last bucket
+    _needs_gpu()
+    _tied(100, fused)
+
+
+@pytest.mark.parametrize("fused", [0, 1])
+def test_tied_scores_taken_by_id(fused):
+    # 600 tied blocks: the top bucket cannot be split by score, ids decide
+    _needs_gpu()
+    _tied(600, fused)
+
+
+@pytest.mark.parametrize("fused", [0, 1])
+def test_zero_query_every_score_equal(fused):
+    # q = 0: every candidate has the same score; sink, current and the
+    # smallest ids are selected, attention is uniform
+    _needs_gpu()
+    from tests.spla_parity import ParityRun
+    w = small(name="zero_q", t0=(64 * 700 + 5,), steps=2)
+    run = ParityRun(w, steps=2, page_order="shuffled", fused_select=fused)
+    run.prefill()
+    for s in range(2):
+        st = run.append_step(s)
+        rep = run.check_decode(s, np.zeros_like(st["q"]))
+        assert not rep.failures, rep.failures[:5]
+        assert rep.sel_equal

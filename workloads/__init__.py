@@ -81,9 +81,9 @@ class Workload:
       ``outlier``  K, V ~ N(0, 1), then per KV head ``n_outlier`` seeded
                    channels scaled by ``outlier_scale`` in both K and V
       ``planted``  K, V ~ N(0, 1) plus ``n_plant`` planted blocks per sequence
-                   whose keys are 3*u + 0.1*N(0, I), u the unit direction of
-                   the sequence/KV head's base query q0; step queries are
-                   q0 + 0.25*N(0, I)
+                   whose keys are 3*u + plant_noise*N(0, I) (plant_noise 0.1
+                   by default), u the unit direction of the sequence/KV
+                   head's base query q0; step queries are q0 + 0.25*N(0, I)
       ``mixture``  keys c_m(i) + 0.3*N(0, I) with 64 centres c_m ~ N(0, I) per
                    KV head and m(i) constant over runs of length
                    round(exp(U[ln 16, ln 2048])), centre uniform per run;
@@ -105,6 +105,7 @@ class Workload:
     # planted
     n_plant: int = 0
     plant_shared_heads: bool = True
+    plant_noise: float = 0.1  # 0: every planted block of a head holds the same keys (tied scores)
     # outlier
     n_outlier: int = 0
     outlier_scale: float = 4.0
@@ -242,7 +243,7 @@ class Workload:
                         rp = _rng(self.seed, _S_PLANT, b, g, int(j))
                         noise = rp.standard_normal((bk, self.head_dim)).astype(np.float32)
                         k[a - pos0:e - pos0, g, :] = (np.float32(3.0) * u[g][None, :]
-                                                      + np.float32(0.1) * noise[a - j * bk:e - j * bk])
+                                                      + np.float32(self.plant_noise) * noise[a - j * bk:e - j * bk])
             yield pos0, self.round(k), self.round(v)
 
     def prefill(self, b: int) -> Tuple[np.ndarray, np.ndarray]:
