@@ -28,6 +28,10 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-ffp-contract=fast",
+    # the leading scalar / pointer arguments of the decode kernels arrive in
+    # SGPRs at wave start (the code object keeps a loading prologue for
+    # firmware that does not preload)
+    "-mllvm", "-amdgpu-kernarg-preload-count=8",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

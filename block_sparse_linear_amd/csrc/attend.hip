@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(const DecodeArgs a) {
   SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.top_k), "s"(a.sel_in), "s"(a.sel), "s"(a.sel_page),
                      "s"(a.G), "s"(a.q), "s"(a.H), "s"(a.k_pages), "s"(a.v_pages));
   uint4 qraw[D / 32];
-  load_q_mfma<R, D>(a, g, b, qraw);  // independent of the selection: issued first
+  load_q_mfma<R, D>(a.q, a.H, g, b, qraw);  // independent of the selection: issued first
   const size_t srow = ((size_t)b * a.G + g) * a.top_k + slot;
   int j, page;
   if (a.sel_in) {

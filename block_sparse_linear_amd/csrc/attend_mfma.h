@@ -59,14 +59,14 @@ __device__ __forceinline__ void phi_hilo(const uint4& raw, uint4& hi, uint4& lo)
 // holds query m (m < R) or phi(q) of query m - WB; other rows load query 0
 // and are masked when the operands are formed
 template <int R, int D>
-__device__ __forceinline__ void load_q_mfma(const DecodeArgs& a, int g, int b, uint4 (&qraw)[D / 32]) {
+__device__ __forceinline__ void load_q_mfma(const void* q, int H, int g, int b, uint4 (&qraw)[D / 32]) {
   constexpr int WB = R <= 4 ? 4 : 8;
   const int lane = threadIdx.x % 64, m = lane % 16, lg4 = lane / 16;
   const int hq = m < R ? m : ((m >= WB && m < WB + R) ? m - WB : 0);
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks)
-    qraw[ks] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
-                                               ((size_t)b * a.H + g * R + hq) * D + 32 * ks + 8 * lg4);
+    qraw[ks] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) +
+                                               ((size_t)b * H + g * R + hq) * D + 32 * ks + 8 * lg4);
 }
 
 // Block j (page `page`) of (b, g), all R query heads, bf16 K/V; writes the

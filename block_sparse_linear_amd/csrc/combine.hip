@@ -17,7 +17,9 @@ namespace {
 // SG thread groups whose float4 sums meet in LDS.  Every global load is
 // issued before the first wait.
 template <bool BF16, int R, int D>
-__global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void k_combine(const float* s_all, const void* q, const float* z_all,
+                                                       const float* part, const int32_t* sel, int32_t G, int32_t H,
+                                                       int32_t top_k, const DecodeArgs a) {
   constexpr int CS = 32;                 // channels per workgroup
   constexpr int RG = kThreads / CS;      // row groups of the S contraction
   constexpr int RPG = D / RG;            // rows per group
@@ -34,19 +36,16 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
   __shared__ float4 red4[SG][NIT];
   __shared__ float s_sw[R], s_dz[R];
   const int cc = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.top_k), "s"(a.sel_in), "s"(a.sel), "s"(a.G), "s"(a.H),
-                     "s"(a.part), "s"(a.s_all), "s"(a.q), "s"(a.z_all));
-  const int nb = n_blocks(a, b);
-  const bool covers_all = nb <= a.top_k;
-  const int top_k = a.top_k;
-  const int32_t* srow = (a.sel_in ? a.sel_in : a.sel) + ((size_t)b * a.G + g) * top_k;
+  // (sel is the selection the attend kernel used: the caller's override or
+  // the selector's; the leading arguments address every first load)
+  const int32_t* srow = sel + ((size_t)b * G + g) * top_k;
   const int rec = 2 * D + kPartHdr;
-  const float* P0 = a.part + ((size_t)b * a.H + g * R) * top_k * (size_t)rec;
+  const float* P0 = part + ((size_t)b * H + g * R) * top_k * (size_t)rec;
   const int c0 = cc * CS;
   const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
   // ---- loads
   const int sc = threadIdx.x % CS, rg = threadIdx.x / CS;
-  const float* S = a.s_all + ((size_t)b * a.G + g) * D * (size_t)D + (size_t)(rg * RPG) * D + c0 + sc;
+  const float* S = s_all + ((size_t)b * G + g) * D * (size_t)D + (size_t)(rg * RPG) * D + c0 + sc;
   float sv[RPG];
 #pragma unroll
   for (int x = 0; x < RPG; ++x) sv[x] = S[(size_t)x * D];
@@ -54,11 +53,11 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
     const int i = threadIdx.x + k * kThreads;
-    qv[k] = load_elem<BF16>(a.q, ((size_t)b * a.H + g * R) * D + min(i, R * D - 1));
+    qv[k] = load_elem<BF16>(q, ((size_t)b * H + g * R) * D + min(i, R * D - 1));
   }
   float zv[(D + 63) / 64];
 #pragma unroll
-  for (int k = 0; k < (D + 63) / 64; ++k) zv[k] = a.z_all[((size_t)b * a.G + g) * D + lane + 64 * k];
+  for (int k = 0; k < (D + 63) / 64; ++k) zv[k] = z_all[((size_t)b * G + g) * D + lane + 64 * k];
   int vs[SPL];
 #pragma unroll
   for (int u = 0; u < SPL; ++u) {
@@ -89,6 +88,11 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
     dv[u] = *reinterpret_cast<const float4*>(PD + (size_t)min(s, top_k - 1) * rec);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // the rest of the arguments, while the loads are in flight
+  SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.gate), "s"(a.out), "s"(a.o_sparse_out), "s"(a.o_rla_out),
+                     "s"(a.d_rla_out), "s"(a.sel_out));
+  const int nb = n_blocks(a, b);
+  const bool covers_all = nb <= top_k;
   // ---- phi(q), validity, merge weights and phi(q).z per head
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
@@ -200,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
         orl[e] = obar - otv[e];
       }
     }
-    const size_t oi = ((size_t)b * a.H + g * R + h) * D + c0 + 4 * q4;
+    const size_t oi = ((size_t)b * H + g * R + h) * D + c0 + 4 * q4;
     const float gh = a.gate[g * R + h];
     *reinterpret_cast<float4*>(a.out + oi) =
         make_float4(fmaf(gh, orl[0], os.x), fmaf(gh, orl[1], os.y), fmaf(gh, orl[2], os.z), fmaf(gh, orl[3], os.w));
@@ -208,10 +212,10 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
     if (a.o_rla_out) *reinterpret_cast<float4*>(a.o_rla_out + oi) = make_float4(orl[0], orl[1], orl[2], orl[3]);
   }
   if (cc == 0 && (int)threadIdx.x < top_k && a.sel_out)
-    a.sel_out[((size_t)b * a.G + g) * top_k + threadIdx.x] = srow[threadIdx.x];
+    a.sel_out[((size_t)b * G + g) * top_k + threadIdx.x] = srow[threadIdx.x];
   if (cc == 0 && (int)threadIdx.x < R && a.d_rla_out) {
     const int h = threadIdx.x;
-    a.d_rla_out[(size_t)b * a.H + g * R + h] = covers_all ? 0.f : s_dz[h] - s_sw[h];
+    a.d_rla_out[(size_t)b * H + g * R + h] = covers_all ? 0.f : s_dz[h] - s_sw[h];
   }
 }
 
@@ -219,8 +223,12 @@ __global__ __launch_bounds__(kThreads) void k_combine(const DecodeArgs a) {
 
 hipError_t launch_combine(const DecodeArgs& a, bool bf16, const Launch& l) {
   const dim3 grid(a.d / 32, a.G, a.B);
-  if (bf16) SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<true, RR, DD>, grid, l, a))
-  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<false, RR, DD>, grid, l, a))
+  const int32_t* sel = a.sel_in ? a.sel_in : a.sel;
+  if (bf16)
+    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<true, RR, DD>, grid, l, a.s_all, a.q, a.z_all, a.part, sel,
+                                             a.G, a.H, a.top_k, a))
+  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<false, RR, DD>, grid, l, a.s_all, a.q, a.z_all, a.part, sel,
+                                           a.G, a.H, a.top_k, a))
 }
 
 

@@ -9,24 +9,33 @@ namespace spla {
 namespace {
 
 // ============================================================== score
+// Arguments the first loads of a score tile need.  The kernels take them
+// ahead of their argument struct, so with kernel-argument preloading they are
+// in SGPRs when the wave starts.
+struct ScorePre {
+  const float* mean;
+  const float* var;
+  const void* q;
+  int32_t n_tiles, G, H;
+  int32_t tiles_all;  // tiles every sequence of the batch has: their loads need no length
+};
+
 // grid (score_tiles, G, B); lane = block within a 64-block tile, the four
 // wavefronts split the channels and meet in LDS.  Every wavefront issues its
 // query loads and then all of its statistics loads before the first wait.
 template <bool BF16, int R, int D>
-__device__ void score_tile(const DecodeArgs& a, const int t, const int g, const int b) {
+__device__ void score_tile(const DecodeArgs& a, const int t, const int g, const int b, const ScorePre& p) {
   constexpr int NC4 = D / 16;  // channel quartets per wavefront
   constexpr int CW = D / 4;    // channels per wavefront
   constexpr int QPL = (R * CW + 63) / 64;  // query elements per lane
   __shared__ float4 qs[4][R][CW / 4];
   __shared__ float4 q2s[4][R][CW / 4];
   __shared__ float red[4][2 * R][kTile];
-  const int T = a.lens[b];
-  SPLA_SCALARS_READY("s"(T), "s"(a.bk), "s"(a.top_k), "s"(a.H), "s"(a.G), "s"(a.n_tiles), "s"(a.q),
-                     "s"(a.blk_mean), "s"(a.blk_var));
-  const int nb = (T + a.bk - 1) / a.bk;
-  if (nb <= a.top_k) return;  // every block is selected, nothing to rank
-  const int j0 = t * kTile;
-  if (j0 > nb - 2) return;
+  if (t >= p.tiles_all) {
+    // a tile that only some sequences have: this one's length decides first
+    const int nbs = n_blocks(a, b);
+    if (nbs <= a.top_k || t * kTile > nbs - 2) return;
+  }
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int lane = threadIdx.x % 64;
   // queries of this wavefront's channel quarter
@@ -37,12 +46,12 @@ __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const 
   for (int i = 0; i < QPL; ++i) {
     const int e = min(lane + 64 * i, R * CW - 1);
     const int h = e / CW, c = e - h * CW;
-    qv[i] = load_elem<BF16>(a.q, ((size_t)b * a.H + g * R + h) * D + w * CW + c);
+    qv[i] = load_elem<BF16>(p.q, ((size_t)b * p.H + g * R + h) * D + w * CW + c);
   }
   // statistics of the tile: 64 blocks x this wavefront's channels
-  const float4* mean4 = reinterpret_cast<const float4*>(a.blk_mean);
-  const float4* var4 = reinterpret_cast<const float4*>(a.blk_var);
-  const size_t base = (((size_t)b * a.G + g) * a.n_tiles + t) * (size_t)(D / 4) * kTile + (size_t)(w * NC4) * kTile + lane;
+  const float4* mean4 = reinterpret_cast<const float4*>(p.mean);
+  const float4* var4 = reinterpret_cast<const float4*>(p.var);
+  const size_t base = (((size_t)b * p.G + g) * p.n_tiles + t) * (size_t)(D / 4) * kTile + (size_t)(w * NC4) * kTile + lane;
   float4 m[NC4], v[NC4];
 #pragma unroll
   for (int i = 0; i < NC4; ++i) m[i] = mean4[base + (size_t)i * kTile];
@@ -51,6 +60,11 @@ __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const 
   // keep every load above this point: the whole tile is in flight before the
   // first use
   __builtin_amdgcn_sched_barrier(0);
+  // the rest of the arguments, while the tile is in flight
+  const int T = a.lens[b];
+  SPLA_SCALARS_READY("s"(T), "s"(a.bk), "s"(a.lg), "s"(a.lg_out), "s"(a.max_blocks), "s"(a.inv_sqrt_d));
+  const int nb = (T + a.bk - 1) / a.bk;
+  const int j0 = t * kTile;
   // wavefront-private staging of q and q^2 (LDS operations of one wavefront
   // complete in order, so no barrier is needed)
   float* qf = reinterpret_cast<float*>(&qs[w][0][0]);
@@ -113,15 +127,18 @@ __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const 
     const int j = j0 + blk;
     if (h == 0) {
       const bool cand = j >= 1 && j <= nb - 2;
-      a.lg[((size_t)b * a.G + g) * (size_t)(a.n_tiles * kTile) + j] = cand ? lg : -INFINITY;
-      if (a.lg_out && cand) a.lg_out[((size_t)b * a.G + g) * a.max_blocks + j] = lg;
+      a.lg[((size_t)b * p.G + g) * (size_t)(p.n_tiles * kTile) + j] = cand ? lg : -INFINITY;
+      if (a.lg_out && cand) a.lg_out[((size_t)b * p.G + g) * a.max_blocks + j] = lg;
     }
   }
 }
 
 template <bool BF16, int R, int D>
-__global__ __launch_bounds__(kThreads) void k_score(const DecodeArgs a) {
-  score_tile<BF16, R, D>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+__global__ __launch_bounds__(kThreads) void k_score(const float* mean, const float* var, const void* q,
+                                                     int32_t n_tiles, int32_t G, int32_t H, int32_t tiles_all,
+                                                     const DecodeArgs a) {
+  const ScorePre p{mean, var, q, n_tiles, G, H, tiles_all};
+  score_tile<BF16, R, D>(a, blockIdx.x, blockIdx.y, blockIdx.z, p);
 }
 
 // Fused decode step, first launch, grid (score_tiles + chunks + 1, G, B):
@@ -131,22 +148,23 @@ __global__ __launch_bounds__(kThreads) void k_score(const DecodeArgs a) {
 // statistics of candidate blocks 1..nb-2 only, all completed by earlier
 // appends, and neither pages nor S_all.
 template <bool BF16, int R, int D>
-__global__ __launch_bounds__(kThreads) void k_step_score(const StepArgs a) {
+__global__ __launch_bounds__(kThreads) void k_step_score(const float* mean, const float* var, const void* q,
+                                                          int32_t n_tiles, int32_t G, int32_t H, int32_t tiles_all,
+                                                          int32_t score_tiles, const StepArgs a) {
   constexpr int kChunks = D / (1024 / D);  // S_all row chunks per (b, g)
   const DecodeArgs& dc = a.dec;
   const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tiles = dc.score_tiles;
-  const int T = dc.lens[b];  // after the append
-  SPLA_SCALARS_READY("s"(tiles), "s"(T), "s"(dc.bk), "s"(dc.top_k), "s"(dc.H), "s"(dc.G), "s"(dc.n_tiles),
-                     "s"(dc.q), "s"(dc.blk_mean), "s"(dc.blk_var), "s"(a.st.k_new), "s"(a.st.v_new),
-                     "s"(a.st.s_all), "s"(a.st.z_all));
-  if (x < tiles) {
-    score_tile<BF16, R, D>(dc, x, g, b);
+  if (x < score_tiles) {
+    const ScorePre p{mean, var, q, n_tiles, G, H, tiles_all};
+    score_tile<BF16, R, D>(dc, x, g, b, p);
     return;
   }
+  const int T = dc.lens[b];  // after the append
+  SPLA_SCALARS_READY("s"(T), "s"(dc.bk), "s"(a.st.k_new), "s"(a.st.v_new), "s"(a.st.s_all), "s"(a.st.z_all),
+                     "s"(a.st.block_table), "s"(a.st.k_pages), "s"(a.st.v_pages));
   const AppendEntry E{b, 1, T - 1, b};
-  if (x < tiles + kChunks) {
-    append_state_rows<BF16>(a.st, E, g, x - tiles);
+  if (x < score_tiles + kChunks) {
+    append_state_rows<BF16>(a.st, E, g, x - score_tiles);
     return;
   }
   append_page_row_head<BF16>(a.st, E, g);
@@ -158,15 +176,22 @@ __global__ __launch_bounds__(kThreads) void k_step_score(const StepArgs a) {
 hipError_t launch_score(const DecodeArgs& a, bool bf16, const Launch& l) {
   const dim3 grid(a.score_tiles, a.G, a.B);
   if (a.score_tiles == 0) return hipSuccess;
-  if (bf16) SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_score<true, RR, DD>, grid, l, a))
-  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_score<false, RR, DD>, grid, l, a))
+  if (bf16)
+    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_score<true, RR, DD>, grid, l, a.blk_mean, a.blk_var, a.q, a.n_tiles,
+                                             a.G, a.H, a.tiles_all, a))
+  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_score<false, RR, DD>, grid, l, a.blk_mean, a.blk_var, a.q, a.n_tiles,
+                                           a.G, a.H, a.tiles_all, a))
 }
 
 hipError_t launch_step_score(const StepArgs& a, bool bf16, const Launch& l) {
   const int chunks = a.dec.d / (1024 / a.dec.d);
   const dim3 grid(a.dec.score_tiles + chunks + 1, a.dec.G, a.dec.B);
-  if (bf16) SPLA_DISPATCH_RD(a.dec.r, a.dec.d, launch_kernel(k_step_score<true, RR, DD>, grid, l, a))
-  SPLA_DISPATCH_RD(a.dec.r, a.dec.d, launch_kernel(k_step_score<false, RR, DD>, grid, l, a))
+  const DecodeArgs& d = a.dec;
+  if (bf16)
+    SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<true, RR, DD>, grid, l, d.blk_mean, d.blk_var, d.q,
+                                             d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
+  SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<false, RR, DD>, grid, l, d.blk_mean, d.blk_var, d.q,
+                                           d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
 }
 
 }  // namespace spla

@@ -7,14 +7,15 @@ namespace spla {
 namespace {
 
 template <int KPT>
-__global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void k_select(const float* lg, const int32_t* block_table, int32_t n_tiles,
+                                                      int32_t max_blocks, int32_t G, const DecodeArgs a) {
   __shared__ SelectLds L;
   const int g = blockIdx.x, b = blockIdx.y;
-  SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.top_k), "s"(a.max_blocks), "s"(a.block_table), "s"(a.lg),
-                     "s"(a.G), "s"(a.n_tiles));
-  const int nb = n_blocks(a, b);
   SelectKeys<KPT> k;
-  select_load<KPT>(a, g, b, nb, k);  // first: nothing else waits on memory before it
+  select_load<KPT>(lg, block_table, n_tiles, max_blocks, G, g, b, k);  // first: needs no other argument
+  SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.top_k), "s"(a.sel), "s"(a.sel_out), "s"(a.sel_page));
+  const int nb = n_blocks(a, b);
+  select_pages<KPT>(block_table, max_blocks, b, nb, k);
   const size_t row = ((size_t)b * a.G + g) * a.top_k;
   int32_t* out = a.sel + row;
   int32_t* out2 = a.sel_out ? a.sel_out + row : nullptr;
@@ -37,7 +38,8 @@ __global__ __launch_bounds__(kThreads) void k_select(const DecodeArgs a) {
 
 template <int K, int... Ks>
 hipError_t launch_select_sized(const DecodeArgs& a, const Launch& l, int nc, SelectSizes<K, Ks...>) {
-  if (nc <= K * kThreads) return launch_kernel(k_select<K>, dim3(a.G, a.B), l, a);
+  if (nc <= K * kThreads)
+    return launch_kernel(k_select<K>, dim3(a.G, a.B), l, a.lg, a.block_table, a.n_tiles, a.max_blocks, a.G, a);
   if constexpr (sizeof...(Ks) == 0) {
     return hipErrorInvalidValue;
   } else {

@@ -14,23 +14,27 @@ namespace spla {
 namespace {
 
 template <int KPT, int R, int D>
-__global__ __launch_bounds__(kThreads) void k_select_attend(const DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, const int32_t* block_table,
+                                                             const void* q, int32_t n_tiles, int32_t max_blocks,
+                                                             int32_t G, int32_t H, const DecodeArgs a) {
   __shared__ SelectLds L;
   __shared__ int s_j, s_page;
   const int slot = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.top_k), "s"(a.max_blocks), "s"(a.block_table), "s"(a.lg),
-                     "s"(a.G), "s"(a.n_tiles), "s"(a.q), "s"(a.H), "s"(a.k_pages), "s"(a.v_pages));
-  const int nb = n_blocks(a, b);
-  // every load that does not depend on the selection goes out first: the
-  // scores and page ids it ranks (issued whatever nb is) and the queries
+  // every load that does not depend on the selection goes out first, from
+  // the leading kernel arguments alone: the scores and page ids it ranks and
+  // the queries
   SelectKeys<KPT> k;
-  select_load<KPT>(a, g, b, nb, k);
+  select_load<KPT>(lg, block_table, n_tiles, max_blocks, G, g, b, k);
   uint4 qraw[D / 32];
-  load_q_mfma<R, D>(a, g, b, qraw);
+  load_q_mfma<R, D>(q, H, g, b, qraw);
+  SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.top_k), "s"(a.sel), "s"(a.k_pages), "s"(a.v_pages),
+                     "s"(a.part), "s"(a.num_pages), "s"(a.inv_sqrt_d));
+  const int nb = n_blocks(a, b);
+  select_pages<KPT>(block_table, max_blocks, b, nb, k);
   int j, page;
   if (nb <= a.top_k) {
     j = slot < nb ? slot : -1;
-    page = j >= 0 ? a.block_table[(size_t)b * a.max_blocks + j] : -1;
+    page = j >= 0 ? block_table[(size_t)b * max_blocks + j] : -1;
   } else {
     select_core<KPT>(a, nb, k, L, [&](int pos, int id, int pg) {
       if (pos == slot) {
@@ -51,7 +55,8 @@ template <int K, int... Ks>
 hipError_t launch_select_attend_sized(const DecodeArgs& a, const Launch& l, int nc, SelectSizes<K, Ks...>) {
   if (nc <= K * kThreads) {
     const dim3 grid(a.top_k, a.G, a.B);
-    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_select_attend<K, RR, DD>, grid, l, a))
+    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_select_attend<K, RR, DD>, grid, l, a.lg, a.block_table, a.q,
+                                             a.n_tiles, a.max_blocks, a.G, a.H, a))
   }
   if constexpr (sizeof...(Ks) == 0) {
     return hipErrorInvalidValue;

@@ -51,23 +51,32 @@ struct SelectKeys {
   int pg_sink, pg_cur;
 };
 
-// Issue the loads of a selection.  Valid for any nb >= 1 (addresses are
-// clamped into the score row and the block table row), so a kernel can issue
-// them first, before it knows whether there is anything to rank.
+// Issue the candidate loads of a selection: scores and page ids of
+// candidates 0 .. KPT * 256 - 1, clamped into the score row and the block
+// table row.  They need no sequence length, so a kernel can issue them first
+// (lg, block_table and the sizes are kernel arguments ahead of the argument
+// struct).  The pages of the sink and the current block come with
+// select_pages once the length is known.
 template <int KPT>
-__device__ __forceinline__ void select_load(const DecodeArgs& a, int g, int b, int nb, SelectKeys<KPT>& k) {
-  const int nc = max(nb - 2, 1);
-  const int last = a.max_blocks - 1;
-  const int32_t* btab = a.block_table + (size_t)b * a.max_blocks;
-  const float* row = a.lg + ((size_t)b * a.G + g) * (size_t)(a.n_tiles * kTile) + 1;  // row[i] = LG(i + 1)
+__device__ __forceinline__ void select_load(const float* lg, const int32_t* block_table, int n_tiles, int max_blocks,
+                                            int G, int g, int b, SelectKeys<KPT>& k) {
+  const int cap = max(min(n_tiles * kTile, max_blocks) - 2, 0);  // last candidate index inside both rows
+  const int32_t* btab = block_table + (size_t)b * max_blocks;
+  const float* row = lg + ((size_t)b * G + g) * (size_t)(n_tiles * kTile) + 1;  // row[i] = LG(i + 1)
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
-    const int i = min((int)threadIdx.x + u * kThreads, nc - 1);
+    const int i = min((int)threadIdx.x + u * kThreads, cap);
     k.x[u] = row[i];
-    k.pg[u] = btab[min(i + 1, last)];
+    k.pg[u] = btab[min(i + 1, max_blocks - 1)];
   }
+}
+
+template <int KPT>
+__device__ __forceinline__ void select_pages(const int32_t* block_table, int max_blocks, int b, int nb,
+                                             SelectKeys<KPT>& k) {
+  const int32_t* btab = block_table + (size_t)b * max_blocks;
   k.pg_sink = btab[0];
-  k.pg_cur = btab[min(max(nb - 1, 0), last)];
+  k.pg_cur = btab[min(max(nb - 1, 0), max_blocks - 1)];
 }
 
 // Append the keys flagged in `flags` (bit u: key u of this thread) to an LDS

@@ -88,16 +88,16 @@ spla_status fill_decode_args(const spla_handle* h, const void* q, const float* g
   a->num_pages = c.num_pages;
   a->n_tiles = h->n_tiles;
   a->inv_sqrt_d = (float)(1.0 / sqrt((double)c.head_dim));
-  int max_tiles = 0;
+  int max_tiles = 0, min_tiles = 1 << 30;
   for (int b = 0; b < c.batch; ++b) {
     a->lens[b] = h->lens[b];
     const int nb = (h->lens[b] + c.block_size - 1) / c.block_size;
-    if (nb > c.top_k) {
-      const int tiles = (nb - 2) / kTile + 1;  // tiles holding candidates 1..nb-2
-      if (tiles > max_tiles) max_tiles = tiles;
-    }
+    const int tiles = nb > c.top_k ? (nb - 2) / kTile + 1 : 0;  // tiles holding candidates 1..nb-2
+    if (tiles > max_tiles) max_tiles = tiles;
+    if (tiles < min_tiles) min_tiles = tiles;
   }
   a->score_tiles = max_tiles;
+  a->tiles_all = min_tiles;
   return SPLA_OK;
 }
 

@@ -6,6 +6,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <type_traits>
+#include <utility>
+
 namespace spla {
 
 constexpr int kMaxBatch = 256;
@@ -50,6 +54,7 @@ struct DecodeArgs {
   float* d_rla_out;
   int32_t B, H, G, d, r, bk, top_k, max_blocks, num_pages, n_tiles;
   int32_t score_tiles;  // grid.x of the scorer
+  int32_t tiles_all;    // score tiles that every sequence of the batch has
   float inv_sqrt_d;
   int32_t lens[kMaxBatch];
 };
@@ -96,13 +101,24 @@ struct Launch {
   hipEvent_t stop = nullptr;
 };
 
-// launch a kernel that takes one argument struct; returns this launch's status
-template <typename Args>
-inline hipError_t launch_kernel(void (*kernel)(Args), dim3 grid, const Launch& l, const Args& a) {
-  void* args[] = {const_cast<Args*>(&a)};
+// launch a kernel with 256-thread workgroups; returns this launch's status.
+// Kernels on the decode path take, ahead of their argument struct, the few
+// scalars and pointers their first memory accesses need: the library is
+// built with kernel-argument preloading, so those arrive in SGPRs at wave
+// start instead of through a scalar load from the argument buffer.
+template <typename Kernel, typename Tuple, size_t... I>
+inline hipError_t launch_tuple(Kernel kernel, dim3 grid, const Launch& l, Tuple& vals, std::index_sequence<I...>) {
+  void* argv[] = {static_cast<void*>(&std::get<I>(vals))...};
   const void* f = reinterpret_cast<const void*>(kernel);
-  if (l.start || l.stop) return hipExtLaunchKernel(f, grid, dim3(kThreads), args, 0, l.s, l.start, l.stop, 0);
-  return hipLaunchKernel(f, grid, dim3(kThreads), args, 0, l.s);
+  if (l.start || l.stop) return hipExtLaunchKernel(f, grid, dim3(kThreads), argv, 0, l.s, l.start, l.stop, 0);
+  return hipLaunchKernel(f, grid, dim3(kThreads), argv, 0, l.s);
+}
+
+template <typename... P, typename... A>
+inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, const Launch& l, const A&... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<std::decay_t<P>...> vals(args...);  // each argument in the kernel's own parameter type
+  return launch_tuple(kernel, grid, l, vals, std::index_sequence_for<P...>{});
 }
 
 // host-side launchers (defined next to their kernels)
