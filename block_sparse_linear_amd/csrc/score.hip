@@ -133,20 +133,90 @@ __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const 
   }
 }
 
+// ============================================================== S_all rows
+// One chunk of 1024 / D rows x of S_all for (b, g) (thread = row x, value
+// channel quartet c4), in the first kernel of a decode:
+//   update   (fused step) S[x][:] += phi(k[x]) v and z[x] += phi(k[x]) for
+//            the step's token, with the same rounding as the append kernel
+//            (phi(k) v formed alone, then added);
+//   o_bar    partial phi(q_h)^T S and phi(q_h).z over the chunk's rows for
+//            every query head h of the group, from the rows just read or
+//            updated (so the token attends to itself): the combine sums the
+//            D * D / 1024 chunks and never reads S_all.
+template <bool BF16, int R, int D, bool UPDATE>
+__device__ void state_rows(const DecodeArgs& dc, const StateRefs& st, int b, int g, int rc) {
+  constexpr int ROWS = 1024 / D, C4N = D / 4, CHUNKS = D / ROWS;
+  __shared__ float4 red[R][ROWS][C4N];
+  __shared__ float zred[R][ROWS];
+  const int xr = threadIdx.x / C4N, c4 = threadIdx.x % C4N;
+  const int x = rc * ROWS + xr;
+  const size_t bg = (size_t)b * dc.G + g;
+  float4* S = reinterpret_cast<float4*>(st.s_all) + (bg * D + x) * C4N + c4;
+  float* z = st.z_all + bg * D + x;
+  float4 s = *S;
+  float zx = *z;
+  float qx[R];
+#pragma unroll
+  for (int h = 0; h < R; ++h) qx[h] = load_elem<BF16>(dc.q, ((size_t)b * dc.H + g * R + h) * D + x);
+  if constexpr (UPDATE) {
+    const float f = phi_f(load_elem<BF16>(st.k_new, bg * D + x));
+    const float4 v = load4<BF16>(st.v_new, bg * D + c4 * 4);
+    s = make_float4(s.x + fmaf(f, v.x, 0.f), s.y + fmaf(f, v.y, 0.f), s.z + fmaf(f, v.z, 0.f),
+                    s.w + fmaf(f, v.w, 0.f));
+    zx = zx + (0.f + f);
+    *S = s;
+    if (c4 == 0) *z = zx;
+  }
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    const float fq = phi_f(qx[h]);
+    red[h][xr][c4] = make_float4(fq * s.x, fq * s.y, fq * s.z, fq * s.w);
+    if (c4 == 0) zred[h][xr] = fq * zx;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < R * C4N; i += kThreads) {
+    const int h = i / C4N, c = i % C4N;
+    float4 acc = red[h][0][c];
+#pragma unroll
+    for (int r = 1; r < ROWS; ++r) {
+      const float4 t = red[h][r][c];
+      acc = make_float4(acc.x + t.x, acc.y + t.y, acc.z + t.z, acc.w + t.w);
+    }
+    reinterpret_cast<float4*>(dc.obar_part)[((bg * CHUNKS + rc) * R + h) * C4N + c] = acc;
+  }
+  if ((int)threadIdx.x < R) {
+    const int h = threadIdx.x;
+    float acc = zred[h][0];
+#pragma unroll
+    for (int r = 1; r < ROWS; ++r) acc += zred[h][r];
+    dc.dz_part[(bg * CHUNKS + rc) * R + h] = acc;
+  }
+}
+
+// spla_decode, first launch, grid (score_tiles + D * D / 1024, G, B): for
+// each (b, g) the scorer's tiles, then the o_bar partials of the S_all row
+// chunks.
 template <bool BF16, int R, int D>
 __global__ __launch_bounds__(kThreads) void k_score(const float* mean, const float* var, const void* q,
                                                      int32_t n_tiles, int32_t G, int32_t H, int32_t tiles_all,
-                                                     const DecodeArgs a) {
-  const ScorePre p{mean, var, q, n_tiles, G, H, tiles_all};
-  score_tile<BF16, R, D>(a, blockIdx.x, blockIdx.y, blockIdx.z, p);
+                                                     int32_t score_tiles, const StepArgs a) {
+  const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  if (x < score_tiles) {
+    const ScorePre p{mean, var, q, n_tiles, G, H, tiles_all};
+    score_tile<BF16, R, D>(a.dec, x, g, b, p);
+    return;
+  }
+  SPLA_SCALARS_READY("s"(a.st.s_all), "s"(a.st.z_all), "s"(a.dec.obar_part), "s"(a.dec.dz_part));
+  state_rows<BF16, R, D, false>(a.dec, a.st, b, g, x - score_tiles);
 }
 
-// Fused decode step, first launch, grid (score_tiles + chunks + 1, G, B):
-// for each (b, g), the scorer's tiles, then the S_all / z_all update of this
-// step's token in row chunks, then the token's page row and the statistics
-// of the block it completes.  The two parts are independent: the scorer reads
-// statistics of candidate blocks 1..nb-2 only, all completed by earlier
-// appends, and neither pages nor S_all.
+// Fused decode step, first launch, grid (score_tiles + D * D / 1024 + 1, G,
+// B): for each (b, g), the scorer's tiles, then the S_all / z_all update of
+// this step's token in row chunks (with their o_bar partials), then the
+// token's page row and the statistics of the block it completes.  The two
+// parts are independent: the scorer reads statistics of candidate blocks
+// 1..nb-2 only, all completed by earlier appends, and neither pages nor
+// S_all.
 template <bool BF16, int R, int D>
 __global__ __launch_bounds__(kThreads) void k_step_score(const float* mean, const float* var, const void* q,
                                                           int32_t n_tiles, int32_t G, int32_t H, int32_t tiles_all,
@@ -159,28 +229,30 @@ __global__ __launch_bounds__(kThreads) void k_step_score(const float* mean, cons
     score_tile<BF16, R, D>(dc, x, g, b, p);
     return;
   }
-  const int T = dc.lens[b];  // after the append
-  SPLA_SCALARS_READY("s"(T), "s"(dc.bk), "s"(a.st.k_new), "s"(a.st.v_new), "s"(a.st.s_all), "s"(a.st.z_all),
-                     "s"(a.st.block_table), "s"(a.st.k_pages), "s"(a.st.v_pages));
-  const AppendEntry E{b, 1, T - 1, b};
+  SPLA_SCALARS_READY("s"(dc.bk), "s"(a.st.k_new), "s"(a.st.v_new), "s"(a.st.s_all), "s"(a.st.z_all),
+                     "s"(dc.obar_part), "s"(dc.dz_part), "s"(a.st.block_table), "s"(a.st.k_pages),
+                     "s"(a.st.v_pages));
   if (x < score_tiles + kChunks) {
-    append_state_rows<BF16>(a.st, E, g, x - score_tiles);
+    state_rows<BF16, R, D, true>(dc, a.st, b, g, x - score_tiles);
     return;
   }
+  const int T = dc.lens[b];  // after the append
+  const AppendEntry E{b, 1, T - 1, b};
   append_page_row_head<BF16>(a.st, E, g);
   if (T % dc.bk == 0) append_block_stats<BF16>(a.st, E, T / dc.bk - 1, g);
 }
 
 }  // namespace
 
-hipError_t launch_score(const DecodeArgs& a, bool bf16, const Launch& l) {
-  const dim3 grid(a.score_tiles, a.G, a.B);
-  if (a.score_tiles == 0) return hipSuccess;
+hipError_t launch_score(const StepArgs& a, bool bf16, const Launch& l) {
+  const DecodeArgs& d = a.dec;
+  const int chunks = d.d / (1024 / d.d);
+  const dim3 grid(d.score_tiles + chunks, d.G, d.B);
   if (bf16)
-    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_score<true, RR, DD>, grid, l, a.blk_mean, a.blk_var, a.q, a.n_tiles,
-                                             a.G, a.H, a.tiles_all, a))
-  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_score<false, RR, DD>, grid, l, a.blk_mean, a.blk_var, a.q, a.n_tiles,
-                                           a.G, a.H, a.tiles_all, a))
+    SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_score<true, RR, DD>, grid, l, d.blk_mean, d.blk_var, d.q, d.n_tiles,
+                                             d.G, d.H, d.tiles_all, d.score_tiles, a))
+  SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_score<false, RR, DD>, grid, l, d.blk_mean, d.blk_var, d.q, d.n_tiles,
+                                           d.G, d.H, d.tiles_all, d.score_tiles, a))
 }
 
 hipError_t launch_step_score(const StepArgs& a, bool bf16, const Launch& l) {

@@ -21,7 +21,7 @@ struct spla_handle {
   hipError_t last_hip = hipSuccess;  // status of the last launch that failed
   int32_t fused_select = -1;         // SPLA_TUNE_FUSED_SELECT
   // workspace layout (bytes)
-  size_t off_lg = 0, off_sel = 0, off_page = 0, off_part = 0, ws_bytes = 0;
+  size_t off_lg = 0, off_sel = 0, off_page = 0, off_part = 0, off_obar = 0, off_dz = 0, ws_bytes = 0;
 };
 
 namespace {
@@ -42,6 +42,11 @@ void layout(spla_handle* h) {
   off = align256(off + B * G * k * sizeof(int32_t));
   h->off_part = off;
   off = align256(off + B * H * k * (2 * d + kPartHdr) * sizeof(float));
+  const size_t chunks = d * d / 1024;  // S_all row chunks per (sequence, KV head)
+  h->off_obar = off;
+  off = align256(off + B * G * chunks * (H / G) * d * sizeof(float));
+  h->off_dz = off;
+  off = align256(off + B * G * chunks * (H / G) * sizeof(float));
   h->ws_bytes = off;
 }
 
@@ -68,6 +73,8 @@ spla_status fill_decode_args(const spla_handle* h, const void* q, const float* g
   a->sel = ws_ptr<int32_t>(h, h->off_sel);
   a->sel_page = ws_ptr<int32_t>(h, h->off_page);
   a->part = ws_ptr<float>(h, h->off_part);
+  a->obar_part = ws_ptr<float>(h, h->off_obar);
+  a->dz_part = ws_ptr<float>(h, h->off_dz);
   a->err = ws_ptr<uint32_t>(h, 0);
   if (aux) {
     a->sel_in = aux->sel_in;
@@ -182,11 +189,9 @@ bool use_fused_select(const spla_handle* h, const DecodeArgs& a, bool bf16) {
 int decode_plan(const spla_handle* h, const DecodeArgs& a, int32_t call, int32_t* k) {
   const bool bf16 = h->cfg.kv_dtype == SPLA_BF16;
   int n = 0;
-  if (call == SPLA_CALL_DECODE_STEP) {
-    k[n++] = SPLA_KERNEL_STEP_SCORE;
-  } else if (call == SPLA_CALL_DECODE && a.score_tiles > 0) {
-    k[n++] = SPLA_KERNEL_SCORE;
-  }
+  // the first kernel also forms the phi(q)^T S_all partials the combine needs,
+  // so it runs even when there is nothing to score
+  k[n++] = call == SPLA_CALL_DECODE_STEP ? SPLA_KERNEL_STEP_SCORE : SPLA_KERNEL_SCORE;
   if (call == SPLA_CALL_DECODE_SEL_IN) {
     k[n++] = SPLA_KERNEL_ATTEND;
   } else if (use_fused_select(h, a, bf16)) {
@@ -201,16 +206,17 @@ int decode_plan(const spla_handle* h, const DecodeArgs& a, int32_t call, int32_t
 
 constexpr int kMaxPlan = 4;
 
-// launch a plan; `step` carries the fused first kernel of spla_decode_step
-hipError_t run_plan(const spla_handle* h, const DecodeArgs& a, const StepArgs* step, const int32_t* plan, int n,
-                    LaunchSeq& ls) {
+// launch a plan; sa.dec are the decode arguments, sa.st the state (with the
+// step's k / v for spla_decode_step)
+hipError_t run_plan(const spla_handle* h, const StepArgs& sa, const int32_t* plan, int n, LaunchSeq& ls) {
   const bool bf16 = h->cfg.kv_dtype == SPLA_BF16;
+  const DecodeArgs& a = sa.dec;
   for (int i = 0; i < n; ++i) {
     const Launch l = ls.next();
     hipError_t e = hipErrorInvalidValue;
     switch (plan[i]) {
-      case SPLA_KERNEL_SCORE: e = launch_score(a, bf16, l); break;
-      case SPLA_KERNEL_STEP_SCORE: e = step ? launch_step_score(*step, bf16, l) : hipErrorInvalidValue; break;
+      case SPLA_KERNEL_SCORE: e = launch_score(sa, bf16, l); break;
+      case SPLA_KERNEL_STEP_SCORE: e = launch_step_score(sa, bf16, l); break;
       case SPLA_KERNEL_SELECT: e = launch_select(a, l); break;
       case SPLA_KERNEL_ATTEND: e = launch_attend(a, bf16, l); break;
       case SPLA_KERNEL_SELECT_ATTEND: e = launch_select_attend(a, l); break;
@@ -400,12 +406,14 @@ spla_status spla_decode(spla_handle* h, const void* q, const float* gate, float*
   const spla_config& c = h->cfg;
   for (int b = 0; b < c.batch; ++b)
     if (h->lens[b] <= 0) return SPLA_ERR_INVALID_ARG;
-  DecodeArgs a;
-  fill_decode_args(h, q, gate, out, aux, &a);
+  StepArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  fill_decode_args(h, q, gate, out, aux, &sa.dec);
+  fill_state_refs(h, nullptr, nullptr, &sa.st);
   int32_t plan[kMaxPlan];
-  const int n = decode_plan(h, a, a.sel_in ? SPLA_CALL_DECODE_SEL_IN : SPLA_CALL_DECODE, plan);
+  const int n = decode_plan(h, sa.dec, sa.dec.sel_in ? SPLA_CALL_DECODE_SEL_IN : SPLA_CALL_DECODE, plan);
   LaunchSeq ls(reinterpret_cast<hipStream_t>(stream), aux);
-  const hipError_t e = run_plan(h, a, nullptr, plan, n, ls);
+  const hipError_t e = run_plan(h, sa, plan, n, ls);
   return e == hipSuccess ? SPLA_OK : hip_fail(h, e);
 }
 
@@ -427,7 +435,7 @@ spla_status spla_decode_step(spla_handle* h, const void* k_new, const void* v_ne
   int32_t plan[kMaxPlan];
   const int n = decode_plan(h, a.dec, SPLA_CALL_DECODE_STEP, plan);
   LaunchSeq ls(reinterpret_cast<hipStream_t>(stream), aux);
-  const hipError_t e = run_plan(h, a.dec, &a, plan, n, ls);
+  const hipError_t e = run_plan(h, a, plan, n, ls);
   // the mirror advances once the append is enqueued (the first kernel)
   if (e != hipSuccess && ls.k <= 1) return hip_fail(h, e);
   for (int b = 0; b < c.batch; ++b) h->lens[b] += 1;

@@ -45,6 +45,8 @@ struct DecodeArgs {
   int32_t* sel;     // workspace [B][G][top_k] selected block ids
   int32_t* sel_page;  // workspace [B][G][top_k] their page ids
   float* part;      // workspace [B][H][top_k][2d + kPartHdr]
+  float* obar_part;  // workspace [B][G][d * d / 1024][R][d]: phi(q)^T S_all over one chunk of S rows
+  float* dz_part;    // workspace [B][G][d * d / 1024][R]: phi(q).z_all over the same rows
   uint32_t* err;    // workspace error word
   const int32_t* sel_in;
   int32_t* sel_out;
@@ -123,7 +125,7 @@ inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, const Launch& l
 
 // host-side launchers (defined next to their kernels)
 hipError_t launch_append(const AppendArgs& a, bool bf16, const Launch& l);
-hipError_t launch_score(const DecodeArgs& a, bool bf16, const Launch& l);
+hipError_t launch_score(const StepArgs& a, bool bf16, const Launch& l);  // st: no new k / v
 hipError_t launch_select(const DecodeArgs& a, const Launch& l);
 hipError_t launch_attend(const DecodeArgs& a, bool bf16, const Launch& l);
 hipError_t launch_combine(const DecodeArgs& a, bool bf16, const Launch& l);

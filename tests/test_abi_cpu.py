@@ -138,11 +138,14 @@ def test_sizes(lib):
     assert st == OK
     n_tiles = -(-130 // 64)
     assert lib.spla_stats_floats(h) == 3 * 2 * n_tiles * 64 * 64
-    # error word + scores + two index lists + per-head partials, each part
-    # rounded up to 256 bytes
-    need = 256 + 3 * 2 * n_tiles * 64 * 4 + 2 * 3 * 2 * 20 * 4 + 3 * 8 * 20 * (2 * 64 + 4) * 4
+    # error word + scores + two index lists + per-head partials + the
+    # phi(q)^T S_all and phi(q).z partials of the d * d / 1024 row chunks,
+    # each part rounded up to 256 bytes
+    chunks = 64 * 64 // 1024
+    need = (256 + 3 * 2 * n_tiles * 64 * 4 + 2 * 3 * 2 * 20 * 4 + 3 * 8 * 20 * (2 * 64 + 4) * 4
+            + 3 * 8 * chunks * 64 * 4 + 3 * 8 * chunks * 4)
     ws = lib.spla_workspace_bytes(h)
-    assert need <= ws <= need + 4 * 256 and ws % 256 == 0
+    assert need <= ws <= need + 6 * 256 and ws % 256 == 0
     assert lib.spla_workspace_bytes(None) == 0 and lib.spla_stats_floats(None) == 0
     lib.spla_destroy(h)
 
@@ -272,7 +275,7 @@ def test_launch_plan(lib):
     h, c = bound(lib)
     assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]  # automatic: 4 (b, g) pairs -> fused
     assert plan(lib, h, 0) == [SCORE, SELECT_ATTEND, COMBINE]
-    assert plan(lib, h, 1) == [ATTEND, COMBINE]                     # selection override
+    assert plan(lib, h, 1) == [SCORE, ATTEND, COMBINE]              # selection override
     assert lib.spla_set_tuning(h, 0, 0) == OK
     assert plan(lib, h, 2) == [STEP_SCORE, SELECT, ATTEND, COMBINE]
     assert lib.spla_set_tuning(h, 0, 1) == OK
@@ -281,9 +284,10 @@ def test_launch_plan(lib):
     assert lib.spla_launch_plan(h, 2, None, 0) == 3                 # count only
     assert lens_of(lib, h, 2) == [100, 2000]                       # the query changes nothing
     lib.spla_destroy(h)
-    # every sequence short: no scorer launch for spla_decode
+    # every sequence short: the first kernel still runs (it forms the
+    # phi(q)^T S_all partials of the combine)
     h, c = bound(lib, lens=(5, 64 * 16))
-    assert plan(lib, h, 0) == [SELECT_ATTEND, COMBINE]
+    assert plan(lib, h, 0) == [SCORE, SELECT_ATTEND, COMBINE]
     assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
     lib.spla_destroy(h)
     # the fused kernel needs bf16 and Bk = 64
