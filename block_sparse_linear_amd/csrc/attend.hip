@@ -164,8 +164,8 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(const DecodeArgs a) {
   const int slot = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.top_k), "s"(a.sel_in), "s"(a.sel), "s"(a.sel_page),
                      "s"(a.G), "s"(a.q), "s"(a.H), "s"(a.k_pages), "s"(a.v_pages));
-  uint4 qraw[D / 32];
-  load_q_mfma<R, D>(a.q, a.H, g, b, qraw);  // independent of the selection: issued first
+  uint4 qraw[D / 32], fh[D / 32], fl[D / 32];
+  load_q_mfma<R, D>(a.q, a.phq, a.H, g, b, qraw, fh, fl);  // independent of the selection: issued first
   const size_t srow = ((size_t)b * a.G + g) * a.top_k + slot;
   int j, page;
   if (a.sel_in) {
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(const DecodeArgs a) {
     j = a.sel[srow];
     page = a.sel_page[srow];
   }
-  attend_block_mfma<R, D, BK>(a, slot, g, b, j, page, qraw);
+  attend_block_mfma<R, D, BK>(a, slot, g, b, j, page, qraw, fh, fl);
 }
 
 }  // namespace

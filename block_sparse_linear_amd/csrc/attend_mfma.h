@@ -14,15 +14,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// two floats -> packed bf16 pair (round to nearest even, hardware conversion)
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ float bf16_lo_f(uint32_t p) { return __uint_as_float(p << 16); }
-__device__ __forceinline__ float bf16_hi_f(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
@@ -40,33 +31,25 @@ __device__ __forceinline__ uint4 phi_bf16(const uint4& raw) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// phi of 8 packed bf16 values split into bf16 hi + lo parts (hi + lo carries
-// phi to ~2^-16 relative)
-__device__ __forceinline__ void phi_hilo(const uint4& raw, uint4& hi, uint4& lo) {
-  const uint32_t in[4] = {raw.x, raw.y, raw.z, raw.w};
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float f0 = phi_fast(bf16_lo_f(in[k])), f1 = phi_fast(bf16_hi_f(in[k]));
-    h[k] = pack_bf16(f0, f1);
-    l[k] = pack_bf16(f0 - bf16_lo_f(h[k]), f1 - bf16_hi_f(h[k]));
-  }
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
-// queries of product (1) for this lane: row m = lane % 16 of the A operand
-// holds query m (m < R) or phi(q) of query m - WB; other rows load query 0
-// and are masked when the operands are formed
+// A operands of product (1) for this lane: row m = lane % 16 holds query m
+// (m < R), or bf16 hi / lo of phi(query m - WB) (from the phi(q) array the
+// first kernel of the decode wrote); other rows read row 0 and are masked
+// when the operands are formed
 template <int R, int D>
-__device__ __forceinline__ void load_q_mfma(const void* q, int H, int g, int b, uint4 (&qraw)[D / 32]) {
+__device__ __forceinline__ void load_q_mfma(const void* q, const uint16_t* phq, int H, int g, int b,
+                                            uint4 (&qraw)[D / 32], uint4 (&fh)[D / 32], uint4 (&fl)[D / 32]) {
   constexpr int WB = R <= 4 ? 4 : 8;
   const int lane = threadIdx.x % 64, m = lane % 16, lg4 = lane / 16;
-  const int hq = m < R ? m : ((m >= WB && m < WB + R) ? m - WB : 0);
+  const int hq = m < R ? m : 0;
+  const int hw = (m >= WB && m < WB + R) ? m - WB : 0;
+  const uint16_t* fq = phq + ((size_t)b * H + g * R + hw) * 2 * D;
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
+  for (int ks = 0; ks < D / 32; ++ks) {
     qraw[ks] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) +
                                                ((size_t)b * H + g * R + hq) * D + 32 * ks + 8 * lg4);
+    fh[ks] = *reinterpret_cast<const uint4*>(fq + 32 * ks + 8 * lg4);
+    fl[ks] = *reinterpret_cast<const uint4*>(fq + D + 32 * ks + 8 * lg4);
+  }
 }
 
 // Block j (page `page`) of (b, g), all R query heads, bf16 K/V; writes the
@@ -84,7 +67,8 @@ __device__ __forceinline__ void load_q_mfma(const void* q, int H, int g, int b, 
 // the workgroup.
 template <int R, int D, int BK>
 __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot, int g, int b, int j, int page,
-                                                  const uint4 (&qraw)[D / 32]) {
+                                                  const uint4 (&qraw)[D / 32], const uint4 (&fh)[D / 32],
+                                                  const uint4 (&fl)[D / 32]) {
   constexpr int NKS = D / 32;              // k-steps per channel block
   constexpr int NT1W = BK / 64;            // 16-token tiles per wavefront
   constexpr int WB = R <= 4 ? 4 : 8;       // first linear-weight row of product (1)
@@ -146,11 +130,9 @@ __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot,
   uint4 aq[NKS], afh[NKS], afl[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    uint4 hi, lo;
-    phi_hilo(qraw[ks], hi, lo);
     aq[ks] = make_uint4(qraw[ks].x & mq, qraw[ks].y & mq, qraw[ks].z & mq, qraw[ks].w & mq);
-    afh[ks] = make_uint4(hi.x & mw, hi.y & mw, hi.z & mw, hi.w & mw);
-    afl[ks] = make_uint4(lo.x & mw, lo.y & mw, lo.z & mw, lo.w & mw);
+    afh[ks] = make_uint4(fh[ks].x & mw, fh[ks].y & mw, fh[ks].z & mw, fh[ks].w & mw);
+    afl[ks] = make_uint4(fl[ks].x & mw, fl[ks].y & mw, fl[ks].z & mw, fl[ks].w & mw);
   }
 
   // ---- product (1): logits and linear weights of this wavefront's tokens

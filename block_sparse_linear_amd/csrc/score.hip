@@ -171,7 +171,16 @@ __device__ void state_rows(const DecodeArgs& dc, const StateRefs& st, int b, int
   for (int h = 0; h < R; ++h) {
     const float fq = phi_f(qx[h]);
     red[h][xr][c4] = make_float4(fq * s.x, fq * s.y, fq * s.z, fq * s.w);
-    if (c4 == 0) zred[h][xr] = fq * zx;
+    if (c4 == 0) {
+      zred[h][xr] = fq * zx;
+      // phi(q) of row x as bf16 hi + lo for the attend kernel's matrix-core
+      // operands (hi + lo carries phi to ~2^-16 relative)
+      const uint32_t hi = pack_bf16(fq, 0.f) & 0xffffu;
+      const uint32_t lo = pack_bf16(fq - bf16_lo_f(hi), 0.f) & 0xffffu;
+      uint16_t* dst = dc.phq + ((size_t)b * dc.H + g * R + h) * 2 * D + x;
+      dst[0] = (uint16_t)hi;
+      dst[D] = (uint16_t)lo;
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < R * C4N; i += kThreads) {

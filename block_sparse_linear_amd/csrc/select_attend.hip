@@ -15,8 +15,9 @@ namespace {
 
 template <int KPT, int R, int D>
 __global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, const int32_t* block_table,
-                                                             const void* q, int32_t n_tiles, int32_t max_blocks,
-                                                             int32_t G, int32_t H, const DecodeArgs a) {
+                                                             const void* q, const uint16_t* phq, int32_t n_tiles,
+                                                             int32_t max_blocks, int32_t G, int32_t H,
+                                                             const DecodeArgs a) {
   __shared__ SelectLds L;
   __shared__ int s_j, s_page;
   const int slot = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -25,8 +26,8 @@ __global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, con
   // the queries
   SelectKeys<KPT> k;
   select_load<KPT>(lg, block_table, n_tiles, max_blocks, G, g, b, k);
-  uint4 qraw[D / 32];
-  load_q_mfma<R, D>(q, H, g, b, qraw);
+  uint4 qraw[D / 32], fh[D / 32], fl[D / 32];
+  load_q_mfma<R, D>(q, phq, H, g, b, qraw, fh, fl);
   SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.top_k), "s"(a.sel), "s"(a.k_pages), "s"(a.v_pages),
                      "s"(a.part), "s"(a.num_pages), "s"(a.inv_sqrt_d));
   const int nb = n_blocks(a, b);
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, con
   }
   // the combine reads the selection to tell used slots from unused ones
   if (threadIdx.x == 0) a.sel[((size_t)b * a.G + g) * a.top_k + slot] = j;
-  attend_block_mfma<R, D, 64>(a, slot, g, b, j, page, qraw);
+  attend_block_mfma<R, D, 64>(a, slot, g, b, j, page, qraw, fh, fl);
 }
 
 template <int K, int... Ks>
@@ -56,7 +57,7 @@ hipError_t launch_select_attend_sized(const DecodeArgs& a, const Launch& l, int 
   if (nc <= K * kThreads) {
     const dim3 grid(a.top_k, a.G, a.B);
     SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_select_attend<K, RR, DD>, grid, l, a.lg, a.block_table, a.q,
-                                             a.n_tiles, a.max_blocks, a.G, a.H, a))
+                                             a.phq, a.n_tiles, a.max_blocks, a.G, a.H, a))
   }
   if constexpr (sizeof...(Ks) == 0) {
     return hipErrorInvalidValue;

@@ -28,18 +28,19 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
-// LDS of the selector (lists padded with sentinels so the rank counts read
-// them four at a time)
+// LDS of the selector (the ranking list is padded with sentinels so the rank
+// counts read it four at a time)
 struct __attribute__((aligned(16))) SelectLds {
   int hist[4][256];  // one histogram per wavefront
+  uint32_t bits[(kSelMax + 31) / 32 + 3];  // chosen candidates (bit i: candidate i)
+  int pre[(kSelMax + 31) / 32];            // chosen candidates in the words before word w
+  int s_wt[2][4];
   float mkey[kSelRank];
   int midx[kSelRank];
-  int slist[256];
-  int spage[256];          // page of slist[i]
   int mpage[kSelRank];     // page of midx[i]
   float s_mn[4], s_mx[4];
   int s_cnt[4];
-  int s_bt, s_above, s_cbt, s_n, s_nm;
+  int s_bt, s_above, s_cbt, s_nm;
 };
 
 // one thread's candidates: scores and page ids (candidate i = thread + 256 u,
@@ -109,7 +110,8 @@ __device__ __forceinline__ void append_flagged(Mask flags, int* counter, Store&&
 // same way until it holds at most kSelRank candidates (then ranked exactly by
 // (score desc, id asc)) or only equal scores (then taken by ascending id).
 // The bucket index is a monotone function of the score, so the result is the
-// exact top k'.  The chosen ids are put in ascending order by a rank count.
+// exact top k'.  The chosen ids are put in ascending order by counting, for
+// each, the chosen candidates with a smaller index in a bitmap of the set.
 //
 // Requires nb > top_k and the keys of select_load; every thread of the
 // workgroup must call it.  For each output position pos in [0, top_k),
@@ -124,13 +126,10 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
   Mask memb = 0, above = 0;  // bit u: key u still in the threshold bucket / already taken
 #pragma unroll
   for (int u = 0; u < KPT; ++u) memb |= (Mask)((int)threadIdx.x + u * kThreads < nc) << u;
-  if (threadIdx.x == 0) {
-    L.s_n = 0;
-    L.s_nm = 0;
-  }
+  if (threadIdx.x == 0) L.s_nm = 0;
   L.mkey[threadIdx.x] = -INFINITY;
   L.midx[threadIdx.x] = 0x7fffffff;
-  L.slist[threadIdx.x] = 0x7fffffff;
+  for (int i = threadIdx.x; i < (nc + 31) / 32 + 3; i += kThreads) L.bits[i] = 0u;
   // the counters and sentinels above are used by every wavefront (the loop
   // below may not run at all); this barrier waits on LDS only, not on the
   // score loads in flight
@@ -227,12 +226,16 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
     above |= low;
     memb = 0;
   }
-  // every key above a threshold bucket (or taken by id) goes to the chosen
-  // list; the final bucket's keys go to the ranking list
-  append_flagged<KPT>(above, &L.s_n, [&](int u, int pos) {
-    L.slist[pos] = threadIdx.x + u * kThreads;
-    L.spage[pos] = k.pg[u];
-  });
+  // every key above a threshold bucket (or taken by id) is chosen: its bit
+  // goes into the bitmap (an LDS atomic with no return); the threshold
+  // bucket's keys go to the ranking list
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    if ((above >> u) & 1) {
+      const int i = threadIdx.x + u * kThreads;
+      atomicOr(&L.bits[i >> 5], 1u << (i & 31));
+    }
+  }
   append_flagged<KPT>(memb, &L.s_nm, [&](int u, int pos) {
     L.mkey[pos] = k.x[u];
     L.midx[pos] = threadIdx.x + u * kThreads;
@@ -241,13 +244,11 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
   __syncthreads();
   // the final bucket (<= kSelRank candidates): exact rank by (score desc, id asc)
   const int nm = L.s_nm;
+  int took = -1, took_pg = 0;
   if (nm > 0) {
-    bool take = false;
-    int my = 0, mypg = 0;
     if ((int)threadIdx.x < nm) {
       const float xv = L.mkey[threadIdx.x];
-      my = L.midx[threadIdx.x];
-      mypg = L.mpage[threadIdx.x];
+      const int my = L.midx[threadIdx.x];
       int rank = 0;
 #pragma unroll 4
       for (int v = 0; v < nm; v += 4) {
@@ -258,29 +259,50 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
         rank += (y.z > xv) || (y.z == xv && iy.z < my);
         rank += (y.w > xv) || (y.w == xv && iy.w < my);
       }
-      take = rank < need;
+      if (rank < need) {
+        took = my;
+        took_pg = L.mpage[threadIdx.x];
+        atomicOr(&L.bits[my >> 5], 1u << (my & 31));
+      }
     }
-    append_flagged<1>((uint32_t)take, &L.s_n, [&](int, int pos) {
-      L.slist[pos] = my;
-      L.spage[pos] = mypg;
-    });
     __syncthreads();
   }
-  // ascending order by a rank count over the kp chosen ids
-  if ((int)threadIdx.x < kp) {
-    const int v = L.slist[threadIdx.x];
-    int pos = 0;
-#pragma unroll 4
-    for (int u = 0; u < kp; u += 4) {
-      const int4 y = *reinterpret_cast<const int4*>(&L.slist[u]);
-      pos += (y.x < v) + (y.y < v) + (y.z < v) + (y.w < v);
+  // exclusive prefix counts of the bitmap words (a block-wide scan over at
+  // most 2 * 256 words), then the output position of chosen candidate i is
+  // 1 + the chosen candidates below it
+  {
+    const int nw = (nc + 31) / 32;
+    const int w0 = threadIdx.x, w1 = threadIdx.x + kThreads;
+    const int c0 = w0 < nw ? __popc(L.bits[w0]) : 0;
+    const int c1 = w1 < nw ? __popc(L.bits[w1]) : 0;
+    const int i0 = wave_incl_scan_i(c0), i1 = wave_incl_scan_i(c1);
+    if (lane == 63) {
+      L.s_wt[0][wv] = i0;
+      L.s_wt[1][wv] = i1;
     }
-    emit(1 + pos, v + 1, L.spage[threadIdx.x]);
-  } else if ((int)threadIdx.x == kp) {
-    emit(0, 0, k.pg_sink);
-  } else if ((int)threadIdx.x == kp + 1) {
-    emit(kp + 1, nb - 1, k.pg_cur);
+    __syncthreads();
+    int off0 = 0, off1 = 0, tot0 = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tot0 += L.s_wt[0][q];
+      off0 += q < wv ? L.s_wt[0][q] : 0;
+      off1 += q < wv ? L.s_wt[1][q] : 0;
+    }
+    if (w0 < nw) L.pre[w0] = off0 + i0 - c0;
+    if (w1 < nw) L.pre[w1] = tot0 + off1 + i1 - c1;
+    __syncthreads();
   }
+  auto position = [&](int i) { return 1 + L.pre[i >> 5] + __popc(L.bits[i >> 5] & ((1u << (i & 31)) - 1u)); };
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    if ((above >> u) & 1) {
+      const int i = threadIdx.x + u * kThreads;
+      emit(position(i), i + 1, k.pg[u]);
+    }
+  }
+  if (took >= 0) emit(position(took), took + 1, took_pg);
+  if (threadIdx.x == 0) emit(0, 0, k.pg_sink);
+  if (threadIdx.x == kThreads - 1) emit(kp + 1, nb - 1, k.pg_cur);
 }
 
 // keys-per-thread sizes compiled for a selector: the smallest one that holds

@@ -21,7 +21,8 @@ struct spla_handle {
   hipError_t last_hip = hipSuccess;  // status of the last launch that failed
   int32_t fused_select = -1;         // SPLA_TUNE_FUSED_SELECT
   // workspace layout (bytes)
-  size_t off_lg = 0, off_sel = 0, off_page = 0, off_part = 0, off_obar = 0, off_dz = 0, ws_bytes = 0;
+  size_t off_lg = 0, off_sel = 0, off_page = 0, off_part = 0, off_obar = 0, off_dz = 0, off_phq = 0;
+  size_t ws_bytes = 0;
 };
 
 namespace {
@@ -47,6 +48,8 @@ void layout(spla_handle* h) {
   off = align256(off + B * G * chunks * (H / G) * d * sizeof(float));
   h->off_dz = off;
   off = align256(off + B * G * chunks * (H / G) * sizeof(float));
+  h->off_phq = off;
+  off = align256(off + B * H * 2 * d * sizeof(uint16_t));
   h->ws_bytes = off;
 }
 
@@ -75,6 +78,7 @@ spla_status fill_decode_args(const spla_handle* h, const void* q, const float* g
   a->part = ws_ptr<float>(h, h->off_part);
   a->obar_part = ws_ptr<float>(h, h->off_obar);
   a->dz_part = ws_ptr<float>(h, h->off_dz);
+  a->phq = ws_ptr<uint16_t>(h, h->off_phq);
   a->err = ws_ptr<uint32_t>(h, 0);
   if (aux) {
     a->sel_in = aux->sel_in;

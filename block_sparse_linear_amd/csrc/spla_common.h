@@ -47,6 +47,7 @@ struct DecodeArgs {
   float* part;      // workspace [B][H][top_k][2d + kPartHdr]
   float* obar_part;  // workspace [B][G][d * d / 1024][R][d]: phi(q)^T S_all over one chunk of S rows
   float* dz_part;    // workspace [B][G][d * d / 1024][R]: phi(q).z_all over the same rows
+  uint16_t* phq;     // workspace [B][H][2][d]: phi(q) as bf16 hi, then the bf16 rounding of the rest
   uint32_t* err;    // workspace error word
   const int32_t* sel_in;
   int32_t* sel_out;
@@ -242,6 +243,16 @@ __device__ __forceinline__ int wave_incl_scan_i(int v) {
   t += dpp_i<kDppRowBcast31, 0xc>(0, t);
   return t;
 }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair (round to nearest even, hardware conversion)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo_f(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi_f(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
 
 // order-preserving map float -> uint32 (larger float -> larger key)
 __device__ __forceinline__ uint32_t float_key(float x) {
