@@ -24,10 +24,6 @@ __device__ __forceinline__ int sel_bucket(float x, float lo, float scale) {
   return f >= 255.f ? 255 : (f <= 0.f ? 0 : (int)f);
 }
 
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-}
-
 // LDS of the selector (the ranking list is padded with sentinels so the rank
 // counts read it four at a time)
 struct __attribute__((aligned(16))) SelectLds {
@@ -72,35 +68,18 @@ __device__ __forceinline__ void select_load(const float* lg, const int32_t* bloc
   }
 }
 
+// Pages of the sink and the current block.  They are read with vector
+// loads (the offset is a zero the compiler cannot see as uniform): a scalar
+// load would be waited for at every LDS barrier of the selection, which waits
+// on the scalar-load counter too.
 template <int KPT>
 __device__ __forceinline__ void select_pages(const int32_t* block_table, int max_blocks, int b, int nb,
                                              SelectKeys<KPT>& k) {
+  int zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
   const int32_t* btab = block_table + (size_t)b * max_blocks;
-  k.pg_sink = btab[0];
-  k.pg_cur = btab[min(max(nb - 1, 0), max_blocks - 1)];
-}
-
-// Append the keys flagged in `flags` (bit u: key u of this thread) to an LDS
-// list, one LDS atomic per wavefront; store(u, position) is called for each.
-// A key step where no lane of the wavefront has a flag costs one ballot and
-// a scalar branch.
-template <int KPT, typename Mask, typename Store>
-__device__ __forceinline__ void append_flagged(Mask flags, int* counter, Store&& store) {
-  int total = 0;
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) total += __popcll(__ballot((flags >> u) & 1));
-  if (total == 0) return;
-  int base = 0;
-  if ((threadIdx.x & 63) == 0) base = atomicAdd(counter, total);
-  base = __builtin_amdgcn_readfirstlane(base);
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const uint64_t m = __ballot((flags >> u) & 1);
-    if (m != 0) {
-      if ((flags >> u) & 1) store(u, base + lanes_below(m));
-      base += __popcll(m);
-    }
-  }
+  k.pg_sink = btab[zero];
+  k.pg_cur = btab[min(max(nb - 1, 0), max_blocks - 1) + zero];
 }
 
 // Bucket select over the scores held in registers (KPT per thread,
@@ -227,20 +206,27 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
     memb = 0;
   }
   // every key above a threshold bucket (or taken by id) is chosen: its bit
-  // goes into the bitmap (an LDS atomic with no return); the threshold
-  // bucket's keys go to the ranking list
+  // goes into the bitmap (an LDS atomic with no return).  The threshold
+  // bucket's keys go to the ranking list: lanes count theirs, one LDS atomic
+  // per wavefront reserves the places, then every lane stores its own.
+  {
+    const int mine = __popcll((uint64_t)memb);
+    const int incl = wave_incl_scan_i(mine);
+    int base = 0;
+    if (lane == 63 && incl > 0) base = atomicAdd(&L.s_nm, incl);  // lane 63: the wavefront's total
+    int p = __builtin_amdgcn_readlane(base, 63) + incl - mine;
 #pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    if ((above >> u) & 1) {
+    for (int u = 0; u < KPT; ++u) {
       const int i = threadIdx.x + u * kThreads;
-      atomicOr(&L.bits[i >> 5], 1u << (i & 31));
+      if ((above >> u) & 1) atomicOr(&L.bits[i >> 5], 1u << (i & 31));
+      if ((memb >> u) & 1) {
+        L.mkey[p] = k.x[u];
+        L.midx[p] = i;
+        L.mpage[p] = k.pg[u];
+        ++p;
+      }
     }
   }
-  append_flagged<KPT>(memb, &L.s_nm, [&](int u, int pos) {
-    L.mkey[pos] = k.x[u];
-    L.midx[pos] = threadIdx.x + u * kThreads;
-    L.mpage[pos] = k.pg[u];
-  });
   __syncthreads();
   // the final bucket (<= kSelRank candidates): exact rank by (score desc, id asc)
   const int nm = L.s_nm;
@@ -270,8 +256,18 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
   // exclusive prefix counts of the bitmap words (a block-wide scan over at
   // most 2 * 256 words), then the output position of chosen candidate i is
   // 1 + the chosen candidates below it
-  {
-    const int nw = (nc + 31) / 32;
+  const int nw = (nc + 31) / 32;
+  if (nw <= 128) {
+    // one wavefront: two words per lane
+    if (wv == 0) {
+      const int c0 = 2 * lane < nw ? __popc(L.bits[2 * lane]) : 0;
+      const int c1 = 2 * lane + 1 < nw ? __popc(L.bits[2 * lane + 1]) : 0;
+      const int ex = wave_incl_scan_i(c0 + c1) - (c0 + c1);
+      if (2 * lane < nw) L.pre[2 * lane] = ex;
+      if (2 * lane + 1 < nw) L.pre[2 * lane + 1] = ex + c0;
+    }
+    __syncthreads();
+  } else {
     const int w0 = threadIdx.x, w1 = threadIdx.x + kThreads;
     const int c0 = w0 < nw ? __popc(L.bits[w0]) : 0;
     const int c1 = w1 < nw ? __popc(L.bits[w1]) : 0;
@@ -293,11 +289,24 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
     __syncthreads();
   }
   auto position = [&](int i) { return 1 + L.pre[i >> 5] + __popc(L.bits[i >> 5] & ((1u << (i & 31)) - 1u)); };
+  // positions of this thread's chosen keys: every read issued first (indices
+  // clamped into the bitmap), one wait, then the emits
+  {
+    int pw[KPT];
+    uint32_t bw[KPT];
+    const int last = max(nw - 1, 0);
 #pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    if ((above >> u) & 1) {
-      const int i = threadIdx.x + u * kThreads;
-      emit(position(i), i + 1, k.pg[u]);
+    for (int u = 0; u < KPT; ++u) {
+      const int wd = min((int)(threadIdx.x + u * kThreads) >> 5, last);
+      pw[u] = L.pre[wd];
+      bw[u] = L.bits[wd];
+    }
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      if ((above >> u) & 1) {
+        const int i = threadIdx.x + u * kThreads;
+        emit(1 + pw[u] + __popc(bw[u] & ((1u << (i & 31)) - 1u)), i + 1, k.pg[u]);
+      }
     }
   }
   if (took >= 0) emit(position(took), took + 1, took_pg);
