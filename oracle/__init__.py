@@ -5,11 +5,15 @@ leg may import this package.  See ``spla_oracle`` for the definitions, the
 passages they follow and the readings taken where the pages are silent.
 """
 from .spla_oracle import (  # noqa: F401
+    RLA_NORMALIZED,
+    RLA_PLAIN,
+    RLA_RMSNORM,
     SplaOracle,
     block_stats,
     group_log_score,
     linear_attention_numerator,
     phi,
+    rla_branch,
     select_blocks,
     softmax_attention,
     taylor_log_score,

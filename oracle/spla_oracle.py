@@ -46,7 +46,15 @@ with its reason in the design notes):
       difference D = phi(q).(z_all - z_sel) is reported beside them;
   R9  o_rla (and D) is exactly 0 when the selection covers every token;
   R10 a decode step first appends the new token to the state, then decodes
-      (the token attends to itself).
+      (the token attends to itself);
+  R11 output forms of the RLA branch (the specification's combine uses o_rla
+      as it is; the two others are options): "normalised" divides o_rla by
+      D, which makes it the standard normalised linear attention over the
+      unselected tokens; "RMS-normalised" is gamma * o_rla / sqrt(mean_c
+      o_rla_c^2 + eps) over the d channels of one query head, with a scale
+      gamma per (query head, channel) and eps > 0 given by the caller.  The
+      gate multiplies the branch in every form, and the branch is 0 in every
+      form when the selection covers every token.
 
 Parity of this module is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, library special cases and brute force; the readings R4, R7 and
@@ -149,6 +157,38 @@ def linear_attention_numerator(f: np.ndarray, k: np.ndarray, v: np.ndarray):
     return w @ np.asarray(v, dtype=F64), w.sum()
 
 
+# ------------------------------------------- output forms of the RLA branch
+RLA_PLAIN, RLA_NORMALIZED, RLA_RMSNORM = 0, 1, 2
+
+
+def rla_branch(o_rla: np.ndarray, d_rla: float, mode: int, gamma: Optional[np.ndarray] = None,
+               eps: float = 1e-6, covers_all: bool = False) -> np.ndarray:
+    """The RLA branch of one query head as it enters the gated sum (R11).
+
+    RLA_PLAIN       o_rla (the specification's combine).
+    RLA_NORMALIZED  o_rla / D.  By the subtraction form of [TS] 2.2, o_rla
+                    and D are the numerator phi(q)^T sum phi(k) v^T and the
+                    denominator phi(q) . sum phi(k) of linear attention over
+                    the unselected tokens, so the ratio is the normalised
+                    kernel form phi(Q)(phi(K)^T V) / phi(Q)(phi(K)^T 1) of
+                    [SA] 7 restricted to them.
+    RLA_RMSNORM     gamma * o_rla / sqrt(mean_c o_rla_c^2 + eps): [TS] 2.3
+                    normalises the RLA output with an RMS norm whose scale
+                    parameters are the method's only added weights.
+    Zero in every form when the selection covers every token (R9)."""
+    o_rla = np.asarray(o_rla, dtype=F64)
+    if covers_all:
+        return np.zeros_like(o_rla)
+    if mode == RLA_PLAIN:
+        return o_rla
+    if mode == RLA_NORMALIZED:
+        return o_rla / float(d_rla)
+    if mode == RLA_RMSNORM:
+        ms = float(np.mean(o_rla * o_rla))
+        return np.asarray(gamma, dtype=F64) * o_rla / math.sqrt(ms + float(eps))
+    raise ValueError(f"unknown RLA output form {mode}")
+
+
 class SplaOracle:
     """The decode state of one SPLA attention layer and its two operations.
 
@@ -227,14 +267,18 @@ class SplaOracle:
 
     def decode(self, q: np.ndarray, gate: np.ndarray,
                sel_override: Optional[np.ndarray] = None,
-               brute_rla: bool = False) -> Dict[str, object]:
+               brute_rla: bool = False, rla_mode: int = RLA_PLAIN,
+               gamma: Optional[np.ndarray] = None, eps: float = 1e-6) -> Dict[str, object]:
         """One decode step for every sequence (after that step's append).
 
         q: [B][H][d] queries, gate: [H].  sel_override: optional [B][G][k]
         block ids (-1 padded) used instead of the oracle's own selection
-        (the scores are still computed and returned).
+        (the scores are still computed and returned).  rla_mode, gamma
+        ([H][d]) and eps choose the output form of the RLA branch
+        (rla_branch); o = o_sparse + gate * branch.
 
-        Returns a dict with o, o_sparse, o_rla, o_bar, o_tilde ([B][H][d]),
+        Returns a dict with o, o_sparse, o_rla, o_bar, o_tilde, rla_out
+        (the branch in the chosen form) ([B][H][d]),
         d_rla [B][H], sel [B][G][top_k] (ascending, -1 padded), lg (list per
         b of list per g of {block: LG}), and, with brute_rla, o_rla_direct /
         d_rla_direct summed directly over the unselected tokens."""
@@ -242,7 +286,9 @@ class SplaOracle:
         q = np.asarray(q, dtype=F64)
         gate = np.asarray(gate, dtype=F64)
         out = {k: np.zeros((B, H, d), F64) for k in
-               ("o", "o_sparse", "o_rla", "o_bar", "o_tilde")}
+               ("o", "o_sparse", "o_rla", "o_bar", "o_tilde", "rla_out")}
+        if rla_mode == RLA_RMSNORM and gamma is None:
+            raise ValueError("the RMS-normalised form needs gamma")
         out["d_rla"] = np.zeros((B, H), F64)
         out["sel"] = np.full((B, G, self.top_k), -1, np.int64)
         out["lg"] = [[None] * G for _ in range(B)]
@@ -292,7 +338,10 @@ class SplaOracle:
                     out["o_tilde"][b, h] = o_til
                     out["o_rla"][b, h] = o_rla
                     out["d_rla"][b, h] = d_rla
-                    out["o"][b, h] = o_sp + gate[h] * o_rla
+                    branch = rla_branch(o_rla, d_rla, rla_mode,
+                                        None if gamma is None else gamma[h], eps, covers_all)
+                    out["rla_out"][b, h] = branch
+                    out["o"][b, h] = o_sp + gate[h] * branch
                     if brute_rla:
                         num, den = linear_attention_numerator(f, kn, vn)
                         out["o_rla_direct"][b, h] = num

@@ -295,11 +295,87 @@ def pin_planted_blocks_selected():
         assert set(plant[g]).issubset(set(res["sel"][0, g])), (plant[g], res["sel"][0, g])
 
 
+def _rla_setup(rng, K_unsel=None, V_unsel=None):
+    """T = 24 tokens (6 blocks of 4) of one KV head, selection fixed to
+    {0, 2, 5} by override, so tokens 4..7 and 12..19 are the unselected
+    ones; their K or V rows can be set."""
+    T, d = 24, 8
+    K = dyadic_normal(rng, (T, 1, d))
+    V = dyadic_normal(rng, (T, 1, d))
+    unsel = np.r_[4:8, 12:20]
+    if K_unsel is not None:
+        K[unsel, 0] = K_unsel
+    if V_unsel is not None:
+        V[unsel, 0] = V_unsel
+    o = fresh_oracle(B=1, H=2, G=1, d=d, bk=4, top_k=3)
+    fill(o, 0, K, V)
+    sel = np.array([[[0, 2, 5]]])
+    return o, K, V, unsel, sel
+
+
+def pin_rla_normalized_is_unselected_mean():
+    """Normalised form = linear attention over the unselected tokens with
+    weights normalised to 1: equal unselected keys give equal weights, so
+    the branch is the plain mean of their value rows; equal unselected
+    values give that value whatever the keys."""
+    rng = np.random.default_rng(21)
+    gate = np.array([0.75, -0.5])
+    kc = dyadic_normal(rng, (8,))
+    o, K, V, unsel, sel = _rla_setup(rng, K_unsel=kc)
+    q = rng.standard_normal((1, 2, 8))
+    res = o.decode(q, gate, sel_override=sel, rla_mode=so.RLA_NORMALIZED)
+    want = V[unsel, 0].mean(axis=0)
+    for h in range(2):
+        assert np.allclose(res["rla_out"][0, h], want, rtol=1e-12, atol=1e-12)
+        assert np.allclose(res["o"][0, h], res["o_sparse"][0, h] + gate[h] * want, rtol=1e-12, atol=1e-12)
+    c = dyadic_normal(rng, (8,))
+    o, K, V, unsel, sel = _rla_setup(rng, V_unsel=c)
+    res = o.decode(q, gate, sel_override=sel, rla_mode=so.RLA_NORMALIZED)
+    for h in range(2):
+        assert np.allclose(res["rla_out"][0, h], c, rtol=1e-12, atol=1e-12)
+
+
+def pin_rla_rmsnorm_is_torch_rms_norm():
+    """RMS-normalised form = torch's rms_norm over the head's d channels
+    with weight gamma[h] (a library special case), and it is scale-free:
+    values scaled by 8 give the same branch."""
+    rng = np.random.default_rng(22)
+    gate = np.array([0.25, 1.5])
+    gamma = rng.uniform(0.5, 2.0, (2, 8))
+    q = rng.standard_normal((1, 2, 8))
+    for eps in (1e-3, 1e-6):
+        o, K, V, unsel, sel = _rla_setup(rng)
+        res = o.decode(q, gate, sel_override=sel, rla_mode=so.RLA_RMSNORM, gamma=gamma, eps=eps)
+        for h in range(2):
+            x = torch.tensor(res["o_rla"][0, h], dtype=torch.float64)
+            ref = torch.nn.functional.rms_norm(x, (8,), weight=torch.tensor(gamma[h]), eps=eps).numpy()
+            assert np.allclose(res["rla_out"][0, h], ref, rtol=1e-12, atol=1e-12)
+            assert np.allclose(res["o"][0, h], res["o_sparse"][0, h] + gate[h] * ref, rtol=1e-12, atol=1e-12)
+    o2 = fresh_oracle(B=1, H=2, G=1, d=8, bk=4, top_k=3)
+    fill(o2, 0, K, 8 * V)
+    res2 = o2.decode(q, gate, sel_override=sel, rla_mode=so.RLA_RMSNORM, gamma=gamma, eps=1e-12)
+    res1 = o.decode(q, gate, sel_override=sel, rla_mode=so.RLA_RMSNORM, gamma=gamma, eps=1e-12)
+    assert np.allclose(res2["rla_out"], res1["rla_out"], rtol=1e-9, atol=1e-12)
+
+
+def pin_rla_forms_vanish_when_all_selected():
+    """Every form of the branch is 0 when the selection covers every token,
+    so o is the exact attention output."""
+    rng = np.random.default_rng(23)
+    o = fresh_oracle(B=1, H=2, G=1, d=8, bk=4, top_k=3)
+    fill(o, 0, dyadic_normal(rng, (10, 1, 8)), dyadic_normal(rng, (10, 1, 8)))
+    q = rng.standard_normal((1, 2, 8))
+    for mode in (so.RLA_PLAIN, so.RLA_NORMALIZED, so.RLA_RMSNORM):
+        res = o.decode(q, np.array([0.5, 2.0]), rla_mode=mode, gamma=np.ones((2, 8)))
+        assert np.all(res["rla_out"] == 0) and np.array_equal(res["o"], res["o_sparse"])
+
+
 ALL_PINS = [
     pin_phi, pin_block_stats_factorial, pin_score_identical_keys, pin_score_factorial_closed_form,
     pin_score_vs_bruteforce_low_variance, pin_group_score, pin_selection_properties,
     pin_all_selected_is_dense_attention, pin_sparse_is_masked_attention_and_rla_is_direct,
     pin_global_state_is_phiK_T_V, pin_gqa_head_map, pin_edge_lengths, pin_planted_blocks_selected,
+    pin_rla_normalized_is_unselected_mean, pin_rla_rmsnorm_is_torch_rms_norm, pin_rla_forms_vanish_when_all_selected,
 ]
 
 
@@ -406,6 +482,39 @@ def _mut_la_transposed(f, k, v):
     return w @ np.asarray(k, F64), w.sum()
 
 
+def _mut_rla_no_divide(o_rla, d_rla, mode, gamma=None, eps=1e-6, covers_all=False):
+    if mode == so.RLA_NORMALIZED and not covers_all:
+        return np.asarray(o_rla, F64)
+    return _ORIG_RLA_BRANCH(o_rla, d_rla, mode, gamma, eps, covers_all)
+
+
+def _mut_rla_rms_sum(o_rla, d_rla, mode, gamma=None, eps=1e-6, covers_all=False):
+    if mode == so.RLA_RMSNORM and not covers_all:
+        x = np.asarray(o_rla, F64)
+        return np.asarray(gamma) * x / math.sqrt(float(np.sum(x * x)) + eps)
+    return _ORIG_RLA_BRANCH(o_rla, d_rla, mode, gamma, eps, covers_all)
+
+
+def _mut_rla_rms_eps_outside(o_rla, d_rla, mode, gamma=None, eps=1e-6, covers_all=False):
+    if mode == so.RLA_RMSNORM and not covers_all:
+        x = np.asarray(o_rla, F64)
+        return np.asarray(gamma) * x / (math.sqrt(float(np.mean(x * x))) + eps)
+    return _ORIG_RLA_BRANCH(o_rla, d_rla, mode, gamma, eps, covers_all)
+
+
+def _mut_rla_rms_no_gamma(o_rla, d_rla, mode, gamma=None, eps=1e-6, covers_all=False):
+    return _ORIG_RLA_BRANCH(o_rla, d_rla, mode, None if gamma is None else np.ones_like(gamma), eps, covers_all)
+
+
+def _mut_rla_no_zero_when_covered(o_rla, d_rla, mode, gamma=None, eps=1e-6, covers_all=False):
+    x = np.asarray(o_rla, F64) + 1.0
+    return _ORIG_RLA_BRANCH(x, d_rla, mode, gamma, eps, False) if covers_all else \
+        _ORIG_RLA_BRANCH(o_rla, d_rla, mode, gamma, eps, covers_all)
+
+
+_ORIG_RLA_BRANCH = so.rla_branch
+
+
 class _MutOracleSTransposed(SplaOracle):
     def append(self, seq_ids, n_new, k_new, v_new):
         super().append(seq_ids, n_new, k_new, v_new)
@@ -425,6 +534,11 @@ MUTANTS = {
     "ascending": ("select_blocks", _mut_select_ascending),
     "softmax_no_scale": ("softmax_attention", _mut_softmax_no_scale),
     "la_swapped": ("linear_attention_numerator", _mut_la_transposed),
+    "rla_normalized_no_divide": ("rla_branch", _mut_rla_no_divide),
+    "rla_rms_over_sum": ("rla_branch", _mut_rla_rms_sum),
+    "rla_rms_eps_outside_sqrt": ("rla_branch", _mut_rla_rms_eps_outside),
+    "rla_rms_without_gamma": ("rla_branch", _mut_rla_rms_no_gamma),
+    "rla_not_zero_when_covered": ("rla_branch", _mut_rla_no_zero_when_covered),
 }
 
 
@@ -452,8 +566,8 @@ def test_mutant_transposed_state_is_caught(monkeypatch):
 def test_mutant_rla_sign_is_caught(monkeypatch):
     orig = so.SplaOracle.decode
 
-    def bad(self, q, gate, sel_override=None, brute_rla=False):
-        r = orig(self, q, gate, sel_override, brute_rla)
+    def bad(self, q, gate, sel_override=None, brute_rla=False, **kw):
+        r = orig(self, q, gate, sel_override, brute_rla, **kw)
         r["o_rla"] = r["o_bar"] + r["o_tilde"]
         return r
 
