@@ -123,7 +123,11 @@ def read_traffic(workload: str):
             "fetch_scale": fetch_scale, "write_scale": write_scale}, None
 
 
-def cpu_baseline(w, n_steps: int, budget_s: float) -> dict:
+RLA_FORMS = {0: "plain", 1: "normalized", 2: "rmsnorm"}
+RLA_EPS = 1e-6
+
+
+def cpu_baseline(w, n_steps: int, budget_s: float, rla_form: int = 0) -> dict:
     """Time the fp64 oracle's append + decode per step on the host cores."""
     import numpy as np
     from oracle import SplaOracle
@@ -141,6 +145,7 @@ def cpu_baseline(w, n_steps: int, budget_s: float) -> dict:
             o.append([b], [k.shape[0]], k, v)
     log(f"oracle prefill {time.time() - t0:.1f}s")
     gate = w.gate()
+    gamma = w.rla_gamma() if rla_form == 2 else None
     mix = w.mixture_state()
     done = 0
     spent = 0.0
@@ -151,7 +156,7 @@ def cpu_baseline(w, n_steps: int, budget_s: float) -> dict:
         if cs:
             o.append(cs, [w.chunk_len] * len(cs), st["chunk_k"], st["chunk_v"])
         o.append(list(range(w.batch)), [1] * w.batch, st["k"], st["v"])
-        o.decode(st["q"], gate)
+        o.decode(st["q"], gate, rla_mode=rla_form, gamma=gamma, eps=RLA_EPS)
         spent += time.perf_counter() - t
         done += 1
         if spent >= budget_s:
@@ -174,6 +179,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-select", type=int, default=-1, choices=(-1, 0, 1),
                     help="selector placement: -1 automatic, 0 stand-alone kernel, 1 fused into attend")
+    ap.add_argument("--rla-form", type=int, default=0, choices=sorted(RLA_FORMS),
+                    help="output form of the RLA branch: 0 plain, 1 normalised (o_rla / D), 2 RMS-normalised")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -199,10 +206,13 @@ def main() -> int:
     tdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
     mb = w.max_blocks_per_seq(total_steps)
 
+    gamma = torch.from_numpy(w.rla_gamma()).to(dev) if args.rla_form == 2 else None
+
     def new_layer():
         layer = SplaLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k, mb,
                           kv_dtype=w.kv_dtype, device="cuda:0")
         layer.set_fused_select(args.fused_select)
+        layer.set_rla_output(args.rla_form, gamma, RLA_EPS)
         return layer
 
     t0 = time.time()
@@ -356,7 +366,7 @@ def main() -> int:
         "data": "synthetic (seeded; see workloads/)",
         "config": {"workload": w.name, "batch": w.batch, "context": max(w.t0), "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
-                   "top_k": w.top_k, "l_rot": L},
+                   "top_k": w.top_k, "l_rot": L, "rla_output": RLA_FORMS[args.rla_form]},
         "step_bytes": bytes_avg,
         "step_GBps": bytes_avg / t_step / 1e9,
         "step_frac_of_peak": bytes_avg / t_step / 1e9 / HBM_PEAK_GBS,
@@ -368,7 +378,7 @@ def main() -> int:
                      "copy_probe_GBps": probe_gbs},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, K + W, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, K + W, args.cpu_budget, args.rla_form)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -31,13 +31,15 @@ SPLA_F32, SPLA_BF16 = 0, 1
 EXPORTED = [
     "spla_create", "spla_destroy", "spla_workspace_bytes", "spla_stats_floats", "spla_bind",
     "spla_append_kv", "spla_decode", "spla_decode_step", "spla_get_lens", "spla_status_str", "spla_abi_version",
-    "spla_last_hip_error", "spla_set_tuning", "spla_launch_plan",
+    "spla_last_hip_error", "spla_set_tuning", "spla_launch_plan", "spla_set_rla_output",
 ]
 
 # spla_kernel ids (include/spla.h) -> kernel names
 KERNELS = {1: "score", 2: "step_score", 3: "select", 4: "attend", 5: "select_attend", 6: "combine"}
 CALL_DECODE, CALL_DECODE_SEL_IN, CALL_DECODE_STEP = 0, 1, 2
 TUNE_FUSED_SELECT = 0
+# output forms of the RLA branch (spla_rla_form)
+RLA_PLAIN, RLA_NORMALIZED, RLA_RMSNORM = 0, 1, 2
 
 
 class SplaConfig(ctypes.Structure):
@@ -110,6 +112,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spla_set_tuning.restype = ctypes.c_int
     lib.spla_launch_plan.argtypes = [ctypes.c_void_p, ctypes.c_int32, I32P, ctypes.c_int32]
     lib.spla_launch_plan.restype = ctypes.c_int32
+    lib.spla_set_rla_output.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float]
+    lib.spla_set_rla_output.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -176,6 +180,9 @@ class SplaHandle:
 
     def set_tuning(self, key: int, value: int) -> None:
         _check(self.lib.spla_set_tuning(self.h, key, value), "spla_set_tuning")
+
+    def set_rla_output(self, form: int, gamma_ptr: int = 0, eps: float = 0.0) -> None:
+        _check(self.lib.spla_set_rla_output(self.h, form, ctypes.c_void_p(gamma_ptr), eps), "spla_set_rla_output")
 
     def launch_plan(self, call: int):
         """Names of the kernels the next call of kind `call` launches, in order."""
@@ -262,6 +269,23 @@ class SplaLayer:
     def set_fused_select(self, mode: int) -> None:
         """-1 automatic, 0 stand-alone selector, 1 fused select + attend where supported."""
         self.handle.set_tuning(TUNE_FUSED_SELECT, mode)
+
+    def set_rla_output(self, form: int = RLA_PLAIN, gamma=None, eps: float = 1e-6) -> None:
+        """Output form of the RLA branch: RLA_PLAIN (o_rla), RLA_NORMALIZED
+        (o_rla / D) or RLA_RMSNORM (gamma * o_rla / rms(o_rla), gamma a float32
+        device tensor [H][d] that the layer keeps a reference to)."""
+        if form == RLA_RMSNORM:
+            t = self.torch
+            if gamma is None:
+                raise ValueError("the RMS-normalised form needs gamma")
+            g = gamma.to(device=self.device, dtype=t.float32).contiguous()
+            if tuple(g.shape) != (self.H, self.d):
+                raise ValueError(f"gamma must be [{self.H}][{self.d}], got {tuple(g.shape)}")
+            self.handle.set_rla_output(form, g.data_ptr(), float(eps))
+            self._rla_gamma = g
+        else:
+            self.handle.set_rla_output(form, 0, 0.0)
+            self._rla_gamma = None
 
     def launch_plan(self, step: bool = True, sel_in: bool = False):
         call = CALL_DECODE_STEP if step else (CALL_DECODE_SEL_IN if sel_in else CALL_DECODE)

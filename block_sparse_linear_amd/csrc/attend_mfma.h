@@ -22,13 +22,19 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32
 
 __device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
-// phi of 8 packed bf16 values rounded to bf16
-__device__ __forceinline__ uint4 phi_bf16(const uint4& raw) {
+// phi of 8 packed bf16 values as bf16 hi + lo pairs (hi = phi rounded to
+// bf16, lo = the rounding of what is left), so hi + lo holds phi to ~2^-16
+__device__ __forceinline__ void phi_bf16_split(const uint4& raw, uint4& hi, uint4& lo) {
   const uint32_t in[4] = {raw.x, raw.y, raw.z, raw.w};
-  uint32_t o[4];
+  uint32_t oh[4], ol[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) o[k] = pack_bf16(phi_fast(bf16_lo_f(in[k])), phi_fast(bf16_hi_f(in[k])));
-  return make_uint4(o[0], o[1], o[2], o[3]);
+  for (int k = 0; k < 4; ++k) {
+    const float x0 = phi_fast(bf16_lo_f(in[k])), x1 = phi_fast(bf16_hi_f(in[k]));
+    oh[k] = pack_bf16(x0, x1);
+    ol[k] = pack_bf16(x0 - bf16_lo_f(oh[k]), x1 - bf16_hi_f(oh[k]));
+  }
+  hi = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+  lo = make_uint4(ol[0], ol[1], ol[2], ol[3]);
 }
 
 // A operands of product (1) for this lane: row m = lane % 16 holds query m
@@ -142,12 +148,16 @@ __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot,
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      // phi(k) in bf16 (its rounding is independent per token and averages
-      // out of o_tilde); phi(q) keeps hi + lo (shared by every token)
-      const uint4 fk = phi_bf16(kraw[nt][ks]);
+      // w = phi(q).phi(k) from hi / lo pairs of both (the lo x lo product,
+      // ~2^-18 relative, is left out).  A single bf16 phi(k) would leave
+      // ~1e-4 relative error in sum w, which the subtraction
+      // D = phi(q).z_all - sum w magnifies when few tokens are unselected.
+      uint4 fkh, fkl;
+      phi_bf16_split(kraw[nt][ks], fkh, fkl);
       c = mfma_bf16(aq[ks], kraw[nt][ks], c);
-      c = mfma_bf16(afh[ks], fk, c);
-      c = mfma_bf16(afl[ks], fk, c);
+      c = mfma_bf16(afh[ks], fkh, c);
+      c = mfma_bf16(afl[ks], fkh, c);
+      c = mfma_bf16(afh[ks], fkl, c);
     }
     c1[nt] = c;
   }

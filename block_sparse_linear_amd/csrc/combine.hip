@@ -1,30 +1,41 @@
 // Combine: merge of the per-block partials of one query head, o_bar =
 // phi(q)^T S_all from the row-chunk partials of the first kernel, o_rla =
-// o_bar - o_tilde, D = phi(q).z_all - sum w, o = o_sparse + g_h o_rla (SPLA
-// Technical Summary 2.2, IO-efficient formulation; 2.3, hybrid strategy).
+// o_bar - o_tilde, D = phi(q).z_all - sum w, o = o_sparse + g_h * branch
+// (SPLA Technical Summary 2.2, IO-efficient formulation; 2.3, hybrid
+// strategy).  The branch is o_rla itself, o_rla / D (linear attention over
+// the unselected tokens with its normaliser, the kernelised form of the Baidu
+// Cloud sparse-attention article, section 7), or gamma * o_rla / rms(o_rla)
+// (the RMS norm of the RLA output, Technical Summary 2.3).
 #include "decode_common.h"
 
 namespace spla {
 
 namespace {
 
-// grid (D / 32, H, B): one 32-channel slice of one query head.  Item =
-// (kind, channel quartet) with kind 0 the softmax numerators (weighted by
+// output forms of the RLA branch (spla_rla_form)
+constexpr int kRlaPlain = 0, kRlaNormalized = 1, kRlaRms = 2;
+
+// grid (D / CS, H, B): one CS-channel slice of one query head (the whole head
+// for the RMS form, whose norm runs over all D channels).  Item = (kind,
+// channel quartet) with kind 0 the softmax numerators (weighted by
 // exp(m_s - m) / L) and kind 1 the linear-attention sums; the slots are split
-// over 16 slot groups whose float4 sums meet in LDS.  Every global load is
-// issued before the first wait; the leading arguments address all of them.
-template <bool BF16, int R, int D>
+// over kThreads / (2 CS / 4) slot groups whose float4 sums meet in LDS.  Every
+// global load is issued before the first wait; the leading arguments address
+// all of them.
+template <int R, int D, int FORM>
 __global__ __launch_bounds__(kThreads) void k_combine(const float* part, const float* obar_part, const float* dz_part,
                                                        const int32_t* sel, int32_t G, int32_t H, int32_t top_k,
                                                        const DecodeArgs a) {
-  constexpr int CS = 32;                 // channels per workgroup
-  constexpr int NQ = CS / 4;             // channel quartets
-  constexpr int NIT = 2 * NQ;            // float4 items (kind, quartet)
-  constexpr int SG = kThreads / NIT;     // slot groups
-  constexpr int SPT = 4;                 // slots per thread per load batch
-  constexpr int SPL = 4;                 // slots per lane in the header pass (top_k <= 256)
-  constexpr int CHUNKS = D / (1024 / D); // o_bar partials per head
-  __shared__ float wsl[256];             // exp(m_s - m) / L (0 for unused slots)
+  constexpr int CS = FORM == kRlaRms ? D : 32;  // channels per workgroup
+  constexpr int NQ = CS / 4;                    // channel quartets
+  constexpr int NIT = 2 * NQ;                   // float4 items (kind, quartet)
+  constexpr int SG = kThreads / NIT;            // slot groups
+  constexpr int SPT = 4;                        // slots per thread per load batch
+  constexpr int SPL = 4;                        // slots per lane in the header pass (top_k <= 256)
+  constexpr int CHUNKS = D / (1024 / D);        // o_bar partials per head
+  constexpr int OBN = (CHUNKS * NQ + kThreads - 1) / kThreads;  // o_bar partial float4s per thread
+  static_assert(OBN <= 2, "at most two o_bar partial loads per thread");
+  __shared__ float wsl[256];                    // exp(m_s - m) / L (0 for unused slots)
   __shared__ int valid[256];
   __shared__ float4 obp[CHUNKS][NQ];
   __shared__ float dzp[CHUNKS];
@@ -57,14 +68,24 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float* part, const f
 #pragma unroll
   for (int u = 0; u < SPT; ++u)
     dv[u] = *reinterpret_cast<const float4*>(PD + (size_t)min(sg + SG * u, top_k - 1) * rec);
-  const int ob_rc = min((int)threadIdx.x / NQ, CHUNKS - 1), ob_q4 = threadIdx.x % NQ;
-  const float4 obv =
-      reinterpret_cast<const float4*>(obar_part)[((bg * CHUNKS + ob_rc) * R + h) * (D / 4) + c0 / 4 + ob_q4];
+  auto obar_at = [&](int i) {  // o_bar partial float4 i of this slice (clamped)
+    i = min(i, CHUNKS * NQ - 1);
+    return reinterpret_cast<const float4*>(obar_part)[((bg * CHUNKS + i / NQ) * R + h) * (D / 4) + c0 / 4 + i % NQ];
+  };
+  const float4 obv0 = obar_at(threadIdx.x);
+  const float4 obv1 = OBN > 1 ? obar_at(threadIdx.x + kThreads) : obv0;
   const float dzv = dz_part[(bg * CHUNKS + min((int)threadIdx.x, CHUNKS - 1)) * R + h];
   __builtin_amdgcn_sched_barrier(0);
   // the rest of the arguments, while the loads are in flight
-  SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.gate), "s"(a.out), "s"(a.o_sparse_out), "s"(a.o_rla_out),
-                     "s"(a.d_rla_out), "s"(a.sel_out));
+  float4 gm = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (FORM == kRlaRms) {
+    SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.gate), "s"(a.out), "s"(a.o_sparse_out), "s"(a.o_rla_out),
+                       "s"(a.d_rla_out), "s"(a.sel_out), "s"(a.rla_gamma), "s"(a.rla_eps));
+    gm = reinterpret_cast<const float4*>(a.rla_gamma + (size_t)hq * D)[min(lane, NQ - 1)];
+  } else {
+    SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.gate), "s"(a.out), "s"(a.o_sparse_out), "s"(a.o_rla_out),
+                       "s"(a.d_rla_out), "s"(a.sel_out));
+  }
   const int nb = n_blocks(a, b);
   const bool covers_all = nb <= top_k;
   // ---- merge weights of the slots (wavefront 0), o_bar / D partials to LDS
@@ -97,7 +118,9 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float* part, const f
     }
     if (lane == 0) s_sw = sw;
   }
-  if ((int)threadIdx.x < CHUNKS * NQ) obp[ob_rc][ob_q4] = obv;
+  if ((int)threadIdx.x < CHUNKS * NQ) obp[threadIdx.x / NQ][threadIdx.x % NQ] = obv0;
+  if (OBN > 1 && (int)threadIdx.x + kThreads < CHUNKS * NQ)
+    obp[(threadIdx.x + kThreads) / NQ][(threadIdx.x + kThreads) % NQ] = obv1;
   if ((int)threadIdx.x < CHUNKS) dzp[threadIdx.x] = dzv;
   __syncthreads();
   // ---- this thread's slots of its item
@@ -121,9 +144,16 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float* part, const f
   }
   red4[sg][it] = acc;
   __syncthreads();
-  // ---- finalise: thread = channel quartet, both kinds from LDS
-  if ((int)threadIdx.x < NQ) {
-    const int qq = threadIdx.x;
+  // D = phi(q).z_all - sum w of this head (0 when every block is selected)
+  auto d_rla = [&]() {
+    float dz = dzp[0];
+#pragma unroll
+    for (int rc = 1; rc < CHUNKS; ++rc) dz += dzp[rc];
+    return covers_all ? 0.f : dz - s_sw;
+  };
+  // ---- finalise: lane = channel quartet of wavefront 0, both kinds from LDS
+  if (w == 0) {
+    const int qq = min(lane, NQ - 1);
     float4 os = make_float4(0.f, 0.f, 0.f, 0.f), ot = os;
 #pragma unroll
     for (int k = 0; k < SG; ++k) {
@@ -140,33 +170,49 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float* part, const f
     }
     const float4 orl = covers_all ? make_float4(0.f, 0.f, 0.f, 0.f)
                                   : make_float4(ob.x - ot.x, ob.y - ot.y, ob.z - ot.z, ob.w - ot.w);
-    const size_t oi = ((size_t)b * H + hq) * D + c0 + 4 * qq;
-    const float gh = a.gate[hq];
-    *reinterpret_cast<float4*>(a.out + oi) =
-        make_float4(fmaf(gh, orl.x, os.x), fmaf(gh, orl.y, os.y), fmaf(gh, orl.z, os.z), fmaf(gh, orl.w, os.w));
-    if (a.o_sparse_out) *reinterpret_cast<float4*>(a.o_sparse_out + oi) = os;
-    if (a.o_rla_out) *reinterpret_cast<float4*>(a.o_rla_out + oi) = orl;
+    float4 br = orl;  // the branch in its output form
+    if constexpr (FORM == kRlaNormalized) {
+      const float dh = d_rla();
+      const float inv = covers_all ? 0.f : 1.f / dh;
+      br = make_float4(orl.x * inv, orl.y * inv, orl.z * inv, orl.w * inv);
+    } else if constexpr (FORM == kRlaRms) {
+      float ss = lane < NQ ? orl.x * orl.x + orl.y * orl.y + orl.z * orl.z + orl.w * orl.w : 0.f;
+      ss = wave_sum(ss);  // over the head's D channels
+      const float inv = covers_all ? 0.f : 1.f / sqrtf(ss * (1.f / D) + a.rla_eps);
+      br = make_float4(gm.x * orl.x * inv, gm.y * orl.y * inv, gm.z * orl.z * inv, gm.w * orl.w * inv);
+    }
+    if (lane < NQ) {
+      const size_t oi = ((size_t)b * H + hq) * D + c0 + 4 * lane;
+      const float gh = a.gate[hq];
+      *reinterpret_cast<float4*>(a.out + oi) =
+          make_float4(fmaf(gh, br.x, os.x), fmaf(gh, br.y, os.y), fmaf(gh, br.z, os.z), fmaf(gh, br.w, os.w));
+      if (a.o_sparse_out) *reinterpret_cast<float4*>(a.o_sparse_out + oi) = os;
+      if (a.o_rla_out) *reinterpret_cast<float4*>(a.o_rla_out + oi) = orl;
+    }
   }
-  if (cc == 0 && (int)threadIdx.x == NQ && a.d_rla_out) {
-    float dz = dzp[0];
-#pragma unroll
-    for (int rc = 1; rc < CHUNKS; ++rc) dz += dzp[rc];
-    a.d_rla_out[(size_t)b * H + hq] = covers_all ? 0.f : dz - s_sw;
-  }
+  if (cc == 0 && (int)threadIdx.x == 64 && a.d_rla_out) a.d_rla_out[(size_t)b * H + hq] = d_rla();
   if (cc == 0 && h == 0 && a.sel_out)
     for (int s = threadIdx.x; s < top_k; s += kThreads) a.sel_out[bg * top_k + s] = srow[s];
 }
 
+template <int FORM>
+hipError_t launch_combine_form(const DecodeArgs& a, const Launch& l) {
+  const int cs = FORM == kRlaRms ? a.d : 32;
+  const dim3 grid(a.d / cs, a.H, a.B);
+  const int32_t* sel = a.sel_in ? a.sel_in : a.sel;
+  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<RR, DD, FORM>, grid, l, a.part, a.obar_part, a.dz_part, sel,
+                                           a.G, a.H, a.top_k, a))
+}
+
 }  // namespace
 
-hipError_t launch_combine(const DecodeArgs& a, bool bf16, const Launch& l) {
-  const dim3 grid(a.d / 32, a.H, a.B);
-  const int32_t* sel = a.sel_in ? a.sel_in : a.sel;
-  if (bf16)
-    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<true, RR, DD>, grid, l, a.part, a.obar_part, a.dz_part, sel,
-                                             a.G, a.H, a.top_k, a))
-  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<false, RR, DD>, grid, l, a.part, a.obar_part, a.dz_part, sel,
-                                           a.G, a.H, a.top_k, a))
+hipError_t launch_combine(const DecodeArgs& a, const Launch& l) {
+  switch (a.rla_form) {
+    case kRlaPlain: return launch_combine_form<kRlaPlain>(a, l);
+    case kRlaNormalized: return launch_combine_form<kRlaNormalized>(a, l);
+    case kRlaRms: return launch_combine_form<kRlaRms>(a, l);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace spla

@@ -20,6 +20,9 @@ struct spla_handle {
   std::vector<int32_t> lens;
   hipError_t last_hip = hipSuccess;  // status of the last launch that failed
   int32_t fused_select = -1;         // SPLA_TUNE_FUSED_SELECT
+  int32_t rla_form = SPLA_RLA_PLAIN;  // output form of the RLA branch
+  const float* rla_gamma = nullptr;
+  float rla_eps = 0.f;
   // workspace layout (bytes)
   size_t off_lg = 0, off_sel = 0, off_page = 0, off_part = 0, off_obar = 0, off_dz = 0, off_phq = 0;
   size_t ws_bytes = 0;
@@ -88,6 +91,9 @@ spla_status fill_decode_args(const spla_handle* h, const void* q, const float* g
     a->o_rla_out = aux->o_rla;
     a->d_rla_out = aux->d_rla;
   }
+  a->rla_form = h->rla_form;
+  a->rla_gamma = h->rla_gamma;
+  a->rla_eps = h->rla_eps;
   a->B = c.batch;
   a->H = c.n_q_heads;
   a->G = c.n_kv_heads;
@@ -224,7 +230,7 @@ hipError_t run_plan(const spla_handle* h, const StepArgs& sa, const int32_t* pla
       case SPLA_KERNEL_SELECT: e = launch_select(a, l); break;
       case SPLA_KERNEL_ATTEND: e = launch_attend(a, bf16, l); break;
       case SPLA_KERNEL_SELECT_ATTEND: e = launch_select_attend(a, l); break;
-      case SPLA_KERNEL_COMBINE: e = launch_combine(a, bf16, l); break;
+      case SPLA_KERNEL_COMBINE: e = launch_combine(a, l); break;
     }
     if (e != hipSuccess) return e;
   }
@@ -452,6 +458,26 @@ spla_status spla_set_tuning(spla_handle* h, int32_t key, int32_t value) {
     case SPLA_TUNE_FUSED_SELECT:
       if (value < -1 || value > 1) return SPLA_ERR_INVALID_ARG;
       h->fused_select = value;
+      return SPLA_OK;
+  }
+  return SPLA_ERR_INVALID_ARG;
+}
+
+spla_status spla_set_rla_output(spla_handle* h, int32_t form, const float* gamma, float eps) {
+  if (!h) return SPLA_ERR_INVALID_ARG;
+  switch (form) {
+    case SPLA_RLA_PLAIN:
+    case SPLA_RLA_NORMALIZED:
+      h->rla_form = form;
+      h->rla_gamma = nullptr;
+      h->rla_eps = 0.f;
+      return SPLA_OK;
+    case SPLA_RLA_RMSNORM:
+      if (!gamma || !(eps > 0.f) || !isfinite(eps)) return SPLA_ERR_INVALID_ARG;
+      if (!aligned16(gamma)) return SPLA_ERR_ALIGNMENT;
+      h->rla_form = form;
+      h->rla_gamma = gamma;
+      h->rla_eps = eps;
       return SPLA_OK;
   }
   return SPLA_ERR_INVALID_ARG;

@@ -55,6 +55,9 @@ struct DecodeArgs {
   float* o_sparse_out;
   float* o_rla_out;
   float* d_rla_out;
+  const float* rla_gamma;  // [H][d] scale of the RMS-normalised RLA branch
+  float rla_eps;
+  int32_t rla_form;        // spla_rla_form
   int32_t B, H, G, d, r, bk, top_k, max_blocks, num_pages, n_tiles;
   int32_t score_tiles;  // grid.x of the scorer
   int32_t tiles_all;    // score tiles that every sequence of the batch has
@@ -129,7 +132,7 @@ hipError_t launch_append(const AppendArgs& a, bool bf16, const Launch& l);
 hipError_t launch_score(const StepArgs& a, bool bf16, const Launch& l);  // st: no new k / v
 hipError_t launch_select(const DecodeArgs& a, const Launch& l);
 hipError_t launch_attend(const DecodeArgs& a, bool bf16, const Launch& l);
-hipError_t launch_combine(const DecodeArgs& a, bool bf16, const Launch& l);
+hipError_t launch_combine(const DecodeArgs& a, const Launch& l);
 hipError_t launch_step_score(const StepArgs& a, bool bf16, const Launch& l);
 // fused select + attend: supported for bf16 K/V, block size 64, no selection
 // override and at most 16 * 256 candidates per sequence

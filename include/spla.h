@@ -169,7 +169,8 @@ spla_status spla_append_kv(spla_handle *h, int32_t n_seqs, const int32_t *seq_id
 
 /* Decode one query token per sequence.  q: device [B][H][d] kv_dtype;
  * gate: device [H] float32; out: device [B][H][d] float32 receives
- * o = o_sparse + gate[h] * o_rla.  Query head h uses KV head h / (H/G).
+ * o = o_sparse + gate[h] * o_rla (o_rla in the output form set by
+ * spla_set_rla_output; plain by default).  Query head h uses KV head h / (H/G).
  * Every sequence must be non-empty (SPLA_ERR_INVALID_ARG otherwise).
  * Selection per (b, g): nb = ceil(T/Bk); if nb <= top_k every block;
  * otherwise blocks 0 and nb-1 plus the top_k-2 candidates 1..nb-2 with the
@@ -206,6 +207,32 @@ const char *spla_status_str(spla_status st);
  * SPLA_ERR_INVALID_ARG for an unknown key or value. */
 typedef enum { SPLA_TUNE_FUSED_SELECT = 0 } spla_tune_key;
 spla_status spla_set_tuning(spla_handle *h, int32_t key, int32_t value);
+
+/* Output form of the residual-linear-attention branch in o = o_sparse +
+ * gate[h] * branch (per handle, host only; applies to spla_decode and
+ * spla_decode_step from the next call on).  aux->o_rla and aux->d_rla keep
+ * reporting o_rla and D themselves in every form.  The branch is 0 in every
+ * form when the selection covers every token.
+ *   SPLA_RLA_PLAIN       o_rla (the default).
+ *   SPLA_RLA_NORMALIZED  o_rla / D.  By the subtraction form (Technical
+ *                        Summary 2.2) o_rla and D are the numerator and the
+ *                        normaliser of linear attention over the unselected
+ *                        tokens, so this is that attention normalised, the
+ *                        kernelised form phi(Q)(phi(K)^T V) / phi(Q)(phi(K)^T 1)
+ *                        (Baidu Cloud sparse-attention article, section 7).
+ *   SPLA_RLA_RMSNORM     gamma[h][c] * o_rla[c] / sqrt(mean_c o_rla[c]^2 + eps)
+ *                        over the head_dim channels of each query head: the
+ *                        RMS norm of the RLA output whose scale is the
+ *                        method's only added parameter (Technical Summary
+ *                        2.3).  gamma: device [H][d] float32, caller-owned,
+ *                        read at every decode (keep it alive and unchanged
+ *                        while the handle uses it); eps > 0 and finite.
+ * gamma and eps are ignored (and forgotten) for the other forms.
+ * SPLA_ERR_INVALID_ARG for an unknown form, a NULL gamma or a bad eps with
+ * SPLA_RLA_RMSNORM; SPLA_ERR_ALIGNMENT for a misaligned gamma.  On error
+ * the handle keeps its previous form. */
+typedef enum { SPLA_RLA_PLAIN = 0, SPLA_RLA_NORMALIZED = 1, SPLA_RLA_RMSNORM = 2 } spla_rla_form;
+spla_status spla_set_rla_output(spla_handle *h, int32_t form, const float *gamma, float eps);
 
 /* The kernels the next call of kind `call` on this handle would launch, in
  * launch order (the order of spla_decode_aux.kernel_events), from the

@@ -90,7 +90,7 @@ class ParityRun:
     def __init__(self, w: Workload, page_order: str = "identity", steps: Optional[int] = None,
                  device: str = "cuda", prefill_chunk: int = 4096, use_step: bool = False,
                  seqs: Optional[List[int]] = None, kv_heads: Optional[List[int]] = None,
-                 fused_select: int = -1):
+                 fused_select: int = -1, rla_form: int = 0, rla_eps: float = 1e-6):
         import torch
         from block_sparse_linear_amd import SplaLayer
 
@@ -113,6 +113,11 @@ class ParityRun:
                                  w.top_k, w.max_tokens(self.steps))
         self.gate_np = w.gate()
         self.gate = torch.from_numpy(self.gate_np).to(device)
+        # output form of the RLA branch (0 plain, 1 normalised, 2 RMS-normalised)
+        self.rla_form, self.rla_eps = rla_form, rla_eps
+        self.gamma_np = w.rla_gamma() if rla_form == 2 else None
+        self.layer.set_rla_output(rla_form, None if self.gamma_np is None else torch.from_numpy(self.gamma_np),
+                                  rla_eps)
         self.mix = w.mixture_state()
 
     def dev(self, x: np.ndarray):
@@ -184,8 +189,10 @@ class ParityRun:
              "d_rla": g["d_rla"][bs][:, hs], "sel_idx": g["sel_idx"][bs][:, gs], "lg": g["lg"][bs][:, gs]}
         q_o = q_np[bs][:, hs]
         gate_o = self.gate_np[hs]
+        form = dict(rla_mode=self.rla_form, eps=self.rla_eps,
+                    gamma=None if self.gamma_np is None else self.gamma_np[hs])
         sel_o = None if sel_in is None else np.asarray(sel_in)[bs][:, gs]
-        ref = self.oracle.decode(q_o, gate_o, sel_override=sel_o)
+        ref = self.oracle.decode(q_o, gate_o, sel_override=sel_o, **form)
         sel_gpu = g["sel_idx"]
         if sel_in is None:
             for b in range(len(bs)):
@@ -204,7 +211,7 @@ class ParityRun:
                         rep.errors["lg_abs"] = max(rep.errors.get("lg_abs", 0.0),
                                                    float(np.abs(g["lg"][b, gg, js] - lg_ref).max()))
             if not rep.sel_equal:
-                ref = self.oracle.decode(q_o, gate_o, sel_override=sel_gpu)
+                ref = self.oracle.decode(q_o, gate_o, sel_override=sel_gpu, **form)
         else:
             if not np.array_equal(sel_gpu, sel_o):
                 rep.failures.append("sel_idx output != sel_in")
@@ -213,6 +220,15 @@ class ParityRun:
             rep.errors[k] = e
             if e > tol:
                 rep.failures.append(f"step {s}: {k} rel err {e:.3g} > {tol}")
+        if self.rla_form != 0:
+            # the branch itself, (o - o_sparse) / g, on heads whose gate is not small
+            big = np.abs(gate_o) > 0.25
+            if big.any():
+                br = (g["o"].astype(np.float64) - g["o_sparse"]) / gate_o[None, :, None]
+                e = rel_err(br[:, big], ref["rla_out"][:, big])
+                rep.errors["rla_out"] = e
+                if e > OUT_REL:
+                    rep.failures.append(f"step {s}: RLA branch rel err {e:.3g} > {OUT_REL}")
         return rep
 
     def check_state(self) -> Dict[str, float]:

@@ -301,3 +301,20 @@ def test_launch_plan(lib):
     assert lib.spla_set_tuning(h, 0, 1) == OK
     assert plan(lib, h, 0) == [SCORE, SELECT, ATTEND, COMBINE]
     lib.spla_destroy(h)
+
+
+def test_rla_output_validation(lib):
+    h, c = bound(lib)
+    nan, inf = float("nan"), float("inf")
+    assert lib.spla_set_rla_output(h, 0, None, 0.0) == OK
+    assert lib.spla_set_rla_output(h, 1, None, 0.0) == OK
+    assert lib.spla_set_rla_output(h, 2, FAKE, 1e-6) == OK
+    for gamma, eps, want in ((None, 1e-6, INVALID), (FAKE, 0.0, INVALID), (FAKE, -1e-6, INVALID),
+                             (FAKE, nan, INVALID), (FAKE, inf, INVALID), (FAKE + 4, 1e-6, ALIGN)):
+        assert lib.spla_set_rla_output(h, 2, gamma, eps) == want, (gamma, eps)
+    assert lib.spla_set_rla_output(h, 3, None, 0.0) == INVALID
+    assert lib.spla_set_rla_output(h, -1, None, 0.0) == INVALID
+    assert lib.spla_set_rla_output(None, 0, None, 0.0) == INVALID
+    # the form changes the combine's arithmetic, not the kernels a call launches
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
+    lib.spla_destroy(h)

@@ -16,12 +16,12 @@ from workloads import Workload, make_workload
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def _run(w, steps, seqs=None, kv_heads=None, page_order="shuffled", fused_select=-1):
+def _run(w, steps, seqs=None, kv_heads=None, page_order="shuffled", fused_select=-1, rla_form=0):
     print(f"[fullsize] {w.name}: B={w.batch} H={w.n_q_heads} G={w.n_kv_heads} d={w.head_dim} "
           f"Bk={w.block_size} k={w.top_k} t0={w.t0[:4]}{'...' if w.batch > 4 else ''} steps={steps} "
-          f"seqs={seqs} kv_heads={kv_heads} fused_select={fused_select}", flush=True)
+          f"seqs={seqs} kv_heads={kv_heads} fused_select={fused_select} rla_form={rla_form}", flush=True)
     run = ParityRun(w, page_order=page_order, steps=steps, use_step=True, seqs=seqs, kv_heads=kv_heads,
-                    fused_select=fused_select)
+                    fused_select=fused_select, rla_form=rla_form)
     print(f"[fullsize] kernels: {run.layer.launch_plan()}", flush=True)
     failures = run.run(verbose=True)
     assert not failures, "\n".join(failures[:20])
@@ -31,6 +31,13 @@ def _run(w, steps, seqs=None, kv_heads=None, page_order="shuffled", fused_select
 def test_llama_gqa_128k_full():
     # B=1, 128K context, GQA 32/8 x 128, Bk=64, k=32: every head checked
     _run(make_workload("llama_gqa_128k"), steps=3)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("form", [1, 2], ids=["normalized", "rmsnorm"])
+def test_llama_gqa_128k_rla_forms(form):
+    # the output forms of the RLA branch at the benchmark's workload: 2 KV heads
+    _run(make_workload("llama_gqa_128k"), steps=2, kv_heads=[0, 6], rla_form=form)
 
 
 @pytest.mark.timeout(600)

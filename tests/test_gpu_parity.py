@@ -63,6 +63,14 @@ def test_short_sequences_all_selected(t0):
     _run(small(name=f"short{t0}", t0=(t0,), steps=2))
 
 
+@pytest.mark.parametrize("bk", [64, 128])
+def test_one_unselected_block(bk):
+    # nb = top_k + 1 after the append: a single unselected block, so D and
+    # o_rla are differences of sums several times larger than themselves
+    # (the case that needs w = phi(q).phi(k) to ~2^-16 on the matrix cores)
+    _run(small(name=f"one_out_bk{bk}", block_size=bk, head_dim=128 if bk == 64 else 64, t0=(bk * 8,), steps=3))
+
+
 def test_ragged_batch_with_chunks():
     w = small(name="ragged", batch=5, t0=(1, 700, 64 * 40 + 13, 64 * 9, 3000), steps=3, chunk_seqs=2,
               chunk_len=100, top_k=6)

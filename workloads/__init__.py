@@ -49,6 +49,7 @@ _S_CHUNK_KV = 9
 _S_OUTLIER = 10
 _S_MIXTURE = 11
 _S_QBASE = 12
+_S_RLA_GAMMA = 13
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -187,6 +188,11 @@ class Workload:
         if self.gate_ones:
             return np.ones(self.n_q_heads, np.float32)
         return _rng(self.seed, _S_GATE).uniform(0.0, 1.0, self.n_q_heads).astype(np.float32)
+
+    def rla_gamma(self) -> np.ndarray:
+        """[H][d] scale of the RMS-normalised RLA branch (float32, U(0.5, 1.5));
+        a stand-in for trained norm weights, which are not available."""
+        return _rng(self.seed, _S_RLA_GAMMA).uniform(0.5, 1.5, (self.n_q_heads, self.head_dim)).astype(np.float32)
 
     def _keys(self, r: np.random.Generator, b: int, pos0: int, n: int, mix=None) -> np.ndarray:
         G, d = self.n_kv_heads, self.head_dim
