@@ -8,10 +8,14 @@ from .spla_oracle import (  # noqa: F401
     RLA_NORMALIZED,
     RLA_PLAIN,
     RLA_RMSNORM,
+    SCORE_MEAN,
+    SCORE_TAYLOR,
     SplaOracle,
     block_stats,
+    exact_block_log_mass,
     group_log_score,
     linear_attention_numerator,
+    mean_pool_log_score,
     phi,
     rla_branch,
     select_blocks,

@@ -54,7 +54,11 @@ with its reason in the design notes):
       o_rla_c^2 + eps) over the d channels of one query head, with a scale
       gamma per (query head, channel) and eps > 0 given by the caller.  The
       gate multiplies the branch in every form, and the branch is 0 in every
-      form when the selection covers every token.
+      form when the selection covers every token;
+  R12 selection fidelity: a block's exact mass is the per-token mean of
+      exp(q_hat . k) over its keys (the form of the score formula, R1),
+      summed over the group's query heads as in R4; the mean-pooling
+      baseline keeps only the first-order term q_hat . k_bar.
 
 Parity of this module is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, library special cases and brute force; the readings R4, R7 and
@@ -111,6 +115,31 @@ def taylor_log_score(q: np.ndarray, mean: np.ndarray, var: np.ndarray) -> np.nda
     return first + np.log1p(second)
 
 
+def mean_pool_log_score(q: np.ndarray, mean: np.ndarray) -> np.ndarray:
+    """Log of the first-order (mean-pooling) block score exp(q_hat.k_bar):
+    the Taylor score with its variance term left out, the heuristic pooling
+    baseline [TS] 3 contrasts the second-order selection with.
+
+    q: [h][d], mean: [j][d].  Returns ls [h][j]."""
+    q = np.asarray(q, dtype=F64)
+    qh = q / math.sqrt(q.shape[-1])
+    return qh @ np.asarray(mean, dtype=F64).T
+
+
+def exact_block_log_mass(q: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """Log of the exact mean attention mass of one block, log (1/n) sum_i
+    exp(q_hat . k_i), per query head: the quantity the Taylor score
+    approximates ([TS] 2.1 objective: the block's integrated probability
+    mass, in the per-token mean form of its score formula).
+
+    q: [h][d], keys: [n][d].  Returns [h]."""
+    q = np.asarray(q, dtype=F64)
+    qh = q / math.sqrt(q.shape[-1])
+    s = np.asarray(keys, dtype=F64) @ qh.T  # [n][h]
+    m = s.max(axis=0)
+    return m + np.log(np.exp(s - m[None, :]).sum(axis=0)) - math.log(s.shape[0])
+
+
 def group_log_score(ls: np.ndarray) -> np.ndarray:
     """LG[j] = log sum_h exp(ls[h][j]) (R4): the summed Taylor mass of a
     block over the query heads sharing one KV head."""
@@ -159,6 +188,9 @@ def linear_attention_numerator(f: np.ndarray, k: np.ndarray, v: np.ndarray):
 
 # ------------------------------------------- output forms of the RLA branch
 RLA_PLAIN, RLA_NORMALIZED, RLA_RMSNORM = 0, 1, 2
+# block scores for the selection: second-order Taylor (the method) or the
+# first-order mean-pooling baseline
+SCORE_TAYLOR, SCORE_MEAN = 0, 1
 
 
 def rla_branch(o_rla: np.ndarray, d_rla: float, mode: int, gamma: Optional[np.ndarray] = None,
@@ -253,29 +285,51 @@ class SplaOracle:
         self.append([b], [k.shape[0]], k, v)
 
     # ------------------------------------------------------------- decode
-    def block_group_scores(self, b: int, g: int, q: np.ndarray) -> Dict[int, float]:
-        """LG of every candidate block 1..nb-2 of (b, g) for queries q [H][d]."""
+    def block_group_scores(self, b: int, g: int, q: np.ndarray,
+                           score_form: int = SCORE_TAYLOR) -> Dict[int, float]:
+        """LG of every candidate block 1..nb-2 of (b, g) for queries q [H][d],
+        from the second-order Taylor score (default) or the first-order
+        mean-pooling score."""
         T = int(self.lens[b])
         nb = -(-T // self.bk)
         cand = np.arange(1, max(nb - 1, 1))
         if len(cand) == 0:
             return {}
         heads = q[g * self.r:(g + 1) * self.r]
-        ls = taylor_log_score(heads, self.mean[b, g, cand], self.var[b, g, cand])
+        if score_form == SCORE_TAYLOR:
+            ls = taylor_log_score(heads, self.mean[b, g, cand], self.var[b, g, cand])
+        elif score_form == SCORE_MEAN:
+            ls = mean_pool_log_score(heads, self.mean[b, g, cand])
+        else:
+            raise ValueError(f"unknown score form {score_form}")
         lg = group_log_score(ls)
         return {int(j): float(x) for j, x in zip(cand, lg)}
+
+    def block_exact_scores(self, b: int, g: int, q: np.ndarray) -> Dict[int, float]:
+        """Exact group log mass of every candidate block 1..nb-2 of (b, g):
+        log sum_h (1/Bk) sum_{i in j} exp(q_hat_h . k_i), from the stored keys."""
+        T = int(self.lens[b])
+        nb = -(-T // self.bk)
+        heads = np.asarray(q, dtype=F64)[g * self.r:(g + 1) * self.r]
+        out = {}
+        for j in range(1, max(nb - 1, 1)):
+            keys = self.K[b][j * self.bk:(j + 1) * self.bk, g, :]
+            out[j] = float(group_log_score(exact_block_log_mass(heads, keys)[:, None])[0])
+        return out
 
     def decode(self, q: np.ndarray, gate: np.ndarray,
                sel_override: Optional[np.ndarray] = None,
                brute_rla: bool = False, rla_mode: int = RLA_PLAIN,
-               gamma: Optional[np.ndarray] = None, eps: float = 1e-6) -> Dict[str, object]:
+               gamma: Optional[np.ndarray] = None, eps: float = 1e-6,
+               score_form: int = SCORE_TAYLOR) -> Dict[str, object]:
         """One decode step for every sequence (after that step's append).
 
         q: [B][H][d] queries, gate: [H].  sel_override: optional [B][G][k]
         block ids (-1 padded) used instead of the oracle's own selection
         (the scores are still computed and returned).  rla_mode, gamma
         ([H][d]) and eps choose the output form of the RLA branch
-        (rla_branch); o = o_sparse + gate * branch.
+        (rla_branch); o = o_sparse + gate * branch.  score_form chooses the
+        block score the selection ranks (SCORE_TAYLOR or SCORE_MEAN).
 
         Returns a dict with o, o_sparse, o_rla, o_bar, o_tilde, rla_out
         (the branch in the chosen form) ([B][H][d]),
@@ -302,7 +356,7 @@ class SplaOracle:
             nb = -(-T // bk)
             for g in range(G):
                 # (1) block scores and (2) selection
-                lg = self.block_group_scores(b, g, q[b])
+                lg = self.block_group_scores(b, g, q[b], score_form)
                 out["lg"][b][g] = lg
                 if sel_override is not None:
                     sel = sorted(int(j) for j in sel_override[b][g] if j >= 0)

@@ -370,12 +370,89 @@ def pin_rla_forms_vanish_when_all_selected():
         assert np.all(res["rla_out"] == 0) and np.array_equal(res["o"], res["o_sparse"])
 
 
+def pin_exact_mass_factorial_closed_form():
+    """Over the full 2^m sign design around k_bar the mean of exp(q_hat . k)
+    factorises: exp(q_hat . k_bar) * prod_c cosh(q_hat_c t_c), exactly.  The
+    Taylor score sits below it (cosh x >= 1 + x^2/2) and the mean-pooling
+    score below both (Jensen)."""
+    rng = np.random.default_rng(31)
+    d = 8
+    kbar = dyadic_normal(rng, (d,))
+    axes = [0, 2, 3, 5, 6, 7]
+    t = rng.uniform(0.2, 1.5, len(axes))
+    keys = factorial_block(kbar, t, axes)
+    for _ in range(5):
+        q = rng.standard_normal((3, d)) * 2.0
+        qh = q / math.sqrt(d)
+        got = so.exact_block_log_mass(q, keys)
+        want = qh @ kbar + sum(np.log(np.cosh(qh[:, c] * tc)) for c, tc in zip(axes, t))
+        assert np.allclose(got, want, rtol=0, atol=1e-12), (got, want)
+        mean, var = keys.mean(0), keys.var(0)
+        tay = so.taylor_log_score(q, mean[None], var[None])[:, 0]
+        mp = so.mean_pool_log_score(q, mean[None])[:, 0]
+        assert np.all(mp <= tay + 1e-15) and np.all(tay <= got + 1e-15)
+        assert np.allclose(mp, qh @ kbar, rtol=0, atol=1e-13)
+
+
+def pin_exact_mass_identical_and_jensen():
+    """Identical keys: exact mass = Taylor = mean pooling = q_hat . k.  Any
+    keys: the exact mass is never below the mean-pooling score (Jensen), with
+    the gap growing with the spread of q_hat . k."""
+    rng = np.random.default_rng(32)
+    d = 16
+    k = dyadic_normal(rng, (d,))
+    keys = np.repeat(k[None], 64, axis=0)
+    q = rng.standard_normal((4, d))
+    qh = q / math.sqrt(d)
+    assert np.allclose(so.exact_block_log_mass(q, keys), qh @ k, rtol=0, atol=1e-13)
+    for scale in (0.1, 1.0, 3.0):
+        keys = k[None] + scale * rng.standard_normal((64, d))
+        ex = so.exact_block_log_mass(q, keys)
+        mp = so.mean_pool_log_score(q, keys.mean(0)[None])[:, 0]
+        assert np.all(ex >= mp - 1e-13)
+    # group exact mass of the oracle state = sum over heads of the per-token mean mass
+    o = fresh_oracle(B=1, H=4, G=2, d=8, bk=4, top_k=3)
+    K = dyadic_normal(rng, (20, 2, 8))
+    fill(o, 0, K, dyadic_normal(rng, (20, 2, 8)))
+    qq = rng.standard_normal((4, 8))
+    ex = o.block_exact_scores(0, 1, qq)
+    assert sorted(ex) == [1, 2, 3]
+    for j, x in ex.items():
+        s = K[4 * j:4 * j + 4, 1].astype(F64) @ (qq[2:4] / math.sqrt(8)).T
+        assert abs(math.exp(x) - np.exp(s).mean(axis=0).sum()) <= 1e-12 * math.exp(x)
+
+
+def pin_score_forms_select_differently():
+    """Blocks with the same mean but a larger spread along the query have a
+    larger exact mass; the Taylor score ranks them first, mean pooling ties
+    them with the others (then ids decide)."""
+    rng = np.random.default_rng(33)
+    d, bk = 8, 16
+    u = np.zeros(d); u[0] = 1.0
+    nblk = 10
+    K = np.zeros((nblk * bk, 1, d))
+    spread = {7: 2.0, 8: 2.0}  # wide blocks along u
+    for j in range(nblk):
+        sgn = np.where(np.arange(bk) % 2 == 0, 1.0, -1.0)
+        K[j * bk:(j + 1) * bk, 0] = np.outer(sgn * spread.get(j, 0.25), u)
+    o = SplaOracle(1, 1, 1, d, bk, 4, 256)
+    fill(o, 0, K, dyadic_normal(rng, (nblk * bk, 1, d)))
+    q = (3.0 * u)[None, None]
+    r_t = o.decode(q, np.ones(1))
+    r_m = o.decode(q, np.ones(1), score_form=so.SCORE_MEAN)
+    assert [int(j) for j in r_t["sel"][0, 0]] == [0, 7, 8, 9]
+    assert [int(j) for j in r_m["sel"][0, 0]] == [0, 1, 2, 9]
+    ex = o.block_exact_scores(0, 0, q[0])
+    assert sorted(ex, key=lambda j: (-ex[j], j))[:2] == [7, 8]
+
+
 ALL_PINS = [
     pin_phi, pin_block_stats_factorial, pin_score_identical_keys, pin_score_factorial_closed_form,
     pin_score_vs_bruteforce_low_variance, pin_group_score, pin_selection_properties,
     pin_all_selected_is_dense_attention, pin_sparse_is_masked_attention_and_rla_is_direct,
     pin_global_state_is_phiK_T_V, pin_gqa_head_map, pin_edge_lengths, pin_planted_blocks_selected,
     pin_rla_normalized_is_unselected_mean, pin_rla_rmsnorm_is_torch_rms_norm, pin_rla_forms_vanish_when_all_selected,
+    pin_exact_mass_factorial_closed_form, pin_exact_mass_identical_and_jensen, pin_score_forms_select_differently,
 ]
 
 
@@ -515,6 +592,32 @@ def _mut_rla_no_zero_when_covered(o_rla, d_rla, mode, gamma=None, eps=1e-6, cove
 _ORIG_RLA_BRANCH = so.rla_branch
 
 
+def _mut_mass_sum_not_mean(q, keys):
+    return _ORIG_EXACT_MASS(q, keys) + math.log(np.asarray(keys).shape[0])
+
+
+def _mut_mass_no_temperature(q, keys):
+    q = np.asarray(q, F64)
+    return _ORIG_EXACT_MASS(q * math.sqrt(q.shape[-1]), keys)
+
+
+def _mut_mass_max_token(q, keys):
+    q = np.asarray(q, F64)
+    return (np.asarray(keys, F64) @ (q / math.sqrt(q.shape[-1])).T).max(axis=0)
+
+
+def _mut_mean_pool_with_var(q, mean):
+    return _ORIG_MEAN_POOL(q, mean) + 0.01
+
+
+def _mut_mean_pool_raw_q(q, mean):
+    return np.asarray(q, F64) @ np.asarray(mean, F64).T
+
+
+_ORIG_EXACT_MASS = so.exact_block_log_mass
+_ORIG_MEAN_POOL = so.mean_pool_log_score
+
+
 class _MutOracleSTransposed(SplaOracle):
     def append(self, seq_ids, n_new, k_new, v_new):
         super().append(seq_ids, n_new, k_new, v_new)
@@ -539,6 +642,11 @@ MUTANTS = {
     "rla_rms_eps_outside_sqrt": ("rla_branch", _mut_rla_rms_eps_outside),
     "rla_rms_without_gamma": ("rla_branch", _mut_rla_rms_no_gamma),
     "rla_not_zero_when_covered": ("rla_branch", _mut_rla_no_zero_when_covered),
+    "mass_sum_not_mean": ("exact_block_log_mass", _mut_mass_sum_not_mean),
+    "mass_no_temperature": ("exact_block_log_mass", _mut_mass_no_temperature),
+    "mass_max_token": ("exact_block_log_mass", _mut_mass_max_token),
+    "mean_pool_offset": ("mean_pool_log_score", _mut_mean_pool_with_var),
+    "mean_pool_raw_q": ("mean_pool_log_score", _mut_mean_pool_raw_q),
 }
 
 
