@@ -32,6 +32,7 @@ EXPORTED = [
     "spla_create", "spla_destroy", "spla_workspace_bytes", "spla_stats_floats", "spla_bind",
     "spla_append_kv", "spla_decode", "spla_decode_step", "spla_get_lens", "spla_status_str", "spla_abi_version",
     "spla_last_hip_error", "spla_set_tuning", "spla_launch_plan", "spla_set_rla_output",
+    "spla_set_score_form", "spla_block_mass",
 ]
 
 # spla_kernel ids (include/spla.h) -> kernel names
@@ -40,6 +41,8 @@ CALL_DECODE, CALL_DECODE_SEL_IN, CALL_DECODE_STEP = 0, 1, 2
 TUNE_FUSED_SELECT = 0
 # output forms of the RLA branch (spla_rla_form)
 RLA_PLAIN, RLA_NORMALIZED, RLA_RMSNORM = 0, 1, 2
+# block scores the selection can rank (spla_score_form)
+SCORE_TAYLOR, SCORE_MEAN = 0, 1
 
 
 class SplaConfig(ctypes.Structure):
@@ -114,6 +117,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spla_launch_plan.restype = ctypes.c_int32
     lib.spla_set_rla_output.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float]
     lib.spla_set_rla_output.restype = ctypes.c_int
+    lib.spla_set_score_form.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    lib.spla_set_score_form.restype = ctypes.c_int
+    lib.spla_block_mass.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.spla_block_mass.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -183,6 +190,13 @@ class SplaHandle:
 
     def set_rla_output(self, form: int, gamma_ptr: int = 0, eps: float = 0.0) -> None:
         _check(self.lib.spla_set_rla_output(self.h, form, ctypes.c_void_p(gamma_ptr), eps), "spla_set_rla_output")
+
+    def set_score_form(self, form: int) -> None:
+        _check(self.lib.spla_set_score_form(self.h, form), "spla_set_score_form")
+
+    def block_mass_raw(self, q_ptr: int, lgx_ptr: int, stream: int) -> int:
+        return self.lib.spla_block_mass(self.h, ctypes.c_void_p(q_ptr), ctypes.c_void_p(lgx_ptr),
+                                        ctypes.c_void_p(stream))
 
     def launch_plan(self, call: int):
         """Names of the kernels the next call of kind `call` launches, in order."""
@@ -286,6 +300,24 @@ class SplaLayer:
         else:
             self.handle.set_rla_output(form, 0, 0.0)
             self._rla_gamma = None
+
+    def set_score_form(self, form: int = SCORE_TAYLOR) -> None:
+        """Block score the selection ranks: SCORE_TAYLOR or SCORE_MEAN."""
+        self.handle.set_score_form(form)
+
+    def block_mass(self, q, lgx=None):
+        """Exact group log mass of every candidate block ([B][G][MB] float32;
+        entries outside 1..nb-2 keep what lgx held, -inf for a new tensor)."""
+        t = self.torch
+        if q.dtype != self.dtype or tuple(q.shape) != (self.B, self.H, self.d) or not q.is_contiguous():
+            raise ValueError("q must be a contiguous [B][H][d] tensor of the layer dtype")
+        if lgx is None:
+            lgx = t.full((self.B, self.G, self.mb), float("-inf"), dtype=t.float32, device=self.device)
+        if lgx.dtype != t.float32 or tuple(lgx.shape) != (self.B, self.G, self.mb) or not lgx.is_contiguous():
+            raise ValueError("lgx must be a contiguous float32 [B][G][MB] tensor")
+        st = self.handle.block_mass_raw(q.data_ptr(), lgx.data_ptr(), self._stream())
+        _check(st, "spla_block_mass", self.handle.lib, self.handle.h)
+        return lgx
 
     def launch_plan(self, step: bool = True, sel_in: bool = False):
         call = CALL_DECODE_STEP if step else (CALL_DECODE_SEL_IN if sel_in else CALL_DECODE)

@@ -23,7 +23,10 @@ struct ScorePre {
 // grid (score_tiles, G, B); lane = block within a 64-block tile, the four
 // wavefronts split the channels and meet in LDS.  Every wavefront issues its
 // query loads and then all of its statistics loads before the first wait.
-template <bool BF16, int R, int D>
+// TAYLOR = false is the first-order (mean-pooling) score q_hat . mean, which
+// reads no variances: the baseline the second-order selection is measured
+// against.
+template <bool BF16, int R, int D, bool TAYLOR>
 __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const int b, const ScorePre& p) {
   constexpr int NC4 = D / 16;  // channel quartets per wavefront
   constexpr int CW = D / 4;    // channels per wavefront
@@ -56,7 +59,7 @@ __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const 
 #pragma unroll
   for (int i = 0; i < NC4; ++i) m[i] = mean4[base + (size_t)i * kTile];
 #pragma unroll
-  for (int i = 0; i < NC4; ++i) v[i] = var4[base + (size_t)i * kTile];
+  for (int i = 0; i < NC4; ++i) v[i] = TAYLOR ? var4[base + (size_t)i * kTile] : make_float4(0.f, 0.f, 0.f, 0.f);
   // keep every load above this point: the whole tile is in flight before the
   // first use
   __builtin_amdgcn_sched_barrier(0);
@@ -90,6 +93,7 @@ __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const 
       dot[h] = fmaf(q.y, m[i].y, dot[h]);
       dot[h] = fmaf(q.z, m[i].z, dot[h]);
       dot[h] = fmaf(q.w, m[i].w, dot[h]);
+      if (!TAYLOR) continue;
       qq[h] = fmaf(q2.x, v[i].x, qq[h]);
       qq[h] = fmaf(q2.y, v[i].y, qq[h]);
       qq[h] = fmaf(q2.z, v[i].z, qq[h]);
@@ -111,7 +115,7 @@ __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const 
     const int blk = blk0 + lane / R;
     const float dd = (red[0][h][blk] + red[1][h][blk]) + (red[2][h][blk] + red[3][h][blk]);
     const float vv = (red[0][R + h][blk] + red[1][R + h][blk]) + (red[2][R + h][blk] + red[3][R + h][blk]);
-    const float ls = dd * a.inv_sqrt_d + __logf(1.f + fmaxf(vv, 0.f) * half_inv_d);
+    const float ls = TAYLOR ? dd * a.inv_sqrt_d + __logf(1.f + fmaxf(vv, 0.f) * half_inv_d) : dd * a.inv_sqrt_d;
     float lg = ls;
     if constexpr (R > 1) {
       float mx = ls;
@@ -205,14 +209,14 @@ __device__ void state_rows(const DecodeArgs& dc, const StateRefs& st, int b, int
 // spla_decode, first launch, grid (score_tiles + D * D / 1024, G, B): for
 // each (b, g) the scorer's tiles, then the o_bar partials of the S_all row
 // chunks.
-template <bool BF16, int R, int D>
+template <bool BF16, int R, int D, bool TAYLOR>
 __global__ __launch_bounds__(kThreads) void k_score(const float* mean, const float* var, const void* q,
                                                      int32_t n_tiles, int32_t G, int32_t H, int32_t tiles_all,
                                                      int32_t score_tiles, const StepArgs a) {
   const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   if (x < score_tiles) {
     const ScorePre p{mean, var, q, n_tiles, G, H, tiles_all};
-    score_tile<BF16, R, D>(a.dec, x, g, b, p);
+    score_tile<BF16, R, D, TAYLOR>(a.dec, x, g, b, p);
     return;
   }
   SPLA_SCALARS_READY("s"(a.st.s_all), "s"(a.st.z_all), "s"(a.dec.obar_part), "s"(a.dec.dz_part));
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void k_score(const float* mean, const flo
 // parts are independent: the scorer reads statistics of candidate blocks
 // 1..nb-2 only, all completed by earlier appends, and neither pages nor
 // S_all.
-template <bool BF16, int R, int D>
+template <bool BF16, int R, int D, bool TAYLOR>
 __global__ __launch_bounds__(kThreads) void k_step_score(const float* mean, const float* var, const void* q,
                                                           int32_t n_tiles, int32_t G, int32_t H, int32_t tiles_all,
                                                           int32_t score_tiles, const StepArgs a) {
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void k_step_score(const float* mean, cons
   const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   if (x < score_tiles) {
     const ScorePre p{mean, var, q, n_tiles, G, H, tiles_all};
-    score_tile<BF16, R, D>(dc, x, g, b, p);
+    score_tile<BF16, R, D, TAYLOR>(dc, x, g, b, p);
     return;
   }
   SPLA_SCALARS_READY("s"(dc.bk), "s"(a.st.k_new), "s"(a.st.v_new), "s"(a.st.s_all), "s"(a.st.z_all),
@@ -251,28 +255,39 @@ __global__ __launch_bounds__(kThreads) void k_step_score(const float* mean, cons
   if (T % dc.bk == 0) append_block_stats<BF16>(a.st, E, T / dc.bk - 1, g);
 }
 
-}  // namespace
-
-hipError_t launch_score(const StepArgs& a, bool bf16, const Launch& l) {
+template <bool TAYLOR>
+hipError_t launch_score_form(const StepArgs& a, bool bf16, const Launch& l) {
   const DecodeArgs& d = a.dec;
   const int chunks = d.d / (1024 / d.d);
   const dim3 grid(d.score_tiles + chunks, d.G, d.B);
   if (bf16)
-    SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_score<true, RR, DD>, grid, l, d.blk_mean, d.blk_var, d.q, d.n_tiles,
-                                             d.G, d.H, d.tiles_all, d.score_tiles, a))
-  SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_score<false, RR, DD>, grid, l, d.blk_mean, d.blk_var, d.q, d.n_tiles,
-                                           d.G, d.H, d.tiles_all, d.score_tiles, a))
+    SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_score<true, RR, DD, TAYLOR>, grid, l, d.blk_mean, d.blk_var, d.q,
+                                             d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
+  SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_score<false, RR, DD, TAYLOR>, grid, l, d.blk_mean, d.blk_var, d.q,
+                                           d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
 }
 
-hipError_t launch_step_score(const StepArgs& a, bool bf16, const Launch& l) {
+template <bool TAYLOR>
+hipError_t launch_step_score_form(const StepArgs& a, bool bf16, const Launch& l) {
   const int chunks = a.dec.d / (1024 / a.dec.d);
   const dim3 grid(a.dec.score_tiles + chunks + 1, a.dec.G, a.dec.B);
   const DecodeArgs& d = a.dec;
   if (bf16)
-    SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<true, RR, DD>, grid, l, d.blk_mean, d.blk_var, d.q,
-                                             d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
-  SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<false, RR, DD>, grid, l, d.blk_mean, d.blk_var, d.q,
-                                           d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
+    SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<true, RR, DD, TAYLOR>, grid, l, d.blk_mean, d.blk_var,
+                                             d.q, d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
+  SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<false, RR, DD, TAYLOR>, grid, l, d.blk_mean, d.blk_var,
+                                           d.q, d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
+}
+
+}  // namespace
+
+hipError_t launch_score(const StepArgs& a, bool bf16, const Launch& l) {
+  return a.dec.score_form == kScoreMean ? launch_score_form<false>(a, bf16, l) : launch_score_form<true>(a, bf16, l);
+}
+
+hipError_t launch_step_score(const StepArgs& a, bool bf16, const Launch& l) {
+  return a.dec.score_form == kScoreMean ? launch_step_score_form<false>(a, bf16, l)
+                                        : launch_step_score_form<true>(a, bf16, l);
 }
 
 }  // namespace spla

@@ -23,6 +23,7 @@ struct spla_handle {
   int32_t rla_form = SPLA_RLA_PLAIN;  // output form of the RLA branch
   const float* rla_gamma = nullptr;
   float rla_eps = 0.f;
+  int32_t score_form = SPLA_SCORE_TAYLOR;  // block score the selection ranks
   // workspace layout (bytes)
   size_t off_lg = 0, off_sel = 0, off_page = 0, off_part = 0, off_obar = 0, off_dz = 0, off_phq = 0;
   size_t ws_bytes = 0;
@@ -94,6 +95,7 @@ spla_status fill_decode_args(const spla_handle* h, const void* q, const float* g
   a->rla_form = h->rla_form;
   a->rla_gamma = h->rla_gamma;
   a->rla_eps = h->rla_eps;
+  a->score_form = h->score_form;
   a->B = c.batch;
   a->H = c.n_q_heads;
   a->G = c.n_kv_heads;
@@ -461,6 +463,33 @@ spla_status spla_set_tuning(spla_handle* h, int32_t key, int32_t value) {
       return SPLA_OK;
   }
   return SPLA_ERR_INVALID_ARG;
+}
+
+spla_status spla_set_score_form(spla_handle* h, int32_t form) {
+  if (!h || (form != SPLA_SCORE_TAYLOR && form != SPLA_SCORE_MEAN)) return SPLA_ERR_INVALID_ARG;
+  h->score_form = form;
+  return SPLA_OK;
+}
+
+spla_status spla_block_mass(spla_handle* h, const void* q, float* lgx, void* stream) {
+  if (!h) return SPLA_ERR_INVALID_ARG;
+  if (!h->bound) return SPLA_ERR_STATE;
+  if (!q || !lgx) return SPLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(lgx)) return SPLA_ERR_ALIGNMENT;
+  const spla_config& c = h->cfg;
+  for (int b = 0; b < c.batch; ++b)
+    if (h->lens[b] <= 0) return SPLA_ERR_INVALID_ARG;
+  DecodeArgs a;
+  fill_decode_args(h, q, nullptr, nullptr, nullptr, &a);
+  int max_cand = 0;
+  for (int b = 0; b < c.batch; ++b) {
+    const int nb = (h->lens[b] + c.block_size - 1) / c.block_size;
+    if (nb - 2 > max_cand) max_cand = nb - 2;
+  }
+  if (max_cand == 0) return SPLA_OK;
+  const hipError_t e = launch_block_mass(a, c.kv_dtype == SPLA_BF16, lgx, max_cand,
+                                         Launch{reinterpret_cast<hipStream_t>(stream), nullptr, nullptr});
+  return e == hipSuccess ? SPLA_OK : hip_fail(h, e);
 }
 
 spla_status spla_set_rla_output(spla_handle* h, int32_t form, const float* gamma, float eps) {

@@ -19,6 +19,9 @@ constexpr int kTile = 64;              // blocks per statistics tile (= wavefron
 constexpr int kThreads = 256;          // threads per workgroup of every kernel
 constexpr int kPartHdr = 4;            // m, l, sum_w, pad ahead of acc[d], o_tilde[d]
 
+// block score forms (spla_score_form)
+constexpr int kScoreTaylor = 0, kScoreMean = 1;
+
 // error word bits (workspace bytes [0, 4))
 constexpr uint32_t kErrPage = 1u;
 constexpr uint32_t kErrSel = 2u;
@@ -58,6 +61,7 @@ struct DecodeArgs {
   const float* rla_gamma;  // [H][d] scale of the RMS-normalised RLA branch
   float rla_eps;
   int32_t rla_form;        // spla_rla_form
+  int32_t score_form;      // spla_score_form
   int32_t B, H, G, d, r, bk, top_k, max_blocks, num_pages, n_tiles;
   int32_t score_tiles;  // grid.x of the scorer
   int32_t tiles_all;    // score tiles that every sequence of the batch has
@@ -134,6 +138,8 @@ hipError_t launch_select(const DecodeArgs& a, const Launch& l);
 hipError_t launch_attend(const DecodeArgs& a, bool bf16, const Launch& l);
 hipError_t launch_combine(const DecodeArgs& a, const Launch& l);
 hipError_t launch_step_score(const StepArgs& a, bool bf16, const Launch& l);
+// exact group log mass of every candidate block (a dense pass over the keys)
+hipError_t launch_block_mass(const DecodeArgs& a, bool bf16, float* lgx, int max_cand, const Launch& l);
 // fused select + attend: supported for bf16 K/V, block size 64, no selection
 // override and at most 16 * 256 candidates per sequence
 bool select_attend_supported(const DecodeArgs& a, bool bf16);

@@ -234,6 +234,31 @@ spla_status spla_set_tuning(spla_handle *h, int32_t key, int32_t value);
 typedef enum { SPLA_RLA_PLAIN = 0, SPLA_RLA_NORMALIZED = 1, SPLA_RLA_RMSNORM = 2 } spla_rla_form;
 spla_status spla_set_rla_output(spla_handle *h, int32_t form, const float *gamma, float eps);
 
+/* Block score the selection ranks (per handle, host only; from the next
+ * decode on).
+ *   SPLA_SCORE_TAYLOR  the second-order Taylor score (default; Technical
+ *                      Summary 2.1).
+ *   SPLA_SCORE_MEAN    its first-order term q_hat . mean alone: the
+ *                      mean-pooling heuristic the second-order selection is
+ *                      compared with (Technical Summary 3).  It reads no
+ *                      variances.  aux->lg then reports this score.
+ * SPLA_ERR_INVALID_ARG for an unknown form. */
+typedef enum { SPLA_SCORE_TAYLOR = 0, SPLA_SCORE_MEAN = 1 } spla_score_form;
+spla_status spla_set_score_form(spla_handle *h, int32_t form);
+
+/* Exact attention mass of every candidate block, for measuring how well a
+ * block score ranks blocks: lgx[b][g][j] = log sum_h (1/Bk) sum_{i in j}
+ * exp(q_hat_h . k_i) for j in 1 .. nb-2 (the other entries untouched), with
+ * the heads h of KV head g and q_hat = q / sqrt(d) (Technical Summary 2.1:
+ * the block's integrated probability mass, which the Taylor score
+ * estimates; per-token mean form, summed over the group like the score).
+ * q: device [B][H][d] kv_dtype; lgx: device [B][G][MB] float32.  It reads
+ * every key of every candidate block (a dense pass, not part of a decode)
+ * and changes no state.  Every sequence must be non-empty
+ * (SPLA_ERR_INVALID_ARG); an out-of-range page id sets bit 0 of the error
+ * word and leaves that block's entry untouched. */
+spla_status spla_block_mass(spla_handle *h, const void *q, float *lgx, void *stream);
+
 /* The kernels the next call of kind `call` on this handle would launch, in
  * launch order (the order of spla_decode_aux.kernel_events), from the
  * current lengths and tuning.  Writes min(n, cap) entries of kernels

@@ -90,7 +90,7 @@ class ParityRun:
     def __init__(self, w: Workload, page_order: str = "identity", steps: Optional[int] = None,
                  device: str = "cuda", prefill_chunk: int = 4096, use_step: bool = False,
                  seqs: Optional[List[int]] = None, kv_heads: Optional[List[int]] = None,
-                 fused_select: int = -1, rla_form: int = 0, rla_eps: float = 1e-6):
+                 fused_select: int = -1, rla_form: int = 0, rla_eps: float = 1e-6, score_form: int = 0):
         import torch
         from block_sparse_linear_amd import SplaLayer
 
@@ -118,6 +118,9 @@ class ParityRun:
         self.gamma_np = w.rla_gamma() if rla_form == 2 else None
         self.layer.set_rla_output(rla_form, None if self.gamma_np is None else torch.from_numpy(self.gamma_np),
                                   rla_eps)
+        # block score the selection ranks (0 Taylor, 1 mean pooling)
+        self.score_form = score_form
+        self.layer.set_score_form(score_form)
         self.mix = w.mixture_state()
 
     def dev(self, x: np.ndarray):
@@ -189,7 +192,7 @@ class ParityRun:
              "d_rla": g["d_rla"][bs][:, hs], "sel_idx": g["sel_idx"][bs][:, gs], "lg": g["lg"][bs][:, gs]}
         q_o = q_np[bs][:, hs]
         gate_o = self.gate_np[hs]
-        form = dict(rla_mode=self.rla_form, eps=self.rla_eps,
+        form = dict(rla_mode=self.rla_form, eps=self.rla_eps, score_form=self.score_form,
                     gamma=None if self.gamma_np is None else self.gamma_np[hs])
         sel_o = None if sel_in is None else np.asarray(sel_in)[bs][:, gs]
         ref = self.oracle.decode(q_o, gate_o, sel_override=sel_o, **form)

@@ -318,3 +318,29 @@ def test_rla_output_validation(lib):
     # the form changes the combine's arithmetic, not the kernels a call launches
     assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
     lib.spla_destroy(h)
+
+
+def test_score_form_and_block_mass_validation(lib):
+    st, h = create(lib, cfg())
+    assert lib.spla_block_mass(h, FAKE, FAKE, None) == STATE      # before spla_bind
+    assert lib.spla_set_score_form(h, 0) == OK and lib.spla_set_score_form(h, 1) == OK
+    assert lib.spla_set_score_form(h, 2) == INVALID and lib.spla_set_score_form(h, -1) == INVALID
+    assert lib.spla_set_score_form(None, 0) == INVALID
+    lib.spla_destroy(h)
+    h, c = bound(lib)
+    assert lib.spla_block_mass(h, None, FAKE, None) == INVALID
+    assert lib.spla_block_mass(h, FAKE, None, None) == INVALID
+    assert lib.spla_block_mass(h, FAKE + 2, FAKE, None) == ALIGN
+    assert lib.spla_block_mass(h, FAKE, FAKE + 8, None) == ALIGN
+    assert lib.spla_block_mass(None, FAKE, FAKE, None) == INVALID
+    lib.spla_destroy(h)
+    h, c = bound(lib, lens=(0, 2000))                              # an empty sequence
+    assert lib.spla_block_mass(h, FAKE, FAKE, None) == INVALID
+    # every sequence has at most two blocks: nothing to launch, nothing touched
+    lib.spla_destroy(h)
+    h, c = bound(lib, lens=(64, 128))
+    assert lib.spla_block_mass(h, FAKE, FAKE, None) == OK
+    # the score form changes which score the selection ranks, not the kernels
+    assert lib.spla_set_score_form(h, 1) == OK
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
+    lib.spla_destroy(h)
