@@ -58,7 +58,12 @@ with its reason in the design notes):
   R12 selection fidelity: a block's exact mass is the per-token mean of
       exp(q_hat . k) over its keys (the form of the score formula, R1),
       summed over the group's query heads as in R4; the mean-pooling
-      baseline keeps only the first-order term q_hat . k_bar.
+      baseline keeps only the first-order term q_hat . k_bar;
+  R13 chunked prefill of one sequence: every new token gets the decode result
+      at its own position, as if the chunk were appended and decoded one
+      token at a time (the token attends to itself and to every earlier
+      token, R10; its selection, exact attention and linear-attention state
+      are those of its own prefix).
 
 Parity of this module is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, library special cases and brute force; the readings R4, R7 and
@@ -317,11 +322,34 @@ class SplaOracle:
             out[j] = float(group_log_score(exact_block_log_mass(heads, keys)[:, None])[0])
         return out
 
+    def prefill_sequence(self, b: int, k_new: np.ndarray, v_new: np.ndarray, q_new: np.ndarray,
+                         gate: np.ndarray, **decode_kw) -> Dict[str, np.ndarray]:
+        """Chunked prefill of sequence b (R13): for each new token t in order,
+        append k_new[t], v_new[t] ([n][G][d]) and decode q_new[t] ([n][H][d])
+        for sequence b alone.  decode_kw go to decode (output form, score form,
+        brute_rla).  Returns o, o_sparse, o_rla, rla_out [n][H][d], d_rla
+        [n][H], sel [n][G][top_k] (and o_rla_direct / d_rla_direct with
+        brute_rla)."""
+        n = int(k_new.shape[0])
+        keys = ["o", "o_sparse", "o_rla", "rla_out", "d_rla", "sel"]
+        if decode_kw.get("brute_rla"):
+            keys += ["o_rla_direct", "d_rla_direct"]
+        res = {k: [] for k in keys}
+        q = np.zeros((self.B, self.H, self.d), F64)
+        for t in range(n):
+            self.append([b], [1], k_new[t:t + 1], v_new[t:t + 1])
+            q[b] = q_new[t]
+            r = self.decode(q, gate, seqs=[b], **decode_kw)
+            for k in keys:
+                res[k].append(np.array(r[k][b]))
+        return {k: np.stack(v) if v else np.zeros((0,)) for k, v in res.items()}
+
     def decode(self, q: np.ndarray, gate: np.ndarray,
                sel_override: Optional[np.ndarray] = None,
                brute_rla: bool = False, rla_mode: int = RLA_PLAIN,
                gamma: Optional[np.ndarray] = None, eps: float = 1e-6,
-               score_form: int = SCORE_TAYLOR) -> Dict[str, object]:
+               score_form: int = SCORE_TAYLOR,
+               seqs: Optional[Sequence[int]] = None) -> Dict[str, object]:
         """One decode step for every sequence (after that step's append).
 
         q: [B][H][d] queries, gate: [H].  sel_override: optional [B][G][k]
@@ -329,7 +357,8 @@ class SplaOracle:
         (the scores are still computed and returned).  rla_mode, gamma
         ([H][d]) and eps choose the output form of the RLA branch
         (rla_branch); o = o_sparse + gate * branch.  score_form chooses the
-        block score the selection ranks (SCORE_TAYLOR or SCORE_MEAN).
+        block score the selection ranks (SCORE_TAYLOR or SCORE_MEAN).  seqs:
+        decode only these sequences (the other rows of the results stay 0).
 
         Returns a dict with o, o_sparse, o_rla, o_bar, o_tilde, rla_out
         (the branch in the chosen form) ([B][H][d]),
@@ -349,7 +378,7 @@ class SplaOracle:
         if brute_rla:
             out["o_rla_direct"] = np.zeros((B, H, d), F64)
             out["d_rla_direct"] = np.zeros((B, H), F64)
-        for b in range(B):
+        for b in (range(B) if seqs is None else [int(x) for x in seqs]):
             T = int(self.lens[b])
             if T == 0:
                 raise ValueError("decode on an empty sequence")

@@ -446,6 +446,56 @@ def pin_score_forms_select_differently():
     assert sorted(ex, key=lambda j: (-ex[j], j))[:2] == [7, 8]
 
 
+def pin_prefill_all_selected_is_causal_sdpa():
+    """While every block of a token's prefix is selected, its prefill output
+    is causal softmax attention over its prefix (torch SDPA with a causal
+    mask, fp64 on the CPU) and its RLA branch is 0; the first token of an
+    empty sequence returns its own value."""
+    rng = np.random.default_rng(41)
+    G, H, d, bk, k = 2, 4, 8, 4, 3
+    n = bk * k  # every prefix fits in top_k blocks
+    o = SplaOracle(2, H, G, d, bk, k, 64)
+    K = dyadic_normal(rng, (n, G, d))
+    V = dyadic_normal(rng, (n, G, d))
+    Q = rng.standard_normal((n, H, d))
+    res = o.prefill_sequence(1, K.astype(np.float32), V.astype(np.float32), Q, np.full(H, 0.7))
+    assert np.all(res["o_rla"] == 0) and np.allclose(res["o"], res["o_sparse"], rtol=0, atol=0)
+    for h in range(H):
+        g = h // (H // G)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(Q[None, :, h]), torch.tensor(K[None, :, g]), torch.tensor(V[None, :, g]),
+            is_causal=True)[0].numpy()
+        assert np.allclose(res["o"][:, h], ref, rtol=1e-12, atol=1e-12), h
+    assert np.allclose(res["o"][0, 0], V[0, 0], rtol=0, atol=1e-15)
+    assert list(o.lens) == [0, n]
+
+
+def pin_prefill_rla_is_direct_over_each_prefix():
+    """Past the selection's reach, each prefill token's RLA branch equals the
+    direct sum over the unselected tokens of its own prefix (brute force), so
+    the linear-attention state is the prefix state of that token; a chunk
+    split in two gives the same outputs."""
+    rng = np.random.default_rng(42)
+    G, H, d, bk, k = 1, 2, 8, 4, 3
+    T0, n = 21, 14
+    K = dyadic_normal(rng, (T0 + n, G, d))
+    V = dyadic_normal(rng, (T0 + n, G, d))
+    Q = rng.standard_normal((n, H, d))
+    gate = np.array([0.5, 1.5])
+    o = SplaOracle(1, H, G, d, bk, k, 64)
+    fill(o, 0, K[:T0], V[:T0])
+    res = o.prefill_sequence(0, K[T0:].astype(np.float32), V[T0:].astype(np.float32), Q, gate, brute_rla=True)
+    assert np.abs(res["o_rla"]).max() > 0
+    scale = np.abs(res["o_rla_direct"]).max()
+    assert np.abs(res["o_rla"] - res["o_rla_direct"]).max() <= 1e-11 * scale
+    assert np.abs(res["d_rla"] - res["d_rla_direct"]).max() <= 1e-11 * np.abs(res["d_rla_direct"]).max()
+    o2 = SplaOracle(1, H, G, d, bk, k, 64)
+    fill(o2, 0, K[:T0], V[:T0])
+    a = o2.prefill_sequence(0, K[T0:T0 + 5].astype(np.float32), V[T0:T0 + 5].astype(np.float32), Q[:5], gate)
+    b2 = o2.prefill_sequence(0, K[T0 + 5:].astype(np.float32), V[T0 + 5:].astype(np.float32), Q[5:], gate)
+    assert np.allclose(np.concatenate([a["o"], b2["o"]]), res["o"], rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [
     pin_phi, pin_block_stats_factorial, pin_score_identical_keys, pin_score_factorial_closed_form,
     pin_score_vs_bruteforce_low_variance, pin_group_score, pin_selection_properties,
@@ -453,6 +503,7 @@ ALL_PINS = [
     pin_global_state_is_phiK_T_V, pin_gqa_head_map, pin_edge_lengths, pin_planted_blocks_selected,
     pin_rla_normalized_is_unselected_mean, pin_rla_rmsnorm_is_torch_rms_norm, pin_rla_forms_vanish_when_all_selected,
     pin_exact_mass_factorial_closed_form, pin_exact_mass_identical_and_jensen, pin_score_forms_select_differently,
+    pin_prefill_all_selected_is_causal_sdpa, pin_prefill_rla_is_direct_over_each_prefix,
 ]
 
 
@@ -618,6 +669,31 @@ _ORIG_EXACT_MASS = so.exact_block_log_mass
 _ORIG_MEAN_POOL = so.mean_pool_log_score
 
 
+class _MutOracleChunkFirst(SplaOracle):
+    """prefill that appends the whole chunk before decoding its tokens"""
+    def prefill_sequence(self, b, k_new, v_new, q_new, gate, **kw):
+        n = k_new.shape[0]
+        self.append([b], [n], k_new, v_new)
+        keys = ["o", "o_sparse", "o_rla", "rla_out", "d_rla", "sel"] + (
+            ["o_rla_direct", "d_rla_direct"] if kw.get("brute_rla") else [])
+        res = {k: [] for k in keys}
+        q = np.zeros((self.B, self.H, self.d))
+        for t in range(n):
+            q[b] = q_new[t]
+            r = self.decode(q, gate, seqs=[b], **kw)
+            for k in keys:
+                res[k].append(np.array(r[k][b]))
+        return {k: np.stack(v) for k, v in res.items()}
+
+
+class _MutOracleStateAfterToken(SplaOracle):
+    """prefill whose linear-attention state lags one token behind"""
+    def prefill_sequence(self, b, k_new, v_new, q_new, gate, **kw):
+        res = super().prefill_sequence(b, k_new, v_new, q_new, gate, **kw)
+        res["o_rla"] = np.concatenate([np.zeros_like(res["o_rla"][:1]), res["o_rla"][:-1]])
+        return res
+
+
 class _MutOracleSTransposed(SplaOracle):
     def append(self, seq_ids, n_new, k_new, v_new):
         super().append(seq_ids, n_new, k_new, v_new)
@@ -668,6 +744,12 @@ def test_mutants_are_caught(name, monkeypatch):
 
 def test_mutant_transposed_state_is_caught(monkeypatch):
     monkeypatch.setitem(globals(), "SplaOracle", _MutOracleSTransposed)
+    assert _any_pin_fails()
+
+
+@pytest.mark.parametrize("cls", [_MutOracleChunkFirst, _MutOracleStateAfterToken], ids=lambda c: c.__name__)
+def test_mutant_prefill_is_caught(cls, monkeypatch):
+    monkeypatch.setitem(globals(), "SplaOracle", cls)
     assert _any_pin_fails()
 
 
