@@ -32,7 +32,7 @@ EXPORTED = [
     "spla_create", "spla_destroy", "spla_workspace_bytes", "spla_stats_floats", "spla_bind",
     "spla_append_kv", "spla_decode", "spla_decode_step", "spla_get_lens", "spla_status_str", "spla_abi_version",
     "spla_last_hip_error", "spla_set_tuning", "spla_launch_plan", "spla_set_rla_output",
-    "spla_set_score_form", "spla_block_mass",
+    "spla_set_score_form", "spla_block_mass", "spla_prefill_workspace_bytes", "spla_prefill",
 ]
 
 # spla_kernel ids (include/spla.h) -> kernel names
@@ -121,6 +121,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spla_set_score_form.restype = ctypes.c_int
     lib.spla_block_mass.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.spla_block_mass.restype = ctypes.c_int
+    lib.spla_prefill_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    lib.spla_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.spla_prefill.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_size_t, ctypes.c_void_p]
+    lib.spla_prefill.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -193,6 +199,16 @@ class SplaHandle:
 
     def set_score_form(self, form: int) -> None:
         _check(self.lib.spla_set_score_form(self.h, form), "spla_set_score_form")
+
+    def prefill_workspace_bytes(self, chunk: int) -> int:
+        return int(self.lib.spla_prefill_workspace_bytes(self.h, chunk))
+
+    def prefill_raw(self, seq: int, n: int, k_ptr: int, v_ptr: int, q_ptr: int, gate_ptr: int, out_ptr: int,
+                    sel_ptr: int, ws_ptr: int, ws_bytes: int, stream: int) -> int:
+        return self.lib.spla_prefill(self.h, seq, n, ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
+                                     ctypes.c_void_p(q_ptr), ctypes.c_void_p(gate_ptr), ctypes.c_void_p(out_ptr),
+                                     ctypes.c_void_p(sel_ptr or None), ctypes.c_void_p(ws_ptr), ws_bytes,
+                                     ctypes.c_void_p(stream))
 
     def block_mass_raw(self, q_ptr: int, lgx_ptr: int, stream: int) -> int:
         return self.lib.spla_block_mass(self.h, ctypes.c_void_p(q_ptr), ctypes.c_void_p(lgx_ptr),
@@ -304,6 +320,34 @@ class SplaLayer:
     def set_score_form(self, form: int = SCORE_TAYLOR) -> None:
         """Block score the selection ranks: SCORE_TAYLOR or SCORE_MEAN."""
         self.handle.set_score_form(form)
+
+    def prefill(self, seq: int, k_new, v_new, q, gate, out=None, chunk: int = 256, workspace=None, sel_idx=None):
+        """Chunked prefill of sequence seq: append k_new / v_new ([n][G][d]) and
+        return out [n][H][d] float32, the decode output of every new token's
+        query q ([n][H][d]) at its own position.  chunk: tokens per group of
+        launches (the prefill workspace is sized for it unless given).
+        sel_idx: optional int32 [n][G][top_k] receiving the selections."""
+        t = self.torch
+        n = int(k_new.shape[0])
+        self._check_kv(k_new, v_new, n)
+        if q.dtype != self.dtype or tuple(q.shape) != (n, self.H, self.d) or not q.is_contiguous():
+            raise ValueError(f"q must be a contiguous [{n}][{self.H}][{self.d}] tensor of the layer dtype")
+        if gate.dtype != t.float32 or gate.numel() != self.H:
+            raise ValueError("gate must be float32 [H]")
+        if out is None:
+            out = t.empty((n, self.H, self.d), dtype=t.float32, device=self.device)
+        if workspace is None:
+            nbytes = self.handle.prefill_workspace_bytes(max(1, min(chunk, 256)))
+            workspace = t.empty(nbytes // 4 + 64, dtype=t.int32, device=self.device)
+        if sel_idx is not None and (sel_idx.dtype != t.int32 or tuple(sel_idx.shape) != (n, self.G, self.top_k)
+                                    or not sel_idx.is_contiguous()):
+            raise ValueError(f"sel_idx must be a contiguous int32 [{n}][{self.G}][{self.top_k}] tensor")
+        st = self.handle.prefill_raw(seq, n, k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), gate.data_ptr(),
+                                     out.data_ptr(), 0 if sel_idx is None else sel_idx.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                     self._stream())
+        _check(st, "spla_prefill", self.handle.lib, self.handle.h)
+        return out
 
     def block_mass(self, q, lgx=None):
         """Exact group log mass of every candidate block ([B][G][MB] float32;

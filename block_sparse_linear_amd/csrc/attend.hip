@@ -35,7 +35,9 @@ __global__ __launch_bounds__(kThreads) void k_attend(const DecodeArgs a) {
     if (threadIdx.x == 0) atomicOr(a.err, kErrSel);
     return;
   }
-  const int page = a.block_table[(size_t)b * a.max_blocks + j];
+  // the selector's page ids (the block table only for the test hook)
+  const int page = a.sel_in ? a.block_table[(size_t)b * a.max_blocks + j]
+                            : a.sel_page[((size_t)b * a.G + g) * a.top_k + slot];
   if (page < 0 || page >= a.num_pages) {
     if (threadIdx.x == 0) atomicOr(a.err, kErrPage);
     return;

@@ -25,7 +25,7 @@ __global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, con
   // the leading kernel arguments alone: the scores and page ids it ranks and
   // the queries
   SelectKeys<KPT> k;
-  select_load<KPT>(lg, block_table, n_tiles, max_blocks, G, g, b, k);
+  select_load<KPT>(lg, block_table, n_tiles, max_blocks, G, g, b, b, k);
   uint4 qraw[D / 32], fh[D / 32], fl[D / 32];
   load_q_mfma<R, D>(q, phq, H, g, b, qraw, fh, fl);
   SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.top_k), "s"(a.sel), "s"(a.k_pages), "s"(a.v_pages),

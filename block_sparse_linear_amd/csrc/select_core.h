@@ -49,16 +49,17 @@ struct SelectKeys {
 };
 
 // Issue the candidate loads of a selection: scores and page ids of
-// candidates 0 .. KPT * 256 - 1, clamped into the score row and the block
-// table row.  They need no sequence length, so a kernel can issue them first
-// (lg, block_table and the sizes are kernel arguments ahead of the argument
-// struct).  The pages of the sink and the current block come with
+// candidates 0 .. KPT * 256 - 1, clamped into the score row of b and the
+// block table row brow (b, or 0 for the virtual queries of one sequence's
+// prefill chunk).  They need no sequence length, so a kernel can issue them
+// first (lg, block_table and the sizes are kernel arguments ahead of the
+// argument struct).  The pages of the sink and the current block come with
 // select_pages once the length is known.
 template <int KPT>
 __device__ __forceinline__ void select_load(const float* lg, const int32_t* block_table, int n_tiles, int max_blocks,
-                                            int G, int g, int b, SelectKeys<KPT>& k) {
+                                            int G, int g, int b, int brow, SelectKeys<KPT>& k) {
   const int cap = max(min(n_tiles * kTile, max_blocks) - 2, 0);  // last candidate index inside both rows
-  const int32_t* btab = block_table + (size_t)b * max_blocks;
+  const int32_t* btab = block_table + (size_t)brow * max_blocks;
   const float* row = lg + ((size_t)b * G + g) * (size_t)(n_tiles * kTile) + 1;  // row[i] = LG(i + 1)
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
@@ -73,11 +74,11 @@ __device__ __forceinline__ void select_load(const float* lg, const int32_t* bloc
 // load would be waited for at every LDS barrier of the selection, which waits
 // on the scalar-load counter too.
 template <int KPT>
-__device__ __forceinline__ void select_pages(const int32_t* block_table, int max_blocks, int b, int nb,
+__device__ __forceinline__ void select_pages(const int32_t* block_table, int max_blocks, int brow, int nb,
                                              SelectKeys<KPT>& k) {
   int zero;
   asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-  const int32_t* btab = block_table + (size_t)b * max_blocks;
+  const int32_t* btab = block_table + (size_t)brow * max_blocks;
   k.pg_sink = btab[zero];
   k.pg_cur = btab[min(max(nb - 1, 0), max_blocks - 1) + zero];
 }

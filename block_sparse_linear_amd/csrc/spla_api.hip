@@ -29,32 +29,52 @@ struct spla_handle {
   size_t ws_bytes = 0;
 };
 
+// offsets (bytes) of the per-query decode scratch in a workspace sized for nq
+// queries: the handle's own workspace (nq = batch) or a prefill workspace
+// (nq = virtual queries of one chunk)
+struct WsLayout {
+  size_t lg, sel, page, part, obar, dz, phq, bytes;
+};
+
 namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-void layout(spla_handle* h) {
-  const spla_config& c = h->cfg;
-  const size_t B = c.batch, H = c.n_q_heads, G = c.n_kv_heads, d = c.head_dim, k = c.top_k;
+WsLayout ws_layout(const spla_config& c, int n_tiles, size_t nq) {
+  const size_t H = c.n_q_heads, G = c.n_kv_heads, d = c.head_dim, k = c.top_k;
+  WsLayout w;
   size_t off = 256;  // error word + spare
-  h->off_lg = off;
-  off = align256(off + B * G * (size_t)h->n_tiles * kTile * sizeof(float));
-  h->off_sel = off;
-  off = align256(off + B * G * k * sizeof(int32_t));
-  h->off_page = off;
-  off = align256(off + B * G * k * sizeof(int32_t));
-  h->off_part = off;
-  off = align256(off + B * H * k * (2 * d + kPartHdr) * sizeof(float));
-  const size_t chunks = d * d / 1024;  // S_all row chunks per (sequence, KV head)
-  h->off_obar = off;
-  off = align256(off + B * G * chunks * (H / G) * d * sizeof(float));
-  h->off_dz = off;
-  off = align256(off + B * G * chunks * (H / G) * sizeof(float));
-  h->off_phq = off;
-  off = align256(off + B * H * 2 * d * sizeof(uint16_t));
-  h->ws_bytes = off;
+  w.lg = off;
+  off = align256(off + nq * G * (size_t)n_tiles * kTile * sizeof(float));
+  w.sel = off;
+  off = align256(off + nq * G * k * sizeof(int32_t));
+  w.page = off;
+  off = align256(off + nq * G * k * sizeof(int32_t));
+  w.part = off;
+  off = align256(off + nq * H * k * (2 * d + kPartHdr) * sizeof(float));
+  const size_t chunks = d * d / 1024;  // S_all row chunks per (query, KV head)
+  w.obar = off;
+  off = align256(off + nq * G * chunks * (H / G) * d * sizeof(float));
+  w.dz = off;
+  off = align256(off + nq * G * chunks * (H / G) * sizeof(float));
+  w.phq = off;
+  off = align256(off + nq * H * 2 * d * sizeof(uint16_t));
+  w.bytes = off;
+  return w;
+}
+
+void layout(spla_handle* h) {
+  const WsLayout w = ws_layout(h->cfg, h->n_tiles, h->cfg.batch);
+  h->off_lg = w.lg;
+  h->off_sel = w.sel;
+  h->off_page = w.page;
+  h->off_part = w.part;
+  h->off_obar = w.obar;
+  h->off_dz = w.dz;
+  h->off_phq = w.phq;
+  h->ws_bytes = w.bytes;
 }
 
 template <typename T>
@@ -463,6 +483,109 @@ spla_status spla_set_tuning(spla_handle* h, int32_t key, int32_t value) {
       return SPLA_OK;
   }
   return SPLA_ERR_INVALID_ARG;
+}
+
+size_t spla_prefill_workspace_bytes(const spla_handle* h, int32_t chunk) {
+  if (!h || chunk < 1 || chunk > kMaxBatch) return 0;
+  return ws_layout(h->cfg, h->n_tiles, chunk).bytes;
+}
+
+spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_new, const void* v_new, const void* q,
+                         const float* gate, float* out, int32_t* sel_idx, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (!h) return SPLA_ERR_INVALID_ARG;
+  if (!h->bound) return SPLA_ERR_STATE;
+  const spla_config& c = h->cfg;
+  if (seq < 0 || seq >= c.batch || n < 0) return SPLA_ERR_INVALID_ARG;
+  if (n == 0) return SPLA_OK;
+  if (!k_new || !v_new || !q || !gate || !out || !workspace) return SPLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {k_new, v_new, q, gate, out, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPLA_ERR_ALIGNMENT;
+  if (sel_idx && !aligned16(sel_idx)) return SPLA_ERR_ALIGNMENT;
+  if ((int64_t)h->lens[seq] + n > (int64_t)c.max_blocks_per_seq * c.block_size) return SPLA_ERR_CAPACITY;
+  if ((int64_t)n > (int64_t)INT32_MAX / (c.n_q_heads * c.head_dim)) return SPLA_ERR_INVALID_ARG;
+  int chunk = kMaxBatch;  // virtual queries per launch: the most the workspace holds
+  while (chunk > 0 && ws_layout(c, h->n_tiles, chunk).bytes > workspace_bytes) --chunk;
+  if (chunk == 0) return SPLA_ERR_INVALID_ARG;
+  const WsLayout wl = ws_layout(c, h->n_tiles, chunk);
+  const bool bf16 = c.kv_dtype == SPLA_BF16;
+  const size_t es = bf16 ? 2 : 4;
+  const size_t G = c.n_kv_heads, H = c.n_q_heads, d = c.head_dim;
+  const size_t stats_row = G * (size_t)h->n_tiles * kTile * d;  // floats of one sequence's statistics
+  const Launch l{reinterpret_cast<hipStream_t>(stream), nullptr, nullptr};
+  char* wsb = static_cast<char*>(workspace);
+  const int chunks = c.head_dim / (1024 / c.head_dim);
+  for (int c0 = 0; c0 < n; c0 += chunk) {
+    const int m = n - c0 < chunk ? n - c0 : chunk;
+    const int t0 = h->lens[seq];
+    const char* kc = static_cast<const char*>(k_new) + (size_t)c0 * G * d * es;
+    const char* vc = static_cast<const char*>(v_new) + (size_t)c0 * G * d * es;
+    // (1) the chunk's pages and the statistics of the blocks it completes
+    AppendArgs ap;
+    memset(&ap, 0, sizeof(ap));
+    fill_state_refs(h, kc, vc, &ap.st);
+    ap.n_entries = 1;
+    ap.e[0] = AppendEntry{seq, m, t0, 0};
+    ap.page_prefix[0] = ap.stat_prefix[0] = 0;
+    ap.page_items = ap.page_prefix[1] = (m + 63) / 64;
+    ap.stat_items = ap.stat_prefix[1] = ((t0 + m) / c.block_size - t0 / c.block_size) * c.n_kv_heads;
+    hipError_t e = launch_append(ap, bf16, l);
+    if (e != hipSuccess) return hip_fail(h, e);
+    // (2) every token of the chunk decoded as a virtual query of this
+    // sequence, against the state before the chunk
+    StepArgs sa;
+    memset(&sa, 0, sizeof(sa));
+    DecodeArgs& a = sa.dec;
+    fill_decode_args(h, static_cast<const char*>(q) + (size_t)c0 * H * d * es, gate, out + (size_t)c0 * H * d,
+                     nullptr, &a);
+    a.B = m;
+    a.virtual_queries = 1;
+    a.sel_out = sel_idx ? sel_idx + (size_t)c0 * G * c.top_k : nullptr;
+    a.block_table = h->buf.block_table + (size_t)seq * c.max_blocks_per_seq;
+    a.blk_mean = h->buf.blk_mean + (size_t)seq * stats_row;
+    a.blk_var = h->buf.blk_var + (size_t)seq * stats_row;
+    a.s_all = h->buf.s_all + (size_t)seq * G * d * d;
+    a.z_all = h->buf.z_all + (size_t)seq * G * d;
+    a.lg = reinterpret_cast<float*>(wsb + wl.lg);
+    a.sel = reinterpret_cast<int32_t*>(wsb + wl.sel);
+    a.sel_page = reinterpret_cast<int32_t*>(wsb + wl.page);
+    a.part = reinterpret_cast<float*>(wsb + wl.part);
+    a.obar_part = reinterpret_cast<float*>(wsb + wl.obar);
+    a.dz_part = reinterpret_cast<float*>(wsb + wl.dz);
+    a.phq = reinterpret_cast<uint16_t*>(wsb + wl.phq);
+    int max_tiles = 0, min_tiles = 1 << 30;
+    for (int i = 0; i < m; ++i) {
+      a.lens[i] = t0 + i + 1;
+      const int nb = (a.lens[i] + c.block_size - 1) / c.block_size;
+      const int tiles = nb > c.top_k ? (nb - 2) / kTile + 1 : 0;
+      if (tiles > max_tiles) max_tiles = tiles;
+      if (tiles < min_tiles) min_tiles = tiles;
+    }
+    a.score_tiles = max_tiles;
+    a.tiles_all = min_tiles;
+    fill_state_refs(h, kc, vc, &sa.st);
+    sa.st.block_table = a.block_table;
+    sa.st.blk_mean = h->buf.blk_mean + (size_t)seq * stats_row;
+    sa.st.blk_var = h->buf.blk_var + (size_t)seq * stats_row;
+    sa.st.s_all = h->buf.s_all + (size_t)seq * G * d * d;
+    sa.st.z_all = h->buf.z_all + (size_t)seq * G * d;
+    if ((e = launch_score(sa, bf16, l)) != hipSuccess) return hip_fail(h, e);
+    if ((e = launch_chunk_la(a, bf16, kc, vc, l)) != hipSuccess) return hip_fail(h, e);
+    if ((e = launch_select(a, l)) != hipSuccess) return hip_fail(h, e);
+    if ((e = launch_attend(a, bf16, l)) != hipSuccess) return hip_fail(h, e);
+    if ((e = launch_combine(a, l)) != hipSuccess) return hip_fail(h, e);
+    // (3) the chunk's tokens into S_all / z_all
+    AppendArgs as;
+    memset(&as, 0, sizeof(as));
+    fill_state_refs(h, kc, vc, &as.st);
+    as.n_entries = 1;
+    as.e[0] = AppendEntry{seq, m, t0, 0};
+    as.s_items = c.n_kv_heads * chunks;
+    if ((e = launch_append(as, bf16, l)) != hipSuccess) return hip_fail(h, e);
+    h->lens[seq] = t0 + m;
+  }
+  return SPLA_OK;
 }
 
 spla_status spla_set_score_form(spla_handle* h, int32_t form) {

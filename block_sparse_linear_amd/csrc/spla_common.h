@@ -62,6 +62,8 @@ struct DecodeArgs {
   float rla_eps;
   int32_t rla_form;        // spla_rla_form
   int32_t score_form;      // spla_score_form
+  int32_t virtual_queries;  // 1: the batch is the tokens of one sequence's prefill chunk (state pointers
+                            // address that sequence; every b reads its row 0 of statistics, state, block table)
   int32_t B, H, G, d, r, bk, top_k, max_blocks, num_pages, n_tiles;
   int32_t score_tiles;  // grid.x of the scorer
   int32_t tiles_all;    // score tiles that every sequence of the batch has
@@ -138,6 +140,9 @@ hipError_t launch_select(const DecodeArgs& a, const Launch& l);
 hipError_t launch_attend(const DecodeArgs& a, bool bf16, const Launch& l);
 hipError_t launch_combine(const DecodeArgs& a, const Launch& l);
 hipError_t launch_step_score(const StepArgs& a, bool bf16, const Launch& l);
+// chunked prefill: the chunk's own tokens added into the o_bar / phi(q).z
+// partials of its virtual queries (k_new / v_new address the chunk's first row)
+hipError_t launch_chunk_la(const DecodeArgs& a, bool bf16, const void* k_new, const void* v_new, const Launch& l);
 // exact group log mass of every candidate block (a dense pass over the keys)
 hipError_t launch_block_mass(const DecodeArgs& a, bool bf16, float* lgx, int max_cand, const Launch& l);
 // fused select + attend: supported for bf16 K/V, block size 64, no selection

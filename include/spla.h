@@ -234,6 +234,32 @@ spla_status spla_set_tuning(spla_handle *h, int32_t key, int32_t value);
 typedef enum { SPLA_RLA_PLAIN = 0, SPLA_RLA_NORMALIZED = 1, SPLA_RLA_RMSNORM = 2 } spla_rla_form;
 spla_status spla_set_rla_output(spla_handle *h, int32_t form, const float *gamma, float eps);
 
+/* Chunked prefill of one sequence: append the n tokens k_new, v_new (device
+ * [n][G][d] kv_dtype) to sequence seq and write, for each new token t, the
+ * output its query q[t] (device [n][H][d] kv_dtype) gets as a decode at its
+ * own position: out[t] (device [n][H][d] float32) equals what spla_append_kv
+ * of token t alone followed by a spla_decode of q[t] would give that
+ * sequence (Technical Summary 2.1-2.3 applied at every position; the token
+ * attends to itself and to every earlier token, causally inside its own
+ * block).  Other sequences are untouched.  The handle's output form and
+ * score form apply.  sel_idx (optional, device [n][G][top_k] int32) receives
+ * every token's selected block ids, ascending, -1 padded.
+ * workspace: device scratch of workspace_bytes >= spla_prefill_workspace_bytes
+ * (h, 1), caller-owned; the call processes up to 256 tokens per group of
+ * launches, as many as the workspace holds (spla_prefill_workspace_bytes(h,
+ * c) bytes hold c), and its contents are undefined afterwards.  It may not
+ * be the handle's own workspace.  Each group appends its tokens' pages and
+ * block statistics, decodes its tokens against the state before the group
+ * (adding the group's own earlier tokens to the linear-attention sums), then
+ * adds the group to S_all / z_all.
+ * Errors as for spla_append_kv (capacity, alignment, seq out of range);
+ * n = 0 does nothing.  On SPLA_ERR_HIP the state of sequence seq is
+ * undefined (part of the tokens may be in it). */
+size_t spla_prefill_workspace_bytes(const spla_handle *h, int32_t chunk);
+spla_status spla_prefill(spla_handle *h, int32_t seq, int32_t n, const void *k_new, const void *v_new,
+                         const void *q, const float *gate, float *out, int32_t *sel_idx, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 /* Block score the selection ranks (per handle, host only; from the next
  * decode on).
  *   SPLA_SCORE_TAYLOR  the second-order Taylor score (default; Technical

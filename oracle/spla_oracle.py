@@ -323,15 +323,17 @@ class SplaOracle:
         return out
 
     def prefill_sequence(self, b: int, k_new: np.ndarray, v_new: np.ndarray, q_new: np.ndarray,
-                         gate: np.ndarray, **decode_kw) -> Dict[str, np.ndarray]:
+                         gate: np.ndarray, sel_per_token: Optional[np.ndarray] = None,
+                         **decode_kw) -> Dict[str, object]:
         """Chunked prefill of sequence b (R13): for each new token t in order,
         append k_new[t], v_new[t] ([n][G][d]) and decode q_new[t] ([n][H][d])
-        for sequence b alone.  decode_kw go to decode (output form, score form,
-        brute_rla).  Returns o, o_sparse, o_rla, rla_out [n][H][d], d_rla
-        [n][H], sel [n][G][top_k] (and o_rla_direct / d_rla_direct with
-        brute_rla)."""
+        for sequence b alone.  sel_per_token: optional [n][G][k] selections to
+        use instead of the oracle's own (per token).  decode_kw go to decode
+        (output form, score form, brute_rla).  Returns o, o_sparse, o_rla,
+        rla_out [n][H][d], d_rla [n][H], sel [n][G][top_k], lg (per token, per
+        KV head {block: LG}) (and o_rla_direct / d_rla_direct with brute_rla)."""
         n = int(k_new.shape[0])
-        keys = ["o", "o_sparse", "o_rla", "rla_out", "d_rla", "sel"]
+        keys = ["o", "o_sparse", "o_rla", "rla_out", "d_rla", "sel", "lg"]
         if decode_kw.get("brute_rla"):
             keys += ["o_rla_direct", "d_rla_direct"]
         res = {k: [] for k in keys}
@@ -339,10 +341,14 @@ class SplaOracle:
         for t in range(n):
             self.append([b], [1], k_new[t:t + 1], v_new[t:t + 1])
             q[b] = q_new[t]
-            r = self.decode(q, gate, seqs=[b], **decode_kw)
+            ov = None
+            if sel_per_token is not None:
+                ov = np.full((self.B, self.G, self.top_k), -1, np.int64)
+                ov[b] = sel_per_token[t]
+            r = self.decode(q, gate, sel_override=ov, seqs=[b], **decode_kw)
             for k in keys:
-                res[k].append(np.array(r[k][b]))
-        return {k: np.stack(v) if v else np.zeros((0,)) for k, v in res.items()}
+                res[k].append(r[k][b] if k == "lg" else np.array(r[k][b]))
+        return {k: (v if k == "lg" else (np.stack(v) if v else np.zeros((0,)))) for k, v in res.items()}
 
     def decode(self, q: np.ndarray, gate: np.ndarray,
                sel_override: Optional[np.ndarray] = None,

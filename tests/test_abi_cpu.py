@@ -344,3 +344,32 @@ def test_score_form_and_block_mass_validation(lib):
     assert lib.spla_set_score_form(h, 1) == OK
     assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
     lib.spla_destroy(h)
+
+
+def test_prefill_workspace_and_validation(lib):
+    st, h = create(lib, cfg())
+    one = lib.spla_prefill_workspace_bytes(h, 1)
+    assert 0 < one < lib.spla_prefill_workspace_bytes(h, 2) < lib.spla_prefill_workspace_bytes(h, 256)
+    assert lib.spla_prefill_workspace_bytes(h, 0) == 0 and lib.spla_prefill_workspace_bytes(h, 257) == 0
+    assert lib.spla_prefill_workspace_bytes(None, 1) == 0
+    big = lib.spla_prefill_workspace_bytes(h, 256)
+    args = (FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, FAKE + 16384, None, FAKE + (1 << 31))
+    assert lib.spla_prefill(h, 0, 4, *args, big, None) == STATE    # before spla_bind
+    lib.spla_destroy(h)
+    h, c = bound(lib, lens=(100, 2000))
+    for seq, n, want in ((-1, 4, INVALID), (2, 4, INVALID), (0, -1, INVALID), (0, 0, OK)):
+        assert lib.spla_prefill(h, seq, n, *args, big, None) == want, (seq, n)
+    assert lib.spla_prefill(h, 0, 4, *args, one - 1, None) == INVALID   # workspace below one token
+    for i in (0, 1, 2, 3, 4, 6):
+        bad = list(args)
+        bad[i] = None
+        assert lib.spla_prefill(h, 0, 4, *bad, big, None) == INVALID, i
+        bad[i] = args[i] + 4
+        assert lib.spla_prefill(h, 0, 4, *bad, big, None) == ALIGN, i
+    bad = list(args)
+    bad[5] = FAKE + 20484                                          # misaligned sel_idx
+    assert lib.spla_prefill(h, 0, 4, *bad, big, None) == ALIGN
+    cap = c.max_blocks_per_seq * c.block_size
+    assert lib.spla_prefill(h, 1, cap - 2000 + 1, *args, big, None) == CAPACITY
+    assert lens_of(lib, h, 2) == [100, 2000]                       # nothing enqueued, mirror unchanged
+    lib.spla_destroy(h)

@@ -685,6 +685,8 @@ class _MutOracleChunkFirst(SplaOracle):
                 res[k].append(np.array(r[k][b]))
         return {k: np.stack(v) for k, v in res.items()}
 
+    # (lg is not needed by the pins)
+
 
 class _MutOracleStateAfterToken(SplaOracle):
     """prefill whose linear-attention state lags one token behind"""

@@ -50,6 +50,7 @@ _S_OUTLIER = 10
 _S_MIXTURE = 11
 _S_QBASE = 12
 _S_RLA_GAMMA = 13
+_S_PREFILL_Q = 14
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -188,6 +189,26 @@ class Workload:
         if self.gate_ones:
             return np.ones(self.n_q_heads, np.float32)
         return _rng(self.seed, _S_GATE).uniform(0.0, 1.0, self.n_q_heads).astype(np.float32)
+
+    def prefill_queries(self, b: int, pos0: int, n: int) -> np.ndarray:
+        """[n][H][d] queries of prefill positions pos0 .. pos0 + n - 1 of sequence
+        b, distributed like the decode steps' queries; drawn per prefill_chunk
+        unit so any split regenerates the same values."""
+        unit = self.prefill_chunk
+        out = []
+        p = pos0
+        while p < pos0 + n:
+            ui = p // unit
+            lo = p - ui * unit
+            take = min(unit - lo, pos0 + n - p)
+            noise = _rng(self.seed, _S_PREFILL_Q, b, ui).standard_normal(
+                (unit, self.n_q_heads, self.head_dim)).astype(np.float32)[lo:lo + take]
+            if self.kind == "planted":
+                gidx = np.arange(self.n_q_heads) // self.group
+                noise = self.q_base()[b][gidx][None] + np.float32(0.25) * noise
+            out.append(noise)
+            p += take
+        return self.round(np.concatenate(out, 0))
 
     def rla_gamma(self) -> np.ndarray:
         """[H][d] scale of the RMS-normalised RLA branch (float32, U(0.5, 1.5));
