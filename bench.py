@@ -167,6 +167,72 @@ def cpu_baseline(w, n_steps: int, budget_s: float, rla_form: int = 0) -> dict:
                       f"untimed prefill ({spent:.1f}s timed, {t_step * 1e3:.1f} ms/step)"}
 
 
+def run_prefill(args) -> int:
+    """Chunked prefill: time spla_prefill of args.prefill tokens appended to
+    sequence 0 of the workload (after its untimed prefill), each timed call on
+    a fresh copy of the prefilled state (the copy is outside the timed region).
+    Prints one JSON line: tokens/s of the prefilled tokens."""
+    import numpy as np
+    import torch
+
+    from block_sparse_linear_amd import SplaLayer
+    from workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    n = args.prefill
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    mb = -(-(max(w.t0) + n) // w.block_size) + 1
+    L = SplaLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k, mb,
+                  kv_dtype=w.kv_dtype, device="cuda:0")
+    L.set_fused_select(args.fused_select)
+    gamma = torch.from_numpy(w.rla_gamma()).to(dev) if args.rla_form == 2 else None
+    L.set_rla_output(args.rla_form, gamma, RLA_EPS)
+    t0 = time.time()
+    for b in range(w.batch):
+        for _, k, v in w.prefill_chunks(b):
+            L.append([b], [k.shape[0]], torch.from_numpy(k).to(dev).to(tdt), torch.from_numpy(v).to(dev).to(tdt))
+    torch.cuda.synchronize()
+    log(f"prefill of the context {time.time() - t0:.1f}s lens={L.lens[:4]}")
+    seq = 0
+    rng = np.random.default_rng([w.seed, 99])
+    kk = torch.from_numpy(w.round(rng.standard_normal((n, w.n_kv_heads, w.head_dim)).astype(np.float32))).to(dev).to(tdt)
+    vv = torch.from_numpy(w.round(rng.standard_normal((n, w.n_kv_heads, w.head_dim)).astype(np.float32))).to(dev).to(tdt)
+    qq = torch.from_numpy(w.prefill_queries(seq, L.lens[seq], n)).to(dev).to(tdt)
+    gate = torch.from_numpy(w.gate()).to(dev)
+    out = torch.empty((n, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(L.handle.prefill_workspace_bytes(args.prefill_chunk) // 4 + 64, dtype=torch.int32, device=dev)
+    snap = L.snapshot()
+    times = []
+    for it in range(args.warmup + args.steps):
+        L.restore(snap)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        L.prefill(seq, kk, vv, qq, gate, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            times.append(e0.elapsed_time(e1) * 1e-3)
+    t_call = float(np.median(times))
+    log(f"prefill of {n} tokens: median {t_call * 1e3:.3f} ms over {len(times)} calls "
+        f"(min {min(times) * 1e3:.3f}, max {max(times) * 1e3:.3f})")
+    result = {
+        "metric": f"SPLA chunked-prefill tokens/s ({n} tokens onto {max(w.t0)} context, GQA "
+                  f"{w.n_q_heads}/{w.n_kv_heads}x{w.head_dim})",
+        "value": n / t_call, "unit": "tokens/s", "n_gpus": 1, "steps": len(times), "warmup": args.warmup,
+        "ms_per_call": t_call * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.kv_dtype, "data": "synthetic (seeded; see workloads/)",
+        "config": {"workload": w.name, "mode": "prefill", "prefill_tokens": n, "group": args.prefill_chunk,
+                   "context": max(w.t0), "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size, "top_k": w.top_k,
+                   "rla_output": RLA_FORMS[args.rla_form]},
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +247,9 @@ def main() -> int:
                     help="selector placement: -1 automatic, 0 stand-alone kernel, 1 fused into attend")
     ap.add_argument("--rla-form", type=int, default=0, choices=sorted(RLA_FORMS),
                     help="output form of the RLA branch: 0 plain, 1 normalised (o_rla / D), 2 RMS-normalised")
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="time chunked prefill of this many tokens instead of decode steps")
+    ap.add_argument("--prefill-chunk", type=int, default=256, help="tokens per group of prefill launches")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -190,6 +259,8 @@ def main() -> int:
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
         log("WORLD_SIZE > 1 is not supported")
         return 2
+    if args.prefill > 0:
+        return run_prefill(args)
 
     import numpy as np
     import torch
