@@ -24,16 +24,15 @@ __device__ __forceinline__ int sel_bucket(float x, float lo, float scale) {
   return f >= 255.f ? 255 : (f <= 0.f ? 0 : (int)f);
 }
 
-// LDS of the selector (the ranking list is padded with sentinels so the rank
-// counts read it four at a time)
+// LDS of the selector (the ranking and chosen lists are padded with sentinels
+// so the rank and position counts read them four at a time)
 struct __attribute__((aligned(16))) SelectLds {
   int hist[4][256];  // one histogram per wavefront
-  uint32_t bits[(kSelMax + 31) / 32 + 3];  // chosen candidates (bit i: candidate i)
-  int pre[(kSelMax + 31) / 32];            // chosen candidates in the words before word w
-  int s_wt[2][4];
-  float mkey[kSelRank];
-  int midx[kSelRank];
-  int mpage[kSelRank];     // page of midx[i]
+  float mkey[kSelRank + 4];  // ranking list: keys of the threshold bucket
+  int midx[kSelRank + 4];    // their candidate indices
+  int mpage[kSelRank];       // page of midx[i]
+  int cid[kThreads + 4];     // chosen list: candidate indices (top_k - 2 <= 254 entries)
+  int cpg[kThreads];         // page of cid[i]
   float s_mn[4], s_mx[4];
   int s_cnt[4];
   int s_bt, s_above, s_cbt, s_nm;
@@ -90,8 +89,10 @@ __device__ __forceinline__ void select_pages(const int32_t* block_table, int max
 // same way until it holds at most kSelRank candidates (then ranked exactly by
 // (score desc, id asc)) or only equal scores (then taken by ascending id).
 // The bucket index is a monotone function of the score, so the result is the
-// exact top k'.  The chosen ids are put in ascending order by counting, for
-// each, the chosen candidates with a smaller index in a bitmap of the set.
+// exact top k'.  The k' chosen candidates are gathered in a list (those above
+// the threshold bucket by reserved places, the threshold bucket's picks at
+// their rank), and each one's ascending output position is the count of
+// chosen candidates with a smaller index.
 //
 // Requires nb > top_k and the keys of select_load; every thread of the
 // workgroup must call it.  For each output position pos in [0, top_k),
@@ -109,11 +110,16 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
   if (threadIdx.x == 0) L.s_nm = 0;
   L.mkey[threadIdx.x] = -INFINITY;
   L.midx[threadIdx.x] = 0x7fffffff;
-  for (int i = threadIdx.x; i < (nc + 31) / 32 + 3; i += kThreads) L.bits[i] = 0u;
-  // the counters and sentinels above are used by every wavefront (the loop
-  // below may not run at all); this barrier waits on LDS only, not on the
-  // score loads in flight
-  __syncthreads();
+  L.cid[threadIdx.x] = 0x7fffffff;
+  if (threadIdx.x < 4) {
+    L.mkey[kSelRank + threadIdx.x] = -INFINITY;
+    L.midx[kSelRank + threadIdx.x] = 0x7fffffff;
+    L.cid[kThreads + threadIdx.x] = 0x7fffffff;
+  }
+  // the counters and sentinels above are used by every wavefront after the
+  // bucket loop; its first barrier orders them when it runs (more than
+  // kSelRank candidates), otherwise this one does (nc is uniform)
+  if (nc <= kSelRank) __syncthreads();
   int need = kp;
   bool equal_mode = false;
   // members of the threshold bucket: all candidates at first, then the count
@@ -206,32 +212,38 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
     above |= low;
     memb = 0;
   }
-  // every key above a threshold bucket (or taken by id) is chosen: its bit
-  // goes into the bitmap (an LDS atomic with no return).  The threshold
-  // bucket's keys go to the ranking list: lanes count theirs, one LDS atomic
-  // per wavefront reserves the places, then every lane stores its own.
+  // every key above a threshold bucket (or taken by id) goes to the chosen
+  // list, the threshold bucket's keys to the ranking list: lanes count theirs
+  // (both counts packed in one int, members in the low 16 bits), one LDS
+  // atomic per wavefront reserves the places in both, then every lane stores
+  // its own
   {
-    const int mine = __popcll((uint64_t)memb);
-    const int incl = wave_incl_scan_i(mine);
+    const int packed = (__popcll((uint64_t)above) << 16) | __popcll((uint64_t)memb);
+    const int incl = wave_incl_scan_i(packed);
     int base = 0;
-    if (lane == 63 && incl > 0) base = atomicAdd(&L.s_nm, incl);  // lane 63: the wavefront's total
-    int p = __builtin_amdgcn_readlane(base, 63) + incl - mine;
+    if (lane == 63 && incl > 0) base = atomicAdd(&L.s_nm, incl);  // lane 63: the wavefront's totals
+    const int b0 = __builtin_amdgcn_readlane(base, 63) + incl - packed;
+    int pa = b0 >> 16, pm = b0 & 0xffff;
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
       const int i = threadIdx.x + u * kThreads;
-      if ((above >> u) & 1) atomicOr(&L.bits[i >> 5], 1u << (i & 31));
+      if ((above >> u) & 1) {
+        L.cid[pa] = i;
+        L.cpg[pa] = k.pg[u];
+        ++pa;
+      }
       if ((memb >> u) & 1) {
-        L.mkey[p] = k.x[u];
-        L.midx[p] = i;
-        L.mpage[p] = k.pg[u];
-        ++p;
+        L.mkey[pm] = k.x[u];
+        L.midx[pm] = i;
+        L.mpage[pm] = k.pg[u];
+        ++pm;
       }
     }
   }
   __syncthreads();
-  // the final bucket (<= kSelRank candidates): exact rank by (score desc, id asc)
-  const int nm = L.s_nm;
-  int took = -1, took_pg = 0;
+  // the final bucket (<= kSelRank candidates): exact rank by (score desc, id
+  // asc); the first `need` go to the chosen list after the na keys above it
+  const int nm = L.s_nm & 0xffff, na = L.s_nm >> 16;  // na + need == kp
   if (nm > 0) {
     if ((int)threadIdx.x < nm) {
       const float xv = L.mkey[threadIdx.x];
@@ -247,70 +259,23 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
         rank += (y.w > xv) || (y.w == xv && iy.w < my);
       }
       if (rank < need) {
-        took = my;
-        took_pg = L.mpage[threadIdx.x];
-        atomicOr(&L.bits[my >> 5], 1u << (my & 31));
+        L.cid[na + rank] = my;
+        L.cpg[na + rank] = L.mpage[threadIdx.x];
       }
     }
     __syncthreads();
   }
-  // exclusive prefix counts of the bitmap words (a block-wide scan over at
-  // most 2 * 256 words), then the output position of chosen candidate i is
-  // 1 + the chosen candidates below it
-  const int nw = (nc + 31) / 32;
-  if (nw <= 128) {
-    // one wavefront: two words per lane
-    if (wv == 0) {
-      const int c0 = 2 * lane < nw ? __popc(L.bits[2 * lane]) : 0;
-      const int c1 = 2 * lane + 1 < nw ? __popc(L.bits[2 * lane + 1]) : 0;
-      const int ex = wave_incl_scan_i(c0 + c1) - (c0 + c1);
-      if (2 * lane < nw) L.pre[2 * lane] = ex;
-      if (2 * lane + 1 < nw) L.pre[2 * lane + 1] = ex + c0;
+  // output position of chosen entry t: 1 + the chosen candidates with a
+  // smaller index (the list is padded with sentinels past kp)
+  if ((int)threadIdx.x < kp) {
+    const int my = L.cid[threadIdx.x];
+    int pos = 1;
+    for (int v = 0; v < kp; v += 4) {
+      const int4 c = *reinterpret_cast<const int4*>(&L.cid[v]);
+      pos += (c.x < my) + (c.y < my) + (c.z < my) + (c.w < my);
     }
-    __syncthreads();
-  } else {
-    const int w0 = threadIdx.x, w1 = threadIdx.x + kThreads;
-    const int c0 = w0 < nw ? __popc(L.bits[w0]) : 0;
-    const int c1 = w1 < nw ? __popc(L.bits[w1]) : 0;
-    const int i0 = wave_incl_scan_i(c0), i1 = wave_incl_scan_i(c1);
-    if (lane == 63) {
-      L.s_wt[0][wv] = i0;
-      L.s_wt[1][wv] = i1;
-    }
-    __syncthreads();
-    int off0 = 0, off1 = 0, tot0 = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tot0 += L.s_wt[0][q];
-      off0 += q < wv ? L.s_wt[0][q] : 0;
-      off1 += q < wv ? L.s_wt[1][q] : 0;
-    }
-    if (w0 < nw) L.pre[w0] = off0 + i0 - c0;
-    if (w1 < nw) L.pre[w1] = tot0 + off1 + i1 - c1;
-    __syncthreads();
+    emit(pos, my + 1, L.cpg[threadIdx.x]);
   }
-  auto position = [&](int i) { return 1 + L.pre[i >> 5] + __popc(L.bits[i >> 5] & ((1u << (i & 31)) - 1u)); };
-  // positions of this thread's chosen keys: every read issued first (indices
-  // clamped into the bitmap), one wait, then the emits
-  {
-    int pw[KPT];
-    uint32_t bw[KPT];
-    const int last = max(nw - 1, 0);
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int wd = min((int)(threadIdx.x + u * kThreads) >> 5, last);
-      pw[u] = L.pre[wd];
-      bw[u] = L.bits[wd];
-    }
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      if ((above >> u) & 1) {
-        const int i = threadIdx.x + u * kThreads;
-        emit(1 + pw[u] + __popc(bw[u] & ((1u << (i & 31)) - 1u)), i + 1, k.pg[u]);
-      }
-    }
-  }
-  if (took >= 0) emit(position(took), took + 1, took_pg);
   if (threadIdx.x == 0) emit(0, 0, k.pg_sink);
   if (threadIdx.x == kThreads - 1) emit(kp + 1, nb - 1, k.pg_cur);
 }
