@@ -5,7 +5,7 @@
 // before the chunk, S_0; this kernel adds the chunk's own tokens up to t:
 //   o_bar_t += sum_{i <= t} (phi(q_t) . phi(k_i)) v_i,   phi(q_t).z += sum_{i <= t} phi(q_t) . phi(k_i),
 // into the first row chunk of the o_bar / phi(q).z partials the combine sums.
-#include "decode_common.h"
+#include "attend_mfma.h"
 
 namespace spla {
 
@@ -90,6 +90,368 @@ hipError_t launch_chunk_la(const DecodeArgs& a, bool bf16, const void* k_new, co
                                              a.dz_part, a.G, a.H))
   SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_chunk_la<false, RR, DD>, grid, l, k_new, v_new, a.q, a.obar_part,
                                            a.dz_part, a.G, a.H))
+}
+
+}  // namespace spla
+
+// ====================================================================
+// Block-centric attend of a prefill group (bf16 K/V, matrix cores).  The
+// group's m virtual queries select up to top_k blocks each; a block chosen by
+// several of them is read once per work item of up to kPfQ queries instead of
+// once per (query, slot).  Three launches:
+//   k_pf_bucket  files every (query, slot) under its block: lists[g][j][cap]
+//   k_pf_items   turns the non-empty lists into work items (KV head, block,
+//                page, up to kPfQ query codes) and clears the counts
+//   k_pf_attend  one item per workgroup: the block's K tile in registers
+//                (with phi(K) hi / lo), its V tile transposed in LDS, the
+//                item's queries staged in LDS, then per query the same
+//                products and partial record as the decode attend
+// A query code is vq * 256 + slot.
+namespace spla {
+
+namespace {
+
+// grid (ceil(G * max_blocks / 256)): the per-block counts start at zero
+__global__ __launch_bounds__(kThreads) void k_pf_clear(int32_t* cnt, int32_t n) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) cnt[i] = 0;
+}
+
+// grid (m, G): thread = slot of query vq
+__global__ __launch_bounds__(kThreads) void k_pf_bucket(const int32_t* sel, int32_t* cnt, int32_t* lists,
+                                                         int32_t* n_items, int32_t G, int32_t top_k,
+                                                         int32_t max_blocks, int32_t cap) {
+  const int vq = blockIdx.x, g = blockIdx.y, s = threadIdx.x;
+  if (vq == 0 && g == 0 && s == 0) *n_items = 0;
+  if (s >= top_k) return;
+  const int j = sel[((size_t)vq * G + g) * top_k + s];
+  if (j < 0 || j >= max_blocks) return;
+  const size_t cell = (size_t)g * max_blocks + j;
+  const int idx = atomicAdd(&cnt[cell], 1);  // < cap: a query selects a block at most once
+  if (idx < cap) lists[cell * cap + idx] = vq * 256 + s;
+}
+
+// grid (ceil(max_blocks / 256), G): thread = block j; items of kPfQ codes
+__global__ __launch_bounds__(kThreads) void k_pf_items(int32_t* cnt, const int32_t* lists, int4* items,
+                                                        int32_t* n_items, const int32_t* block_table, int32_t G,
+                                                        int32_t max_blocks, int32_t cap, int32_t max_items) {
+  const int j = blockIdx.x * kThreads + threadIdx.x, g = blockIdx.y;
+  const int lane = threadIdx.x % 64;
+  const size_t cell = (size_t)g * max_blocks + j;
+  const int c = j < max_blocks ? min(cnt[cell], cap) : 0;
+  const int nch = (c + kPfQ - 1) / kPfQ;
+  const int incl = wave_incl_scan_i(nch);
+  int base = 0;
+  if (lane == 63 && incl > 0) base = atomicAdd(n_items, incl);
+  base = __builtin_amdgcn_readlane(base, 63) + incl - nch;
+  if (c == 0) return;
+  const int page = block_table[j];
+  for (int i = 0; i < nch && base + i < max_items; ++i) {  // max_items bounds the sum of nch
+    const int n = min(kPfQ, c - i * kPfQ);
+    int code[kPfQ];
+#pragma unroll
+    for (int e = 0; e < kPfQ; ++e) code[e] = e < n ? lists[cell * cap + i * kPfQ + e] : 0;
+    int4* it = items + (size_t)(base + i) * kPfItemInts / 4;
+    it[0] = make_int4(g, j, n, page);
+#pragma unroll
+    for (int e = 0; e < kPfQ; e += 4) it[1 + e / 4] = make_int4(code[e], code[e + 1], code[e + 2], code[e + 3]);
+  }
+  cnt[cell] = 0;
+}
+
+// one work item per workgroup (grid: an upper bound of the item count)
+template <int R, int D, int BK>
+__global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const int32_t* n_items,
+                                                         const DecodeArgs a) {
+  constexpr int NKS = D / 32;              // k-steps per channel block
+  constexpr int NT1W = BK / 64;            // 16-token tiles per wavefront
+  constexpr int WB = R <= 4 ? 4 : 8;       // first linear-weight row of product (1)
+  constexpr int NT2W = D / 64;             // 16-channel tiles per wavefront
+  constexpr int MT2 = (4 * R + 15) / 16;   // row tiles of product (2): hi/lo rows of p and w
+  constexpr int KS2 = BK / 32;             // token k-steps of product (2)
+  constexpr int VS = BK + 8;               // row stride (elements) of the transposed V tile
+  constexpr int PS = BK + 8;               // row stride of the p / w rows
+  constexpr int NV = BK * D / (16 * kThreads);  // token-pair x 8-channel pieces per thread
+  constexpr int QE = R * 3 * D;            // staged elements per query: raw q, phi(q) hi, lo per head
+  __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t pw[MT2 * 16 * PS];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[kPfQ * QE];
+  __shared__ float s_max[4][R], s_l[4][R], s_sw[4][R];
+  __shared__ int s_code[kPfQ];
+  // the item (the array holds max_items records, so any workgroup may read
+  // its own) and the count, in one round trip
+  const int4* itp = items + (size_t)blockIdx.x * kPfItemInts / 4;
+  const int* codes = reinterpret_cast<const int*>(itp) + 4;  // kPfQ codes (0 past n)
+  const int4 hd = itp[0];
+  const int my_code = codes[min((int)threadIdx.x, kPfQ - 1)];  // first of all vector loads
+  __builtin_amdgcn_sched_barrier(0);
+  SPLA_SCALARS_READY("s"(a.q), "s"(a.phq), "s"(a.H), "s"(a.k_pages), "s"(a.v_pages), "s"(a.G), "s"(a.num_pages));
+  if ((int)blockIdx.x >= *n_items) return;
+  const int g = hd.x, j = hd.y, n = hd.z, page = hd.w;
+  if (page < 0 || page >= a.num_pages) {
+    if (threadIdx.x == 0) atomicOr(a.err, kErrPage);
+    return;
+  }
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64, l16 = lane % 16, lg4 = lane / 16;
+  const int m = l16;  // A-operand row of this lane in product (1)
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k_pages) + ((size_t)page * a.G + g) * BK * D;
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v_pages) + ((size_t)page * a.G + g) * BK * D;
+  // ---- every global load first: K operands, V pieces, the item's queries
+  uint4 kraw[NT1W][NKS];
+#pragma unroll
+  for (int nt = 0; nt < NT1W; ++nt) {
+    const int tok = (w * NT1W + nt) * 16 + l16;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      kraw[nt][ks] = *reinterpret_cast<const uint4*>(kp + (size_t)tok * D + 32 * ks + 8 * lg4);
+  }
+  uint4 vr[NV][2];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = threadIdx.x + kThreads * i;
+    const int tp = idx % (BK / 2), cg = idx / (BK / 2);
+    vr[i][0] = *reinterpret_cast<const uint4*>(vp + (size_t)(2 * tp) * D + 8 * cg);
+    vr[i][1] = *reinterpret_cast<const uint4*>(vp + (size_t)(2 * tp + 1) * D + 8 * cg);
+  }
+  // the codes through LDS (each piece needs the code of its own query), then
+  // the item's queries: q and phi(q) hi / lo, staged for every query of the loop
+  if (threadIdx.x < kPfQ) s_code[threadIdx.x] = my_code;
+  __syncthreads();
+  constexpr int QPT = (kPfQ * QE / 8 + kThreads - 1) / kThreads;  // 8-element pieces per thread
+  static_assert(QPT <= 12, "at most 12 staged query pieces per thread");
+  // piece i of this thread: q (kind 0) or phi(q) hi / lo (kind 1, 2) of head h
+  // of the item's query e, 8 channels; pieces past the end repeat the last
+  auto pidx = [&](int i) { return min((int)threadIdx.x + kThreads * i, kPfQ * QE / 8 - 1); };
+  // the code of each piece's query first (a code past n is 0: query 0, read
+  // and unused), then every load; named registers, not arrays (an array here
+  // ends up in scratch)
+  auto code_of = [&](int i) { return s_code[pidx(i) / (QE / 8)]; };
+  const int k0 = code_of(0), k1 = QPT > 1 ? code_of(1) : 0, k2 = QPT > 2 ? code_of(2) : 0;
+  const int k3 = QPT > 3 ? code_of(3) : 0, k4 = QPT > 4 ? code_of(4) : 0, k5 = QPT > 5 ? code_of(5) : 0;
+  const int k6 = QPT > 6 ? code_of(6) : 0, k7 = QPT > 7 ? code_of(7) : 0, k8 = QPT > 8 ? code_of(8) : 0;
+  const int k9 = QPT > 9 ? code_of(9) : 0, k10 = QPT > 10 ? code_of(10) : 0, k11 = QPT > 11 ? code_of(11) : 0;
+  const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q);
+  const uint16_t* fbase = a.phq;
+  const int H = a.H;
+  auto piece = [&](int i, int cd) {
+    const int rem = pidx(i) % (QE / 8);
+    const int h = rem / (3 * D / 8), rem2 = rem % (3 * D / 8);
+    const int kind = rem2 / (D / 8), c8 = rem2 % (D / 8);
+    const size_t row = (size_t)(cd >> 8) * H + g * R + h;
+    const uint16_t* src = kind == 0 ? qbase + row * D : fbase + (row * 2 + (kind - 1)) * D;
+    return *reinterpret_cast<const uint4*>(src + 8 * c8);
+  };
+  const uint4 q0 = piece(0, k0);
+  const uint4 q1 = QPT > 1 ? piece(1, k1) : q0, q2 = QPT > 2 ? piece(2, k2) : q0, q3 = QPT > 3 ? piece(3, k3) : q0;
+  const uint4 q4 = QPT > 4 ? piece(4, k4) : q0, q5 = QPT > 5 ? piece(5, k5) : q0, q6 = QPT > 6 ? piece(6, k6) : q0;
+  const uint4 q7 = QPT > 7 ? piece(7, k7) : q0, q8 = QPT > 8 ? piece(8, k8) : q0, q9 = QPT > 9 ? piece(9, k9) : q0;
+  const uint4 q10 = QPT > 10 ? piece(10, k10) : q0, q11 = QPT > 11 ? piece(11, k11) : q0;
+  __builtin_amdgcn_sched_barrier(0);
+  SPLA_SCALARS_READY("s"(a.bk), "s"(a.top_k), "s"(a.part), "s"(a.inv_sqrt_d), "s"(a.H), "s"(a.B));
+  // rows of the tile past the group's last token: never attended, zeroed so
+  // that 0 x (stale data) cannot make NaN
+  const int nvalid = min(BK, a.lens[a.B - 1] - j * BK);
+  if constexpr (R < 4) {
+    for (int i = threadIdx.x; i < MT2 * 16 * PS / 2; i += kThreads) reinterpret_cast<uint32_t*>(pw)[i] = 0u;
+  }
+  {
+    // clamped like the loads: a repeated piece rewrites the same value
+    uint4* qd = reinterpret_cast<uint4*>(qs);
+    auto put = [&](int i, const uint4& v) { qd[min((int)threadIdx.x + kThreads * i, kPfQ * QE / 8 - 1)] = v; };
+    put(0, q0);
+    if (QPT > 1) put(1, q1);
+    if (QPT > 2) put(2, q2);
+    if (QPT > 3) put(3, q3);
+    if (QPT > 4) put(4, q4);
+    if (QPT > 5) put(5, q5);
+    if (QPT > 6) put(6, q6);
+    if (QPT > 7) put(7, q7);
+    if (QPT > 8) put(8, q8);
+    if (QPT > 9) put(9, q9);
+    if (QPT > 10) put(10, q10);
+    if (QPT > 11) put(11, q11);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int idx = threadIdx.x + kThreads * i;
+    const int tp = idx % (BK / 2), cg = idx / (BK / 2);
+    const bool v0 = 2 * tp < nvalid, v1 = 2 * tp + 1 < nvalid;
+    const uint32_t r0[4] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w};
+    const uint32_t r1[4] = {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
+    uint32_t* dst = reinterpret_cast<uint32_t*>(vt) + (size_t)(8 * cg) * (VS / 2) + tp;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t a0 = v0 ? r0[k] : 0u, a1 = v1 ? r1[k] : 0u;
+      dst[(2 * k) * (VS / 2)] = (a0 & 0xffffu) | (a1 << 16);
+      dst[(2 * k + 1) * (VS / 2)] = (a0 >> 16) | (a1 & 0xffff0000u);
+    }
+  }
+  // phi(K) of the tile as bf16 hi + lo, once for every query
+  uint4 fkh[NT1W][NKS], fkl[NT1W][NKS];
+#pragma unroll
+  for (int nt = 0; nt < NT1W; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) phi_bf16_split(kraw[nt][ks], fkh[nt][ks], fkl[nt][ks]);
+  __syncthreads();
+  const bool is_q = m < R, is_w = m >= WB && m < WB + R;
+  const int hq = is_q ? m : 0, hw = is_w ? m - WB : 0;
+  const uint32_t mq = is_q ? 0xffffffffu : 0u, mw = is_w ? 0xffffffffu : 0u;
+  const float inv_sqrt_d = a.inv_sqrt_d;
+  const int rec = 2 * D + kPartHdr;
+  for (int e = 0; e < n; ++e) {
+    const int cd = s_code[e];
+    const int vq = cd >> 8, slot = cd & 255;
+    const uint16_t* qe = qs + e * QE;
+    // ---- A operands of product (1) from the staged query
+    uint4 aq[NKS], afh[NKS], afl[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(qe + (hq * 3 + 0) * D + 32 * ks + 8 * lg4);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(qe + (hw * 3 + 1) * D + 32 * ks + 8 * lg4);
+      const uint4 x2 = *reinterpret_cast<const uint4*>(qe + (hw * 3 + 2) * D + 32 * ks + 8 * lg4);
+      aq[ks] = make_uint4(x0.x & mq, x0.y & mq, x0.z & mq, x0.w & mq);
+      afh[ks] = make_uint4(x1.x & mw, x1.y & mw, x1.z & mw, x1.w & mw);
+      afl[ks] = make_uint4(x2.x & mw, x2.y & mw, x2.z & mw, x2.w & mw);
+    }
+    // ---- product (1): logits and linear weights of this wavefront's tokens
+    f32x4_t c1[NT1W];
+#pragma unroll
+    for (int nt = 0; nt < NT1W; ++nt) {
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        c = mfma_bf16(aq[ks], kraw[nt][ks], c);
+        c = mfma_bf16(afh[ks], fkh[nt][ks], c);
+        c = mfma_bf16(afl[ks], fkh[nt][ks], c);
+        c = mfma_bf16(afh[ks], fkl[nt][ks], c);
+      }
+      c1[nt] = c;
+    }
+    const int ntok = min(BK, a.lens[vq] - j * BK);
+    float mloc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int nt = 0; nt < NT1W; ++nt) {
+      const int tok = (w * NT1W + nt) * 16 + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * lg4 + i;
+        if (row < R && tok < ntok) mloc[i] = fmaxf(mloc[i], c1[nt][i] * inv_sqrt_d);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mloc[i] = row16_max(mloc[i]);
+    if (l16 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * lg4 + i;
+        if (row < R) s_max[w][row] = mloc[i];
+      }
+    }
+    __syncthreads();
+    // ---- p = exp(s - m) and w, split hi/lo, into the rows of product (2)
+    float lsum[4] = {0.f, 0.f, 0.f, 0.f}, wsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < NT1W; ++nt) {
+      const int tok = (w * NT1W + nt) * 16 + l16;
+      const bool valid = tok < ntok;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * lg4 + i;
+        int kind = -1, h = 0;
+        float x = 0.f;
+        if (row < R) {
+          h = row;
+          const float mh = fmaxf(fmaxf(s_max[0][h], s_max[1][h]), fmaxf(s_max[2][h], s_max[3][h]));
+          x = valid ? __expf(c1[nt][i] * inv_sqrt_d - mh) : 0.f;
+          lsum[i] += x;
+          kind = 0;
+        } else if (row >= WB && row < WB + R) {
+          h = row - WB;
+          x = valid ? c1[nt][i] : 0.f;
+          wsum[i] += x;
+          kind = 1;
+        }
+        if (kind >= 0) {
+          const uint32_t hb = pack_bf16(x, 0.f) & 0xffffu;
+          const uint32_t lb = pack_bf16(x - bf16_lo_f(hb), 0.f) & 0xffffu;
+          const int rh = 2 * (kind * R + h);
+          pw[rh * PS + tok] = (uint16_t)hb;
+          pw[(rh + 1) * PS + tok] = (uint16_t)lb;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lsum[i] = row16_sum(lsum[i]);
+      wsum[i] = row16_sum(wsum[i]);
+    }
+    if (l16 == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * lg4 + i;
+        if (row < R) s_l[w][row] = lsum[i];
+        if (row >= WB && row < WB + R) s_sw[w][row - WB] = wsum[i];
+      }
+    }
+    __syncthreads();
+    // ---- product (2) and the partial record of (vq, slot)
+    float* part0 = a.part + (((size_t)vq * a.H + g * R) * a.top_k + slot) * rec;
+#pragma unroll
+    for (int nt2 = 0; nt2 < NT2W; ++nt2) {
+      const int ch = (w * NT2W + nt2) * 16 + l16;
+#pragma unroll
+      for (int mt = 0; mt < MT2; ++mt) {
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS2; ++ks) {
+          const uint4 av = *reinterpret_cast<const uint4*>(&pw[(mt * 16 + l16) * PS + 32 * ks + 8 * lg4]);
+          const uint4 bv = *reinterpret_cast<const uint4*>(&vt[ch * VS + 32 * ks + 8 * lg4]);
+          c = mfma_bf16(av, bv, c);
+        }
+#pragma unroll
+        for (int ee = 0; ee < 2; ++ee) {
+          const int pi = 8 * mt + 2 * lg4 + ee;
+          if (pi < 2 * R) {
+            const int kind = pi / R, h = pi % R;
+            part0[(size_t)h * a.top_k * rec + kPartHdr + (kind ? D : 0) + ch] = c[2 * ee] + c[2 * ee + 1];
+          }
+        }
+      }
+    }
+    if (threadIdx.x < R) {
+      const int h = threadIdx.x;
+      float* dst = part0 + (size_t)h * a.top_k * rec;
+      dst[0] = fmaxf(fmaxf(s_max[0][h], s_max[1][h]), fmaxf(s_max[2][h], s_max[3][h]));
+      dst[1] = (s_l[0][h] + s_l[1][h]) + (s_l[2][h] + s_l[3][h]);
+      dst[2] = (s_sw[0][h] + s_sw[1][h]) + (s_sw[2][h] + s_sw[3][h]);
+      dst[3] = 0.f;
+    }
+    __syncthreads();  // s_max / pw / s_l are rewritten by the next query
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pf_clear(const PfBuffers& pb, int G, int max_blocks, const Launch& l) {
+  const int n = G * max_blocks;
+  return launch_kernel(k_pf_clear, dim3((n + kThreads - 1) / kThreads), l, pb.cnt, n);
+}
+
+hipError_t launch_pf_attend(const DecodeArgs& a, const PfBuffers& pb, const Launch& l) {
+  hipError_t e = launch_kernel(k_pf_bucket, dim3(a.B, a.G), l, a.sel, pb.cnt, pb.lists, pb.n_items, a.G, a.top_k,
+                               a.max_blocks, pb.cap);
+  if (e != hipSuccess) return e;
+  e = launch_kernel(k_pf_items, dim3((a.max_blocks + kThreads - 1) / kThreads, a.G), l, pb.cnt,
+                    static_cast<const int32_t*>(pb.lists), pb.items, pb.n_items, a.block_table, a.G, a.max_blocks,
+                    pb.cap, pb.max_items);
+  if (e != hipSuccess) return e;
+  const dim3 grid(pb.max_items);
+  if (a.bk == 64)
+    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_pf_attend<RR, DD, 64>, grid, l,
+                                             static_cast<const int4*>(pb.items), static_cast<const int32_t*>(pb.n_items), a))
+  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_pf_attend<RR, DD, 128>, grid, l,
+                                           static_cast<const int4*>(pb.items), static_cast<const int32_t*>(pb.n_items), a))
 }
 
 }  // namespace spla

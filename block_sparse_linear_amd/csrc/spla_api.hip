@@ -65,6 +65,33 @@ WsLayout ws_layout(const spla_config& c, int n_tiles, size_t nq) {
   return w;
 }
 
+// a prefill workspace for groups of `chunk` tokens: the per-query scratch of
+// ws_layout, then the block-centric attend's per-block lists and work items
+struct PfLayout {
+  WsLayout q;
+  size_t cnt, lists, items, n_items, bytes;
+  int32_t max_items;
+};
+
+PfLayout pf_layout(const spla_config& c, int n_tiles, int chunk) {
+  PfLayout p;
+  p.q = ws_layout(c, n_tiles, chunk);
+  const size_t G = c.n_kv_heads, MB = c.max_blocks_per_seq, k = c.top_k;
+  const size_t pairs = (size_t)chunk * k;  // (query, slot) pairs per KV head
+  p.max_items = (int32_t)(G * ((pairs + kPfQ - 1) / kPfQ + (pairs < MB ? pairs : MB)));
+  size_t off = p.q.bytes;
+  p.cnt = off;
+  off = align256(off + G * MB * sizeof(int32_t));
+  p.lists = off;
+  off = align256(off + G * MB * (size_t)chunk * sizeof(int32_t));
+  p.items = off;
+  off = align256(off + (size_t)p.max_items * kPfItemInts * sizeof(int32_t));
+  p.n_items = off;
+  off = align256(off + sizeof(int32_t));
+  p.bytes = off;
+  return p;
+}
+
 void layout(spla_handle* h) {
   const WsLayout w = ws_layout(h->cfg, h->n_tiles, h->cfg.batch);
   h->off_lg = w.lg;
@@ -487,7 +514,7 @@ spla_status spla_set_tuning(spla_handle* h, int32_t key, int32_t value) {
 
 size_t spla_prefill_workspace_bytes(const spla_handle* h, int32_t chunk) {
   if (!h || chunk < 1 || chunk > kMaxBatch) return 0;
-  return ws_layout(h->cfg, h->n_tiles, chunk).bytes;
+  return pf_layout(h->cfg, h->n_tiles, chunk).bytes;
 }
 
 spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_new, const void* v_new, const void* q,
@@ -506,9 +533,10 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
   if ((int64_t)h->lens[seq] + n > (int64_t)c.max_blocks_per_seq * c.block_size) return SPLA_ERR_CAPACITY;
   if ((int64_t)n > (int64_t)INT32_MAX / (c.n_q_heads * c.head_dim)) return SPLA_ERR_INVALID_ARG;
   int chunk = kMaxBatch;  // virtual queries per launch: the most the workspace holds
-  while (chunk > 0 && ws_layout(c, h->n_tiles, chunk).bytes > workspace_bytes) --chunk;
+  while (chunk > 0 && pf_layout(c, h->n_tiles, chunk).bytes > workspace_bytes) --chunk;
   if (chunk == 0) return SPLA_ERR_INVALID_ARG;
-  const WsLayout wl = ws_layout(c, h->n_tiles, chunk);
+  const PfLayout pl = pf_layout(c, h->n_tiles, chunk);
+  const WsLayout& wl = pl.q;
   const bool bf16 = c.kv_dtype == SPLA_BF16;
   const size_t es = bf16 ? 2 : 4;
   const size_t G = c.n_kv_heads, H = c.n_q_heads, d = c.head_dim;
@@ -516,6 +544,17 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
   const Launch l{reinterpret_cast<hipStream_t>(stream), nullptr, nullptr};
   char* wsb = static_cast<char*>(workspace);
   const int chunks = c.head_dim / (1024 / c.head_dim);
+  PfBuffers pb;
+  pb.cnt = reinterpret_cast<int32_t*>(wsb + pl.cnt);
+  pb.lists = reinterpret_cast<int32_t*>(wsb + pl.lists);
+  pb.items = reinterpret_cast<int4*>(wsb + pl.items);
+  pb.n_items = reinterpret_cast<int32_t*>(wsb + pl.n_items);
+  pb.cap = chunk;
+  pb.max_items = pl.max_items;
+  if (bf16) {
+    const hipError_t e = launch_pf_clear(pb, c.n_kv_heads, c.max_blocks_per_seq, l);
+    if (e != hipSuccess) return hip_fail(h, e);
+  }
   for (int c0 = 0; c0 < n; c0 += chunk) {
     const int m = n - c0 < chunk ? n - c0 : chunk;
     const int t0 = h->lens[seq];
@@ -573,7 +612,8 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
     if ((e = launch_score(sa, bf16, l)) != hipSuccess) return hip_fail(h, e);
     if ((e = launch_chunk_la(a, bf16, kc, vc, l)) != hipSuccess) return hip_fail(h, e);
     if ((e = launch_select(a, l)) != hipSuccess) return hip_fail(h, e);
-    if ((e = launch_attend(a, bf16, l)) != hipSuccess) return hip_fail(h, e);
+    // bf16: every selected block read once per item of up to kPfQ queries
+    if ((e = bf16 ? launch_pf_attend(a, pb, l) : launch_attend(a, bf16, l)) != hipSuccess) return hip_fail(h, e);
     if ((e = launch_combine(a, l)) != hipSuccess) return hip_fail(h, e);
     // (3) the chunk's tokens into S_all / z_all
     AppendArgs as;

@@ -140,6 +140,20 @@ hipError_t launch_select(const DecodeArgs& a, const Launch& l);
 hipError_t launch_attend(const DecodeArgs& a, bool bf16, const Launch& l);
 hipError_t launch_combine(const DecodeArgs& a, const Launch& l);
 hipError_t launch_step_score(const StepArgs& a, bool bf16, const Launch& l);
+// chunked prefill, block-centric attend (bf16): per-block lists of the
+// group's (query, slot) pairs and the work items made from them
+constexpr int kPfQ = 8;           // queries per work item
+constexpr int kPfItemInts = 16;   // g, j, n, page, kPfQ codes, padding
+struct PfBuffers {
+  int32_t* cnt;      // [G][max_blocks] (query, slot) pairs per block
+  int32_t* lists;    // [G][max_blocks][cap] codes vq * 256 + slot
+  int4* items;       // [max_items][kPfItemInts / 4]
+  int32_t* n_items;  // items of the current group
+  int32_t cap;       // queries per group (list capacity per block)
+  int32_t max_items;
+};
+hipError_t launch_pf_clear(const PfBuffers& pb, int G, int max_blocks, const Launch& l);
+hipError_t launch_pf_attend(const DecodeArgs& a, const PfBuffers& pb, const Launch& l);
 // chunked prefill: the chunk's own tokens added into the o_bar / phi(q).z
 // partials of its virtual queries (k_new / v_new address the chunk's first row)
 hipError_t launch_chunk_la(const DecodeArgs& a, bool bf16, const void* k_new, const void* v_new, const Launch& l);
