@@ -251,7 +251,10 @@ spla_status spla_set_rla_output(spla_handle *h, int32_t form, const float *gamma
  * be the handle's own workspace.  Each group appends its tokens' pages and
  * block statistics, decodes its tokens against the state before the group
  * (adding the group's own earlier tokens to the linear-attention sums), then
- * adds the group to S_all / z_all.
+ * adds the group to S_all / z_all.  With bf16 K/V the group's attention is
+ * block-centric: the (token, slot) pairs are filed under the blocks they
+ * selected (lists in the workspace) and each selected block's tiles are read
+ * once per 8 tokens that chose it.
  * Errors as for spla_append_kv (capacity, alignment, seq out of range);
  * n = 0 does nothing.  On SPLA_ERR_HIP the state of sequence seq is
  * undefined (part of the tokens may be in it). */
