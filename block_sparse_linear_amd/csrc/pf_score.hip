@@ -1,0 +1,196 @@
+// Block scorer of a chunked-prefill group on the matrix cores.  Every virtual
+// query (token) of the group is scored against every candidate block with the
+// decode scorer's log-domain second-order Taylor score (SPLA Technical Summary
+// 2.1, diagonal covariance):
+//   ls_h(j) = q_h . mu_j / sqrt(d) + log(1 + sum_c q_hc^2 var_jc / (2 d)),
+//   LG(j)   = logsumexp over the R query heads of the group,
+// or the first-order (mean-pooling) form.  Over a group both sums are matrix
+// products, [tokens x d] by [d x blocks] per query head, so one workgroup
+// reads a 64-block statistics tile once for 64 tokens instead of once per
+// token, and the fp32 matrix cores (16x16x4, fp32 in and out) do the
+// products at the full fp32 rate.
+#include "decode_common.h"
+
+namespace spla {
+
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float f4_at(const float4& v, int e) {
+  return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+
+// grid (score_tiles, G, ceil(m / 64)).  Wavefront w takes tokens 64 z + 16 w
+// .. + 15, the 16 rows of the A operand, against the 64 blocks of tile t as
+// four 16-column tiles (B operand = statistics, columns = blocks).  Channel
+// c = kk * KS + ks is contracted at k-step ks in k slot kk = lane / 16, so a
+// lane's query channels are contiguous and its statistics arrive as float4s
+// of one channel quartet of the tile layout (64 blocks side by side per
+// quartet).  Accumulators: column tile x query head x (mean, variance); with
+// eight query heads the column tiles go in two passes of two, so that the
+// accumulators stay in registers.
+template <bool BF16, int R, int D, bool TAYLOR>
+__global__ __launch_bounds__(kThreads) void k_pf_score(const float* mean, const float* var, const void* q,
+                                                        int32_t n_tiles, int32_t G, int32_t H, int32_t m,
+                                                        const DecodeArgs a) {
+  constexpr int KS = D / 4;            // k-steps, and channels per k slot
+  constexpr int KQ = KS / 4;           // channel quartets per k slot
+  constexpr int NP = R >= 8 ? 2 : 1;   // passes over the column tiles
+  constexpr int NC = 4 / NP;           // column tiles per pass
+  const int t = blockIdx.x, g = blockIdx.y;
+  const int w = threadIdx.x / 64, lane = threadIdx.x % 64, l16 = lane % 16, kk = lane / 16;
+  const int tok0 = 64 * blockIdx.z + 16 * w;  // first token of this wavefront
+  const int tok = min(tok0 + l16, m - 1);     // A row (rows past the group repeat the last token, never stored)
+
+  // ---- statistics loads of one channel quartet (all four column tiles)
+  const float4* mean4 = reinterpret_cast<const float4*>(mean);
+  const float4* var4 = reinterpret_cast<const float4*>(var);
+  const size_t base = ((size_t)g * n_tiles + t) * (size_t)(D / 4) * kTile + (size_t)(kk * KQ) * kTile + l16;
+  float4 bm[2][NC], bv[2][NC];
+  auto load_b = [&](int pass, int j, int buf) {
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      const size_t at = base + (size_t)j * kTile + 16 * (pass * NC + n);
+      bm[buf][n] = mean4[at];
+      bv[buf][n] = TAYLOR ? var4[at] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  load_b(0, 0, 0);
+
+  // ---- A: this lane's KS query channels of every head, as fp32
+  float qa[R][KS];
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    const size_t off = ((size_t)tok * H + g * R + h) * D + kk * KS;
+    if constexpr (BF16) {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + off);
+#pragma unroll
+      for (int i = 0; i < KS / 8; ++i) {
+        const uint4 u = p[i];
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qa[h][8 * i + 2 * e] = bf16_lo_f(wd[e]);
+          qa[h][8 * i + 2 * e + 1] = bf16_hi_f(wd[e]);
+        }
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q) + off);
+#pragma unroll
+      for (int i = 0; i < KS / 4; ++i) {
+        const float4 u = p[i];
+        qa[h][4 * i] = u.x;
+        qa[h][4 * i + 1] = u.y;
+        qa[h][4 * i + 2] = u.z;
+        qa[h][4 * i + 3] = u.w;
+      }
+    }
+  }
+  SPLA_SCALARS_READY("s"(a.bk), "s"(a.lg), "s"(a.lg_out), "s"(a.max_blocks), "s"(a.inv_sqrt_d));
+
+  const float half_inv_d = 0.5f / (float)D;
+  const size_t row = (size_t)n_tiles * kTile;
+#pragma unroll
+  for (int pass = 0; pass < NP; ++pass) {
+    // ---- products: quartet j of this pass's column tiles, the next quartet in flight
+    f32x4_t cm[NC][R], cv[NC][R];
+#pragma unroll
+    for (int n = 0; n < NC; ++n)
+#pragma unroll
+      for (int h = 0; h < R; ++h) cm[n][h] = cv[n][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KQ; ++j) {
+      if (j + 1 < KQ) load_b(pass, j + 1, (j + 1) & 1);
+      else if (pass + 1 < NP) load_b(pass + 1, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int h = 0; h < R; ++h) {
+          const float qk = qa[h][4 * j + e];
+          const float q2 = qk * qk;
+#pragma unroll
+          for (int n = 0; n < NC; ++n) {
+            cm[n][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(qk, f4_at(bm[j & 1][n], e), cm[n][h], 0, 0, 0);
+            if (TAYLOR)
+              cv[n][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(q2, f4_at(bv[j & 1][n], e), cv[n][h], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // ---- log scores, group logsumexp: lane holds tokens 4 kk + i, block 16 n + l16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tk = tok0 + 4 * kk + i;
+      if (tk >= m) continue;
+      const int nb = (a.lens[tk] + a.bk - 1) / a.bk;
+#pragma unroll
+      for (int n = 0; n < NC; ++n) {
+        float ls[R];
+#pragma unroll
+        for (int h = 0; h < R; ++h)
+          ls[h] = TAYLOR ? cm[n][h][i] * a.inv_sqrt_d + __logf(1.f + fmaxf(cv[n][h][i], 0.f) * half_inv_d)
+                         : cm[n][h][i] * a.inv_sqrt_d;
+        float lg = ls[0];
+        if constexpr (R > 1) {
+          float mx = ls[0];
+#pragma unroll
+          for (int h = 1; h < R; ++h) mx = fmaxf(mx, ls[h]);
+          float e[R];
+#pragma unroll
+          for (int h = 0; h < R; ++h) e[h] = __expf(ls[h] - mx);
+          // pairwise, in the decode scorer's order
+#pragma unroll
+          for (int st = 1; st < R; st *= 2)
+#pragma unroll
+            for (int h = 0; h < R; h += 2 * st) e[h] += e[h + st];
+          lg = mx + __logf(e[0]);
+        }
+        const int jb = t * kTile + 16 * (pass * NC + n) + l16;
+        const bool cand = jb >= 1 && jb <= nb - 2;
+        a.lg[((size_t)tk * G + g) * row + jb] = cand ? lg : -INFINITY;
+        if (a.lg_out && cand) a.lg_out[((size_t)tk * G + g) * a.max_blocks + jb] = lg;
+      }
+    }
+  }
+}
+
+// query heads x head dim up to 512: the A operand (R * D / 4 values per lane)
+// and the accumulators stay in registers
+constexpr int kPfScoreMaxRD = 512;
+
+template <bool BF16, bool TAYLOR>
+hipError_t launch_pf_score_form(const DecodeArgs& a, const Launch& l) {
+  const dim3 grid(a.score_tiles, a.G, (a.B + 63) / 64);
+#define SPLA_PF_SCORE_CASE(R_, D_)                                                                               \
+  case R_ * 1000 + D_:                                                                                         \
+    return launch_kernel(k_pf_score<BF16, R_, D_, TAYLOR>, grid, l, a.blk_mean, a.blk_var, a.q, a.n_tiles, a.G, \
+                         a.H, a.B, a);
+  switch (a.r * 1000 + a.d) {
+    SPLA_PF_SCORE_CASE(1, 64)
+    SPLA_PF_SCORE_CASE(1, 128)
+    SPLA_PF_SCORE_CASE(2, 64)
+    SPLA_PF_SCORE_CASE(2, 128)
+    SPLA_PF_SCORE_CASE(4, 64)
+    SPLA_PF_SCORE_CASE(4, 128)
+    SPLA_PF_SCORE_CASE(8, 64)
+  }
+#undef SPLA_PF_SCORE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool pf_score_supported(const DecodeArgs& a) { return a.r * a.d <= kPfScoreMaxRD; }
+
+// virtual queries only: a.B tokens of one sequence, whose statistics rows the
+// pointers address
+hipError_t launch_pf_score(const DecodeArgs& a, bool bf16, const Launch& l) {
+  if (!a.virtual_queries || a.score_tiles <= 0 || !pf_score_supported(a)) return hipErrorInvalidValue;
+  const bool mean = a.score_form == kScoreMean;
+  if (bf16) return mean ? launch_pf_score_form<true, false>(a, l) : launch_pf_score_form<true, true>(a, l);
+  return mean ? launch_pf_score_form<false, false>(a, l) : launch_pf_score_form<false, true>(a, l);
+}
+
+}  // namespace spla

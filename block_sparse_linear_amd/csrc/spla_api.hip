@@ -609,7 +609,17 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
     sa.st.blk_var = h->buf.blk_var + (size_t)seq * stats_row;
     sa.st.s_all = h->buf.s_all + (size_t)seq * G * d * d;
     sa.st.z_all = h->buf.z_all + (size_t)seq * G * d;
-    if ((e = launch_score(sa, bf16, l)) != hipSuccess) return hip_fail(h, e);
+    if (pf_score_supported(a)) {
+      // the group's block scores on the matrix cores, then the o_bar / phi(q)
+      // partials of the state rows (the first kernel's row chunks alone)
+      if (a.score_tiles > 0 && (e = launch_pf_score(a, bf16, l)) != hipSuccess) return hip_fail(h, e);
+      StepArgs rows = sa;
+      rows.dec.score_tiles = 0;
+      rows.dec.tiles_all = 0;
+      if ((e = launch_score(rows, bf16, l)) != hipSuccess) return hip_fail(h, e);
+    } else if ((e = launch_score(sa, bf16, l)) != hipSuccess) {
+      return hip_fail(h, e);
+    }
     if ((e = launch_chunk_la(a, bf16, kc, vc, l)) != hipSuccess) return hip_fail(h, e);
     if ((e = launch_select(a, l)) != hipSuccess) return hip_fail(h, e);
     // bf16: every selected block read once per item of up to kPfQ queries

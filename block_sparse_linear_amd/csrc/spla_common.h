@@ -157,6 +157,8 @@ hipError_t launch_pf_attend(const DecodeArgs& a, const PfBuffers& pb, const Laun
 // chunked prefill: the chunk's own tokens added into the o_bar / phi(q).z
 // partials of its virtual queries (k_new / v_new address the chunk's first row)
 hipError_t launch_chunk_la(const DecodeArgs& a, bool bf16, const void* k_new, const void* v_new, const Launch& l);
+bool pf_score_supported(const DecodeArgs& a);
+hipError_t launch_pf_score(const DecodeArgs& a, bool bf16, const Launch& l);
 // exact group log mass of every candidate block (a dense pass over the keys)
 hipError_t launch_block_mass(const DecodeArgs& a, bool bf16, float* lgx, int max_cand, const Launch& l);
 // fused select + attend: supported for bf16 K/V, block size 64, no selection

@@ -124,6 +124,15 @@ def test_prefill_group_ratios(r):
     _prefill_case(small(name=f"pf_r{r}", n_q_heads=2 * r, t0=(64 * 70 + 5,)), 0, 64 * 60 + 63, chunk=64)
 
 
+@pytest.mark.parametrize("r", [2, 8])
+def test_prefill_group_ratios_d64(r):
+    # head dim 64: eight query heads per KV head stay on the matrix-core scorer
+    # (the 8 x 128 case above takes the per-token scorer); groups of 130
+    # tokens leave a partly filled last token tile
+    _prefill_case(small(name=f"pf_r{r}_d64", n_q_heads=2 * r, head_dim=64, t0=(64 * 70 + 5,)), 0,
+                  64 * 58 + 3, chunk=130)
+
+
 def test_prefill_block128_d64():
     _prefill_case(small(name="pf_bk128", head_dim=64, block_size=128, top_k=12, t0=(128 * 90 + 100,)), 0,
                   128 * 87 + 5)
