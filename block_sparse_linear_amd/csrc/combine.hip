@@ -22,7 +22,9 @@ constexpr int kRlaPlain = 0, kRlaNormalized = 1, kRlaRms = 2;
 // over kThreads / (2 CS / 4) slot groups whose float4 sums meet in LDS.  Every
 // global load is issued before the first wait; the leading arguments address
 // all of them.
-template <int R, int D, int FORM>
+// ONE: a single o_bar / phi(q).z partial per head (chunked prefill) instead
+// of the first kernel's D * D / 1024 row-chunk partials.
+template <int R, int D, int FORM, bool ONE>
 __global__ __launch_bounds__(kThreads) void k_combine(const float* part, const float* obar_part, const float* dz_part,
                                                        const int32_t* sel, int32_t G, int32_t H, int32_t top_k,
                                                        const DecodeArgs a) {
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float* part, const f
   constexpr int SG = kThreads / NIT;            // slot groups
   constexpr int SPT = 4;                        // slots per thread per load batch
   constexpr int SPL = 4;                        // slots per lane in the header pass (top_k <= 256)
-  constexpr int CHUNKS = D / (1024 / D);        // o_bar partials per head
+  constexpr int CHUNKS = ONE ? 1 : D / (1024 / D);  // o_bar partials per head
   constexpr int OBN = (CHUNKS * NQ + kThreads - 1) / kThreads;  // o_bar partial float4s per thread
   static_assert(OBN <= 2, "at most two o_bar partial loads per thread");
   __shared__ float wsl[256];                    // exp(m_s - m) / L (0 for unused slots)
@@ -200,8 +202,11 @@ hipError_t launch_combine_form(const DecodeArgs& a, const Launch& l) {
   const int cs = FORM == kRlaRms ? a.d : 32;
   const dim3 grid(a.d / cs, a.H, a.B);
   const int32_t* sel = a.sel_in ? a.sel_in : a.sel;
-  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<RR, DD, FORM>, grid, l, a.part, a.obar_part, a.dz_part, sel,
-                                           a.G, a.H, a.top_k, a))
+  if (a.obar_one)
+    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<RR, DD, FORM, true>, grid, l, a.part, a.obar_part, a.dz_part,
+                                             sel, a.G, a.H, a.top_k, a))
+  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<RR, DD, FORM, false>, grid, l, a.part, a.obar_part, a.dz_part,
+                                           sel, a.G, a.H, a.top_k, a))
 }
 
 }  // namespace

@@ -610,17 +610,17 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
     sa.st.s_all = h->buf.s_all + (size_t)seq * G * d * d;
     sa.st.z_all = h->buf.z_all + (size_t)seq * G * d;
     if (pf_score_supported(a)) {
-      // the group's block scores on the matrix cores, then the o_bar / phi(q)
-      // partials of the state rows (the first kernel's row chunks alone)
+      // the group's block scores, then phi(q_t)^T S_t and phi(q_t).z_t in one
+      // partial per head (state before the group plus its own tokens up to
+      // t) and phi(q), all on the matrix cores
       if (a.score_tiles > 0 && (e = launch_pf_score(a, bf16, l)) != hipSuccess) return hip_fail(h, e);
-      StepArgs rows = sa;
-      rows.dec.score_tiles = 0;
-      rows.dec.tiles_all = 0;
-      if ((e = launch_score(rows, bf16, l)) != hipSuccess) return hip_fail(h, e);
-    } else if ((e = launch_score(sa, bf16, l)) != hipSuccess) {
-      return hip_fail(h, e);
+      if ((e = launch_pf_state(a, bf16, kc, vc, l)) != hipSuccess) return hip_fail(h, e);
+      a.obar_one = 1;
+    } else {
+      // per-token scorer with the state-row chunks, then the group's own tokens
+      if ((e = launch_score(sa, bf16, l)) != hipSuccess) return hip_fail(h, e);
+      if ((e = launch_chunk_la(a, bf16, kc, vc, l)) != hipSuccess) return hip_fail(h, e);
     }
-    if ((e = launch_chunk_la(a, bf16, kc, vc, l)) != hipSuccess) return hip_fail(h, e);
     if ((e = launch_select(a, l)) != hipSuccess) return hip_fail(h, e);
     // bf16: every selected block read once per item of up to kPfQ queries
     if ((e = bf16 ? launch_pf_attend(a, pb, l) : launch_attend(a, bf16, l)) != hipSuccess) return hip_fail(h, e);

@@ -50,6 +50,7 @@ struct DecodeArgs {
   float* part;      // workspace [B][H][top_k][2d + kPartHdr]
   float* obar_part;  // workspace [B][G][d * d / 1024][R][d]: phi(q)^T S_all over one chunk of S rows
   float* dz_part;    // workspace [B][G][d * d / 1024][R]: phi(q).z_all over the same rows
+  int32_t obar_one;  // 1: one o_bar / phi(q).z partial per head ([B][G][R][d], [B][G][R]) instead
   uint16_t* phq;     // workspace [B][H][2][d]: phi(q) as bf16 hi, then the bf16 rounding of the rest
   uint32_t* err;    // workspace error word
   const int32_t* sel_in;
@@ -159,6 +160,7 @@ hipError_t launch_pf_attend(const DecodeArgs& a, const PfBuffers& pb, const Laun
 hipError_t launch_chunk_la(const DecodeArgs& a, bool bf16, const void* k_new, const void* v_new, const Launch& l);
 bool pf_score_supported(const DecodeArgs& a);
 hipError_t launch_pf_score(const DecodeArgs& a, bool bf16, const Launch& l);
+hipError_t launch_pf_state(const DecodeArgs& a, bool bf16, const void* k_new, const void* v_new, const Launch& l);
 // exact group log mass of every candidate block (a dense pass over the keys)
 hipError_t launch_block_mass(const DecodeArgs& a, bool bf16, float* lgx, int max_cand, const Launch& l);
 // fused select + attend: supported for bf16 K/V, block size 64, no selection
