@@ -5,7 +5,7 @@
 // grid is a flat list of three kinds of workgroups:
 //   [0, s_items)                        state update: S[x][:] += sum_t phi(k_t[x]) v_t,
 //                                       z[x] += sum_t phi(k_t[x]) for a chunk of rows x
-//   [s_items, +page_items)              page copy of up to 64 appended tokens
+//   [s_items, +page_items)              page copy of up to page_tok appended tokens
 //   [.., +stat_items)                   mean / population variance of one block
 //                                       completed by this append, one KV head
 // The three kinds touch disjoint memory: statistics read tokens older than the
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(kThreads) void k_append(const AppendArgs a) {
   item -= a.s_items;
   if (item < a.page_items) {
     const int e = find_entry(a.page_prefix, a.n_entries, item);
-    append_page_rows<BF16>(a.st, a.e[e], (item - a.page_prefix[e]) * 64);
+    append_page_rows<BF16>(a.st, a.e[e], (item - a.page_prefix[e]) * a.page_tok, a.page_tok);
     return;
   }
   item -= a.page_items;

@@ -57,10 +57,11 @@ __device__ void append_state_rows(const StateRefs& a, const AppendEntry& E, int 
   if (c4 == 0) a.z_all[((size_t)E.seq * G + g) * d + x] += zacc;
 }
 
-// copy appended tokens [i0, i0 + 64) of entry E (all KV heads) into the pages
+// copy appended tokens [i0, i0 + ntok_max) of entry E (all KV heads) into the
+// pages
 template <bool BF16>
-__device__ void append_page_rows(const StateRefs& a, const AppendEntry& E, int i0) {
-  const int ntok = min(64, E.n - i0);
+__device__ void append_page_rows(const StateRefs& a, const AppendEntry& E, int i0, int ntok_max) {
+  const int ntok = min(ntok_max, E.n - i0);
   const int es = BF16 ? 2 : 4;
   const int vec_per_row = a.d * es / 16;
   const int per_tok = a.G * vec_per_row;

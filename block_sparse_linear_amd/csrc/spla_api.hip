@@ -428,6 +428,7 @@ spla_status spla_append_kv(spla_handle* h, int32_t n_seqs, const int32_t* seq_id
     a.st.k_new = static_cast<const char*>(k_new) + row * row_bytes;
     a.st.v_new = static_cast<const char*>(v_new) + row * row_bytes;
     a.n_entries = ne;
+    a.page_tok = append_page_tokens(c.n_kv_heads, c.head_dim, bf16);
     int lrow = 0, pp = 0, sp = 0;
     for (int e = 0; e < ne; ++e) {
       const int s = seq_ids_host[i0 + e];
@@ -439,7 +440,7 @@ spla_status spla_append_kv(spla_handle* h, int32_t n_seqs, const int32_t* seq_id
       a.e[e].row = lrow;
       a.page_prefix[e] = pp;
       a.stat_prefix[e] = sp;
-      pp += (n + 63) / 64;
+      pp += (n + a.page_tok - 1) / a.page_tok;
       sp += ((t0 + n) / c.block_size - t0 / c.block_size) * c.n_kv_heads;
       lrow += n;
     }
@@ -543,7 +544,6 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
   const size_t stats_row = G * (size_t)h->n_tiles * kTile * d;  // floats of one sequence's statistics
   const Launch l{reinterpret_cast<hipStream_t>(stream), nullptr, nullptr};
   char* wsb = static_cast<char*>(workspace);
-  const int chunks = c.head_dim / (1024 / c.head_dim);
   PfBuffers pb;
   pb.cnt = reinterpret_cast<int32_t*>(wsb + pl.cnt);
   pb.lists = reinterpret_cast<int32_t*>(wsb + pl.lists);
@@ -567,7 +567,8 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
     ap.n_entries = 1;
     ap.e[0] = AppendEntry{seq, m, t0, 0};
     ap.page_prefix[0] = ap.stat_prefix[0] = 0;
-    ap.page_items = ap.page_prefix[1] = (m + 63) / 64;
+    ap.page_tok = append_page_tokens(c.n_kv_heads, c.head_dim, bf16);
+    ap.page_items = ap.page_prefix[1] = (m + ap.page_tok - 1) / ap.page_tok;
     ap.stat_items = ap.stat_prefix[1] = ((t0 + m) / c.block_size - t0 / c.block_size) * c.n_kv_heads;
     hipError_t e = launch_append(ap, bf16, l);
     if (e != hipSuccess) return hip_fail(h, e);
@@ -625,14 +626,12 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
     // bf16: every selected block read once per item of up to kPfQ queries
     if ((e = bf16 ? launch_pf_attend(a, pb, l) : launch_attend(a, bf16, l)) != hipSuccess) return hip_fail(h, e);
     if ((e = launch_combine(a, l)) != hipSuccess) return hip_fail(h, e);
-    // (3) the chunk's tokens into S_all / z_all
-    AppendArgs as;
-    memset(&as, 0, sizeof(as));
-    fill_state_refs(h, kc, vc, &as.st);
-    as.n_entries = 1;
-    as.e[0] = AppendEntry{seq, m, t0, 0};
-    as.s_items = c.n_kv_heads * chunks;
-    if ((e = launch_append(as, bf16, l)) != hipSuccess) return hip_fail(h, e);
+    // (3) the chunk's tokens into S_all / z_all: phi(K)^T V on the matrix cores
+    StateRefs sr;
+    fill_state_refs(h, kc, vc, &sr);
+    sr.s_all = h->buf.s_all + (size_t)seq * G * d * d;
+    sr.z_all = h->buf.z_all + (size_t)seq * G * d;
+    if ((e = launch_pf_state_add(sr, bf16, m, l)) != hipSuccess) return hip_fail(h, e);
     h->lens[seq] = t0 + m;
   }
   return SPLA_OK;

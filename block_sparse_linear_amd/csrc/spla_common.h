@@ -92,11 +92,19 @@ struct AppendArgs {
   int32_t n_entries;
   int32_t s_items;     // state-update workgroups (n_entries * G * d / rows_per_item)
   int32_t page_items;  // page-copy workgroups
+  int32_t page_tok;    // appended tokens per page-copy workgroup (append_page_tokens)
   int32_t stat_items;  // block-statistics workgroups
   int32_t page_prefix[kMaxAppendEntries + 1];
   int32_t stat_prefix[kMaxAppendEntries + 1];
   AppendEntry e[kMaxAppendEntries];
 };
+
+// tokens per page-copy workgroup: as many as give every thread one 16-byte
+// piece of k (and one of v), at least one
+inline int append_page_tokens(int G, int d, bool bf16) {
+  const int per_tok = G * d * (bf16 ? 2 : 4) / 16;
+  return per_tok >= kThreads ? 1 : kThreads / per_tok;
+}
 
 // fused decode step: append one token to every sequence (row b of k_new /
 // v_new is sequence b) inside the scorer's launch, then the usual decode
@@ -161,6 +169,7 @@ hipError_t launch_chunk_la(const DecodeArgs& a, bool bf16, const void* k_new, co
 bool pf_score_supported(const DecodeArgs& a);
 hipError_t launch_pf_score(const DecodeArgs& a, bool bf16, const Launch& l);
 hipError_t launch_pf_state(const DecodeArgs& a, bool bf16, const void* k_new, const void* v_new, const Launch& l);
+hipError_t launch_pf_state_add(const StateRefs& st, bool bf16, int m, const Launch& l);
 // exact group log mass of every candidate block (a dense pass over the keys)
 hipError_t launch_block_mass(const DecodeArgs& a, bool bf16, float* lgx, int max_cand, const Launch& l);
 // fused select + attend: supported for bf16 K/V, block size 64, no selection
