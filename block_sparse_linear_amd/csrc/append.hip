@@ -1,14 +1,13 @@
-// spla_append_kv kernel: page write, global linear-attention state update and
-// block statistics of completed blocks (SPLA Technical Summary 2.1 and 2.2).
+// spla_append_kv kernel: page write and block statistics of completed blocks
+// (SPLA Technical Summary 2.1); the global linear-attention state part of an
+// append is k_state_add (fp32 matrix cores).
 //
 // One launch covers up to kMaxAppendEntries (sequence, rows) entries.  The
-// grid is a flat list of three kinds of workgroups:
-//   [0, s_items)                        state update: S[x][:] += sum_t phi(k_t[x]) v_t,
-//                                       z[x] += sum_t phi(k_t[x]) for a chunk of rows x
-//   [s_items, +page_items)              page copy of up to page_tok appended tokens
-//   [.., +stat_items)                   mean / population variance of one block
+// grid is a flat list of two kinds of workgroups:
+//   [0, page_items)                     page copy of up to page_tok appended tokens
+//   [page_items, +stat_items)           mean / population variance of one block
 //                                       completed by this append, one KV head
-// The three kinds touch disjoint memory: statistics read tokens older than the
+// The two kinds touch disjoint memory: statistics read tokens older than the
 // append from the pages (written by earlier launches) and the new tokens from
 // k_new, never the page rows this launch writes.
 #include "append_items.h"
@@ -26,15 +25,6 @@ __device__ __forceinline__ int find_entry(const int32_t* prefix, int n, int item
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_append(const AppendArgs a) {
   int item = blockIdx.x;
-  const int chunks = a.st.d / (1024 / a.st.d);
-  if (item < a.s_items) {
-    const int per = a.st.G * chunks;
-    const int e = item / per;
-    const int rem = item - e * per;
-    append_state_rows<BF16>(a.st, a.e[e], rem / chunks, rem % chunks);
-    return;
-  }
-  item -= a.s_items;
   if (item < a.page_items) {
     const int e = find_entry(a.page_prefix, a.n_entries, item);
     append_page_rows<BF16>(a.st, a.e[e], (item - a.page_prefix[e]) * a.page_tok, a.page_tok);
@@ -51,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void k_append(const AppendArgs a) {
 }  // namespace
 
 hipError_t launch_append(const AppendArgs& a, bool bf16, const Launch& l) {
-  const int n = a.s_items + a.page_items + a.stat_items;
+  const int n = a.page_items + a.stat_items;
   if (n == 0) return hipSuccess;
   return bf16 ? launch_kernel(k_append<true>, dim3(n), l, a) : launch_kernel(k_append<false>, dim3(n), l, a);
 }

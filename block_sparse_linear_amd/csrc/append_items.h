@@ -1,61 +1,11 @@
-// Work items of the state append (SPLA Technical Summary 2.1: block
-// statistics; 2.2: the running global linear-attention state), shared by the
-// append kernel and the fused decode-step kernel.  Each function is executed
-// by a whole 256-thread workgroup.
+// Work items of the append (SPLA Technical Summary 2.1: pages and block
+// statistics), shared by the append kernel and the fused decode-step kernel.
+// Each function is executed by a whole 256-thread workgroup.
 #pragma once
 
 #include "spla_common.h"
 
 namespace spla {
-
-// S[x][:] += sum_t phi(k_t[x]) v_t and z[x] += sum_t phi(k_t[x]) for the
-// rows x of chunk rc (1024 / d rows): 256 threads = rows x (d / 4) quartets.
-template <bool BF16>
-__device__ void append_state_rows(const StateRefs& a, const AppendEntry& E, int g, int rc) {
-  const int d = a.d, G = a.G;
-  const int rows = 1024 / d;
-  if (E.n <= 0) return;
-  const int c4n = d / 4;
-  const int x = rc * rows + threadIdx.x / c4n;  // row of S (key channel)
-  const int c4 = threadIdx.x % c4n;             // column quartet (value channels)
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float zacc = 0.f;
-  const size_t row_stride = (size_t)G * d;
-  size_t base = ((size_t)E.row * G + g) * d;
-  float4* S = reinterpret_cast<float4*>(a.s_all + (((size_t)E.seq * G + g) * d + x) * d) + c4;
-  const float4 s_old = *S;
-  int t = 0;
-  for (; t + 4 <= E.n; t += 4) {
-    float f[4];
-    float4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      f[u] = phi_f(load_elem<BF16>(a.k_new, base + u * row_stride + x));
-      v[u] = load4<BF16>(a.v_new, base + u * row_stride + c4 * 4);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc.x = fmaf(f[u], v[u].x, acc.x);
-      acc.y = fmaf(f[u], v[u].y, acc.y);
-      acc.z = fmaf(f[u], v[u].z, acc.z);
-      acc.w = fmaf(f[u], v[u].w, acc.w);
-      zacc += f[u];
-    }
-    base += 4 * row_stride;
-  }
-  for (; t < E.n; ++t) {
-    const float f = phi_f(load_elem<BF16>(a.k_new, base + x));
-    const float4 v = load4<BF16>(a.v_new, base + c4 * 4);
-    acc.x = fmaf(f, v.x, acc.x);
-    acc.y = fmaf(f, v.y, acc.y);
-    acc.z = fmaf(f, v.z, acc.z);
-    acc.w = fmaf(f, v.w, acc.w);
-    zacc += f;
-    base += row_stride;
-  }
-  *S = make_float4(s_old.x + acc.x, s_old.y + acc.y, s_old.z + acc.z, s_old.w + acc.w);
-  if (c4 == 0) a.z_all[((size_t)E.seq * G + g) * d + x] += zacc;
-}
 
 // copy appended tokens [i0, i0 + ntok_max) of entry E (all KV heads) into the
 // pages

@@ -204,19 +204,23 @@ __global__ __launch_bounds__(kThreads) void k_pf_state(const void* q, const void
   }
 }
 
-// The group into the state: S_all[g] += phi(K)^T V and z_all[g] += sum_t
-// phi(k_t) over the group's m tokens (SPLA Technical Summary 2.2), fp32 on
-// the 16x16x4 fp32 matrix cores.  grid (D / 16, G): rows x of a 16-row tile
-// of S (A rows = key channels, B columns = value channels y = CPL * l16 + c,
-// k = tokens t = 4 ks + kk); wavefront w takes k-steps w, w + 4, ... and the
-// four partial tiles meet in LDS before the one read-modify-write of S.
+// Appended tokens into the state: S_all[seq][g] += phi(K)^T V and
+// z_all[seq][g] += sum_t phi(k_t) over the n tokens of each append entry
+// (SPLA Technical Summary 2.2), fp32 on the 16x16x4 fp32 matrix cores.  grid
+// (D / 16, G, entries): rows x of a 16-row tile of S (A rows = key channels,
+// B columns = value channels y = CPL * l16 + c, k = tokens t = 4 ks + kk);
+// wavefront w takes k-steps w, w + 4, ... and the four partial tiles meet in
+// LDS before the one read-modify-write of S.  A single token adds its exact
+// products phi(k[x]) v[y] (the other terms are zeros), so a one-token append
+// rounds like the decode step's fused append.
 template <bool BF16, int D>
-__global__ __launch_bounds__(kThreads) void k_pf_state_add(const void* k_new, const void* v_new, float* s_all,
-                                                            float* z_all, int32_t m, int32_t G) {
+__global__ __launch_bounds__(kThreads) void k_state_add(const AppendArgs a) {
   constexpr int CPL = D / 16;
   __shared__ __attribute__((aligned(16))) float red[4][16][D];
   __shared__ float zr[4][16];
-  const int xt = blockIdx.x, g = blockIdx.y;
+  const AppendEntry& E = a.e[blockIdx.z];
+  const int xt = blockIdx.x, g = blockIdx.y, G = a.st.G, m = E.n;
+  if (m <= 0) return;
   const int w = threadIdx.x / 64, lane = threadIdx.x % 64, l16 = lane % 16, kk = lane / 16;
   const int x = 16 * xt + l16;  // A row: key channel
   const int nks = (m + 3) / 4;
@@ -227,10 +231,10 @@ __global__ __launch_bounds__(kThreads) void k_pf_state_add(const void* k_new, co
 #pragma unroll 4
   for (int ks = w; ks < nks; ks += 4) {
     const int t = 4 * ks + kk;
-    const int tc = min(t, m - 1);
-    const float kx = load_elem<BF16>(k_new, ((size_t)tc * G + g) * D + x);
+    const size_t row = ((size_t)(E.row + min(t, m - 1)) * G + g) * D;
+    const float kx = load_elem<BF16>(a.st.k_new, row + x);
     float vr[CPL];
-    load_run<BF16, CPL>(v_new, ((size_t)tc * G + g) * D + CPL * l16, vr);
+    load_run<BF16, CPL>(a.st.v_new, row + CPL * l16, vr);
     const float fk = t < m ? phi_f(kx) : 0.f;
     zs += fk;
 #pragma unroll
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void k_pf_state_add(const void* k_new, co
           make_float4(acc[c][r], acc[c + 1][r], acc[c + 2][r], acc[c + 3][r]);
   if (kk == 0) zr[w][l16] = zs;
   __syncthreads();
-  float* S = s_all + ((size_t)g * D + 16 * xt) * D;
+  float* S = a.st.s_all + (((size_t)E.seq * G + g) * D + 16 * xt) * D;
   for (int e = threadIdx.x; e < 16 * (D / 4); e += kThreads) {
     const int xl = e / (D / 4), y4 = e % (D / 4);
     const float4 x0 = *reinterpret_cast<const float4*>(&red[0][xl][4 * y4]);
@@ -260,23 +264,21 @@ __global__ __launch_bounds__(kThreads) void k_pf_state_add(const void* k_new, co
                        o.z + ((x0.z + x1.z) + (x2.z + x3.z)), o.w + ((x0.w + x1.w) + (x2.w + x3.w)));
   }
   if ((int)threadIdx.x < 16)
-    z_all[(size_t)g * D + 16 * xt + threadIdx.x] +=
+    a.st.z_all[((size_t)E.seq * G + g) * D + 16 * xt + threadIdx.x] +=
         (zr[0][threadIdx.x] + zr[1][threadIdx.x]) + (zr[2][threadIdx.x] + zr[3][threadIdx.x]);
 }
 
 }  // namespace
 
-// S_all / z_all of one sequence (the pointers address its rows) += the group's
-// m tokens k_new / v_new [m][G][d]
-hipError_t launch_pf_state_add(const StateRefs& st, bool bf16, int m, const Launch& l) {
-  if (m <= 0) return hipSuccess;
-  const dim3 grid(st.d / 16, st.G);
+// the state part of an append: every entry of a (its k_new / v_new rows from
+// E.row on, [rows][G][d]) into S_all / z_all of its sequence
+hipError_t launch_state_add(const AppendArgs& a, bool bf16, const Launch& l) {
+  if (a.n_entries <= 0) return hipSuccess;
+  const dim3 grid(a.st.d / 16, a.st.G, a.n_entries);
   if (bf16) {
-    SPLA_DISPATCH_D(st.d, launch_kernel(k_pf_state_add<true, DD>, grid, l, st.k_new, st.v_new, st.s_all, st.z_all, m,
-                                        st.G))
+    SPLA_DISPATCH_D(a.st.d, launch_kernel(k_state_add<true, DD>, grid, l, a))
   }
-  SPLA_DISPATCH_D(st.d, launch_kernel(k_pf_state_add<false, DD>, grid, l, st.k_new, st.v_new, st.s_all, st.z_all, m,
-                                      st.G))
+  SPLA_DISPATCH_D(a.st.d, launch_kernel(k_state_add<false, DD>, grid, l, a))
 }
 
 // a.B tokens of one sequence (virtual queries) whose state rows the pointers

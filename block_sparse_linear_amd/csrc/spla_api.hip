@@ -414,7 +414,6 @@ spla_status spla_append_kv(spla_handle* h, int32_t n_seqs, const int32_t* seq_id
 
   const bool bf16 = c.kv_dtype == SPLA_BF16;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int chunks = c.head_dim / (1024 / c.head_dim);
   AppendArgs a;
   memset(&a, 0, sizeof(a));
   fill_state_refs(h, k_new, v_new, &a.st);
@@ -446,10 +445,10 @@ spla_status spla_append_kv(spla_handle* h, int32_t n_seqs, const int32_t* seq_id
     }
     a.page_prefix[ne] = pp;
     a.stat_prefix[ne] = sp;
-    a.s_items = ne * c.n_kv_heads * chunks;
     a.page_items = pp;
     a.stat_items = sp;
-    const hipError_t e = launch_append(a, bf16, Launch{st, nullptr, nullptr});
+    hipError_t e = launch_append(a, bf16, Launch{st, nullptr, nullptr});
+    if (e == hipSuccess) e = launch_state_add(a, bf16, Launch{st, nullptr, nullptr});
     if (e != hipSuccess) return hip_fail(h, e);
     row += lrow;
   }
@@ -627,11 +626,12 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
     if ((e = bf16 ? launch_pf_attend(a, pb, l) : launch_attend(a, bf16, l)) != hipSuccess) return hip_fail(h, e);
     if ((e = launch_combine(a, l)) != hipSuccess) return hip_fail(h, e);
     // (3) the chunk's tokens into S_all / z_all: phi(K)^T V on the matrix cores
-    StateRefs sr;
-    fill_state_refs(h, kc, vc, &sr);
-    sr.s_all = h->buf.s_all + (size_t)seq * G * d * d;
-    sr.z_all = h->buf.z_all + (size_t)seq * G * d;
-    if ((e = launch_pf_state_add(sr, bf16, m, l)) != hipSuccess) return hip_fail(h, e);
+    AppendArgs as;
+    memset(&as, 0, sizeof(as));
+    fill_state_refs(h, kc, vc, &as.st);
+    as.n_entries = 1;
+    as.e[0] = AppendEntry{seq, m, t0, 0};
+    if ((e = launch_state_add(as, bf16, l)) != hipSuccess) return hip_fail(h, e);
     h->lens[seq] = t0 + m;
   }
   return SPLA_OK;

@@ -90,7 +90,6 @@ struct StateRefs {
 struct AppendArgs {
   StateRefs st;
   int32_t n_entries;
-  int32_t s_items;     // state-update workgroups (n_entries * G * d / rows_per_item)
   int32_t page_items;  // page-copy workgroups
   int32_t page_tok;    // appended tokens per page-copy workgroup (append_page_tokens)
   int32_t stat_items;  // block-statistics workgroups
@@ -169,7 +168,7 @@ hipError_t launch_chunk_la(const DecodeArgs& a, bool bf16, const void* k_new, co
 bool pf_score_supported(const DecodeArgs& a);
 hipError_t launch_pf_score(const DecodeArgs& a, bool bf16, const Launch& l);
 hipError_t launch_pf_state(const DecodeArgs& a, bool bf16, const void* k_new, const void* v_new, const Launch& l);
-hipError_t launch_pf_state_add(const StateRefs& st, bool bf16, int m, const Launch& l);
+hipError_t launch_state_add(const AppendArgs& a, bool bf16, const Launch& l);
 // exact group log mass of every candidate block (a dense pass over the keys)
 hipError_t launch_block_mass(const DecodeArgs& a, bool bf16, float* lgx, int max_cand, const Launch& l);
 // fused select + attend: supported for bf16 K/V, block size 64, no selection
