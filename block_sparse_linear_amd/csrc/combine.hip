@@ -23,12 +23,14 @@ constexpr int kRlaPlain = 0, kRlaNormalized = 1, kRlaRms = 2;
 // global load is issued before the first wait; the leading arguments address
 // all of them.
 // ONE: a single o_bar / phi(q).z partial per head (chunked prefill) instead
-// of the first kernel's D * D / 1024 row-chunk partials.
+// of the first kernel's D * D / 1024 row-chunk partials; a prefill group has
+// thousands of (token, head) pairs, so a workgroup then takes a whole head,
+// which spreads its merge-weight pass over four times the data.
 template <int R, int D, int FORM, bool ONE>
 __global__ __launch_bounds__(kThreads) void k_combine(const float* part, const float* obar_part, const float* dz_part,
                                                        const int32_t* sel, int32_t G, int32_t H, int32_t top_k,
                                                        const DecodeArgs a) {
-  constexpr int CS = FORM == kRlaRms ? D : 32;  // channels per workgroup
+  constexpr int CS = (FORM == kRlaRms || ONE) ? D : 32;  // channels per workgroup
   constexpr int NQ = CS / 4;                    // channel quartets
   constexpr int NIT = 2 * NQ;                   // float4 items (kind, quartet)
   constexpr int SG = kThreads / NIT;            // slot groups
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float* part, const f
 
 template <int FORM>
 hipError_t launch_combine_form(const DecodeArgs& a, const Launch& l) {
-  const int cs = FORM == kRlaRms ? a.d : 32;
+  const int cs = (FORM == kRlaRms || a.obar_one) ? a.d : 32;
   const dim3 grid(a.d / cs, a.H, a.B);
   const int32_t* sel = a.sel_in ? a.sel_in : a.sel;
   if (a.obar_one)
