@@ -104,8 +104,9 @@ hipError_t launch_chunk_la(const DecodeArgs& a, bool bf16, const void* k_new, co
 //                page, up to kPfQ query codes) and clears the counts
 //   k_pf_attend  one item per workgroup: the block's K tile in registers
 //                (with phi(K) hi / lo), its V tile transposed in LDS, the
-//                item's queries staged in LDS, then per query the same
-//                products and partial record as the decode attend
+//                item's queries staged in LDS, then the queries in batches
+//                of 16 / R through the decode attend's products (16 A rows
+//                = (query, head) pairs) and partial records
 // A query code is vq * 256 + slot.
 namespace spla {
 
@@ -159,15 +160,21 @@ __global__ __launch_bounds__(kThreads) void k_pf_items(int32_t* cnt, const int32
   cnt[cell] = 0;
 }
 
-// one work item per workgroup (grid: an upper bound of the item count)
+// one work item per workgroup (grid: an upper bound of the item count).  A
+// batch of QB = 16 / R queries fills the 16 rows of the A operands: product
+// (1) forms the logits from the q rows and the linear weights from the
+// phi(q) hi / lo rows (separate accumulators), the softmax max and sums meet
+// across the wavefronts in LDS (one exchange per batch), and product (2)
+// takes the batch's p and w rows (hi / lo, 64 rows) against the V tile.  Each
+// row has its own causal limit (its query's length).
 template <int R, int D, int BK>
 __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const int32_t* n_items,
                                                          const DecodeArgs a) {
   constexpr int NKS = D / 32;              // k-steps per channel block
   constexpr int NT1W = BK / 64;            // 16-token tiles per wavefront
-  constexpr int WB = R <= 4 ? 4 : 8;       // first linear-weight row of product (1)
+  constexpr int QB = 16 / R;               // queries per batch: A rows (query, head) = 16
   constexpr int NT2W = D / 64;             // 16-channel tiles per wavefront
-  constexpr int MT2 = (4 * R + 15) / 16;   // row tiles of product (2): hi/lo rows of p and w
+  constexpr int MT2 = 4;                   // row tiles of product (2): hi/lo rows of p and w of 16 rows
   constexpr int KS2 = BK / 32;             // token k-steps of product (2)
   constexpr int VS = BK + 8;               // row stride (elements) of the transposed V tile
   constexpr int PS = BK + 8;               // row stride of the p / w rows
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
   __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
   __shared__ __attribute__((aligned(16))) uint16_t pw[MT2 * 16 * PS];
   __shared__ __attribute__((aligned(16))) uint16_t qs[kPfQ * QE];
-  __shared__ float s_max[4][R], s_l[4][R], s_sw[4][R];
+  __shared__ float s_max[4][16], s_l[4][16], s_sw[4][16];
   __shared__ int s_code[kPfQ];
   // the item (the array holds max_items records, so any workgroup may read
   // its own) and the count, in one round trip
@@ -194,7 +201,6 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
   }
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int lane = threadIdx.x % 64, l16 = lane % 16, lg4 = lane / 16;
-  const int m = l16;  // A-operand row of this lane in product (1)
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k_pages) + ((size_t)page * a.G + g) * BK * D;
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v_pages) + ((size_t)page * a.G + g) * BK * D;
   // ---- every global load first: K operands, V pieces, the item's queries
@@ -252,9 +258,6 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
   // rows of the tile past the group's last token: never attended, zeroed so
   // that 0 x (stale data) cannot make NaN
   const int nvalid = min(BK, a.lens[a.B - 1] - j * BK);
-  if constexpr (R < 4) {
-    for (int i = threadIdx.x; i < MT2 * 16 * PS / 2; i += kThreads) reinterpret_cast<uint32_t*>(pw)[i] = 0u;
-  }
   {
     // clamped like the loads: a repeated piece rewrites the same value
     uint4* qd = reinterpret_cast<uint4*>(qs);
@@ -294,91 +297,87 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) phi_bf16_split(kraw[nt][ks], fkh[nt][ks], fkl[nt][ks]);
   __syncthreads();
-  const bool is_q = m < R, is_w = m >= WB && m < WB + R;
-  const int hq = is_q ? m : 0, hw = is_w ? m - WB : 0;
-  const uint32_t mq = is_q ? 0xffffffffu : 0u, mw = is_w ? 0xffffffffu : 0u;
   const float inv_sqrt_d = a.inv_sqrt_d;
   const int rec = 2 * D + kPartHdr;
-  for (int e = 0; e < n; ++e) {
-    const int cd = s_code[e];
-    const int vq = cd >> 8, slot = cd & 255;
-    const uint16_t* qe = qs + e * QE;
-    // ---- A operands of product (1) from the staged query
+  // batches of QB queries: row r = 4 lg4 + i of a result tile is (query
+  // b0 + r / R, head r % R); the A operand row of this lane is l16
+  const int eh = l16 % R, ee = l16 / R;
+  for (int b0 = 0; b0 < n; b0 += QB) {
+    const int nb = min(QB, n - b0);
+    // ---- A operands of product (1): q rows and phi(q) hi / lo rows of the batch (zero past its end)
+    const uint32_t mk = ee < nb ? 0xffffffffu : 0u;
+    const uint16_t* qe = qs + min(b0 + ee, n - 1) * QE + eh * 3 * D;
     uint4 aq[NKS], afh[NKS], afl[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const uint4 x0 = *reinterpret_cast<const uint4*>(qe + (hq * 3 + 0) * D + 32 * ks + 8 * lg4);
-      const uint4 x1 = *reinterpret_cast<const uint4*>(qe + (hw * 3 + 1) * D + 32 * ks + 8 * lg4);
-      const uint4 x2 = *reinterpret_cast<const uint4*>(qe + (hw * 3 + 2) * D + 32 * ks + 8 * lg4);
-      aq[ks] = make_uint4(x0.x & mq, x0.y & mq, x0.z & mq, x0.w & mq);
-      afh[ks] = make_uint4(x1.x & mw, x1.y & mw, x1.z & mw, x1.w & mw);
-      afl[ks] = make_uint4(x2.x & mw, x2.y & mw, x2.z & mw, x2.w & mw);
+      const uint4 x0 = *reinterpret_cast<const uint4*>(qe + 0 * D + 32 * ks + 8 * lg4);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(qe + 1 * D + 32 * ks + 8 * lg4);
+      const uint4 x2 = *reinterpret_cast<const uint4*>(qe + 2 * D + 32 * ks + 8 * lg4);
+      aq[ks] = make_uint4(x0.x & mk, x0.y & mk, x0.z & mk, x0.w & mk);
+      afh[ks] = make_uint4(x1.x & mk, x1.y & mk, x1.z & mk, x1.w & mk);
+      afl[ks] = make_uint4(x2.x & mk, x2.y & mk, x2.z & mk, x2.w & mk);
     }
-    // ---- product (1): logits and linear weights of this wavefront's tokens
-    f32x4_t c1[NT1W];
+    // ---- product (1): logits s = q.k and linear weights w = phi(q).phi(k) of this wavefront's tokens
+    f32x4_t cs[NT1W], cw[NT1W];
 #pragma unroll
     for (int nt = 0; nt < NT1W; ++nt) {
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f}, d2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         c = mfma_bf16(aq[ks], kraw[nt][ks], c);
-        c = mfma_bf16(afh[ks], fkh[nt][ks], c);
-        c = mfma_bf16(afl[ks], fkh[nt][ks], c);
-        c = mfma_bf16(afh[ks], fkl[nt][ks], c);
+        d2 = mfma_bf16(afh[ks], fkh[nt][ks], d2);
+        d2 = mfma_bf16(afl[ks], fkh[nt][ks], d2);
+        d2 = mfma_bf16(afh[ks], fkl[nt][ks], d2);
       }
-      c1[nt] = c;
+      cs[nt] = c;
+      cw[nt] = d2;
     }
-    const int ntok = min(BK, a.lens[vq] - j * BK);
+    // causal limit of each of this lane's four rows (its query's own length)
+    int ntok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * lg4 + i;
+      const int e = min(b0 + r / R, n - 1);
+      ntok[i] = min(BK, a.lens[s_code[e] >> 8] - j * BK);
+    }
     float mloc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int nt = 0; nt < NT1W; ++nt) {
       const int tok = (w * NT1W + nt) * 16 + l16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * lg4 + i;
-        if (row < R && tok < ntok) mloc[i] = fmaxf(mloc[i], c1[nt][i] * inv_sqrt_d);
-      }
+      for (int i = 0; i < 4; ++i)
+        if (tok < ntok[i]) mloc[i] = fmaxf(mloc[i], cs[nt][i] * inv_sqrt_d);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) mloc[i] = row16_max(mloc[i]);
     if (l16 == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * lg4 + i;
-        if (row < R) s_max[w][row] = mloc[i];
-      }
+      for (int i = 0; i < 4; ++i) s_max[w][4 * lg4 + i] = mloc[i];
     }
     __syncthreads();
-    // ---- p = exp(s - m) and w, split hi/lo, into the rows of product (2)
+    // ---- p = exp(s - m) and w, split hi/lo, into the rows of product (2):
+    // row pair 2 (kind 16 + r) (hi) and + 1 (lo), kind 0 = p, 1 = w
     float lsum[4] = {0.f, 0.f, 0.f, 0.f}, wsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < NT1W; ++nt) {
-      const int tok = (w * NT1W + nt) * 16 + l16;
-      const bool valid = tok < ntok;
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * lg4 + i;
+      const float mh = fmaxf(fmaxf(s_max[0][r], s_max[1][r]), fmaxf(s_max[2][r], s_max[3][r]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * lg4 + i;
-        int kind = -1, h = 0;
-        float x = 0.f;
-        if (row < R) {
-          h = row;
-          const float mh = fmaxf(fmaxf(s_max[0][h], s_max[1][h]), fmaxf(s_max[2][h], s_max[3][h]));
-          x = valid ? __expf(c1[nt][i] * inv_sqrt_d - mh) : 0.f;
-          lsum[i] += x;
-          kind = 0;
-        } else if (row >= WB && row < WB + R) {
-          h = row - WB;
-          x = valid ? c1[nt][i] : 0.f;
-          wsum[i] += x;
-          kind = 1;
-        }
-        if (kind >= 0) {
-          const uint32_t hb = pack_bf16(x, 0.f) & 0xffffu;
-          const uint32_t lb = pack_bf16(x - bf16_lo_f(hb), 0.f) & 0xffffu;
-          const int rh = 2 * (kind * R + h);
-          pw[rh * PS + tok] = (uint16_t)hb;
-          pw[(rh + 1) * PS + tok] = (uint16_t)lb;
-        }
+      for (int nt = 0; nt < NT1W; ++nt) {
+        const int tok = (w * NT1W + nt) * 16 + l16;
+        const bool valid = tok < ntok[i];
+        const float px = valid ? __expf(cs[nt][i] * inv_sqrt_d - mh) : 0.f;
+        const float wx = valid ? cw[nt][i] : 0.f;
+        lsum[i] += px;
+        wsum[i] += wx;
+        const uint32_t ph = pack_bf16(px, 0.f) & 0xffffu;
+        const uint32_t pl = pack_bf16(px - bf16_lo_f(ph), 0.f) & 0xffffu;
+        const uint32_t wh = pack_bf16(wx, 0.f) & 0xffffu;
+        const uint32_t wl = pack_bf16(wx - bf16_lo_f(wh), 0.f) & 0xffffu;
+        pw[(2 * r) * PS + tok] = (uint16_t)ph;
+        pw[(2 * r + 1) * PS + tok] = (uint16_t)pl;
+        pw[(2 * (16 + r)) * PS + tok] = (uint16_t)wh;
+        pw[(2 * (16 + r) + 1) * PS + tok] = (uint16_t)wl;
       }
     }
 #pragma unroll
@@ -389,14 +388,12 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
     if (l16 == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 4 * lg4 + i;
-        if (row < R) s_l[w][row] = lsum[i];
-        if (row >= WB && row < WB + R) s_sw[w][row - WB] = wsum[i];
+        s_l[w][4 * lg4 + i] = lsum[i];
+        s_sw[w][4 * lg4 + i] = wsum[i];
       }
     }
     __syncthreads();
-    // ---- product (2) and the partial record of (vq, slot)
-    float* part0 = a.part + (((size_t)vq * a.H + g * R) * a.top_k + slot) * rec;
+    // ---- product (2) and the partial records of the batch's (query, slot) pairs
 #pragma unroll
     for (int nt2 = 0; nt2 < NT2W; ++nt2) {
       const int ch = (w * NT2W + nt2) * 16 + l16;
@@ -409,25 +406,32 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
           const uint4 bv = *reinterpret_cast<const uint4*>(&vt[ch * VS + 32 * ks + 8 * lg4]);
           c = mfma_bf16(av, bv, c);
         }
+        // lane group lg4 holds rows 4 lg4 .. 4 lg4 + 3 of tile mt: pairs
+        // pi0 = 8 mt + 2 lg4 (hi + lo in c[0], c[1]) and pi0 + 1 (c[2], c[3])
 #pragma unroll
-        for (int ee = 0; ee < 2; ++ee) {
-          const int pi = 8 * mt + 2 * lg4 + ee;
-          if (pi < 2 * R) {
-            const int kind = pi / R, h = pi % R;
-            part0[(size_t)h * a.top_k * rec + kPartHdr + (kind ? D : 0) + ch] = c[2 * ee] + c[2 * ee + 1];
+        for (int e2 = 0; e2 < 2; ++e2) {
+          const int pi = 8 * mt + 2 * lg4 + e2;
+          const int kind = pi / 16, r = pi % 16, e = r / R, h = r % R;
+          if (e < nb) {
+            const int cd = s_code[b0 + e];
+            float* dst = a.part + (((size_t)(cd >> 8) * a.H + g * R + h) * a.top_k + (cd & 255)) * rec;
+            dst[kPartHdr + (kind ? D : 0) + ch] = c[2 * e2] + c[2 * e2 + 1];
           }
         }
       }
     }
-    if (threadIdx.x < R) {
-      const int h = threadIdx.x;
-      float* dst = part0 + (size_t)h * a.top_k * rec;
-      dst[0] = fmaxf(fmaxf(s_max[0][h], s_max[1][h]), fmaxf(s_max[2][h], s_max[3][h]));
-      dst[1] = (s_l[0][h] + s_l[1][h]) + (s_l[2][h] + s_l[3][h]);
-      dst[2] = (s_sw[0][h] + s_sw[1][h]) + (s_sw[2][h] + s_sw[3][h]);
-      dst[3] = 0.f;
+    if ((int)threadIdx.x < 16) {
+      const int r = threadIdx.x, e = r / R, h = r % R;
+      if (e < nb) {
+        const int cd = s_code[b0 + e];
+        float* dst = a.part + (((size_t)(cd >> 8) * a.H + g * R + h) * a.top_k + (cd & 255)) * rec;
+        dst[0] = fmaxf(fmaxf(s_max[0][r], s_max[1][r]), fmaxf(s_max[2][r], s_max[3][r]));
+        dst[1] = (s_l[0][r] + s_l[1][r]) + (s_l[2][r] + s_l[3][r]);
+        dst[2] = (s_sw[0][r] + s_sw[1][r]) + (s_sw[2][r] + s_sw[3][r]);
+        dst[3] = 0.f;
+      }
     }
-    __syncthreads();  // s_max / pw / s_l are rewritten by the next query
+    __syncthreads();  // s_max / pw / s_l are rewritten by the next batch
   }
 }
 
