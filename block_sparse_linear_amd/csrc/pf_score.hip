@@ -6,7 +6,7 @@
 //   LG(j)   = logsumexp over the R query heads of the group,
 // or the first-order (mean-pooling) form.  Over a group both sums are matrix
 // products, [tokens x d] by [d x blocks] per query head, so one workgroup
-// reads a 64-block statistics tile once for 64 tokens instead of once per
+// reads a 64-block statistics tile once for 32 tokens instead of once per
 // token, and the fp32 matrix cores (16x16x4, fp32 in and out) do the
 // products at the full fp32 rate.
 #include "decode_common.h"
@@ -21,79 +21,71 @@ __device__ __forceinline__ float f4_at(const float4& v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
 
-// grid (score_tiles, G, ceil(m / 64)).  Wavefront w takes tokens 64 z + 16 w
-// .. + 15, the 16 rows of the A operand, against the 64 blocks of tile t as
-// four 16-column tiles (B operand = statistics, columns = blocks).  Channel
-// c = kk * KS + ks is contracted at k-step ks in k slot kk = lane / 16, so a
-// lane's query channels are contiguous and its statistics arrive as float4s
-// of one channel quartet of the tile layout (64 blocks side by side per
-// quartet).  Accumulators: column tile x query head x (mean, variance); with
-// eight query heads the column tiles go in two passes of two, so that the
-// accumulators stay in registers.
+// grid (score_tiles, G, ceil(m / 32)).  Wavefront w takes tokens 32 z +
+// 16 (w / 2) .. + 15, the 16 rows of the A operand, against blocks 32 (w % 2)
+// .. + 31 of tile t as two 16-column tiles (B operand = statistics, columns =
+// blocks).  Channel c = kk * KS + ks is contracted at k-step ks in k slot kk
+// = lane / 16, so a lane's query channels are contiguous and its statistics
+// arrive as float4s of one channel quartet of the tile layout (64 blocks side
+// by side per quartet).  Accumulators: column tile x query head x (mean,
+// variance).  Queries and statistics are loaded two channel quartets ahead of
+// the products, so a wavefront holds few registers and several wavefronts
+// share a SIMD.
 template <bool BF16, int R, int D, bool TAYLOR>
 __global__ __launch_bounds__(kThreads) void k_pf_score(const float* mean, const float* var, const void* q,
                                                         int32_t n_tiles, int32_t G, int32_t H, int32_t m,
                                                         const DecodeArgs a) {
   constexpr int KS = D / 4;            // k-steps, and channels per k slot
   constexpr int KQ = KS / 4;           // channel quartets per k slot
-  constexpr int NP = R >= 8 ? 2 : 1;   // passes over the column tiles
-  constexpr int NC = 4 / NP;           // column tiles per pass
+  constexpr int NC = 2;                // column tiles per wavefront
   const int t = blockIdx.x, g = blockIdx.y;
   const int w = threadIdx.x / 64, lane = threadIdx.x % 64, l16 = lane % 16, kk = lane / 16;
-  const int tok0 = 64 * blockIdx.z + 16 * w;  // first token of this wavefront
+  const int tok0 = 32 * blockIdx.z + 16 * (w >> 1);  // first token of this wavefront
+  const int n0 = NC * (w & 1);                       // its first column tile
   const int tok = min(tok0 + l16, m - 1);     // A row (rows past the group repeat the last token, never stored)
 
   // ---- statistics loads of one channel quartet (all four column tiles)
   const float4* mean4 = reinterpret_cast<const float4*>(mean);
   const float4* var4 = reinterpret_cast<const float4*>(var);
   const size_t base = ((size_t)g * n_tiles + t) * (size_t)(D / 4) * kTile + (size_t)(kk * KQ) * kTile + l16;
-  float4 bm[2][NC], bv[2][NC];
-  auto load_b = [&](int pass, int j, int buf) {
+  constexpr int NBUF = 3;              // quartets in registers: the current one and two in flight
+  float4 bm[NBUF][NC], bv[NBUF][NC];
+  auto load_b = [&](int j, int buf) {
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
-      const size_t at = base + (size_t)j * kTile + 16 * (pass * NC + n);
+      const size_t at = base + (size_t)j * kTile + 16 * (n0 + n);
       bm[buf][n] = mean4[at];
       bv[buf][n] = TAYLOR ? var4[at] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  load_b(0, 0, 0);
-
-  // ---- A: this lane's KS query channels of every head, as fp32
-  float qa[R][KS];
+  // ---- A: channel quartet j of this lane's KS query channels, every head, as
+  // fp32 (loaded two quartets ahead, like the statistics, so that only three
+  // quartets per head are held)
+  float4 qa[NBUF][R];
+  auto load_a = [&](int j, int buf) {
 #pragma unroll
-  for (int h = 0; h < R; ++h) {
-    const size_t off = ((size_t)tok * H + g * R + h) * D + kk * KS;
-    if constexpr (BF16) {
-      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + off);
-#pragma unroll
-      for (int i = 0; i < KS / 8; ++i) {
-        const uint4 u = p[i];
-        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qa[h][8 * i + 2 * e] = bf16_lo_f(wd[e]);
-          qa[h][8 * i + 2 * e + 1] = bf16_hi_f(wd[e]);
-        }
-      }
-    } else {
-      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(q) + off);
-#pragma unroll
-      for (int i = 0; i < KS / 4; ++i) {
-        const float4 u = p[i];
-        qa[h][4 * i] = u.x;
-        qa[h][4 * i + 1] = u.y;
-        qa[h][4 * i + 2] = u.z;
-        qa[h][4 * i + 3] = u.w;
+    for (int h = 0; h < R; ++h) {
+      const size_t off = ((size_t)tok * H + g * R + h) * D + kk * KS + 4 * j;
+      if constexpr (BF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(q) + off);
+        qa[buf][h] = make_float4(bf16_lo_f(u.x), bf16_hi_f(u.x), bf16_lo_f(u.y), bf16_hi_f(u.y));
+      } else {
+        qa[buf][h] = *reinterpret_cast<const float4*>(static_cast<const float*>(q) + off);
       }
     }
+  };
+  load_b(0, 0);
+  load_a(0, 0);
+  if (KQ > 1) {
+    load_b(1, 1);
+    load_a(1, 1);
   }
   SPLA_SCALARS_READY("s"(a.bk), "s"(a.lg), "s"(a.lg_out), "s"(a.max_blocks), "s"(a.inv_sqrt_d));
 
   const float half_inv_d = 0.5f / (float)D;
   const size_t row = (size_t)n_tiles * kTile;
-#pragma unroll
-  for (int pass = 0; pass < NP; ++pass) {
-    // ---- products: quartet j of this pass's column tiles, the next quartet in flight
+  {
+    // ---- products: quartet j of this wavefront's column tiles, the next quartet in flight
     f32x4_t cm[NC][R], cv[NC][R];
 #pragma unroll
     for (int n = 0; n < NC; ++n)
@@ -101,19 +93,21 @@ __global__ __launch_bounds__(kThreads) void k_pf_score(const float* mean, const 
       for (int h = 0; h < R; ++h) cm[n][h] = cv[n][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KQ; ++j) {
-      if (j + 1 < KQ) load_b(pass, j + 1, (j + 1) & 1);
-      else if (pass + 1 < NP) load_b(pass + 1, 0, 0);
+      if (j + 2 < KQ) {
+        load_b(j + 2, (j + 2) % NBUF);
+        load_a(j + 2, (j + 2) % NBUF);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
 #pragma unroll
         for (int h = 0; h < R; ++h) {
-          const float qk = qa[h][4 * j + e];
+          const float qk = f4_at(qa[j % NBUF][h], e);
           const float q2 = qk * qk;
 #pragma unroll
           for (int n = 0; n < NC; ++n) {
-            cm[n][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(qk, f4_at(bm[j & 1][n], e), cm[n][h], 0, 0, 0);
+            cm[n][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(qk, f4_at(bm[j % NBUF][n], e), cm[n][h], 0, 0, 0);
             if (TAYLOR)
-              cv[n][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(q2, f4_at(bv[j & 1][n], e), cv[n][h], 0, 0, 0);
+              cv[n][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(q2, f4_at(bv[j % NBUF][n], e), cv[n][h], 0, 0, 0);
           }
         }
       }
@@ -147,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void k_pf_score(const float* mean, const 
             for (int h = 0; h < R; h += 2 * st) e[h] += e[h + st];
           lg = mx + __logf(e[0]);
         }
-        const int jb = t * kTile + 16 * (pass * NC + n) + l16;
+        const int jb = t * kTile + 16 * (n0 + n) + l16;
         const bool cand = jb >= 1 && jb <= nb - 2;
         a.lg[((size_t)tk * G + g) * row + jb] = cand ? lg : -INFINITY;
         if (a.lg_out && cand) a.lg_out[((size_t)tk * G + g) * a.max_blocks + jb] = lg;
@@ -162,7 +156,7 @@ constexpr int kPfScoreMaxRD = 512;
 
 template <bool BF16, bool TAYLOR>
 hipError_t launch_pf_score_form(const DecodeArgs& a, const Launch& l) {
-  const dim3 grid(a.score_tiles, a.G, (a.B + 63) / 64);
+  const dim3 grid(a.score_tiles, a.G, (a.B + 31) / 32);
 #define SPLA_PF_SCORE_CASE(R_, D_)                                                                               \
   case R_ * 1000 + D_:                                                                                         \
     return launch_kernel(k_pf_score<BF16, R_, D_, TAYLOR>, grid, l, a.blk_mean, a.blk_var, a.q, a.n_tiles, a.G, \
