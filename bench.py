@@ -90,6 +90,40 @@ def step_score_bytes(w, lens, s_kv: int) -> int:
     return tot
 
 
+def kernel_bytes(name: str, w, lens, s_kv: int) -> int:
+    """Algorithmic bytes of one launch of decode kernel ``name`` (a launch-plan
+    name) for sequence lengths ``lens`` (after the step's append): what the
+    method must move through that kernel, not its scratch traffic beyond the
+    partial records it hands to the next kernel."""
+    d, G, H, bk, k = w.head_dim, w.n_kv_heads, w.n_q_heads, w.block_size, w.top_k
+    r = H // G
+    chunks = d * d // 1024
+    rec = (2 * d + 4) * 4  # one partial record: m, l, sum w, pad, acc[d], o_tilde[d]
+    lg = kv = recs = 0
+    for T in lens:
+        nb = -(-T // bk)
+        used = min(nb, k)
+        if nb > k:
+            lg += G * (nb - 2) * 4
+            ntok = (k - 1) * bk + (T - (nb - 1) * bk)
+        else:
+            ntok = T
+        kv += G * ntok * 2 * d * s_kv
+        recs += G * r * used * rec
+    B = w.batch
+    if name == "step_score":
+        return step_score_bytes(w, lens, s_kv)
+    if name == "select":
+        return lg + B * G * k * 4 * 2
+    if name == "attend":
+        return kv + recs + B * H * d * s_kv
+    if name == "select_attend":
+        return lg + kv + recs + B * H * d * s_kv
+    if name == "combine":
+        return recs + B * G * chunks * r * (d + 1) * 4 + B * H * d * 4 + H * 4
+    raise ValueError(name)
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -392,6 +426,7 @@ def main() -> int:
     torch.cuda.synchronize()
     durs = {n: [] for n in names}
     score_launch_bytes = []
+    launch_bytes = {n: [] for n in names}
     lens_p = list(lens_end)
     for sets in ev_sets:
         lens_p = [t + 1 for t in lens_p]
@@ -399,6 +434,8 @@ def main() -> int:
             for i, n in enumerate(names):
                 durs[n].append(evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e-3)
         score_launch_bytes.append(step_score_bytes(w, lens_p, s_kv))
+        for n in names:
+            launch_bytes[n].append(kernel_bytes(n, w, lens_p, s_kv))
     avg = {n: float(np.mean(v)) for n, v in durs.items()}
 
     # calibration copy for the HBM byte counters (see CALIB_BYTES)
@@ -447,6 +484,13 @@ def main() -> int:
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic["bytes"] if traffic else None, "bytes_per_launch": sc_bytes,
                      "copy_probe_GBps": probe_gbs},
+        # every kernel of the step against the same HBM peak: the first kernel
+        # moves most of the step's bytes; the selection kernels take most of
+        # its time and are bound by latency, not bandwidth
+        "kernel_rooflines": [
+            {"kernel": n, "us": avg[n] * 1e6, "bytes_per_launch": float(np.mean(launch_bytes[n])),
+             "GBps": float(np.mean(launch_bytes[n])) / avg[n] / 1e9,
+             "frac": float(np.mean(launch_bytes[n])) / avg[n] / 1e9 / HBM_PEAK_GBS} for n in names],
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, K + W, args.cpu_budget, args.rla_form)

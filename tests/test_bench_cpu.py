@@ -1,0 +1,52 @@
+"""The benchmark's algorithmic byte counts (what the roofline fractions divide
+by), checked on the CPU against counts written out from the workload's shape:
+the 128K GQA step is 16.77 MB of candidate statistics + 8.26 MB of selected
+K/V + 1.06 MB of S_all / z_all, about 26.1 MB in all (the byte model of the
+decode step: statistics of the candidate blocks, the selected blocks' K and V,
+the state read and written)."""
+import importlib.util
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_step_bytes_128k(bench):
+    from workloads import WORKLOADS
+    w = WORKLOADS["llama_gqa_128k"]
+    T = 131073  # the first decode step after the 131072-token prefill
+    b = bench.step_bytes(w, [T], 2)
+    nb = 2049
+    assert b["stats"] == 8 * (nb - 2) * 2 * 128 * 4                     # 2047 candidates x 8 KV heads x 1 KB
+    assert b["kv"] == 8 * (31 * 64 + 1) * 2 * 128 * 2                   # 31 full blocks + the 1-token current one
+    assert b["state"] == 8 * 2 * (128 * 128 * 4 + 128 * 4)
+    assert abs(b["total"] / 26.1e6 - 1) < 0.01
+
+
+def test_kernel_bytes_partition(bench):
+    from workloads import WORKLOADS
+    w = WORKLOADS["llama_gqa_128k"]
+    lens = [131072 + 37]
+    s = bench.step_bytes(w, lens, 2)
+    fused = bench.kernel_bytes("select_attend", w, lens, 2)
+    split = bench.kernel_bytes("select", w, lens, 2) + bench.kernel_bytes("attend", w, lens, 2)
+    # the fused kernel reads the LG row and the selected K/V, reads q and writes
+    # the records; the split plan moves the same plus the selection hand-off
+    rec = 8 * 4 * 32 * (2 * 128 + 4) * 4
+    lg = 8 * ((131072 + 37 + 63) // 64 - 2) * 4
+    assert fused == lg + s["kv"] + rec + 32 * 128 * 2
+    assert split == fused + 8 * 32 * 4 * 2
+    assert bench.kernel_bytes("step_score", w, lens, 2) == bench.step_score_bytes(w, lens, 2)
+    # the combine reads every record once
+    assert bench.kernel_bytes("combine", w, lens, 2) > rec
+    with pytest.raises(ValueError):
+        bench.kernel_bytes("nope", w, lens, 2)
