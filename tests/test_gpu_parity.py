@@ -53,6 +53,16 @@ def test_block128_d64():
     _run(small(name="bk128_d64", head_dim=64, block_size=128, t0=(128 * 90 + 100,), top_k=12, steps=3))
 
 
+@pytest.mark.parametrize("bk", [64, 128])
+def test_split_plan_odd_top_k(bk):
+    # 8 sequences x 8 KV heads = 64 (sequence, KV head) pairs: the stand-alone
+    # selector and attend kernels; an odd top_k, ragged lengths, a sequence
+    # with every block selected
+    t0 = tuple(bk * n + e for n, e in ((40, 5), (3, 0), (61, 17), (25, 1), (50, 0), (33, 9), (12, 3), (70, 2)))
+    _run(small(name=f"split_odd_k_bk{bk}", batch=8, n_q_heads=32, n_kv_heads=8, block_size=bk, top_k=7, t0=t0, steps=2),
+         page_order="shuffled")
+
+
 def test_fp32_d128_outliers():
     _run(small(name="f32_outlier", kv_dtype="f32", kind="outlier", n_outlier=8, t0=(64 * 80,), steps=3))
 
