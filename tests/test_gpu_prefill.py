@@ -142,6 +142,14 @@ def test_prefill_fp32():
     _prefill_case(small(name="pf_f32", kv_dtype="f32", t0=(64 * 40 + 3,)), 0, 64 * 36 + 10, chunk=50)
 
 
+@pytest.mark.parametrize("n,chunk", [(1, 256), (3, 256), (40, 17)])
+def test_prefill_tiny_groups(n, chunk):
+    # one token, three tokens, and groups of 17: partial 16-token tiles of the
+    # linear-attention state, partial 4-token k-steps of the state append, a
+    # score tile of a handful of queries; the prefix ends inside a block
+    _prefill_case(small(name=f"pf_tiny_{n}_{chunk}", t0=(64 * 90 + 11 + n,)), 0, 64 * 90 + 11, chunk=chunk)
+
+
 @pytest.mark.parametrize("form", [1, 2])
 def test_prefill_rla_forms(form):
     _prefill_case(small(name=f"pf_form{form}", t0=(64 * 90 + 11,)), 0, 64 * 85, rla_form=form)
