@@ -150,38 +150,19 @@ __global__ __launch_bounds__(kThreads) void k_pf_score(const float* mean, const 
   }
 }
 
-// query heads x head dim up to 512: the A operand (R * D / 4 values per lane)
-// and the accumulators stay in registers
-constexpr int kPfScoreMaxRD = 512;
-
 template <bool BF16, bool TAYLOR>
 hipError_t launch_pf_score_form(const DecodeArgs& a, const Launch& l) {
   const dim3 grid(a.score_tiles, a.G, (a.B + 31) / 32);
-#define SPLA_PF_SCORE_CASE(R_, D_)                                                                               \
-  case R_ * 1000 + D_:                                                                                         \
-    return launch_kernel(k_pf_score<BF16, R_, D_, TAYLOR>, grid, l, a.blk_mean, a.blk_var, a.q, a.n_tiles, a.G, \
-                         a.H, a.B, a);
-  switch (a.r * 1000 + a.d) {
-    SPLA_PF_SCORE_CASE(1, 64)
-    SPLA_PF_SCORE_CASE(1, 128)
-    SPLA_PF_SCORE_CASE(2, 64)
-    SPLA_PF_SCORE_CASE(2, 128)
-    SPLA_PF_SCORE_CASE(4, 64)
-    SPLA_PF_SCORE_CASE(4, 128)
-    SPLA_PF_SCORE_CASE(8, 64)
-  }
-#undef SPLA_PF_SCORE_CASE
-  return hipErrorInvalidValue;
+  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_pf_score<BF16, RR, DD, TAYLOR>, grid, l, a.blk_mean, a.blk_var, a.q,
+                                           a.n_tiles, a.G, a.H, a.B, a))
 }
 
 }  // namespace
 
-bool pf_score_supported(const DecodeArgs& a) { return a.r * a.d <= kPfScoreMaxRD; }
-
 // virtual queries only: a.B tokens of one sequence, whose statistics rows the
 // pointers address
 hipError_t launch_pf_score(const DecodeArgs& a, bool bf16, const Launch& l) {
-  if (!a.virtual_queries || a.score_tiles <= 0 || !pf_score_supported(a)) return hipErrorInvalidValue;
+  if (!a.virtual_queries || a.score_tiles <= 0) return hipErrorInvalidValue;
   const bool mean = a.score_form == kScoreMean;
   if (bf16) return mean ? launch_pf_score_form<true, false>(a, l) : launch_pf_score_form<true, true>(a, l);
   return mean ? launch_pf_score_form<false, false>(a, l) : launch_pf_score_form<false, true>(a, l);

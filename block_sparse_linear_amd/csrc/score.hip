@@ -25,10 +25,8 @@ struct ScorePre {
 // query loads and then all of its statistics loads before the first wait.
 // TAYLOR = false is the first-order (mean-pooling) score q_hat . mean, which
 // reads no variances: the baseline the second-order selection is measured
-// against.  VQ: the batch is made of virtual queries of one sequence (the
-// tokens of a prefill chunk), whose statistics the pointers already address:
-// every b reads statistics row 0.
-template <bool BF16, int R, int D, bool TAYLOR, bool VQ = false>
+// against.
+template <bool BF16, int R, int D, bool TAYLOR>
 __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const int b, const ScorePre& p) {
   constexpr int NC4 = D / 16;  // channel quartets per wavefront
   constexpr int CW = D / 4;    // channels per wavefront
@@ -56,7 +54,7 @@ __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const 
   // statistics of the tile: 64 blocks x this wavefront's channels
   const float4* mean4 = reinterpret_cast<const float4*>(p.mean);
   const float4* var4 = reinterpret_cast<const float4*>(p.var);
-  const size_t base = (((size_t)(VQ ? 0 : b) * p.G + g) * p.n_tiles + t) * (size_t)(D / 4) * kTile +
+  const size_t base = (((size_t)b * p.G + g) * p.n_tiles + t) * (size_t)(D / 4) * kTile +
                       (size_t)(w * NC4) * kTile + lane;
   float4 m[NC4], v[NC4];
 #pragma unroll
@@ -150,20 +148,16 @@ __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const 
 //            every query head h of the group, from the rows just read or
 //            updated (so the token attends to itself): the combine sums the
 //            D * D / 1024 chunks and never reads S_all.
-// VQ: virtual queries of one sequence, whose state the pointers address (every
-// b reads state row 0; its partials are still per b).
-template <bool BF16, int R, int D, bool UPDATE, bool VQ = false>
+template <bool BF16, int R, int D, bool UPDATE>
 __device__ void state_rows(const DecodeArgs& dc, const StateRefs& st, int b, int g, int rc) {
   constexpr int ROWS = 1024 / D, C4N = D / 4, CHUNKS = D / ROWS;
-  static_assert(!(UPDATE && VQ), "virtual queries do not update the state");
   __shared__ float4 red[R][ROWS][C4N];
   __shared__ float zred[R][ROWS];
   const int xr = threadIdx.x / C4N, c4 = threadIdx.x % C4N;
   const int x = rc * ROWS + xr;
   const size_t bg = (size_t)b * dc.G + g;
-  const size_t sbg = VQ ? (size_t)g : bg;  // state row
-  float4* S = reinterpret_cast<float4*>(st.s_all) + (sbg * D + x) * C4N + c4;
-  float* z = st.z_all + sbg * D + x;
+  float4* S = reinterpret_cast<float4*>(st.s_all) + (bg * D + x) * C4N + c4;
+  float* z = st.z_all + bg * D + x;
   float4 s = *S;
   float zx = *z;
   float qx[R];
@@ -216,18 +210,18 @@ __device__ void state_rows(const DecodeArgs& dc, const StateRefs& st, int b, int
 // spla_decode, first launch, grid (score_tiles + D * D / 1024, G, B): for
 // each (b, g) the scorer's tiles, then the o_bar partials of the S_all row
 // chunks.
-template <bool BF16, int R, int D, bool TAYLOR, bool VQ>
+template <bool BF16, int R, int D, bool TAYLOR>
 __global__ __launch_bounds__(kThreads) void k_score(const float* mean, const float* var, const void* q,
                                                      int32_t n_tiles, int32_t G, int32_t H, int32_t tiles_all,
                                                      int32_t score_tiles, const StepArgs a) {
   const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   if (x < score_tiles) {
     const ScorePre p{mean, var, q, n_tiles, G, H, tiles_all};
-    score_tile<BF16, R, D, TAYLOR, VQ>(a.dec, x, g, b, p);
+    score_tile<BF16, R, D, TAYLOR>(a.dec, x, g, b, p);
     return;
   }
   SPLA_SCALARS_READY("s"(a.st.s_all), "s"(a.st.z_all), "s"(a.dec.obar_part), "s"(a.dec.dz_part));
-  state_rows<BF16, R, D, false, VQ>(a.dec, a.st, b, g, x - score_tiles);
+  state_rows<BF16, R, D, false>(a.dec, a.st, b, g, x - score_tiles);
 }
 
 // Fused decode step, first launch, grid (score_tiles + D * D / 1024 + 1, G,
@@ -262,15 +256,15 @@ __global__ __launch_bounds__(kThreads) void k_step_score(const float* mean, cons
   if (T % dc.bk == 0) append_block_stats<BF16>(a.st, E, T / dc.bk - 1, g);
 }
 
-template <bool TAYLOR, bool VQ>
+template <bool TAYLOR>
 hipError_t launch_score_form(const StepArgs& a, bool bf16, const Launch& l) {
   const DecodeArgs& d = a.dec;
   const int chunks = d.d / (1024 / d.d);
   const dim3 grid(d.score_tiles + chunks, d.G, d.B);
   if (bf16)
-    SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_score<true, RR, DD, TAYLOR, VQ>, grid, l, d.blk_mean, d.blk_var,
+    SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_score<true, RR, DD, TAYLOR>, grid, l, d.blk_mean, d.blk_var,
                                              d.q, d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
-  SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_score<false, RR, DD, TAYLOR, VQ>, grid, l, d.blk_mean, d.blk_var,
+  SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_score<false, RR, DD, TAYLOR>, grid, l, d.blk_mean, d.blk_var,
                                            d.q, d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
 }
 
@@ -289,10 +283,8 @@ hipError_t launch_step_score_form(const StepArgs& a, bool bf16, const Launch& l)
 }  // namespace
 
 hipError_t launch_score(const StepArgs& a, bool bf16, const Launch& l) {
-  const bool mean = a.dec.score_form == kScoreMean;
-  if (a.dec.virtual_queries)
-    return mean ? launch_score_form<false, true>(a, bf16, l) : launch_score_form<true, true>(a, bf16, l);
-  return mean ? launch_score_form<false, false>(a, bf16, l) : launch_score_form<true, false>(a, bf16, l);
+  if (a.dec.virtual_queries) return hipErrorInvalidValue;  // a prefill group is scored by k_pf_score
+  return a.dec.score_form == kScoreMean ? launch_score_form<false>(a, bf16, l) : launch_score_form<true>(a, bf16, l);
 }
 
 hipError_t launch_step_score(const StepArgs& a, bool bf16, const Launch& l) {

@@ -573,9 +573,7 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
     if (e != hipSuccess) return hip_fail(h, e);
     // (2) every token of the chunk decoded as a virtual query of this
     // sequence, against the state before the chunk
-    StepArgs sa;
-    memset(&sa, 0, sizeof(sa));
-    DecodeArgs& a = sa.dec;
+    DecodeArgs a;
     fill_decode_args(h, static_cast<const char*>(q) + (size_t)c0 * H * d * es, gate, out + (size_t)c0 * H * d,
                      nullptr, &a);
     a.B = m;
@@ -603,24 +601,12 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
     }
     a.score_tiles = max_tiles;
     a.tiles_all = min_tiles;
-    fill_state_refs(h, kc, vc, &sa.st);
-    sa.st.block_table = a.block_table;
-    sa.st.blk_mean = h->buf.blk_mean + (size_t)seq * stats_row;
-    sa.st.blk_var = h->buf.blk_var + (size_t)seq * stats_row;
-    sa.st.s_all = h->buf.s_all + (size_t)seq * G * d * d;
-    sa.st.z_all = h->buf.z_all + (size_t)seq * G * d;
-    if (pf_score_supported(a)) {
-      // the group's block scores, then phi(q_t)^T S_t and phi(q_t).z_t in one
-      // partial per head (state before the group plus its own tokens up to
-      // t) and phi(q), all on the matrix cores
-      if (a.score_tiles > 0 && (e = launch_pf_score(a, bf16, l)) != hipSuccess) return hip_fail(h, e);
-      if ((e = launch_pf_state(a, bf16, kc, vc, l)) != hipSuccess) return hip_fail(h, e);
-      a.obar_one = 1;
-    } else {
-      // per-token scorer with the state-row chunks, then the group's own tokens
-      if ((e = launch_score(sa, bf16, l)) != hipSuccess) return hip_fail(h, e);
-      if ((e = launch_chunk_la(a, bf16, kc, vc, l)) != hipSuccess) return hip_fail(h, e);
-    }
+    // the group's block scores, then phi(q_t)^T S_t and phi(q_t).z_t in one
+    // partial per head (state before the group plus its own tokens up to t)
+    // and phi(q), all on the matrix cores
+    if (a.score_tiles > 0 && (e = launch_pf_score(a, bf16, l)) != hipSuccess) return hip_fail(h, e);
+    if ((e = launch_pf_state(a, bf16, kc, vc, l)) != hipSuccess) return hip_fail(h, e);
+    a.obar_one = 1;
     if ((e = launch_select(a, l)) != hipSuccess) return hip_fail(h, e);
     // bf16: every selected block read once per item of up to kPfQ queries
     if ((e = bf16 ? launch_pf_attend(a, pb, l) : launch_attend(a, bf16, l)) != hipSuccess) return hip_fail(h, e);

@@ -164,8 +164,6 @@ hipError_t launch_pf_clear(const PfBuffers& pb, int G, int max_blocks, const Lau
 hipError_t launch_pf_attend(const DecodeArgs& a, const PfBuffers& pb, const Launch& l);
 // chunked prefill: the chunk's own tokens added into the o_bar / phi(q).z
 // partials of its virtual queries (k_new / v_new address the chunk's first row)
-hipError_t launch_chunk_la(const DecodeArgs& a, bool bf16, const void* k_new, const void* v_new, const Launch& l);
-bool pf_score_supported(const DecodeArgs& a);
 hipError_t launch_pf_score(const DecodeArgs& a, bool bf16, const Launch& l);
 hipError_t launch_pf_state(const DecodeArgs& a, bool bf16, const void* k_new, const void* v_new, const Launch& l);
 hipError_t launch_state_add(const AppendArgs& a, bool bf16, const Launch& l);

@@ -126,9 +126,8 @@ def test_prefill_group_ratios(r):
 
 @pytest.mark.parametrize("r", [2, 8])
 def test_prefill_group_ratios_d64(r):
-    # head dim 64: eight query heads per KV head stay on the matrix-core scorer
-    # (the 8 x 128 case above takes the per-token scorer); groups of 130
-    # tokens leave a partly filled last token tile
+    # head dim 64 with two and eight query heads per KV head; groups of 130
+    # tokens leave a partly filled last token tile of the matrix-core scorer
     _prefill_case(small(name=f"pf_r{r}_d64", n_q_heads=2 * r, head_dim=64, t0=(64 * 70 + 5,)), 0,
                   64 * 58 + 3, chunk=130)
 
