@@ -28,11 +28,13 @@ __device__ __forceinline__ float f4_at(const float4& v, int e) {
 // = lane / 16, so a lane's query channels are contiguous and its statistics
 // arrive as float4s of one channel quartet of the tile layout (64 blocks side
 // by side per quartet).  Accumulators: column tile x query head x (mean,
-// variance).  Queries and statistics are loaded two channel quartets ahead of
-// the products, so a wavefront holds few registers and several wavefronts
-// share a SIMD.
+// variance).  bf16 queries are held packed for the whole kernel; the
+// statistics stream one channel quartet ahead of the products, behind a
+// scheduling barrier (left alone, the scheduler sinks the loads to their first
+// use).  Up to four query heads, three wavefronts share a SIMD (168 registers
+// per lane at 4 x 128, a few spilled).
 template <bool BF16, int R, int D, bool TAYLOR>
-__global__ __launch_bounds__(kThreads) void k_pf_score(const float* mean, const float* var, const void* q,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(R <= 4 ? 3 : 1))) void k_pf_score(const float* mean, const float* var, const void* q,
                                                         int32_t n_tiles, int32_t G, int32_t H, int32_t m,
                                                         const DecodeArgs a) {
   constexpr int KS = D / 4;            // k-steps, and channels per k slot
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void k_pf_score(const float* mean, const 
   const float4* mean4 = reinterpret_cast<const float4*>(mean);
   const float4* var4 = reinterpret_cast<const float4*>(var);
   const size_t base = ((size_t)g * n_tiles + t) * (size_t)(D / 4) * kTile + (size_t)(kk * KQ) * kTile + l16;
-  constexpr int NBUF = 3;              // quartets in registers: the current one and two in flight
+  constexpr int NBUF = 2;              // quartets in registers: the current one and one in flight
   float4 bm[NBUF][NC], bv[NBUF][NC];
   auto load_b = [&](int j, int buf) {
 #pragma unroll
@@ -58,28 +60,31 @@ __global__ __launch_bounds__(kThreads) void k_pf_score(const float* mean, const 
       bv[buf][n] = TAYLOR ? var4[at] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
-  // ---- A: channel quartet j of this lane's KS query channels, every head, as
-  // fp32 (loaded two quartets ahead, like the statistics, so that only three
-  // quartets per head are held)
+  // ---- A: this lane's KS query channels of every head.  bf16 queries are
+  // held packed for the whole kernel (KS / 2 registers per head); fp32 ones
+  // stream a channel quartet at a time, two quartets ahead like the
+  // statistics.
+  constexpr int QW = BF16 ? KS / 8 : 1;  // 16-byte pieces of packed bf16 per head
+  uint4 qp[R][QW];
+  if constexpr (BF16) {
+#pragma unroll
+    for (int h = 0; h < R; ++h)
+#pragma unroll
+      for (int i = 0; i < QW; ++i)
+        qp[h][i] = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) +
+                                                  ((size_t)tok * H + g * R + h) * D + kk * KS)[i];
+  }
   float4 qa[NBUF][R];
   auto load_a = [&](int j, int buf) {
+    if constexpr (!BF16) {
 #pragma unroll
-    for (int h = 0; h < R; ++h) {
-      const size_t off = ((size_t)tok * H + g * R + h) * D + kk * KS + 4 * j;
-      if constexpr (BF16) {
-        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(q) + off);
-        qa[buf][h] = make_float4(bf16_lo_f(u.x), bf16_hi_f(u.x), bf16_lo_f(u.y), bf16_hi_f(u.y));
-      } else {
-        qa[buf][h] = *reinterpret_cast<const float4*>(static_cast<const float*>(q) + off);
-      }
+      for (int h = 0; h < R; ++h)
+        qa[buf][h] = *reinterpret_cast<const float4*>(static_cast<const float*>(q) +
+                                                      ((size_t)tok * H + g * R + h) * D + kk * KS + 4 * j);
     }
   };
   load_b(0, 0);
   load_a(0, 0);
-  if (KQ > 1) {
-    load_b(1, 1);
-    load_a(1, 1);
-  }
   SPLA_SCALARS_READY("s"(a.bk), "s"(a.lg), "s"(a.lg_out), "s"(a.max_blocks), "s"(a.inv_sqrt_d));
 
   const float half_inv_d = 0.5f / (float)D;
@@ -93,15 +98,26 @@ __global__ __launch_bounds__(kThreads) void k_pf_score(const float* mean, const 
       for (int h = 0; h < R; ++h) cm[n][h] = cv[n][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KQ; ++j) {
-      if (j + 2 < KQ) {
-        load_b(j + 2, (j + 2) % NBUF);
-        load_a(j + 2, (j + 2) % NBUF);
+      if (j + 1 < KQ) {
+        load_b(j + 1, (j + 1) % NBUF);
+        load_a(j + 1, (j + 1) % NBUF);
       }
+      // the prefetch stays ahead of this step's products (left alone, the
+      // scheduler sinks the loads to their first use)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
 #pragma unroll
         for (int h = 0; h < R; ++h) {
-          const float qk = f4_at(qa[j % NBUF][h], e);
+          float qk;
+          if constexpr (BF16) {
+            const int c = 4 * j + e;  // channel of the lane's run
+            const uint4& u = qp[h][c / 8];
+            const uint32_t wd = (c % 8) / 2 == 0 ? u.x : (c % 8) / 2 == 1 ? u.y : (c % 8) / 2 == 2 ? u.z : u.w;
+            qk = c % 2 == 0 ? bf16_lo_f(wd) : bf16_hi_f(wd);
+          } else {
+            qk = f4_at(qa[j % NBUF][h], e);
+          }
           const float q2 = qk * qk;
 #pragma unroll
           for (int n = 0; n < NC; ++n) {

@@ -228,7 +228,6 @@ __global__ __launch_bounds__(kThreads) void k_state_add(const AppendArgs a) {
 #pragma unroll
   for (int c = 0; c < CPL; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float zs = 0.f;
-#pragma unroll 4
   for (int ks = w; ks < nks; ks += 4) {
     const int t = 4 * ks + kk;
     const size_t row = ((size_t)(E.row + min(t, m - 1)) * G + g) * D;
