@@ -17,6 +17,18 @@ namespace spla {
 
 namespace {
 
+// max of two floats below +inf (finite logits or the -inf of an empty row) in
+// one instruction, the median of x, y and the largest float: fmaxf first quiets
+// signalling NaNs, one more instruction per operand that comes from LDS or
+// another lane, and the median with +inf is folded back into fmaxf
+__device__ __forceinline__ float max_nn(float x, float y) { return __builtin_amdgcn_fmed3f(x, y, 3.402823466e38f); }
+__device__ __forceinline__ float row16_max_nn(float v) {
+  v = max_nn(v, dpp_f<kDppXor1>(v, v));
+  v = max_nn(v, dpp_f<kDppXor2>(v, v));
+  v = max_nn(v, dpp_f<kDppRowHalfMirror>(v, v));
+  return max_nn(v, dpp_f<kDppRowMirror>(v, v));
+}
+
 // grid (ceil(G * max_blocks / 256)): the per-block counts start at zero
 __global__ __launch_bounds__(kThreads) void k_pf_clear(int32_t* cnt, int32_t n) {
   const int i = blockIdx.x * kThreads + threadIdx.x;
@@ -82,14 +94,23 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
   constexpr int MT2 = 4;                   // row tiles of product (2): hi/lo rows of p and w of 16 rows
   constexpr int KS2 = BK / 32;             // token k-steps of product (2)
   constexpr int VS = BK + 8;               // row stride (elements) of the transposed V tile
-  constexpr int PS = BK + 8;               // row stride of the p / w rows
+  // p / w rows: stride BK + 8 elements, odd (lo) rows shifted by 4 more words
+  // into their pad and rows 8 u .. 8 u + 7 by 16 u words (the shifts only
+  // grow, so rows never overlap), so that the 32 words one ds_write_b32 of a
+  // half-wavefront stores (lane groups 0-1 or 2-3, hi and lo rows, 8 token
+  // pairs) fall in 32 different banks.  Three workgroups still fit a CU's LDS
+  // at 4 x 128.
+  constexpr int PS = BK + 8;
+  auto pw_row = [](int row) { return row * PS + 8 * (row & 1) + 32 * (row >> 3); };
   constexpr int NV = BK * D / (16 * kThreads);  // token-pair x 8-channel pieces per thread
   constexpr int QE = R * 3 * D;            // staged elements per query: raw q, phi(q) hi, lo per head
   __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
-  __shared__ __attribute__((aligned(16))) uint16_t pw[MT2 * 16 * PS];
+  __shared__ __attribute__((aligned(16))) uint16_t pw[MT2 * 16 * PS + 8 + 32 * (MT2 * 2 - 1)];
   __shared__ __attribute__((aligned(16))) uint16_t qs[kPfQ * QE];
   __shared__ float s_max[4][16], s_l[4][16], s_sw[4][16];
   __shared__ int s_code[kPfQ];
+  __shared__ int s_len[kPfQ];     // length of each query's sequence prefix (its causal limit)
+  __shared__ size_t s_dst[16];    // partial record (float index) of each A row of the current batch
   // the item (the array holds max_items records, so any workgroup may read
   // its own) and the count, in one round trip
   const int4* itp = items + (size_t)blockIdx.x * kPfItemInts / 4;
@@ -127,7 +148,10 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
   }
   // the codes through LDS (each piece needs the code of its own query), then
   // the item's queries: q and phi(q) hi / lo, staged for every query of the loop
-  if (threadIdx.x < kPfQ) s_code[threadIdx.x] = my_code;
+  if (threadIdx.x < kPfQ) {
+    s_code[threadIdx.x] = my_code;
+    s_len[threadIdx.x] = a.lens[my_code >> 8];
+  }
   __syncthreads();
   constexpr int QPT = (kPfQ * QE / 8 + kThreads - 1) / kThreads;  // 8-element pieces per thread
   static_assert(QPT <= 12, "at most 12 staged query pieces per thread");
@@ -209,18 +233,21 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
   const int eh = l16 % R, ee = l16 / R;
   for (int b0 = 0; b0 < n; b0 += QB) {
     const int nb = min(QB, n - b0);
-    // ---- A operands of product (1): q rows and phi(q) hi / lo rows of the batch (zero past its end)
-    const uint32_t mk = ee < nb ? 0xffffffffu : 0u;
+    // ---- A operands of product (1): q rows and phi(q) hi / lo rows of the
+    // batch.  Rows past its end repeat its last query: a result row depends on
+    // its own A row only, and those rows are never stored.
     const uint16_t* qe = qs + min(b0 + ee, n - 1) * QE + eh * 3 * D;
     uint4 aq[NKS], afh[NKS], afl[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const uint4 x0 = *reinterpret_cast<const uint4*>(qe + 0 * D + 32 * ks + 8 * lg4);
-      const uint4 x1 = *reinterpret_cast<const uint4*>(qe + 1 * D + 32 * ks + 8 * lg4);
-      const uint4 x2 = *reinterpret_cast<const uint4*>(qe + 2 * D + 32 * ks + 8 * lg4);
-      aq[ks] = make_uint4(x0.x & mk, x0.y & mk, x0.z & mk, x0.w & mk);
-      afh[ks] = make_uint4(x1.x & mk, x1.y & mk, x1.z & mk, x1.w & mk);
-      afl[ks] = make_uint4(x2.x & mk, x2.y & mk, x2.z & mk, x2.w & mk);
+      aq[ks] = *reinterpret_cast<const uint4*>(qe + 0 * D + 32 * ks + 8 * lg4);
+      afh[ks] = *reinterpret_cast<const uint4*>(qe + 1 * D + 32 * ks + 8 * lg4);
+      afl[ks] = *reinterpret_cast<const uint4*>(qe + 2 * D + 32 * ks + 8 * lg4);
+    }
+    if ((int)threadIdx.x < 16) {
+      const int r = threadIdx.x, e = r / R, h = r % R;
+      const int cd = s_code[min(b0 + e, n - 1)];
+      s_dst[r] = (((size_t)(cd >> 8) * a.H + g * R + h) * a.top_k + (cd & 255)) * rec;
     }
     // ---- product (1): logits s = q.k and linear weights w = phi(q).phi(k) of this wavefront's tokens
     f32x4_t cs[NT1W], cw[NT1W];
@@ -242,8 +269,7 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * lg4 + i;
-      const int e = min(b0 + r / R, n - 1);
-      ntok[i] = min(BK, a.lens[s_code[e] >> 8] - j * BK);
+      ntok[i] = min(BK, s_len[min(b0 + r / R, n - 1)] - j * BK);
     }
     float mloc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
@@ -251,22 +277,26 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
       const int tok = (w * NT1W + nt) * 16 + l16;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (tok < ntok[i]) mloc[i] = fmaxf(mloc[i], cs[nt][i] * inv_sqrt_d);
+        if (tok < ntok[i]) mloc[i] = max_nn(mloc[i], cs[nt][i] * inv_sqrt_d);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mloc[i] = row16_max(mloc[i]);
+    for (int i = 0; i < 4; ++i) mloc[i] = row16_max_nn(mloc[i]);
     if (l16 == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_max[w][4 * lg4 + i] = mloc[i];
     }
     __syncthreads();
     // ---- p = exp(s - m) and w, split hi/lo, into the rows of product (2):
-    // row pair 2 (kind 16 + r) (hi) and + 1 (lo), kind 0 = p, 1 = w
+    // row pair 2 (kind 16 + r) (hi) and + 1 (lo), kind 0 = p, 1 = w.  The
+    // lanes of a token pair (2 u, 2 u + 1) trade values so that each stores
+    // whole words: the even lane the hi row's word of both tokens, the odd
+    // lane the lo row's.
+    const bool odd = l16 & 1;
     float lsum[4] = {0.f, 0.f, 0.f, 0.f}, wsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * lg4 + i;
-      const float mh = fmaxf(fmaxf(s_max[0][r], s_max[1][r]), fmaxf(s_max[2][r], s_max[3][r]));
+      const float mh = max_nn(max_nn(s_max[0][r], s_max[1][r]), max_nn(s_max[2][r], s_max[3][r]));
 #pragma unroll
       for (int nt = 0; nt < NT1W; ++nt) {
         const int tok = (w * NT1W + nt) * 16 + l16;
@@ -275,14 +305,18 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
         const float wx = valid ? cw[nt][i] : 0.f;
         lsum[i] += px;
         wsum[i] += wx;
-        const uint32_t ph = pack_bf16(px, 0.f) & 0xffffu;
-        const uint32_t pl = pack_bf16(px - bf16_lo_f(ph), 0.f) & 0xffffu;
-        const uint32_t wh = pack_bf16(wx, 0.f) & 0xffffu;
-        const uint32_t wl = pack_bf16(wx - bf16_lo_f(wh), 0.f) & 0xffffu;
-        pw[(2 * r) * PS + tok] = (uint16_t)ph;
-        pw[(2 * r + 1) * PS + tok] = (uint16_t)pl;
-        pw[(2 * (16 + r)) * PS + tok] = (uint16_t)wh;
-        pw[(2 * (16 + r) + 1) * PS + tok] = (uint16_t)wl;
+        // residuals below the bf16 hi parts; the even lane sends its residual,
+        // the odd lane its value
+        const float pr = px - bf16_lo_f(pack_bf16(px, 0.f));
+        const float wr = wx - bf16_lo_f(pack_bf16(wx, 0.f));
+        const float ps = odd ? px : pr, ws = odd ? wx : wr;
+        const float pn = dpp_f<kDppXor1>(ps, ps), wn = dpp_f<kDppXor1>(ws, ws);
+        // even: hi(t), hi(t + 1); odd: lo(t - 1), lo(t)
+        const uint32_t pword = odd ? pack_bf16(pn, pr) : pack_bf16(px, pn);
+        const uint32_t wword = odd ? pack_bf16(wn, wr) : pack_bf16(wx, wn);
+        const int col = tok & ~1;
+        *reinterpret_cast<uint32_t*>(&pw[pw_row(2 * r + odd) + col]) = pword;
+        *reinterpret_cast<uint32_t*>(&pw[pw_row(2 * (16 + r) + odd) + col]) = wword;
       }
     }
 #pragma unroll
@@ -307,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
         f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS2; ++ks) {
-          const uint4 av = *reinterpret_cast<const uint4*>(&pw[(mt * 16 + l16) * PS + 32 * ks + 8 * lg4]);
+          const uint4 av = *reinterpret_cast<const uint4*>(&pw[pw_row(mt * 16 + l16) + 32 * ks + 8 * lg4]);
           const uint4 bv = *reinterpret_cast<const uint4*>(&vt[ch * VS + 32 * ks + 8 * lg4]);
           c = mfma_bf16(av, bv, c);
         }
@@ -316,21 +350,16 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
 #pragma unroll
         for (int e2 = 0; e2 < 2; ++e2) {
           const int pi = 8 * mt + 2 * lg4 + e2;
-          const int kind = pi / 16, r = pi % 16, e = r / R, h = r % R;
-          if (e < nb) {
-            const int cd = s_code[b0 + e];
-            float* dst = a.part + (((size_t)(cd >> 8) * a.H + g * R + h) * a.top_k + (cd & 255)) * rec;
-            dst[kPartHdr + (kind ? D : 0) + ch] = c[2 * e2] + c[2 * e2 + 1];
-          }
+          const int kind = pi / 16, r = pi % 16;
+          if (r / R < nb) a.part[s_dst[r] + kPartHdr + (kind ? D : 0) + ch] = c[2 * e2] + c[2 * e2 + 1];
         }
       }
     }
     if ((int)threadIdx.x < 16) {
-      const int r = threadIdx.x, e = r / R, h = r % R;
-      if (e < nb) {
-        const int cd = s_code[b0 + e];
-        float* dst = a.part + (((size_t)(cd >> 8) * a.H + g * R + h) * a.top_k + (cd & 255)) * rec;
-        dst[0] = fmaxf(fmaxf(s_max[0][r], s_max[1][r]), fmaxf(s_max[2][r], s_max[3][r]));
+      const int r = threadIdx.x;
+      if (r / R < nb) {
+        float* dst = a.part + s_dst[r];
+        dst[0] = max_nn(max_nn(s_max[0][r], s_max[1][r]), max_nn(s_max[2][r], s_max[3][r]));
         dst[1] = (s_l[0][r] + s_l[1][r]) + (s_l[2][r] + s_l[3][r]);
         dst[2] = (s_sw[0][r] + s_sw[1][r]) + (s_sw[2][r] + s_sw[3][r]);
         dst[3] = 0.f;
