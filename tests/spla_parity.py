@@ -56,7 +56,7 @@ def check_selection(sel_row, lg: Dict[int, float], nb: int, top_k: int) -> Optio
         return f"expected {top_k} blocks, got {len(valid)}"
     P = [j for j in valid if 0 < j < nb - 1]
     out = [j for j in range(1, nb - 1) if j not in set(P)]
-    if not out:
+    if not out or not P:  # nothing left out, or top_k = 2 (sink and current only)
         return None
     lo = min(lg[j] for j in P)
     hi = max(lg[j] for j in out)
