@@ -14,6 +14,11 @@ fp32 pages, the four input kinds, identity or shuffled pages, the plain and
 the fused decode step, fused or split selection, sometimes chunk appends.
 Prefill cases: 1-600 tokens through one spla_prefill call after a random
 prefix, in groups of 16-256 tokens.
+Long cases: one per keys-per-thread size of the selectors from 2 to 32
+(each a template instance of its own): a single sequence whose candidate
+count falls well inside that size's range (up to 8192 candidates, about 1M
+tokens), one KV head of head dim 64, top_k 2-256, the fused and the split
+selection in turn.
 """
 import random
 
@@ -77,8 +82,30 @@ def _prefill_cases():
     return out
 
 
+# keys-per-thread sizes of the selectors, in order; a selection of nc
+# candidates runs the smallest size K with 256 K >= nc
+SEL_SIZES = [1, 2, 3, 4, 6, 8, 9, 10, 12, 16, 20, 24, 32]
+
+
+def _long_cases():
+    rnd = random.Random(20261205)
+    out = []
+    for i in range(1, len(SEL_SIZES)):
+        lo, hi = 256 * SEL_SIZES[i - 1], 256 * SEL_SIZES[i]
+        nc = rnd.randint(lo + 32, hi - 32)  # candidates after the steps' appends stay inside (lo, hi]
+        bk = 64 if SEL_SIZES[i] <= 12 else 128
+        t0 = (nc + 2) * bk - rnd.randint(8, bk - 1) - 3
+        w = Workload(name=f"randl{SEL_SIZES[i]}", batch=1, n_q_heads=rnd.choice([1, 2, 4, 8]), n_kv_heads=1,
+                     head_dim=64, block_size=bk, top_k=rnd.randint(2, 256),
+                     kv_dtype=rnd.choice(["bf16", "f32"]), t0=(t0,), steps=2,
+                     kind=rnd.choice(["normal", "mixture"]), seed=7000 + i)
+        out.append((w, rnd.choice(["identity", "shuffled"]), rnd.random() < 0.5, i % 2))
+    return out
+
+
 DECODE = _decode_cases()
 PREFILL = _prefill_cases()
+LONG = _long_cases()
 
 
 @pytest.mark.parametrize("i", range(N_DECODE))
@@ -99,3 +126,16 @@ def test_random_prefill_config(i):
     from tests.test_gpu_prefill import _prefill_case
     w, seq, split, chunk = PREFILL[i]
     _prefill_case(w, seq, split, chunk=chunk)
+
+
+@pytest.mark.parametrize("i", range(len(SEL_SIZES) - 1))
+def test_random_long_config(i):
+    _needs_gpu()
+    from tests.spla_parity import ParityRun
+    w, pages, use_step, fused = LONG[i]
+    nb = -(-w.t0[0] // w.block_size)
+    print(f"[case] {w.name} H={w.n_q_heads} G=1 d={w.head_dim} Bk={w.block_size} k={w.top_k} {w.kv_dtype} "
+          f"kind={w.kind} t0={w.t0[0]} candidates={nb - 2}.. pages={pages} step={use_step} fused={fused}", flush=True)
+    run = ParityRun(w, page_order=pages, prefill_chunk=65536, use_step=use_step, fused_select=fused)
+    failures = run.run(verbose=True)
+    assert not failures, "\n".join(failures[:20])
