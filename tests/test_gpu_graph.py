@@ -3,7 +3,9 @@ captured spla_decode agrees bitwise with the eager call on the same inputs,
 replay after replay, with eager decodes of other queries (which overwrite the
 workspace) and synchronisations in between; captured spla_decode_step
 graphs, replayed in step order from a restored state, agree bitwise with the
-eager steps, twice over."""
+eager steps, twice over; a captured spla_prefill (several launch groups),
+replayed from the restored state three times with eager work in between,
+agrees bitwise with the eager call in its outputs, selections and state."""
 import numpy as np
 import pytest
 
@@ -129,4 +131,56 @@ def test_step_graphs_match_eager():
         for a, b in zip(L.state_tensors(), end_state):
             assert torch.equal(a, b), f"round {rnd}: state after the replayed steps differs"
     assert L.lens == [t + n for t in snap[1]]
+    assert L.error_word() == 0
+
+
+def test_prefill_graph_replays_match_eager():
+    _needs_gpu()
+    import torch
+    from tests.spla_parity import ParityRun
+    w = small(name="graph_prefill", batch=2, t0=(64 * 60 + 17, 64 * 20 + 3), steps=1, extra_capacity_tokens=400)
+    seq, n, chunk = 0, 300, 128
+    print(f"[case] graph prefill seq={seq} n={n} chunk={chunk}", flush=True)
+    run = ParityRun(w, steps=1, page_order="shuffled")
+    run.prefill()
+    L = run.layer
+    snap = L.snapshot()
+    rng = np.random.default_rng(11)
+    G, H, d = w.n_kv_heads, w.n_q_heads, w.head_dim
+    k = run.dev(w.round(rng.standard_normal((n, G, d)).astype(np.float32)))
+    v = run.dev(w.round(rng.standard_normal((n, G, d)).astype(np.float32)))
+    q = run.dev(w.round(rng.standard_normal((n, H, d)).astype(np.float32)))
+    ws = torch.empty(L.handle.prefill_workspace_bytes(chunk) // 4 + 64, dtype=torch.int32, device=L.device)
+    # eager call
+    out_e = torch.zeros((n, H, d), dtype=torch.float32, device=L.device)
+    sel_e = torch.zeros((n, G, w.top_k), dtype=torch.int32, device=L.device)
+    L.prefill(seq, k, v, q, run.gate, out=out_e, chunk=chunk, workspace=ws, sel_idx=sel_e)
+    torch.cuda.synchronize()
+    ref_out, ref_sel = out_e.cpu().numpy(), sel_e.cpu().numpy()
+    end_state = [x.clone() for x in L.state_tensors()]
+    # capture the same call from the restored state
+    L.restore(snap)
+    out_g = torch.zeros_like(out_e)
+    sel_g = torch.zeros_like(sel_e)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.prefill(seq, k, v, q, run.gate, out=out_g, chunk=chunk, workspace=ws, sel_idx=sel_g)
+    torch.cuda.synchronize()
+    for rnd in range(3):
+        # back to the state before the call by plain copies, and eager work
+        # on the workspace and outputs in between (the graph carries its own
+        # lengths)
+        for dst, src in zip(L.state_tensors(), snap[0]):
+            dst.copy_(src)
+        ws.fill_(-1)
+        out_g.fill_(float("nan"))
+        sel_g.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out_g.cpu().numpy(), ref_out), f"replay {rnd}: outputs differ"
+        assert np.array_equal(sel_g.cpu().numpy(), ref_sel), f"replay {rnd}: selections differ"
+        for a, b in zip(L.state_tensors(), end_state):
+            assert torch.equal(a, b), f"replay {rnd}: state after the call differs"
+    assert L.lens[seq] == snap[1][seq] + n
     assert L.error_word() == 0
