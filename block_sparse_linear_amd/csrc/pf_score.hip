@@ -166,11 +166,173 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(R <= 4
   }
 }
 
+// The same scorer for bf16 queries on the bf16 matrix cores (16x16x32,
+// fp32 sums).  The products stay exact to fp32 level: q is bf16 already;
+// every statistic is split exactly into three bf16 parts (hi, mid, lo: 8 bits
+// each of its 24) and q^2 into two; q . mean takes the three parts and
+// q^2 . var the five products of the parts above 2^-32 of their sum.  At
+// eight 16x16x32 products per 32 channels and (column tile, head) against
+// sixteen 16x16x4 fp32 ones, the matrix cores take a quarter of the time.
+// Mapping as in k_pf_score; lane (l16, lg4) takes channels 32 ks + 8 lg4 ..
+// + 7 of k-step ks: its A row is token l16's query, its B column block l16's
+// statistics (two float4 channel quartets of the tile layout).
+typedef __bf16 bf16x8s_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16x32(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8s_t, a), __builtin_bit_cast(bf16x8s_t, b),
+                                                  c, 0, 0, 0);
+}
+
+// 8 floats -> bf16 hi, mid, lo parts (hi + mid + lo == x exactly), pairs packed
+__device__ __forceinline__ void split3(const float4& u, const float4& v, uint4& hi, uint4& mid, uint4& lo) {
+  const float x[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    h[p] = pack_bf16(x[2 * p], x[2 * p + 1]);
+    const float r0 = x[2 * p] - bf16_lo_f(h[p]), r1 = x[2 * p + 1] - bf16_hi_f(h[p]);
+    m[p] = pack_bf16(r0, r1);
+    l[p] = pack_bf16(r0 - bf16_lo_f(m[p]), r1 - bf16_hi_f(m[p]));
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  mid = make_uint4(m[0], m[1], m[2], m[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+template <int R, int D, bool TAYLOR>
+__global__ __launch_bounds__(kThreads) void k_pf_score_bf(const float* mean, const float* var, const void* q,
+                                                           int32_t n_tiles, int32_t G, int32_t H, int32_t m,
+                                                           const DecodeArgs a) {
+  constexpr int KS = D / 32;  // k-steps of 32 channels
+  constexpr int NC = 2;       // column tiles per wavefront
+  const int t = blockIdx.x, g = blockIdx.y;
+  const int w = threadIdx.x / 64, lane = threadIdx.x % 64, l16 = lane % 16, lg4 = lane / 16;
+  const int tok0 = 32 * blockIdx.z + 16 * (w >> 1);
+  const int n0 = NC * (w & 1);
+  const int tok = min(tok0 + l16, m - 1);  // A row (rows past the group repeat the last token, never stored)
+  const float4* mean4 = reinterpret_cast<const float4*>(mean);
+  const float4* var4 = reinterpret_cast<const float4*>(var);
+  const size_t base = ((size_t)g * n_tiles + t) * (size_t)(D / 4) * kTile + 16 * n0 + l16;
+  const uint4* qrow = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) +
+                                                     ((size_t)tok * H + g * R) * D + 8 * lg4);
+  // raw operands of one k-step: statistics (two quartets per column tile) and queries
+  struct Raw {
+    float4 bm[NC][2], bv[NC][2];
+    uint4 qa[R];
+  };
+  auto load = [&](int ks, Raw& r) {
+#pragma unroll
+    for (int n = 0; n < NC; ++n)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const size_t at = base + (size_t)(8 * ks + 2 * lg4 + e) * kTile + 16 * n;
+        r.bm[n][e] = mean4[at];
+        r.bv[n][e] = TAYLOR ? var4[at] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int h = 0; h < R; ++h) r.qa[h] = qrow[(size_t)h * D / 8 + 4 * ks];
+  };
+  Raw cur, nxt;
+  load(0, cur);
+  SPLA_SCALARS_READY("s"(a.bk), "s"(a.lg), "s"(a.lg_out), "s"(a.max_blocks), "s"(a.inv_sqrt_d));
+  f32x4_t cm[NC][R], cv[NC][R];
+#pragma unroll
+  for (int n = 0; n < NC; ++n)
+#pragma unroll
+    for (int h = 0; h < R; ++h) cm[n][h] = cv[n][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (ks + 1 < KS) load(ks + 1, nxt);
+    // the next k-step's loads stay ahead of this one's products
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 mh[NC], mm[NC], ml[NC], vh[NC], vm[NC], vl[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      split3(cur.bm[n][0], cur.bm[n][1], mh[n], mm[n], ml[n]);
+      if (TAYLOR) split3(cur.bv[n][0], cur.bv[n][1], vh[n], vm[n], vl[n]);
+    }
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      const uint4 qv = cur.qa[h];
+      uint4 sh, sl;
+      if (TAYLOR) {
+        const uint32_t in[4] = {qv.x, qv.y, qv.z, qv.w};
+        uint32_t oh[4], ol[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float a0 = bf16_lo_f(in[p]), a1 = bf16_hi_f(in[p]);
+          const float s0 = a0 * a0, s1 = a1 * a1;  // exact: 16 significant bits
+          oh[p] = pack_bf16(s0, s1);
+          ol[p] = pack_bf16(s0 - bf16_lo_f(oh[p]), s1 - bf16_hi_f(oh[p]));
+        }
+        sh = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+        sl = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+      }
+#pragma unroll
+      for (int n = 0; n < NC; ++n) {
+        cm[n][h] = mfma_bf16x32(qv, ml[n], cm[n][h]);
+        cm[n][h] = mfma_bf16x32(qv, mm[n], cm[n][h]);
+        cm[n][h] = mfma_bf16x32(qv, mh[n], cm[n][h]);
+        if (TAYLOR) {
+          cv[n][h] = mfma_bf16x32(sl, vm[n], cv[n][h]);
+          cv[n][h] = mfma_bf16x32(sh, vl[n], cv[n][h]);
+          cv[n][h] = mfma_bf16x32(sl, vh[n], cv[n][h]);
+          cv[n][h] = mfma_bf16x32(sh, vm[n], cv[n][h]);
+          cv[n][h] = mfma_bf16x32(sh, vh[n], cv[n][h]);
+        }
+      }
+    }
+    if (ks + 1 < KS) cur = nxt;
+  }
+
+  // ---- log scores, group logsumexp: lane holds tokens 4 lg4 + i, block 16 n + l16
+  const float half_inv_d = 0.5f / (float)D;
+  const size_t row = (size_t)n_tiles * kTile;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tk = tok0 + 4 * lg4 + i;
+    if (tk >= m) continue;
+    const int nb = (a.lens[tk] + a.bk - 1) / a.bk;
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      float ls[R];
+#pragma unroll
+      for (int h = 0; h < R; ++h)
+        ls[h] = TAYLOR ? cm[n][h][i] * a.inv_sqrt_d + __logf(1.f + fmaxf(cv[n][h][i], 0.f) * half_inv_d)
+                       : cm[n][h][i] * a.inv_sqrt_d;
+      float lg = ls[0];
+      if constexpr (R > 1) {
+        float mx = ls[0];
+#pragma unroll
+        for (int h = 1; h < R; ++h) mx = fmaxf(mx, ls[h]);
+        float e[R];
+#pragma unroll
+        for (int h = 0; h < R; ++h) e[h] = __expf(ls[h] - mx);
+        // pairwise, in the decode scorer's order
+#pragma unroll
+        for (int st = 1; st < R; st *= 2)
+#pragma unroll
+          for (int h = 0; h < R; h += 2 * st) e[h] += e[h + st];
+        lg = mx + __logf(e[0]);
+      }
+      const int jb = t * kTile + 16 * (n0 + n) + l16;
+      const bool cand = jb >= 1 && jb <= nb - 2;
+      a.lg[((size_t)tk * G + g) * row + jb] = cand ? lg : -INFINITY;
+      if (a.lg_out && cand) a.lg_out[((size_t)tk * G + g) * a.max_blocks + jb] = lg;
+    }
+  }
+}
+
 template <bool BF16, bool TAYLOR>
 hipError_t launch_pf_score_form(const DecodeArgs& a, const Launch& l) {
   const dim3 grid(a.score_tiles, a.G, (a.B + 31) / 32);
-  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_pf_score<BF16, RR, DD, TAYLOR>, grid, l, a.blk_mean, a.blk_var, a.q,
-                                           a.n_tiles, a.G, a.H, a.B, a))
+  if constexpr (BF16) {
+    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_pf_score_bf<RR, DD, TAYLOR>, grid, l, a.blk_mean, a.blk_var, a.q,
+                                             a.n_tiles, a.G, a.H, a.B, a))
+  } else {
+    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_pf_score<BF16, RR, DD, TAYLOR>, grid, l, a.blk_mean, a.blk_var,
+                                             a.q, a.n_tiles, a.G, a.H, a.B, a))
+  }
 }
 
 }  // namespace
