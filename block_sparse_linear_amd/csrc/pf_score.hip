@@ -7,8 +7,10 @@
 // or the first-order (mean-pooling) form.  Over a group both sums are matrix
 // products, [tokens x d] by [d x blocks] per query head, so one workgroup
 // reads a 64-block statistics tile once for 32 tokens instead of once per
-// token, and the fp32 matrix cores (16x16x4, fp32 in and out) do the
-// products at the full fp32 rate.
+// token.  fp32 queries use the fp32 matrix cores (16x16x4, fp32 in and out,
+// k_pf_score); bf16 queries use the bf16 matrix cores on exact bf16 splits of
+// the fp32 operands (k_pf_score_bf), which gives the same products in a
+// quarter of the matrix-core time.
 #include "decode_common.h"
 
 namespace spla {
