@@ -58,10 +58,23 @@ __global__ __launch_bounds__(kThreads) void k_pf_items(int32_t* cnt, const int32
   const size_t cell = (size_t)g * max_blocks + j;
   const int c = j < max_blocks ? min(cnt[cell], cap) : 0;
   const int nch = (c + kPfQ - 1) / kPfQ;
+  // places in the item list: one atomic per workgroup (nearly every block has
+  // items, and atomics on the one counter queue at the cache), the
+  // wavefronts' totals through LDS
+  __shared__ int s_wsum[kThreads / 64], s_base;
+  const int w = threadIdx.x / 64;
   const int incl = wave_incl_scan_i(nch);
-  int base = 0;
-  if (lane == 63 && incl > 0) base = atomicAdd(n_items, incl);
-  base = __builtin_amdgcn_readlane(base, 63) + incl - nch;
+  if (lane == 63) s_wsum[w] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tot = 0;
+#pragma unroll
+    for (int k = 0; k < kThreads / 64; ++k) tot += s_wsum[k];
+    s_base = tot > 0 ? atomicAdd(n_items, tot) : 0;
+  }
+  __syncthreads();
+  int base = s_base + incl - nch;
+  for (int k = 0; k < w; ++k) base += s_wsum[k];
   if (c == 0) return;
   const int page = block_table[j];
   for (int i = 0; i < nch && base + i < max_items; ++i) {  // max_items bounds the sum of nch
