@@ -177,7 +177,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(R <= 4
 // sixteen 16x16x4 fp32 ones, the matrix cores take a quarter of the time.
 // Mapping as in k_pf_score; lane (l16, lg4) takes channels 32 ks + 8 lg4 ..
 // + 7 of k-step ks: its A row is token l16's query, its B column block l16's
-// statistics (two float4 channel quartets of the tile layout).
+// statistics (two float4 channel quartets of the tile layout).  The splits
+// are made once per workgroup and k-step and shared in LDS.
 typedef __bf16 bf16x8s_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x4_t mfma_bf16x32(const uint4& a, const uint4& b, f32x4_t c) {
@@ -207,32 +208,42 @@ __global__ __launch_bounds__(kThreads) void k_pf_score_bf(const float* mean, con
                                                            const DecodeArgs a) {
   constexpr int KS = D / 32;  // k-steps of 32 channels
   constexpr int NC = 2;       // column tiles per wavefront
+  constexpr int NQ = (2 * R * 64 + kThreads - 1) / kThreads;  // query units per thread
   const int t = blockIdx.x, g = blockIdx.y;
   const int w = threadIdx.x / 64, lane = threadIdx.x % 64, l16 = lane % 16, lg4 = lane / 16;
   const int tok0 = 32 * blockIdx.z + 16 * (w >> 1);
   const int n0 = NC * (w & 1);
-  const int tok = min(tok0 + l16, m - 1);  // A row (rows past the group repeat the last token, never stored)
+  // Each k-step's bf16 operands are formed once per workgroup and shared in
+  // LDS (two wavefronts read every statistics column and every query row):
+  // thread (block b = tid % 64, channel group cg = tid / 64) splits the
+  // statistics the B operand of lane (b % 16, cg) of column tile b / 16
+  // holds; query unit u (lane u % 64, head u / 64 % R, token tile u / 64R)
+  // loads the A operand of that lane and splits its square.
+  __shared__ uint4 sM[3][4][64], sV[TAYLOR ? 3 : 1][4][64];
+  __shared__ uint4 sQ[TAYLOR ? 3 : 1][2][R][64];
+  const int sb = threadIdx.x % 64, scg = threadIdx.x / 64;
   const float4* mean4 = reinterpret_cast<const float4*>(mean);
   const float4* var4 = reinterpret_cast<const float4*>(var);
-  const size_t base = ((size_t)g * n_tiles + t) * (size_t)(D / 4) * kTile + 16 * n0 + l16;
-  const uint4* qrow = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) +
-                                                     ((size_t)tok * H + g * R) * D + 8 * lg4);
-  // raw operands of one k-step: statistics (two quartets per column tile) and queries
+  const size_t sbase = ((size_t)g * n_tiles + t) * (size_t)(D / 4) * kTile + sb;
+  const uint16_t* qg = static_cast<const uint16_t*>(q);
   struct Raw {
-    float4 bm[NC][2], bv[NC][2];
-    uint4 qa[R];
+    float4 bm[2], bv[2];
+    uint4 qa[NQ];
   };
   auto load = [&](int ks, Raw& r) {
 #pragma unroll
-    for (int n = 0; n < NC; ++n)
+    for (int e = 0; e < 2; ++e) {
+      const size_t at = sbase + (size_t)(8 * ks + 2 * scg + e) * kTile;
+      r.bm[e] = mean4[at];
+      r.bv[e] = TAYLOR ? var4[at] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const size_t at = base + (size_t)(8 * ks + 2 * lg4 + e) * kTile + 16 * n;
-        r.bm[n][e] = mean4[at];
-        r.bv[n][e] = TAYLOR ? var4[at] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-    for (int h = 0; h < R; ++h) r.qa[h] = qrow[(size_t)h * D / 8 + 4 * ks];
+    for (int k = 0; k < NQ; ++k) {
+      const int u = min((int)threadIdx.x + kThreads * k, 2 * R * 64 - 1);
+      const int ul = u % 64, uh = (u / 64) % R, ut = u / (64 * R);
+      const int tk = min(32 * (int)blockIdx.z + 16 * ut + ul % 16, m - 1);
+      r.qa[k] = *reinterpret_cast<const uint4*>(qg + ((size_t)tk * H + g * R + uh) * D + 32 * ks + 8 * (ul / 16));
+    }
   };
   Raw cur, nxt;
   load(0, cur);
@@ -244,31 +255,66 @@ __global__ __launch_bounds__(kThreads) void k_pf_score_bf(const float* mean, con
     for (int h = 0; h < R; ++h) cm[n][h] = cv[n][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
+    // ---- form this k-step's operands in LDS
+    {
+      uint4 hi, mid, lo;
+      split3(cur.bm[0], cur.bm[1], hi, mid, lo);
+      sM[0][scg][sb] = hi;
+      sM[1][scg][sb] = mid;
+      sM[2][scg][sb] = lo;
+      if (TAYLOR) {
+        split3(cur.bv[0], cur.bv[1], hi, mid, lo);
+        sV[0][scg][sb] = hi;
+        sV[TAYLOR ? 1 : 0][scg][sb] = mid;
+        sV[TAYLOR ? 2 : 0][scg][sb] = lo;
+      }
+#pragma unroll
+      for (int k = 0; k < NQ; ++k) {
+        const int u = (int)threadIdx.x + kThreads * k;
+        if (u < 2 * R * 64) {
+          const int ul = u % 64, uh = (u / 64) % R, ut = u / (64 * R);
+          const uint4 qv = cur.qa[k];
+          sQ[0][ut][uh][ul] = qv;
+          if (TAYLOR) {
+            const uint32_t in[4] = {qv.x, qv.y, qv.z, qv.w};
+            uint32_t oh[4], ol[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const float a0 = bf16_lo_f(in[p]), a1 = bf16_hi_f(in[p]);
+              const float s0 = a0 * a0, s1 = a1 * a1;  // exact: 16 significant bits
+              oh[p] = pack_bf16(s0, s1);
+              ol[p] = pack_bf16(s0 - bf16_lo_f(oh[p]), s1 - bf16_hi_f(oh[p]));
+            }
+            sQ[TAYLOR ? 1 : 0][ut][uh][ul] = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+            sQ[TAYLOR ? 2 : 0][ut][uh][ul] = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // the next k-step's loads go out while this one's products run
     if (ks + 1 < KS) load(ks + 1, nxt);
-    // the next k-step's loads stay ahead of this one's products
-    __builtin_amdgcn_sched_barrier(0);
+    // ---- products of this wavefront's token tile and column tiles
     uint4 mh[NC], mm[NC], ml[NC], vh[NC], vm[NC], vl[NC];
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
-      split3(cur.bm[n][0], cur.bm[n][1], mh[n], mm[n], ml[n]);
-      if (TAYLOR) split3(cur.bv[n][0], cur.bv[n][1], vh[n], vm[n], vl[n]);
+      const int ct = n0 + n;
+      mh[n] = sM[0][lg4][16 * ct + l16];
+      mm[n] = sM[1][lg4][16 * ct + l16];
+      ml[n] = sM[2][lg4][16 * ct + l16];
+      if (TAYLOR) {
+        vh[n] = sV[0][lg4][16 * ct + l16];
+        vm[n] = sV[TAYLOR ? 1 : 0][lg4][16 * ct + l16];
+        vl[n] = sV[TAYLOR ? 2 : 0][lg4][16 * ct + l16];
+      }
     }
 #pragma unroll
     for (int h = 0; h < R; ++h) {
-      const uint4 qv = cur.qa[h];
+      const uint4 qv = sQ[0][w >> 1][h][lane];
       uint4 sh, sl;
       if (TAYLOR) {
-        const uint32_t in[4] = {qv.x, qv.y, qv.z, qv.w};
-        uint32_t oh[4], ol[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const float a0 = bf16_lo_f(in[p]), a1 = bf16_hi_f(in[p]);
-          const float s0 = a0 * a0, s1 = a1 * a1;  // exact: 16 significant bits
-          oh[p] = pack_bf16(s0, s1);
-          ol[p] = pack_bf16(s0 - bf16_lo_f(oh[p]), s1 - bf16_hi_f(oh[p]));
-        }
-        sh = make_uint4(oh[0], oh[1], oh[2], oh[3]);
-        sl = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+        sh = sQ[TAYLOR ? 1 : 0][w >> 1][h][lane];
+        sl = sQ[TAYLOR ? 2 : 0][w >> 1][h][lane];
       }
 #pragma unroll
       for (int n = 0; n < NC; ++n) {
@@ -284,7 +330,10 @@ __global__ __launch_bounds__(kThreads) void k_pf_score_bf(const float* mean, con
         }
       }
     }
-    if (ks + 1 < KS) cur = nxt;
+    if (ks + 1 < KS) {
+      __syncthreads();  // every wavefront has read this k-step's operands
+      cur = nxt;
+    }
   }
 
   // ---- log scores, group logsumexp: lane holds tokens 4 lg4 + i, block 16 n + l16
