@@ -35,13 +35,16 @@ __global__ __launch_bounds__(kThreads) void k_pf_clear(int32_t* cnt, int32_t n) 
   if (i < n) cnt[i] = 0;
 }
 
-// grid (m, G): thread = slot of query vq
+// grid (ceil(m top_k / 256), G): thread = (query vq, slot s), the slots of
+// consecutive queries side by side (a workgroup per query would leave all but
+// top_k of its threads idle)
 __global__ __launch_bounds__(kThreads) void k_pf_bucket(const int32_t* sel, int32_t* cnt, int32_t* lists,
-                                                         int32_t* n_items, int32_t G, int32_t top_k,
+                                                         int32_t* n_items, int32_t m, int32_t G, int32_t top_k,
                                                          int32_t max_blocks, int32_t cap) {
-  const int vq = blockIdx.x, g = blockIdx.y, s = threadIdx.x;
-  if (vq == 0 && g == 0 && s == 0) *n_items = 0;
-  if (s >= top_k) return;
+  const int flat = blockIdx.x * kThreads + threadIdx.x, g = blockIdx.y;
+  if (flat == 0 && g == 0) *n_items = 0;
+  if (flat >= m * top_k) return;
+  const int vq = flat / top_k, s = flat - vq * top_k;
   const int j = sel[((size_t)vq * G + g) * top_k + s];
   if (j < 0 || j >= max_blocks) return;
   const size_t cell = (size_t)g * max_blocks + j;
@@ -390,8 +393,8 @@ hipError_t launch_pf_clear(const PfBuffers& pb, int G, int max_blocks, const Lau
 }
 
 hipError_t launch_pf_attend(const DecodeArgs& a, const PfBuffers& pb, const Launch& l) {
-  hipError_t e = launch_kernel(k_pf_bucket, dim3(a.B, a.G), l, a.sel, pb.cnt, pb.lists, pb.n_items, a.G, a.top_k,
-                               a.max_blocks, pb.cap);
+  hipError_t e = launch_kernel(k_pf_bucket, dim3((a.B * a.top_k + kThreads - 1) / kThreads, a.G), l, a.sel, pb.cnt,
+                               pb.lists, pb.n_items, a.B, a.G, a.top_k, a.max_blocks, pb.cap);
   if (e != hipSuccess) return e;
   e = launch_kernel(k_pf_items, dim3((a.max_blocks + kThreads - 1) / kThreads, a.G), l, pb.cnt,
                     static_cast<const int32_t*>(pb.lists), pb.items, pb.n_items, a.block_table, a.G, a.max_blocks,
