@@ -17,12 +17,18 @@ each timed step runs every instance in turn on one stream; t_step = timed
 time / (K * L_rot).  Every instance sees identical inputs, so their outputs
 must be bitwise equal (checked after the run).
 
+The timed steps start where a block completion falls in their middle (a few
+untimed lead-in steps after the warm-up move it there), so the statistics
+work of a completed block is part of what is timed.
+
 Prints one JSON line (rank 0) with the throughput, a roofline entry for the
-dominant kernel (the fused append + block scorer: its launch duration from
-HIP events that hipExtLaunchKernel stamps with the kernel's own begin / end
-on its launch stream; its HBM traffic from the committed rocprofv3 counter
-summary when that was taken on the current kernel sources) and a CPU
-baseline (the fp64 oracle timed on a bounded sample of the same workload).
+kernel that takes the largest share of the step's time (its launch duration
+from HIP events that hipExtLaunchKernel stamps with the kernel's own begin /
+end on its launch stream; its HBM traffic from the committed rocprofv3
+counter summary when that was taken on the current kernel sources), the
+same figures for every kernel of the step and for the step as a whole, and a
+CPU baseline (the fp64 oracle timed on a bounded sample of the same
+workload, with all host threads and with one).
 """
 from __future__ import annotations
 
@@ -40,11 +46,20 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
-# sources of the dominant kernel (k_step_score); the counter summary below is
-# only used while their hash matches the one it was taken on
-KERNEL_SOURCES = ["block_sparse_linear_amd/csrc/score.hip", "block_sparse_linear_amd/csrc/append_items.h",
-                  "block_sparse_linear_amd/csrc/decode_common.h", "block_sparse_linear_amd/csrc/spla_common.h"]
-PMC_SUMMARY = "profiles/k_step_score_{workload}_pmc.txt"
+CSRC = "block_sparse_linear_amd/csrc/"
+# sources of each decode kernel (by launch-plan name); a counter summary of a
+# kernel is used only while the hash of its sources matches the one it was
+# taken on
+_COMMON = ["decode_common.h", "spla_common.h", "append_items.h"]
+KERNEL_SOURCES = {
+    "score": ["score.hip"],
+    "step_score": ["score.hip"],
+    "select": ["select.hip", "select_core.h"],
+    "attend": ["attend.hip", "attend_mfma.h"],
+    "select_attend": ["select_attend.hip", "select_core.h", "attend_mfma.h"],
+    "combine": ["combine.hip"],
+}
+PMC_SUMMARY = "profiles/decode_{workload}_pmc.txt"
 # plain copy of known size run by every bench (outside the timed region) so the
 # HBM byte counters can be scaled: reads and writes CALIB_BYTES each
 CALIB_BYTES = 512 << 20
@@ -54,10 +69,17 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def step_bytes(w, lens, s_kv: int) -> dict:
+def step_bytes(w, lens, s_kv: int, chunk_lens=None) -> dict:
     """Algorithmic bytes of one decode step (after the step's append) for
     sequence lengths ``lens``: candidate statistics, selected K/V rows,
-    S_all / z_all read + write, q in, o out, gate, new k/v."""
+    S_all / z_all read + write, q in, o out, gate, the new k / v read and
+    written into the pages, and the statistics of a block the token completes.
+
+    ``chunk_lens``: {sequence: length before its chunk} of the step's chunk
+    appends (ragged serving workload), each adding its n tokens' K and V read
+    and written into the pages, S_all / z_all read + write, and for every
+    block the chunk completes its keys read (those not in the chunk) and its
+    mean and variance written."""
     d, G, H, B, bk, k = w.head_dim, w.n_kv_heads, w.n_q_heads, w.batch, w.block_size, w.top_k
     stats = kv = state = 0
     for T in lens:
@@ -69,8 +91,17 @@ def step_bytes(w, lens, s_kv: int) -> dict:
             ntok = T
         kv += G * ntok * 2 * d * s_kv
         state += G * 2 * (d * d * 4 + d * 4)
-    io = B * H * d * (s_kv + 4) + H * 4 + B * G * d * 2 * s_kv
-    return {"stats": stats, "kv": kv, "state": state, "io": io, "total": stats + kv + state + io}
+        if T % bk == 0:  # the step's token completes block T / bk - 1
+            state += G * ((bk - 1) * d * s_kv + 2 * d * 4)
+    io = B * H * d * (s_kv + 4) + H * 4 + B * G * d * 2 * s_kv * 2
+    chunk = 0
+    for _, t0 in sorted((chunk_lens or {}).items()):
+        n = w.chunk_len
+        chunk += 4 * n * G * d * s_kv + G * 2 * (d * d * 4 + d * 4)
+        for j in range(t0 // bk, (t0 + n) // bk):  # blocks the chunk completes
+            chunk += G * (max(0, t0 - j * bk) * d * s_kv + 2 * d * 4)
+    return {"stats": stats, "kv": kv, "state": state, "io": io, "chunk": chunk,
+            "total": stats + kv + state + io + chunk}
 
 
 def step_score_bytes(w, lens, s_kv: int) -> int:
@@ -87,6 +118,9 @@ def step_score_bytes(w, lens, s_kv: int) -> int:
     tot += w.batch * w.n_q_heads * d * s_kv
     tot += w.batch * G * 2 * (d * d * 4 + d * 4)
     tot += w.batch * G * d * 2 * s_kv * 2
+    for T in lens:
+        if T % bk == 0:  # the token completes a block: its other keys read, mean and variance written
+            tot += G * ((bk - 1) * d * s_kv + 2 * d * 4)
     return tot
 
 
@@ -124,33 +158,49 @@ def kernel_bytes(name: str, w, lens, s_kv: int) -> int:
     raise ValueError(name)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(name: str) -> str:
+    """sha256 prefix of the sources of decode kernel ``name``."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
+    for p in KERNEL_SOURCES[name] + _COMMON:
+        with open(os.path.join(ROOT, CSRC + p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
-    counter reads for the calibration copy), or None when there is no summary
-    for this workload or the kernel sources changed since it was taken."""
+def read_pmc_summary(path: str) -> dict:
+    """The key = value fields of a counter summary: {"": global fields,
+    kernel symbol: that kernel's fields} ([section] lines open a kernel)."""
+    out = {"": {}}
+    cur = out[""]
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("[") and line.endswith("]"):
+                cur = out.setdefault(line[1:-1].strip(), {})
+            elif "=" in line:
+                k, v = line.split("=", 1)
+                cur[k.strip()] = v.strip()
+    return out
+
+
+def read_traffic(workload: str, name: str):
+    """HBM bytes per launch of decode kernel ``name`` from the committed
+    counter summary (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by
+    what the counter reads for the calibration copy), or None when there is
+    no summary of it for this workload or its sources changed since."""
     p = os.path.join(ROOT, PMC_SUMMARY.format(workload=workload))
     if not os.path.exists(p):
         return None, "no counter summary"
-    kv = {}
-    with open(p) as f:
-        for line in f:
-            line = line.strip()
-            if line and not line.startswith("#") and "=" in line:
-                k, v = line.split("=", 1)
-                kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != kernel_source_hash():
+    s = read_pmc_summary(p)
+    g, kv = s[""], s.get("k_" + name)
+    if kv is None:
+        return None, f"no counters of k_{name}"
+    if kv.get("source_sha256") != kernel_source_hash(name):
         return None, "kernel changed since the counters were taken"
-    fetch_scale = float(kv["copy_bytes"]) / (float(kv["copy_fetch_kib"]) * 1024.0)
-    write_scale = float(kv["copy_bytes"]) / (float(kv["copy_write_kib"]) * 1024.0)
+    fetch_scale = float(g["copy_bytes"]) / (float(g["copy_fetch_kib"]) * 1024.0)
+    write_scale = float(g["copy_bytes"]) / (float(g["copy_write_kib"]) * 1024.0)
     fetch = float(kv["fetch_kib_per_dispatch"]) * 1024.0 * fetch_scale
     write = float(kv["write_kib_per_dispatch"]) * 1024.0 * write_scale
     return {"bytes": fetch + write, "fetch": fetch, "write": write,
@@ -161,16 +211,28 @@ RLA_FORMS = {0: "plain", 1: "normalized", 2: "rmsnorm"}
 RLA_EPS = 1e-6
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, n_steps: int, budget_s: float, rla_form: int = 0) -> dict:
-    """Time the fp64 oracle's append + decode per step on the host cores."""
-    import numpy as np
+    """Time the fp64 oracle's append + decode per step on the host cores: the
+    first steps after an untimed prefill with every BLAS thread the process
+    may use, up to budget_s / 2 of oracle time, then the following steps with
+    one thread for as long again."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     from oracle import SplaOracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     o = SplaOracle(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k,
                    w.max_tokens(n_steps))
     t0 = time.time()
@@ -181,24 +243,40 @@ def cpu_baseline(w, n_steps: int, budget_s: float, rla_form: int = 0) -> dict:
     gate = w.gate()
     gamma = w.rla_gamma() if rla_form == 2 else None
     mix = w.mixture_state()
-    done = 0
-    spent = 0.0
-    for s in range(n_steps):
-        st = w.step(s, mix)
-        t = time.perf_counter()
-        cs = [int(x) for x in st["chunk_seqs"]]
-        if cs:
-            o.append(cs, [w.chunk_len] * len(cs), st["chunk_k"], st["chunk_v"])
-        o.append(list(range(w.batch)), [1] * w.batch, st["k"], st["v"])
-        o.decode(st["q"], gate, rla_mode=rla_form, gamma=gamma, eps=RLA_EPS)
-        spent += time.perf_counter() - t
-        done += 1
-        if spent >= budget_s:
-            break
+    s = 0
+
+    def sample(limit_s):
+        nonlocal s
+        done, spent = 0, 0.0
+        while s < n_steps:
+            st = w.step(s, mix)
+            t = time.perf_counter()
+            cs = [int(x) for x in st["chunk_seqs"]]
+            if cs:
+                o.append(cs, [w.chunk_len] * len(cs), st["chunk_k"], st["chunk_v"])
+            o.append(list(range(w.batch)), [1] * w.batch, st["k"], st["v"])
+            o.decode(st["q"], gate, rla_mode=rla_form, gamma=gamma, eps=RLA_EPS)
+            spent += time.perf_counter() - t
+            done += 1
+            s += 1
+            if spent >= limit_s:
+                break
+        return done, spent
+
+    done, spent = sample(budget_s / 2)
+    with threadpool_limits(1):
+        done1, spent1 = sample(budget_s / 2)
     t_step = spent / done
-    return {"value": w.batch / t_step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{w.name}: fp64 NumPy oracle append+decode of the first {done} decode steps after an "
-                      f"untimed prefill ({spent:.1f}s timed, {t_step * 1e3:.1f} ms/step)"}
+    res = {"value": w.batch / t_step, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{w.name}: fp64 NumPy oracle append+decode of decode steps 0..{done - 1} after an untimed "
+                     f"prefill, {threads} BLAS threads ({spent:.1f}s timed, {t_step * 1e3:.1f} ms/step)"}
+    if done1:
+        t1 = spent1 / done1
+        res["value_1_thread"] = w.batch / t1
+        res["sample_1_thread"] = (f"steps {done}..{done + done1 - 1}, 1 BLAS thread ({spent1:.1f}s timed, "
+                                  f"{t1 * 1e3:.1f} ms/step)")
+    return res
 
 
 def run_prefill(args) -> int:
@@ -275,7 +353,7 @@ def main() -> int:
     ap.add_argument("--workload", default="llama_gqa_128k")
     ap.add_argument("--lrot", type=int, default=0, help="layer instances (0 = auto)")
     ap.add_argument("--prof-steps", type=int, default=16, help="steps of the per-kernel event pass")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-select", type=int, default=-1, choices=(-1, 0, 1),
                     help="selector placement: -1 automatic, 0 stand-alone kernel, 1 fused into attend")
@@ -304,7 +382,33 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     K, W, P = args.steps, args.warmup, args.prof_steps
-    total_steps = W + K + P
+    bk = w.block_size
+
+    # sequence lengths after each step's appends (chunk, then the token), and
+    # each step's chunk appends as {sequence: length before the chunk}
+    def simulate(n):
+        lens, after, chunks = list(w.t0), [], []
+        for s in range(n):
+            cs = {int(b): lens[int(b)] for b in w.chunk_plan(s)}
+            for b in cs:
+                lens[b] += w.chunk_len
+            lens = [t + 1 for t in lens]
+            after.append(list(lens))
+            chunks.append(cs)
+        return after, chunks
+
+    # untimed lead-in steps after the warm-up, so that a token of the timed
+    # steps completes a block (at the middle step, or as near as 2 Bk steps allow)
+    lead = 0
+    after, _ = simulate(W + 2 * bk + K)
+    mid = K // 2
+    for x in range(2 * bk):
+        if any(t % bk == 0 for t in after[W + x + mid]):
+            lead = x
+            break
+    W0 = W + lead
+    total_steps = W0 + K + P
+    after, chunk_lens = simulate(total_steps)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     s_kv = 2 if w.kv_dtype == "bf16" else 4
@@ -344,9 +448,10 @@ def main() -> int:
         })
     gate = torch.from_numpy(w.gate()).to(dev)
 
-    lens0 = [t + 1 for t in base.lens]
-    sb = step_bytes(w, lens0, s_kv)
-    L = args.lrot or max(2, math.ceil(512e6 / sb["total"]))
+    timed = range(W0, W0 + K)
+    sbs = [step_bytes(w, after[s], s_kv, chunk_lens[s]) for s in timed]
+    bytes_avg = float(np.mean([x["total"] for x in sbs]))
+    L = args.lrot or max(2, math.ceil(512e6 / bytes_avg))
     layers = [base]
     for _ in range(L - 1):
         x = new_layer()
@@ -355,7 +460,10 @@ def main() -> int:
         x._bind(base.lens)
         layers.append(x)
     torch.cuda.synchronize()
-    log(f"L_rot={L} step_bytes={sb}")
+    parts = {k: float(np.mean([x[k] for x in sbs])) for k in sbs[0]}
+    completions = [s - W0 for s in timed if any(t % bk == 0 for t in after[s])]
+    log(f"L_rot={L} lead-in {lead} steps; timed steps {W0}..{W0 + K - 1}, block completions at timed steps "
+        f"{completions[:8]}; mean step bytes {parts}")
     outs = [torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=dev) for _ in layers]
 
     def run_step(s, layer, out, kernel_events=None):
@@ -366,17 +474,15 @@ def main() -> int:
             layer.append(x["cs"], [w.chunk_len] * len(x["cs"]), x["ck"], x["cv"])
         layer.decode_step(x["k"], x["v"], x["q"], gate, out=out, kernel_events=kernel_events)
 
-    for s in range(W):
+    for s in range(W0):
         for layer, out in zip(layers, outs):
             run_step(s, layer, out)
     torch.cuda.synchronize()
-    lens_t = [t + 1 for t in layers[0].lens]
-    bytes_first = step_bytes(w, lens_t, s_kv)["total"]
 
     # one HIP graph per timed step holding every instance's append + decode
     # (captured ahead of the timed region; replay order = step order)
     graphs = []
-    for s in range(W, W + K):
+    for s in timed:
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr):
             for layer, out in zip(layers, outs):
@@ -392,9 +498,8 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed_ms = start.elapsed_time(end)
     t_step = elapsed_ms / 1e3 / (K * L)
-    lens_end = layers[0].lens
-    bytes_last = step_bytes(w, lens_end, s_kv)["total"]
-    bytes_avg = 0.5 * (bytes_first + bytes_last)
+    if layers[0].lens != after[W0 + K - 1]:
+        raise RuntimeError(f"lengths after the timed steps {layers[0].lens[:4]} != {after[W0 + K - 1][:4]}")
     for o in outs[1:]:
         if not torch.equal(o, outs[0]):
             log("WARNING: layer instances disagree bitwise")
@@ -408,8 +513,9 @@ def main() -> int:
     # GPU, so that the GPU then runs them back to back as in the graphs.
     names = layers[0].launch_plan(step=True)  # e.g. step_score, select_attend, combine
     import ctypes
+    prof = range(W0 + K, W0 + K + P)
     ev_sets = []
-    for s in range(W + K, W + K + P):
+    for s in prof:
         ev_sets.append([[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))] for _ in layers])
     for sets in ev_sets:
         for evs in sets:
@@ -417,7 +523,7 @@ def main() -> int:
                 e.record()  # materialise the handles
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2.4e9 * 0.3))
-    for s, sets in zip(range(W + K, W + K + P), ev_sets):
+    for s, sets in zip(prof, ev_sets):
         for layer, out, evs in zip(layers, outs, sets):
             if layer.launch_plan(step=True) != names:
                 raise RuntimeError("the launch plan changed during the per-kernel pass")
@@ -425,18 +531,15 @@ def main() -> int:
             run_step(s, layer, out, kernel_events=handles)
     torch.cuda.synchronize()
     durs = {n: [] for n in names}
-    score_launch_bytes = []
     launch_bytes = {n: [] for n in names}
-    lens_p = list(lens_end)
-    for sets in ev_sets:
-        lens_p = [t + 1 for t in lens_p]
+    for s, sets in zip(prof, ev_sets):
         for evs in sets:
             for i, n in enumerate(names):
                 durs[n].append(evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e-3)
-        score_launch_bytes.append(step_score_bytes(w, lens_p, s_kv))
         for n in names:
-            launch_bytes[n].append(kernel_bytes(n, w, lens_p, s_kv))
+            launch_bytes[n].append(kernel_bytes(n, w, after[s], s_kv))
     avg = {n: float(np.mean(v)) for n, v in durs.items()}
+    nbytes = {n: float(np.mean(v)) for n, v in launch_bytes.items()}
 
     # calibration copy for the HBM byte counters (see CALIB_BYTES)
     calib = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
@@ -452,13 +555,21 @@ def main() -> int:
     torch.cuda.synchronize()
     probe_gbs = 4 * 2 * CALIB_BYTES / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del calib, calib_out
-    traffic, why = read_traffic(w.name)
-    if traffic is None:
-        log(f"roofline traffic: null ({why})")
-    sc_bytes = float(np.mean(score_launch_bytes))
-    achieved = sc_bytes / avg["step_score"] / 1e9
     log("kernel us (HIP events): " + ", ".join(f"{n}={avg[n] * 1e6:.2f}" for n in names))
 
+    def roof(n):
+        achieved = nbytes[n] / avg[n] / 1e9
+        traffic, why = read_traffic(w.name, n)
+        if traffic is None:
+            log(f"k_{n} traffic: null ({why})")
+        return {"kernel": "k_" + n, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic["bytes"] if traffic else None,
+                "bytes_per_launch": nbytes[n], "us": avg[n] * 1e6, "share_of_step": avg[n] / t_step}
+
+    # the kernel that takes the largest share of the step's time
+    dominant = max(names, key=lambda n: avg[n])
+    top = roof(dominant)
+    top["copy_probe_GBps"] = probe_gbs
     result = {
         "metric": "SPLA decode tokens/s at 128K ctx GQA 32/8x128; achieved HBM GB/s vs peak",
         "value": w.batch / t_step,
@@ -474,26 +585,24 @@ def main() -> int:
         "data": "synthetic (seeded; see workloads/)",
         "config": {"workload": w.name, "batch": w.batch, "context": max(w.t0), "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
-                   "top_k": w.top_k, "l_rot": L, "rla_output": RLA_FORMS[args.rla_form]},
+                   "top_k": w.top_k, "l_rot": L, "lead_in_steps": lead, "rla_output": RLA_FORMS[args.rla_form]},
         "step_bytes": bytes_avg,
+        "step_bytes_parts": parts,
         "step_GBps": bytes_avg / t_step / 1e9,
         "step_frac_of_peak": bytes_avg / t_step / 1e9 / HBM_PEAK_GBS,
         "kernel_us": {n: avg[n] * 1e6 for n in names},
         "kernels": names,
-        "roofline": {"kernel": "k_step_score", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic["bytes"] if traffic else None, "bytes_per_launch": sc_bytes,
-                     "copy_probe_GBps": probe_gbs},
-        # every kernel of the step against the same HBM peak: the first kernel
-        # moves most of the step's bytes; the selection kernels take most of
-        # its time and are bound by latency, not bandwidth
-        "kernel_rooflines": [
-            {"kernel": n, "us": avg[n] * 1e6, "bytes_per_launch": float(np.mean(launch_bytes[n])),
-             "GBps": float(np.mean(launch_bytes[n])) / avg[n] / 1e9,
-             "frac": float(np.mean(launch_bytes[n])) / avg[n] / 1e9 / HBM_PEAK_GBS} for n in names],
+        # the kernel with the largest share of the step's time
+        "roofline": top,
+        # the whole step: algorithmic bytes per step over the graph-timed step
+        "step_roofline": {"bound": "hbm", "achieved": bytes_avg / t_step / 1e9, "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": bytes_avg / t_step / 1e9 / HBM_PEAK_GBS,
+                          "bytes_per_step": bytes_avg, "us": t_step * 1e6},
+        # every kernel of the step against the same HBM peak
+        "kernel_rooflines": [roof(n) for n in names],
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, K + W, args.cpu_budget, args.rla_form)
+        result["cpu_baseline"] = cpu_baseline(w, total_steps, args.cpu_budget, args.rla_form)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -10,6 +10,9 @@ specification:
            log(1 - 1e-5).  Outputs are then compared with the oracle re-run on
            the GPU's selection, because a legal near-tie swap moves o_sparse
            far more than the output tolerance.
+  scores   the exported group log score LG of every candidate: |gpu - ref|
+           <= 1e-6 * max(1, |ref|) (absolute in the log domain; past
+           |LG| = 1 the bar follows the fp32 spacing of LG itself).
   outputs  o, o_sparse and o_rla each: max|gpu - ref| <= 2e-3 * max|ref|
            (o_rla ~ 1e5 dwarfs o_sparse ~ 1 at long context, so each is
            checked on its own); D: <= 1e-4 relative.
@@ -38,6 +41,7 @@ D_REL = 1e-4
 S_REL = 1e-4
 STAT_REL = 1e-5
 TIE_REL = 1e-5
+LG_ABS = 1e-6
 
 
 def check_selection(sel_row, lg: Dict[int, float], nb: int, top_k: int) -> Optional[str]:
@@ -207,12 +211,17 @@ class ParityRun:
                     if not np.array_equal(sel_gpu[b, gg], ref["sel"][b, gg]):
                         rep.sel_equal = False
                         rep.near_ties += 1
-                    # group log scores (diagnostic, absolute in the log domain)
+                    # group log scores: absolute in the log domain, relative past |LG| = 1
                     if nb > w.top_k:
                         js = np.arange(1, nb - 1)
                         lg_ref = np.array([ref["lg"][b][gg][int(j)] for j in js])
-                        rep.errors["lg_abs"] = max(rep.errors.get("lg_abs", 0.0),
-                                                   float(np.abs(g["lg"][b, gg, js] - lg_ref).max()))
+                        dlg = np.abs(g["lg"][b, gg, js].astype(np.float64) - lg_ref)
+                        rep.errors["lg_abs"] = max(rep.errors.get("lg_abs", 0.0), float(dlg.max()))
+                        bad = dlg > LG_ABS * np.maximum(1.0, np.abs(lg_ref))
+                        if bad.any():
+                            i = int(np.argmax(dlg / np.maximum(1.0, np.abs(lg_ref))))
+                            rep.failures.append(f"step {s} b {bs[b]} g {gs[gg]}: group log score of block "
+                                                f"{int(js[i])} off by {dlg[i]:.3g} (oracle {lg_ref[i]:.6g})")
             if not rep.sel_equal:
                 ref = self.oracle.decode(q_o, gate_o, sel_override=sel_gpu, **form)
         else:

@@ -50,3 +50,29 @@ def test_kernel_bytes_partition(bench):
     assert bench.kernel_bytes("combine", w, lens, 2) > rec
     with pytest.raises(ValueError):
         bench.kernel_bytes("nope", w, lens, 2)
+
+
+def test_step_bytes_chunk_and_completion_terms(bench):
+    from workloads import WORKLOADS
+    w = WORKLOADS["ragged_chunked"]  # G = 8, d = 128, bf16, Bk = 64, 256-token chunks
+    lens = [5000 + 7]
+    base = bench.step_bytes(w, lens, 2)
+    assert base["chunk"] == 0
+    # a chunk appended to a sequence of 1000 tokens: K and V of 256 tokens read
+    # and written to the pages, S_all / z_all read and written, blocks 15..18
+    # completed (block 15 = tokens 960..1023 had 40 tokens before the chunk,
+    # which are read back), four mean / variance rows written per KV head
+    with_chunk = bench.step_bytes(w, lens, 2, {3: 1000})
+    expect = (4 * 256 * 8 * 128 * 2 + 8 * 2 * (128 * 128 * 4 + 128 * 4)
+              + 8 * (40 * 128 * 2 + 2 * 128 * 4) + 3 * 8 * (2 * 128 * 4))
+    assert with_chunk["chunk"] == expect == 3268608
+    assert with_chunk["total"] == base["total"] + expect
+    # a block-aligned chunk completes blocks 1..4 and reads no earlier key
+    assert bench.step_bytes(w, lens, 2, {0: 64})["chunk"] == (4 * 256 * 8 * 128 * 2 + 8 * 2 * (128 * 128 * 4 + 128 * 4)
+                                                            + 4 * 8 * (2 * 128 * 4))
+    # the step's own token completing a block: its other 63 keys read, mean and variance written
+    done = bench.step_bytes(w, [64 * 100], 2)
+    part = bench.step_bytes(w, [64 * 100 + 1], 2)
+    assert done["state"] - part["state"] == 8 * (63 * 128 * 2 + 2 * 128 * 4)
+    # q in, o out, gate, and the token's k / v read and written to the pages
+    assert part["io"] == 64 * 32 * 128 * (2 + 4) + 32 * 4 + 64 * 8 * 128 * (2 * 2) * 2

@@ -2,6 +2,13 @@
 benchmark times (spla_decode_step: the one-token append fused into the
 scorer's launch, then select / attend / combine; pages in shuffled order).
 
+Each workload runs its stated number of decode steps (16 / 256 / 128 / 64 /
+64), or more where those steps would not complete a block: the tiny and the
+1M workloads start block-aligned, so they run on until their own token
+completes one (the path that appends a block's mean and variance inside the
+scorer's launch and grows the candidate range by a block).  Every step is
+checked.
+
 The GPU runs the whole batch and every head; the oracle checks sampled
 (sequence, KV head) pairs: the method treats each pair on its own, so the
 oracle run on their slices of the same inputs gives exactly the values the
@@ -16,7 +23,23 @@ from workloads import Workload, make_workload
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-def _run(w, steps, seqs=None, kv_heads=None, page_order="shuffled", fused_select=-1, rla_form=0):
+def _completions(w, steps):
+    """(step, sequence) pairs whose token completes a block within `steps`."""
+    lens, out = list(w.t0), []
+    for s in range(steps):
+        for b in w.chunk_plan(s):
+            lens[int(b)] += w.chunk_len
+        lens = [t + 1 for t in lens]
+        out += [(s, b) for b, t in enumerate(lens) if t % w.block_size == 0]
+    return out
+
+
+def _run(w, steps, seqs=None, kv_heads=None, page_order="shuffled", fused_select=-1, rla_form=0,
+         need_completion=False):
+    if need_completion:
+        done = [c for c in _completions(w, steps) if seqs is None or c[1] in seqs]
+        assert done, "the checked steps must complete a block"
+        print(f"[fullsize] block completions (step, seq): {done[:8]}", flush=True)
     print(f"[fullsize] {w.name}: B={w.batch} H={w.n_q_heads} G={w.n_kv_heads} d={w.head_dim} "
           f"Bk={w.block_size} k={w.top_k} t0={w.t0[:4]}{'...' if w.batch > 4 else ''} steps={steps} "
           f"seqs={seqs} kv_heads={kv_heads} fused_select={fused_select} rla_form={rla_form}", flush=True)
@@ -27,10 +50,18 @@ def _run(w, steps, seqs=None, kv_heads=None, page_order="shuffled", fused_select
     assert not failures, "\n".join(failures[:20])
 
 
+@pytest.mark.timeout(300)
+def test_tiny_fp32_full():
+    # B=1, 2/2 x 64, 4K context, fp32: the 16 stated steps and on to step 80,
+    # past the first block its own tokens complete (step 63)
+    _run(make_workload("tiny_fp32"), steps=80, need_completion=True)
+
+
 @pytest.mark.timeout(600)
 def test_llama_gqa_128k_full():
-    # B=1, 128K context, GQA 32/8 x 128, Bk=64, k=32: every head checked
-    _run(make_workload("llama_gqa_128k"), steps=3)
+    # B=1, 128K context, GQA 32/8 x 128, Bk=64, k=32, 256 steps (4 blocks
+    # completed): every head checked
+    _run(make_workload("llama_gqa_128k"), steps=256, need_completion=True)
 
 
 @pytest.mark.timeout(600)
@@ -42,14 +73,16 @@ def test_llama_gqa_128k_rla_forms(form):
 
 @pytest.mark.timeout(600)
 def test_batched_32k_full():
-    # B=16 x 32K, planted blocks: 3 sequences x 2 KV heads sampled
-    _run(make_workload("batched_32k"), steps=3, seqs=[0, 7, 15], kv_heads=[0, 5])
+    # B=16 x 32K, planted blocks, 128 steps (2 blocks completed): 3 sequences x
+    # 2 KV heads sampled
+    _run(make_workload("batched_32k"), steps=128, seqs=[0, 7, 15], kv_heads=[0, 5], need_completion=True)
 
 
 @pytest.mark.timeout(900)
 def test_million_1m_full():
-    # B=1, 1M context, Bk=128, k=64 (8192 blocks): 2 KV heads sampled
-    _run(make_workload("million_1m"), steps=2, kv_heads=[2, 7])
+    # B=1, 1M context, Bk=128, k=64 (8192 blocks): the 64 stated steps and on
+    # to step 128, whose token completes block 8192; 2 KV heads sampled
+    _run(make_workload("million_1m", steps=128), steps=128, kv_heads=[2, 7], need_completion=True)
 
 
 @pytest.mark.timeout(900)
@@ -60,7 +93,8 @@ def test_ragged_chunked_full():
     lens = list(w.t0)
     chunked = sorted(set(int(b) for s in range(3) for b in w.chunk_plan(s)))
     seqs = sorted({lens.index(min(lens)), lens.index(max(lens))} | set(chunked[:3]))
-    _run(w, steps=3, seqs=seqs, kv_heads=[3])
+    # 64 steps (the survey's reading of this workload's length)
+    _run(w, steps=64, seqs=seqs, kv_heads=[3], need_completion=True)
 
 
 # the selector holds KPT candidates per thread in registers, with one compiled
