@@ -602,7 +602,8 @@ def main() -> int:
         "kernel_rooflines": [roof(n) for n in names],
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, total_steps, args.cpu_budget, args.rla_form)
+        # room for both samples (the steps the GPU ran and 200 more)
+        result["cpu_baseline"] = cpu_baseline(w, total_steps + 200, args.cpu_budget, args.rla_form)
     print(json.dumps(result), flush=True)
     return 0
 
