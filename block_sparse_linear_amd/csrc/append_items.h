@@ -60,50 +60,87 @@ __device__ void append_page_row_head(const StateRefs& a, const AppendEntry& E, i
 
 // mean and population variance (two passes) of block j of entry E's
 // sequence, KV head g, completed by this append: tokens older than the
-// append come from the pages, the new ones from k_new
+// append come from the pages, the new ones from k_new.  Every key of the
+// block is loaded at once, 16 bytes per load (thread = (token group, 16-byte
+// column of the row)), and held in registers for both passes; the per-column
+// sums meet in LDS.
 template <bool BF16>
 __device__ void append_block_stats(const StateRefs& a, const AppendEntry& E, int j, int g) {
-  __shared__ float red[kThreads];
+  constexpr int VE = BF16 ? 8 : 4;  // elements per 16-byte vector
+  constexpr int MAXV = 16;          // vectors per thread (fp32 keys, d = 128, Bk = 128)
+  __shared__ float red[kThreads * VE];
   const int d = a.d, bk = a.bk;
-  const int groups = kThreads / d;
-  const int c = threadIdx.x % d;
-  const int grp = threadIdx.x / d;
-  const int tpg = bk / groups;
+  const int vr = d / VE;            // vectors per token row
+  const int tg = kThreads / vr;     // token groups
+  const int nv = bk / tg;           // vectors (tokens) per thread
+  const int col = threadIdx.x % vr, t0 = threadIdx.x / vr;
   const int page = a.block_table[(size_t)E.seq * a.max_blocks + j];
   const bool page_ok = page >= 0 && page < a.num_pages;
   if (!page_ok && j * bk < E.t0) {
     if (threadIdx.x == 0) atomicOr(a.err, kErrPage);
     return;
   }
-  auto key = [&](int p) -> float {
-    if (p < E.t0) {
-      return load_elem<BF16>(a.k_pages, (((size_t)page * a.G + g) * bk + (p % bk)) * d + c);
+  const uint4* kp = reinterpret_cast<const uint4*>(a.k_pages);
+  const uint4* kn = reinterpret_cast<const uint4*>(a.k_new);
+  uint4 raw[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    if (i < nv) {
+      const int p = j * bk + t0 + tg * i;  // token of this vector
+      raw[i] = p < E.t0 ? kp[(((size_t)page * a.G + g) * bk + (p % bk)) * vr + col]
+                        : kn[((size_t)(E.row + p - E.t0) * a.G + g) * vr + col];
     }
-    return load_elem<BF16>(a.k_new, ((size_t)(E.row + p - E.t0) * a.G + g) * d + c);
-  };
-  const int p0 = j * bk + grp * tpg;
-  float s = 0.f;
-  for (int i = 0; i < tpg; ++i) s += key(p0 + i);
-  red[threadIdx.x] = s;
-  __syncthreads();
-  float tot = 0.f;
-  for (int q = 0; q < groups; ++q) tot += red[q * d + c];
-  const float mean = tot / (float)bk;
-  __syncthreads();
-  float s2 = 0.f;
-  for (int i = 0; i < tpg; ++i) {
-    const float dv = key(p0 + i) - mean;
-    s2 = fmaf(dv, dv, s2);
   }
-  red[threadIdx.x] = s2;
+  auto elem = [&](const uint4& v, int e) -> float {
+    const uint32_t w = e < 2 * (VE / 4) ? (e < VE / 4 ? v.x : v.y) : (e < 3 * (VE / 4) ? v.z : v.w);
+    if constexpr (BF16) return (e & 1) ? bf16_hi_f(w) : bf16_lo_f(w);
+    return __uint_as_float(w);
+  };
+  // pass 1: per-column sums
+  float s[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) s[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i)
+    if (i < nv)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) s[e] += elem(raw[i], e);
+#pragma unroll
+  for (int e = 0; e < VE; ++e) red[(t0 * vr + col) * VE + e] = s[e];
   __syncthreads();
-  if (grp == 0) {
-    float t2 = 0.f;
-    for (int q = 0; q < groups; ++q) t2 += red[q * d + c];
-    const size_t idx = ((((size_t)E.seq * a.G + g) * a.n_tiles + j / kTile) * (d / 4) + c / 4) * (kTile * 4) +
-                       (j % kTile) * 4 + (c % 4);
-    a.blk_mean[idx] = mean;
-    a.blk_var[idx] = t2 / (float)bk;
+  float mean[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) {
+    float tot = 0.f;
+    for (int q = 0; q < tg; ++q) tot += red[(q * vr + col) * VE + e];
+    mean[e] = tot / (float)bk;
+  }
+  __syncthreads();
+  // pass 2: per-column sums of squared deviations, from the same registers
+#pragma unroll
+  for (int e = 0; e < VE; ++e) s[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i)
+    if (i < nv)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const float dv = elem(raw[i], e) - mean[e];
+        s[e] = fmaf(dv, dv, s[e]);
+      }
+#pragma unroll
+  for (int e = 0; e < VE; ++e) red[(t0 * vr + col) * VE + e] = s[e];
+  __syncthreads();
+  if (t0 == 0) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      float t2 = 0.f;
+      for (int q = 0; q < tg; ++q) t2 += red[(q * vr + col) * VE + e];
+      const int c = col * VE + e;
+      const size_t idx = ((((size_t)E.seq * a.G + g) * a.n_tiles + j / kTile) * (d / 4) + c / 4) * (kTile * 4) +
+                         (j % kTile) * 4 + (c % 4);
+      a.blk_mean[idx] = mean[e];
+      a.blk_var[idx] = t2 / (float)bk;
+    }
   }
 }
 

@@ -12,9 +12,6 @@ namespace spla {
 
 namespace {
 
-// output forms of the RLA branch (spla_rla_form)
-constexpr int kRlaPlain = 0, kRlaNormalized = 1, kRlaRms = 2;
-
 // grid (D / CS, H, B): one CS-channel slice of one query head (the whole head
 // for the RMS form, whose norm runs over all D channels).  Item = (kind,
 // channel quartet) with kind 0 the softmax numerators (weighted by

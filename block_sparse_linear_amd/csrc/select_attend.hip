@@ -1,11 +1,15 @@
-// Fused select + attend (bf16 K/V, Bk = 64), grid (top_k, G, B).  Every
-// workgroup of (b, g) runs the selection of (b, g) itself, with the same
-// select_core as the stand-alone selector over the scorer's group log scores,
-// and then attends the block at its own slot of the ascending selection.  The
-// selection is computed top_k times instead of being handed over through
-// memory: idle compute is traded for one kernel boundary and one dependent
-// global round trip, which is what the latency-bound small-batch decode pays
-// for.
+// Fused select + attend (bf16 K/V, Bk = 64).  Every workgroup of (b, g) runs
+// the selection of (b, g) itself, with the same select_core as the
+// stand-alone selector over the scorer's group log scores, and then attends
+// the block at its own slot of the ascending selection.  The selection is
+// computed top_k times instead of being handed over through memory: idle
+// compute is traded for one kernel boundary and one dependent global round
+// trip, which is what the latency-bound small-batch decode pays for.
+//
+// The grid puts the top_k workgroups of a (b, g) on one XCD (workgroups go to
+// the XCDs in turn by linear id, and the ids of a (b, g) are equal modulo 8),
+// so the (b, g)'s score row, block-table row and queries, which each of them
+// reads, come from that XCD's L2 after the first reader.
 #include "attend_mfma.h"
 #include "select_core.h"
 
@@ -13,6 +17,10 @@ namespace spla {
 
 namespace {
 
+// grid (8 top_k, ceil(B G / 8)): workgroup (x, y) takes slot x / 8 of pair
+// (b, g) = 8 y + x % 8, so the linear ids of a pair are equal modulo 8 (the
+// dispatcher hands the XCDs consecutive linear ids in turn, from wherever the
+// previous dispatch left off); the pairs past B G exit at once
 template <int KPT, int R, int D>
 __global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, const int32_t* block_table,
                                                              const void* q, const uint16_t* phq, int32_t n_tiles,
@@ -20,7 +28,10 @@ __global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, con
                                                              const DecodeArgs a) {
   __shared__ SelectLds L;
   __shared__ int s_j, s_page;
-  const int slot = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int slot = blockIdx.x >> 3;
+  const int bgi = (blockIdx.y << 3) + (blockIdx.x & 7);
+  const int b = bgi / G, g = bgi - b * G;
+  if (b >= a.B) return;
   // every load that does not depend on the selection goes out first, from
   // the leading kernel arguments alone: the scores and page ids it ranks and
   // the queries
@@ -33,11 +44,41 @@ __global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, con
   const int nb = n_blocks(a, b);
   select_pages<KPT>(block_table, max_blocks, b, nb, k);
   int j, page;
+  const int kp = a.top_k - 2;
   if (nb <= a.top_k) {
     j = slot < nb ? slot : -1;
     page = j >= 0 ? block_table[(size_t)b * max_blocks + j] : -1;
+  } else if (slot == 0) {  // the sink
+    j = 0;
+    page = k.pg_sink;
+  } else if (slot == kp + 1) {  // the current block
+    j = nb - 1;
+    page = k.pg_cur;
+  } else if (const int n = select_threshold_rank<KPT>(a, nb, k, L)) {
+    // every wavefront finds its slot on its own: passes of 64 listed
+    // candidates in candidate order, counting the chosen ones, until the
+    // pass holding the slot-th chosen candidate
+    const int lane = threadIdx.x & 63;
+    int base = 1, src = -1, m = 0;
+    for (; 64 * m < n; ++m) {
+      bool chosen;
+      const uint64_t mask = sel_chosen_pass(L, n, kp, m, chosen);
+      const int cnt = __popcll(mask);
+      if (slot < base + cnt) {
+        // the (slot - base)-th set bit of the mask
+        const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        src = __ffsll((unsigned long long)__ballot(chosen && pos == slot)) - 1;
+        break;
+      }
+      base += cnt;
+    }
+    int i_, pg_;
+    sel_listed(L, min(64 * m + lane, n - 1), i_, pg_);
+    j = __builtin_amdgcn_readlane(i_ + 1, src);
+    page = __builtin_amdgcn_readlane(pg_, src);
   } else {
-    select_core<KPT>(a, nb, k, L, [&](int pos, int id, int pg) {
+    select_bucket<KPT>(a, nb, k, L, [&](int pos, int id, int pg) {
       if (pos == slot) {
         s_j = id;
         s_page = pg;
@@ -55,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, con
 template <int K, int... Ks>
 hipError_t launch_select_attend_sized(const DecodeArgs& a, const Launch& l, int nc, SelectSizes<K, Ks...>) {
   if (nc <= K * kThreads) {
-    const dim3 grid(a.top_k, a.G, a.B);
+    const dim3 grid(8 * a.top_k, (a.B * a.G + 7) / 8);
     SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_select_attend<K, RR, DD>, grid, l, a.lg, a.block_table, a.q,
                                              a.phq, a.n_tiles, a.max_blocks, a.G, a.H, a))
   }
@@ -71,7 +112,7 @@ constexpr int kFusedMaxKpt = 16;  // largest keys-per-thread size compiled for t
 }  // namespace
 
 bool select_attend_supported(const DecodeArgs& a, bool bf16) {
-  return bf16 && a.bk == 64 && !a.sel_in && max_candidates(a) <= kFusedMaxKpt * kThreads;
+  return bf16 && a.bk == 64 && !a.sel_in && max_candidates(a) <= kFusedMaxKpt * kThreads && !a.virtual_queries;
 }
 
 hipError_t launch_select_attend(const DecodeArgs& a, const Launch& l) {

@@ -24,9 +24,21 @@ __device__ __forceinline__ int sel_bucket(float x, float lo, float scale) {
   return f >= 255.f ? 255 : (f <= 0.f ? 0 : (int)f);
 }
 
+constexpr int kFastCap = 256;  // candidates per wavefront list of the threshold path
+
 // LDS of the selector (the ranking and chosen lists are padded with sentinels
-// so the rank and position counts read them four at a time)
+// so the rank and position counts read them several at a time)
 struct __attribute__((aligned(16))) SelectLds {
+  // threshold path: per-wavefront lists of the candidates at or above the
+  // bound as packed keys (score key << 32 | ~candidate index: one integer
+  // order for (score desc, id asc)) and pages, the group maxima of the bound
+  // and the partial ranks of every listed candidate against each list
+  uint64_t fkey[4][kFastCap + 2];
+  int fpg[4][kFastCap];
+  int4 prank[kThreads];
+  float pool[kThreads];
+  int s_fcnt[4];
+  // bucket path
   int hist[4][256];  // one histogram per wavefront
   float mkey[kSelRank + 4];  // ranking list: keys of the threshold bucket
   int midx[kSelRank + 4];    // their candidate indices
@@ -38,13 +50,19 @@ struct __attribute__((aligned(16))) SelectLds {
   int s_bt, s_above, s_cbt, s_nm;
 };
 
-// one thread's candidates: scores and page ids (candidate i = thread + 256 u,
-// block id i + 1), plus the pages of the sink and the current block
+// One thread's candidates: scores and page ids of candidates i = w * 64 KPT
+// + 64 u + lane of wavefront w (each wavefront a contiguous range, its lanes
+// strided through it: loads are whole-wavefront runs, and a list written in
+// (u, lane) order is in candidate order), block id i + 1; plus the pages of
+// the sink and the current block.
 template <int KPT>
 struct SelectKeys {
   float x[KPT];
   int pg[KPT];
   int pg_sink, pg_cur;
+  __device__ __forceinline__ static int cand(int u) {
+    return (int)(threadIdx.x >> 6) * (64 * KPT) + 64 * u + (int)(threadIdx.x & 63);
+  }
 };
 
 // Issue the candidate loads of a selection: scores and page ids of
@@ -62,7 +80,7 @@ __device__ __forceinline__ void select_load(const float* lg, const int32_t* bloc
   const float* row = lg + ((size_t)b * G + g) * (size_t)(n_tiles * kTile) + 1;  // row[i] = LG(i + 1)
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
-    const int i = min((int)threadIdx.x + u * kThreads, cap);
+    const int i = min(SelectKeys<KPT>::cand(u), cap);
     k.x[u] = row[i];
     k.pg[u] = btab[min(i + 1, max_blocks - 1)];
   }
@@ -82,6 +100,145 @@ __device__ __forceinline__ void select_pages(const int32_t* block_table, int max
   k.pg_cur = btab[min(max(nb - 1, 0), max_blocks - 1) + zero];
 }
 
+// packed key: larger score first, then the smaller candidate index (-0 is
+// taken as +0, so equal scores compare as equal, as floats do)
+__device__ __forceinline__ uint64_t sel_key(float x, int i) {
+  return ((uint64_t)float_key(x == 0.f ? 0.f : x) << 32) | (uint32_t)~(uint32_t)i;
+}
+
+// Threshold path of the selection (the common case): a bound t0 that at
+// least k' candidates reach, the candidates at or above it listed in LDS,
+// and those ranked exactly by (score desc, id asc).
+//  (1) Bound.  Each thread takes the maximum of its own keys and the lanes of
+//      a wavefront are grouped by G = 4, 2 or 1 (k' <= 32, <= 64, more);
+//      the 256 / G group maxima (DPP maxima within each group) are pooled in
+//      LDS.  Each group maximum is a key of its own, so the k'-th largest of
+//      the pool is reached by at least k' candidates.  Every wavefront finds
+//      it in the pool on its own (no second barrier): a radix select over the
+//      top 16 bits of the order-preserving integer form of the scores, with
+//      one ballot count per bit, gives the k'-th largest 16-bit prefix P, and
+//      t0 is the smallest score with prefix P (so t0 <= the pool's k'-th
+//      largest).
+//  (2) List.  Each wavefront writes its candidates >= t0, as packed keys and
+//      pages, into its own LDS list in (u, lane) order (positions from one
+//      ballot per u, no atomics): the four lists one after the other are in
+//      candidate order.
+//  (3) Rank.  Thread (lane, wavefront w) counts, for the listed candidates e
+//      = lane, lane + 64, ..., how many keys of list w are larger; the four
+//      partial counts sum to e's rank.
+// Three barriers.  Returns false (every thread alike) when more than
+// kThreads candidates reach the bound or a list would overflow; the caller
+// then runs the bucket path.  On true, the listed candidates are
+// L.fkey / L.fpg (n of them, see sel_listed) and their partial ranks
+// L.prank[e]; the rank of e is below k' exactly when it is chosen, and its
+// output position is 1 + the chosen candidates listed before it.
+template <int KPT>
+__device__ __forceinline__ int select_threshold_rank(const DecodeArgs& a, int nb, const SelectKeys<KPT>& k,
+                                                     SelectLds& L) {
+  const int nc = nb - 2;
+  const int kp = a.top_k - 2;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // (1) the bound
+  using Mask = typename std::conditional<(KPT <= 32), uint32_t, uint64_t>::type;
+  Mask valid = 0;
+  float mt = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const bool in = SelectKeys<KPT>::cand(u) < nc;
+    valid |= (Mask)in << u;
+    mt = fmaxf(mt, in ? k.x[u] : -INFINITY);
+  }
+  const int gsh = kp <= 32 ? 2 : (kp <= 64 ? 1 : 0);  // log2 of the group size
+  float gm = mt;
+  if (gsh >= 1) gm = fmaxf(gm, dpp_f<kDppXor1>(gm, gm));
+  if (gsh >= 2) gm = fmaxf(gm, dpp_f<kDppXor2>(gm, gm));
+  if ((lane & ((1 << gsh) - 1)) == 0) L.pool[threadIdx.x >> gsh] = gm;
+  __syncthreads();
+  // the k'-th largest 16-bit key prefix of the pool (Q pooled values per lane)
+  auto radix = [&](auto qc) {
+    constexpr int Q = decltype(qc)::value;
+    uint32_t pk[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) pk[q] = float_key(L.pool[lane + 64 * q]) >> 16;
+    uint32_t pre = 0;
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t cand = pre | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) cnt += __popcll(__ballot(pk[q] >= cand));
+      if (cnt >= kp) pre = cand;
+    }
+    return pre;
+  };
+  const uint32_t pre = gsh == 2 ? radix(std::integral_constant<int, 1>{})
+                                : (gsh == 1 ? radix(std::integral_constant<int, 2>{})
+                                            : radix(std::integral_constant<int, 4>{}));
+  // the smallest score whose key has prefix pre (-inf at or below the prefix
+  // of -inf, whose smallest key would be a NaN pattern)
+  const uint32_t key0 = pre << 16;
+  const float t0 = key0 <= float_key(-INFINITY) ? -INFINITY
+                                                 : __uint_as_float((key0 & 0x80000000u) ? (key0 & 0x7fffffffu) : ~key0);
+  // (2) this wavefront's list, in (u, lane) order = candidate order; the
+  // entries past the capacity are dropped and the count decides below
+  int tot = 0;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const bool in = ((valid >> u) & 1) && k.x[u] >= t0;
+    const uint64_t m = __ballot(in);
+    const int pos = tot + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (in && pos < kFastCap) {
+      L.fkey[wv][pos] = sel_key(k.x[u], SelectKeys<KPT>::cand(u));
+      L.fpg[wv][pos] = k.pg[u];
+    }
+    tot += __popcll(m);
+  }
+  if (tot <= kFastCap && lane < 2) L.fkey[wv][tot + lane] = 0;  // smaller than every key: never beats one
+  if (lane == 0) L.s_fcnt[wv] = tot;
+  __syncthreads();
+  const int c0 = L.s_fcnt[0], c1 = L.s_fcnt[1], c2 = L.s_fcnt[2], c3 = L.s_fcnt[3];
+  const int n = (c0 + c1) + (c2 + c3);
+  // (fewer than k' only if the scores are not ordered, e.g. NaN: the bucket path decides)
+  if (max(max(c0, c1), max(c2, c3)) > kFastCap || n > kThreads || n < kp) return 0;
+  // (3) partial ranks against list wv
+  const int cw = wv == 0 ? c0 : (wv == 1 ? c1 : (wv == 2 ? c2 : c3));
+  for (int e = lane; e < n; e += 64) {
+    const int r = e < c0 ? 0 : (e < c0 + c1 ? 1 : (e < c0 + c1 + c2 ? 2 : 3));
+    const int o = e - (r > 0 ? c0 : 0) - (r > 1 ? c1 : 0) - (r > 2 ? c2 : 0);
+    const uint64_t key = L.fkey[r][o];
+    int rank = 0;
+    for (int v = 0; v < cw; v += 2) {
+      const ulonglong2 y = *reinterpret_cast<const ulonglong2*>(&L.fkey[wv][v]);
+      rank += (y.x > key) + (y.y > key);
+    }
+    reinterpret_cast<int*>(&L.prank[e])[wv] = rank;
+  }
+  __syncthreads();
+  return n;
+}
+
+// listed candidate e of the threshold path: its candidate index and page
+__device__ __forceinline__ void sel_listed(const SelectLds& L, int e, int& i, int& pg) {
+  const int c0 = L.s_fcnt[0], c1 = L.s_fcnt[1], c2 = L.s_fcnt[2];
+  const int r = e < c0 ? 0 : (e < c0 + c1 ? 1 : (e < c0 + c1 + c2 ? 2 : 3));
+  const int o = e - (r > 0 ? c0 : 0) - (r > 1 ? c1 : 0) - (r > 2 ? c2 : 0);
+  i = (int)~(uint32_t)L.fkey[r][o];
+  pg = L.fpg[r][o];
+}
+
+// Pass m of the chosen candidates in list order, for one wavefront: listed
+// candidate e = 64 m + lane is chosen when its rank is below k'; its output
+// position is 1 + base + the chosen lanes below it.  Returns the chosen
+// lanes of the pass.
+__device__ __forceinline__ uint64_t sel_chosen_pass(const SelectLds& L, int n, int kp, int m, bool& chosen) {
+  const int e = 64 * m + (threadIdx.x & 63);
+  chosen = false;
+  if (e < n) {
+    const int4 pr = L.prank[e];
+    chosen = (pr.x + pr.y) + (pr.z + pr.w) < kp;
+  }
+  return __ballot(chosen);
+}
+
 // Bucket select over the scores held in registers (KPT per thread,
 // KPT * 256 >= nb - 2): the scores are binned into 256 buckets spread over
 // [min, max] of the remaining candidates; every candidate in a bucket above
@@ -98,15 +255,15 @@ __device__ __forceinline__ void select_pages(const int32_t* block_table, int max
 // workgroup must call it.  For each output position pos in [0, top_k),
 // exactly one thread calls emit(pos, block id, page id).
 template <int KPT, typename Emit>
-__device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const SelectKeys<KPT>& k, SelectLds& L,
-                                            Emit&& emit) {
+__device__ __forceinline__ void select_bucket(const DecodeArgs& a, int nb, const SelectKeys<KPT>& k, SelectLds& L,
+                                              Emit&& emit) {
   using Mask = typename std::conditional<(KPT <= 32), uint32_t, uint64_t>::type;
   const int nc = nb - 2;
   const int kp = a.top_k - 2;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   Mask memb = 0, above = 0;  // bit u: key u still in the threshold bucket / already taken
 #pragma unroll
-  for (int u = 0; u < KPT; ++u) memb |= (Mask)((int)threadIdx.x + u * kThreads < nc) << u;
+  for (int u = 0; u < KPT; ++u) memb |= (Mask)(SelectKeys<KPT>::cand(u) < nc) << u;
   if (threadIdx.x == 0) L.s_nm = 0;
   L.mkey[threadIdx.x] = -INFINITY;
   L.midx[threadIdx.x] = 0x7fffffff;
@@ -197,7 +354,7 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
       const int mid = (lo + hi) >> 1;
       int c = 0;
 #pragma unroll
-      for (int u = 0; u < KPT; ++u) c += ((memb >> u) & 1) && ((int)threadIdx.x + u * kThreads < mid);
+      for (int u = 0; u < KPT; ++u) c += ((memb >> u) & 1) && (SelectKeys<KPT>::cand(u) < mid);
       c = wave_sum_i(c);
       __syncthreads();
       if (lane == 0) L.s_cnt[wv] = c;
@@ -208,7 +365,7 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
     Mask low = 0;
 #pragma unroll
     for (int u = 0; u < KPT; ++u)
-      low |= (((memb >> u) & 1) && (int)threadIdx.x + u * kThreads < lo) ? ((Mask)1 << u) : (Mask)0;
+      low |= (((memb >> u) & 1) && SelectKeys<KPT>::cand(u) < lo) ? ((Mask)1 << u) : (Mask)0;
     above |= low;
     memb = 0;
   }
@@ -226,7 +383,7 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
     int pa = b0 >> 16, pm = b0 & 0xffff;
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-      const int i = threadIdx.x + u * kThreads;
+      const int i = SelectKeys<KPT>::cand(u);
       if ((above >> u) & 1) {
         L.cid[pa] = i;
         L.cpg[pa] = k.pg[u];
@@ -278,6 +435,44 @@ __device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const S
   }
   if (threadIdx.x == 0) emit(0, 0, k.pg_sink);
   if (threadIdx.x == kThreads - 1) emit(kp + 1, nb - 1, k.pg_cur);
+}
+
+// The selection of one (b, g): the sink and the current block alone when
+// top_k = 2, else the threshold path, or the bucket path when the threshold
+// path declines.  Requires nb > top_k and the keys of select_load; every
+// thread of the workgroup must call it.  For each output position pos in
+// [0, top_k), exactly one thread calls emit(pos, block id, page id).
+template <int KPT, typename Emit>
+__device__ __forceinline__ void select_core(const DecodeArgs& a, int nb, const SelectKeys<KPT>& k, SelectLds& L,
+                                            Emit&& emit) {
+  const int kp = a.top_k - 2;
+  if (threadIdx.x == 0) emit(0, 0, k.pg_sink);
+  if (threadIdx.x == kThreads - 1) emit(kp + 1, nb - 1, k.pg_cur);
+  if (kp == 0) return;
+  const int n = select_threshold_rank<KPT>(a, nb, k, L);
+  if (n > 0) {
+    // wavefront 0 takes the listed candidates in passes of 64, in list
+    // (= candidate) order, and emits the chosen ones at their positions
+    if (threadIdx.x < 64) {
+      int base = 1;
+      for (int m = 0; 64 * m < n; ++m) {
+        bool chosen;
+        const uint64_t mask = sel_chosen_pass(L, n, kp, m, chosen);
+        if (chosen) {
+          int i, pg;
+          sel_listed(L, 64 * m + threadIdx.x, i, pg);
+          emit(base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u)),
+               i + 1, pg);
+        }
+        base += __popcll(mask);
+      }
+    }
+    return;
+  }
+  select_bucket<KPT>(a, nb, k, L, [&](int pos, int id, int pg) {
+    if (pos > 0 && pos <= kp) emit(pos, id, pg);  // the sink and the current block are out already
+  });
 }
 
 // keys-per-thread sizes compiled for a selector: the smallest one that holds

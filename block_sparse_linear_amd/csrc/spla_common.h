@@ -22,6 +22,9 @@ constexpr int kPartHdr = 4;            // m, l, sum_w, pad ahead of acc[d], o_ti
 // block score forms (spla_score_form)
 constexpr int kScoreTaylor = 0, kScoreMean = 1;
 
+// output forms of the RLA branch (spla_rla_form)
+constexpr int kRlaPlain = 0, kRlaNormalized = 1, kRlaRms = 2;
+
 // error word bits (workspace bytes [0, 4))
 constexpr uint32_t kErrPage = 1u;
 constexpr uint32_t kErrSel = 2u;
