@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspla.so"
 
 STATUS = {
     0: "SPLA_OK", 1: "SPLA_ERR_INVALID_ARG", 2: "SPLA_ERR_UNSUPPORTED", 3: "SPLA_ERR_CAPACITY",
-    4: "SPLA_ERR_ALIGNMENT", 5: "SPLA_ERR_HIP", 6: "SPLA_ERR_STATE",
+    4: "SPLA_ERR_ALIGNMENT", 5: "SPLA_ERR_HIP", 6: "SPLA_ERR_STATE", 7: "SPLA_ERR_SCRATCH",
 }
 SPLA_F32, SPLA_BF16 = 0, 1
 
@@ -33,7 +33,10 @@ EXPORTED = [
     "spla_append_kv", "spla_decode", "spla_decode_step", "spla_get_lens", "spla_status_str", "spla_abi_version",
     "spla_last_hip_error", "spla_set_tuning", "spla_launch_plan", "spla_set_rla_output",
     "spla_set_score_form", "spla_block_mass", "spla_prefill_workspace_bytes", "spla_prefill",
+    "spla_decode_step_noalloc",
 ]
+# bytes of the library's static scratch (spla_decode_step_noalloc)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # spla_kernel ids (include/spla.h) -> kernel names
 KERNELS = {1: "score", 2: "step_score", 3: "select", 4: "attend", 5: "select_attend", 6: "combine"}
@@ -103,6 +106,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(SplaDecodeAux),
                                      ctypes.c_void_p]
     lib.spla_decode_step.restype = ctypes.c_int
+    lib.spla_decode_step_noalloc.argtypes = lib.spla_decode_step.argtypes
+    lib.spla_decode_step_noalloc.restype = ctypes.c_int
     lib.spla_get_lens.argtypes = [ctypes.c_void_p, I32P]
     lib.spla_get_lens.restype = ctypes.c_int
     lib.spla_status_str.argtypes = [ctypes.c_int]
@@ -238,6 +243,15 @@ class SplaHandle:
                                          ctypes.c_void_p(q_ptr), ctypes.c_void_p(gate_ptr),
                                          ctypes.c_void_p(out_ptr), ctypes.byref(aux) if aux is not None else None,
                                          ctypes.c_void_p(stream))
+
+
+    def decode_step_noalloc_raw(self, k_ptr: int, v_ptr: int, q_ptr: int, gate_ptr: int, out_ptr: int,
+                                aux: Optional[SplaDecodeAux], stream: int) -> int:
+        return self.lib.spla_decode_step_noalloc(self.h, ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
+                                                 ctypes.c_void_p(q_ptr), ctypes.c_void_p(gate_ptr),
+                                                 ctypes.c_void_p(out_ptr),
+                                                 ctypes.byref(aux) if aux is not None else None,
+                                                 ctypes.c_void_p(stream))
 
 
 class SplaLayer:
@@ -422,6 +436,19 @@ class SplaLayer:
         st = self.handle.decode_step_raw(k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), gate.data_ptr(),
                                          out.data_ptr(), ax, self._stream())
         _check(st, "spla_decode_step", self.handle.lib, self.handle.h)
+        return out
+
+    def decode_step_noalloc(self, k_new, v_new, q, gate, out, aux: Optional[Dict[str, object]] = None):
+        """decode_step through spla_decode_step_noalloc: the per-call scratch
+        comes from the library's static device array, not the workspace.  out
+        must be given (device [B][H][d] float32): nothing is allocated."""
+        self._check_kv(k_new, v_new, self.B)
+        if out is None:
+            raise ValueError("decode_step_noalloc needs an output tensor")
+        out, ax = self._decode_inputs(q, gate, out, aux, None)
+        st = self.handle.decode_step_noalloc_raw(k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), gate.data_ptr(),
+                                                 out.data_ptr(), ax, self._stream())
+        _check(st, "spla_decode_step_noalloc", self.handle.lib, self.handle.h)
         return out
 
     def decode(self, q, gate, out=None, aux: Optional[Dict[str, object]] = None, kernel_events=None):

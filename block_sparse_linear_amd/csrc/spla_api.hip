@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -109,8 +110,21 @@ T* ws_ptr(const spla_handle* h, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(h->buf.workspace) + off);
 }
 
+// base of the per-call scratch (score rows, selections, partial records,
+// o_bar partials, phi(q)) of a decode: the bound workspace, or the static
+// scratch of spla_decode_step_noalloc.  The sticky error word always stays in
+// bytes [0, 4) of the bound workspace, where callers read it.
+void fill_decode_args(const spla_handle* h, const void* q, const float* gate, float* out,
+                      const spla_decode_aux* aux, DecodeArgs* a, char* scratch_base);
+
 spla_status fill_decode_args(const spla_handle* h, const void* q, const float* gate, float* out,
                              const spla_decode_aux* aux, DecodeArgs* a) {
+  fill_decode_args(h, q, gate, out, aux, a, static_cast<char*>(h->buf.workspace));
+  return SPLA_OK;
+}
+
+void fill_decode_args(const spla_handle* h, const void* q, const float* gate, float* out,
+                      const spla_decode_aux* aux, DecodeArgs* a, char* scratch_base) {
   const spla_config& c = h->cfg;
   memset(a, 0, sizeof(*a));
   a->q = q;
@@ -123,13 +137,13 @@ spla_status fill_decode_args(const spla_handle* h, const void* q, const float* g
   a->blk_var = h->buf.blk_var;
   a->s_all = h->buf.s_all;
   a->z_all = h->buf.z_all;
-  a->lg = ws_ptr<float>(h, h->off_lg);
-  a->sel = ws_ptr<int32_t>(h, h->off_sel);
-  a->sel_page = ws_ptr<int32_t>(h, h->off_page);
-  a->part = ws_ptr<float>(h, h->off_part);
-  a->obar_part = ws_ptr<float>(h, h->off_obar);
-  a->dz_part = ws_ptr<float>(h, h->off_dz);
-  a->phq = ws_ptr<uint16_t>(h, h->off_phq);
+  a->lg = reinterpret_cast<float*>(scratch_base + h->off_lg);
+  a->sel = reinterpret_cast<int32_t*>(scratch_base + h->off_sel);
+  a->sel_page = reinterpret_cast<int32_t*>(scratch_base + h->off_page);
+  a->part = reinterpret_cast<float*>(scratch_base + h->off_part);
+  a->obar_part = reinterpret_cast<float*>(scratch_base + h->off_obar);
+  a->dz_part = reinterpret_cast<float*>(scratch_base + h->off_dz);
+  a->phq = reinterpret_cast<uint16_t*>(scratch_base + h->off_phq);
   a->err = ws_ptr<uint32_t>(h, 0);
   if (aux) {
     a->sel_in = aux->sel_in;
@@ -164,7 +178,6 @@ spla_status fill_decode_args(const spla_handle* h, const void* q, const float* g
   }
   a->score_tiles = max_tiles;
   a->tiles_all = min_tiles;
-  return SPLA_OK;
 }
 
 void fill_state_refs(const spla_handle* h, const void* k_new, const void* v_new, StateRefs* st) {
@@ -288,13 +301,56 @@ hipError_t run_plan(const spla_handle* h, const StepArgs& sa, const int32_t* pla
 
 // the lengths the decode part of a step sees: after its one-token append
 void fill_step_args(spla_handle* h, const void* k_new, const void* v_new, const void* q, const float* gate,
-                    float* out, const spla_decode_aux* aux, StepArgs* a) {
+                    float* out, const spla_decode_aux* aux, StepArgs* a, char* scratch_base = nullptr) {
   const spla_config& c = h->cfg;
   memset(a, 0, sizeof(*a));
   for (int b = 0; b < c.batch; ++b) h->lens[b] += 1;
-  fill_decode_args(h, q, gate, out, aux, &a->dec);
+  fill_decode_args(h, q, gate, out, aux, &a->dec,
+                   scratch_base ? scratch_base : static_cast<char*>(h->buf.workspace));
   fill_state_refs(h, k_new, v_new, &a->st);
   for (int b = 0; b < c.batch; ++b) h->lens[b] -= 1;
+}
+
+// ------------------------------------------------ static scratch (no-alloc)
+// The per-call scratch of spla_decode_step_noalloc: one array per GPU that
+// the library runs on, held until the process ends.  Host code never uses
+// the array's name as an address (on the host it is only a stand-in): the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(SPLA_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of the scratch on the device that runs `stream` (the
+// current device for the null stream), looked up with that device current
+hipError_t noalloc_scratch(hipStream_t stream, char** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd = 0;
+    if ((e = hipStreamGetDevice(stream, &sd)) != hipSuccess) return e;
+    dev = sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return hipSuccess;
 }
 
 }  // namespace
@@ -310,6 +366,7 @@ const char* spla_status_str(spla_status st) {
     case SPLA_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
     case SPLA_ERR_HIP: return "HIP launch failed";
     case SPLA_ERR_STATE: return "handle not bound";
+    case SPLA_ERR_SCRATCH: return "per-call scratch larger than the library's static scratch";
   }
   return "unknown status";
 }
@@ -496,6 +553,35 @@ spla_status spla_decode_step(spla_handle* h, const void* k_new, const void* v_ne
   LaunchSeq ls(reinterpret_cast<hipStream_t>(stream), aux);
   const hipError_t e = run_plan(h, a, plan, n, ls);
   // the mirror advances once the append is enqueued (the first kernel)
+  if (e != hipSuccess && ls.k <= 1) return hip_fail(h, e);
+  for (int b = 0; b < c.batch; ++b) h->lens[b] += 1;
+  return e == hipSuccess ? SPLA_OK : hip_fail(h, e);
+}
+
+spla_status spla_decode_step_noalloc(spla_handle* h, const void* k_new, const void* v_new, const void* q,
+                                     const float* gate, float* out, const spla_decode_aux* aux, void* stream) {
+  if (!h) return SPLA_ERR_INVALID_ARG;
+  if (!h->bound) return SPLA_ERR_STATE;
+  const spla_status vs = check_decode_args(h, q, gate, out, aux);
+  if (vs != SPLA_OK) return vs;
+  if (aux && aux->sel_in) return SPLA_ERR_INVALID_ARG;
+  if (!k_new || !v_new) return SPLA_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return SPLA_ERR_ALIGNMENT;
+  const spla_config& c = h->cfg;
+  const int64_t cap = (int64_t)c.max_blocks_per_seq * c.block_size;
+  for (int b = 0; b < c.batch; ++b)
+    if ((int64_t)h->lens[b] + 1 > cap) return SPLA_ERR_CAPACITY;
+  if (h->ws_bytes > kNoAllocScratchBytes) return SPLA_ERR_SCRATCH;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* base = nullptr;
+  const hipError_t es = noalloc_scratch(st, &base);
+  if (es != hipSuccess) return hip_fail(h, es);
+  StepArgs a;
+  fill_step_args(h, k_new, v_new, q, gate, out, aux, &a, base);
+  int32_t plan[kMaxPlan];
+  const int n = decode_plan(h, a.dec, SPLA_CALL_DECODE_STEP, plan);
+  LaunchSeq ls(st, aux);
+  const hipError_t e = run_plan(h, a, plan, n, ls);
   if (e != hipSuccess && ls.k <= 1) return hip_fail(h, e);
   for (int b = 0; b < c.batch; ++b) h->lens[b] += 1;
   return e == hipSuccess ? SPLA_OK : hip_fail(h, e);

@@ -88,7 +88,8 @@ typedef enum {
     SPLA_ERR_CAPACITY = 3,     /* append would exceed max_blocks_per_seq * block_size */
     SPLA_ERR_ALIGNMENT = 4,    /* a device pointer is not 16-byte aligned */
     SPLA_ERR_HIP = 5,          /* a kernel launch failed (see spla_last_hip_error) */
-    SPLA_ERR_STATE = 6         /* call before spla_bind */
+    SPLA_ERR_STATE = 6,        /* call before spla_bind */
+    SPLA_ERR_SCRATCH = 7       /* per-call scratch above SPLA_NOALLOC_SCRATCH_BYTES (no-alloc call) */
 } spla_status;
 
 typedef enum { SPLA_F32 = 0, SPLA_BF16 = 1 } spla_dtype;
@@ -189,6 +190,30 @@ spla_status spla_decode(spla_handle *h, const void *q, const float *gate, float 
  * advances; if the first fails, nothing changes. */
 spla_status spla_decode_step(spla_handle *h, const void *k_new, const void *v_new, const void *q,
                              const float *gate, float *out, const spla_decode_aux *aux, void *stream);
+
+/* For callers that cannot allocate device memory at call time (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * spla_decode_step with the per-call scratch (group log scores, selections,
+ * partial records, phi(q)^T S_all partials, phi(q)) taken from one static
+ * device array of the library instead of the bound workspace.  It allocates
+ * nothing and calls no allocating routine; arguments, results, validation
+ * and the sticky error word (bytes [0, 4) of the bound workspace, which is
+ * otherwise not touched) are those of spla_decode_step.
+ *   - The array holds SPLA_NOALLOC_SCRATCH_BYTES (64 MiB); a handle whose
+ *     spla_workspace_bytes() exceeds it gets SPLA_ERR_SCRATCH, with nothing
+ *     enqueued.
+ *   - Each GPU the library runs on holds its own copy until the process
+ *     ends.  Its device address is looked up on the first call on that GPU
+ *     (with the GPU of `stream` made current for the lookup); make that
+ *     first call outside stream capture.
+ *   - Every call on one GPU shares that GPU's array and it keeps the last
+ *     call's contents (every part is written before it is read, so nothing
+ *     needs clearing).  Calls that overlap on one GPU -- on two streams, or
+ *     from two handles -- race on it: order them on one stream. */
+#define SPLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+spla_status spla_decode_step_noalloc(spla_handle *h, const void *k_new, const void *v_new, const void *q,
+                                     const float *gate, float *out, const spla_decode_aux *aux,
+                                     void *stream);
 
 /* Copy the host mirror of the sequence lengths (batch entries). */
 spla_status spla_get_lens(const spla_handle *h, int32_t *lens_host);

@@ -15,7 +15,7 @@ from block_sparse_linear_amd import SplaBuffers, SplaConfig, SplaDecodeAux, load
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "spla.h")
 
-OK, INVALID, UNSUPPORTED, CAPACITY, ALIGN, HIPERR, STATE = range(7)
+OK, INVALID, UNSUPPORTED, CAPACITY, ALIGN, HIPERR, STATE, SCRATCH = range(8)
 FAKE = 0x7F0000000000  # 256-byte aligned stand-in for a device address
 
 
@@ -91,8 +91,8 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    strs = [lib.spla_status_str(i).decode() for i in range(7)]
-    assert all(strs) and len(set(strs)) == 7
+    strs = [lib.spla_status_str(i).decode() for i in range(8)]
+    assert all(strs) and len(set(strs)) == 8
     assert lib.spla_status_str(99).decode() == "unknown status"
 
 
@@ -234,6 +234,38 @@ def test_decode_validation(lib):
     assert lib.spla_decode_step(h, FAKE, FAKE, P(FAKE), P(FAKE), P(FAKE), None, None) == CAPACITY
     assert lens_of(lib, h, 2) == [cap, 1]
     lib.spla_destroy(h)
+
+
+def test_decode_step_noalloc_validation(lib):
+    # the no-alloc step validates like spla_decode_step, on the host, before
+    # it looks up its static scratch (no HIP call in any of these)
+    P = ctypes.c_void_p
+    h, c = bound(lib, lens=(64, 500))
+    aux = SplaDecodeAux()
+    aux.sel_in = FAKE
+    f = lib.spla_decode_step_noalloc
+    assert f(None, FAKE, FAKE, P(FAKE), P(FAKE), P(FAKE), None, None) == INVALID
+    assert f(h, FAKE, FAKE, P(FAKE), P(FAKE), P(FAKE), ctypes.byref(aux), None) == INVALID
+    assert f(h, None, FAKE, P(FAKE), P(FAKE), P(FAKE), None, None) == INVALID
+    assert f(h, FAKE, FAKE, None, P(FAKE), P(FAKE), None, None) == INVALID
+    assert f(h, FAKE, FAKE + 6, P(FAKE), P(FAKE), P(FAKE), None, None) == ALIGN
+    assert lens_of(lib, h, 2) == [64, 500]
+    lib.spla_destroy(h)
+    st, h = create(lib, cfg())
+    assert f(h, FAKE, FAKE, P(FAKE), P(FAKE), P(FAKE), None, None) == STATE
+    lib.spla_destroy(h)
+    h, c = bound(lib, lens=(40 * 64, 1))
+    assert f(h, FAKE, FAKE, P(FAKE), P(FAKE), P(FAKE), None, None) == CAPACITY
+    lib.spla_destroy(h)
+    # a configuration whose per-call scratch exceeds the static array
+    big = dict(batch=256, n_q_heads=32, n_kv_heads=8, top_k=64, max_blocks_per_seq=100, num_pages=100)
+    h, c = bound(lib, lens=[300] * 256, **big)
+    assert lib.spla_workspace_bytes(h) > bsl.NOALLOC_SCRATCH_BYTES
+    assert f(h, FAKE, FAKE, P(FAKE), P(FAKE), P(FAKE), None, None) == SCRATCH
+    assert lens_of(lib, h, 256) == [300] * 256
+    lib.spla_destroy(h)
+    m = re.search(r"#define\s+SPLA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", open(HEADER).read())
+    assert int(m.group(1)) << int(m.group(2)) == bsl.NOALLOC_SCRATCH_BYTES
 
 
 def test_binding_raises_without_library(tmp_path):
