@@ -33,6 +33,7 @@ workload, with all host threads and with one).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -408,6 +409,10 @@ def main() -> int:
             break
     W0 = W + lead
     total_steps = W0 + K + P
+    if total_steps > w.steps:
+        # the workload's draws over more steps than it states (the mixture's
+        # centre ids run on: the first w.steps steps are unchanged)
+        w = dataclasses.replace(w, steps=total_steps)
     after, chunk_lens = simulate(total_steps)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -29,6 +29,7 @@ import argparse
 import csv
 import glob
 import os
+import re
 import sys
 from collections import defaultdict
 
@@ -47,9 +48,10 @@ COPY_MARK = "neg_kernel"
 
 def symbol_of(kernel_name: str):
     """Decode-path symbol of a demangled kernel name, if it is one."""
-    head = kernel_name.split("(")[0].split("<")[0]
-    sym = head.split("::")[-1].strip()
-    return sym if sym in SYMBOLS else None
+    # "void spla::(anonymous namespace)::k_name<...>(args)": the name ahead of
+    # the first template or argument list
+    m = re.search(r"(?:^|::|\s)(k_\w+?)(?:<|\()", kernel_name.replace("(anonymous namespace)", ""))
+    return m.group(1) if m and m.group(1) in SYMBOLS else None
 
 
 def per_dispatch(path: str, counter: str):
@@ -106,7 +108,7 @@ def trace_summary(args) -> int:
     names = {}
     for t0, t1, sym, name in rows:
         by[sym].append((t1 - t0) / 1000.0)
-        names.setdefault(sym, name.split("(")[0])
+        names.setdefault(sym, re.sub(r"^void\s+", "", name.replace("(anonymous namespace)::", "")).split("(")[0])
     out = [f"# Kernel trace: SPLA decode step, {args.workload} workload", "",
            "gfx950 (MI355X), ROCm 7.2, rocprofv3.  Summarised by bench_pmc.py from the run's kernel trace.", "",
            "Command:", "", "```", "cd /tmp && export TMPDIR=/tmp",
@@ -119,7 +121,9 @@ def trace_summary(args) -> int:
         out.append(f"| `{names[sym]}` | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} | {max(d):.2f} | "
                    + (f"{sum(ev) / len(ev):.2f}" if ev else "-") + " |")
     if line:
-        out += ["", "## The bench line of the same command (HIP events, no tracer in the way of the graphs)", ""]
+        out += ["", "## The bench line of the same workload without the tracer (HIP events)", ""]
+        if args.bench_cmd:
+            out += ["```", args.bench_cmd, "```", ""]
         ku = line.get("kernel_us", {})
         out.append("| kernel | bench us |")
         out.append("|---|---|")
@@ -128,8 +132,8 @@ def trace_summary(args) -> int:
         out += ["", f"Step: {line.get('ms_per_step', 0) * 1e3:.2f} us ({line.get('value', 0):.0f} tokens/s); "
                     f"step bytes {line.get('step_bytes', 0) / 1e6:.2f} MB, "
                     f"{line.get('step_frac_of_peak', 0):.3f} of the 8 TB/s peak.  "
-                    "Under the tracer the graph-replayed timed region runs slower, so the bench line's step time "
-                    "is from a run without it when one is given."]
+                    "Under the tracer the graph-replayed timed region runs slower, so the step time is taken "
+                    "from this run without it; the kernel means above are the tracer's own."]
     text = "\n".join(out) + "\n"
     dest = args.out or os.path.join(ROOT, "profiles", f"decode_{args.workload}_trace.md")
     with open(dest, "w") as f:
@@ -145,6 +149,7 @@ def main() -> int:
     ap.add_argument("--write", help="output directory (or CSV) of the WRITE_SIZE run")
     ap.add_argument("--trace", help="output directory of a --kernel-trace --stats run (trace summary mode)")
     ap.add_argument("--bench-line", help="stdout of bench.py (its JSON line) for the trace summary")
+    ap.add_argument("--bench-cmd", default="", help="the untraced bench command whose line is given")
     ap.add_argument("--prof-steps", type=int, default=16, help="steps of the bench's per-kernel event pass")
     ap.add_argument("--cmd", default="python3 /root/repo/bench.py --steps 4 --warmup 1 --prof-steps 1 "
                                      "--no-cpu-baseline", help="the profiled command, as recorded")
