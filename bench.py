@@ -53,12 +53,13 @@ CSRC = "block_sparse_linear_amd/csrc/"
 # taken on
 _COMMON = ["decode_common.h", "spla_common.h", "append_items.h"]
 KERNEL_SOURCES = {
-    "score": ["score.hip"],
-    "step_score": ["score.hip"],
+    "score": ["score.hip", "score_parts.h"],
+    "step_score": ["score.hip", "score_parts.h"],
     "select": ["select.hip", "select_core.h"],
     "attend": ["attend.hip", "attend_mfma.h"],
     "select_attend": ["select_attend.hip", "select_core.h", "attend_mfma.h"],
     "combine": ["combine.hip"],
+    "step_fused": ["step_fused.hip", "score_parts.h", "select_core.h", "attend_mfma.h"],
 }
 PMC_SUMMARY = "profiles/decode_{workload}_pmc.txt"
 # plain copy of known size run by every bench (outside the timed region) so the
@@ -156,6 +157,10 @@ def kernel_bytes(name: str, w, lens, s_kv: int) -> int:
         return lg + kv + recs + B * H * d * s_kv
     if name == "combine":
         return recs + B * G * chunks * r * (d + 1) * 4 + B * H * d * 4 + H * 4
+    if name == "step_fused":
+        # the first kernel's bytes, then the selected K/V and the records (the
+        # scores it hands over inside the kernel are not counted)
+        return step_score_bytes(w, lens, s_kv) + kv + recs
     raise ValueError(name)
 
 
@@ -358,6 +363,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-select", type=int, default=-1, choices=(-1, 0, 1),
                     help="selector placement: -1 automatic, 0 stand-alone kernel, 1 fused into attend")
+    ap.add_argument("--step-kernel", type=int, default=-1, choices=(-1, 0, 1),
+                    help="1: decode step in one kernel plus the combine; -1 automatic, 0: separate kernels")
     ap.add_argument("--rla-form", type=int, default=0, choices=sorted(RLA_FORMS),
                     help="output form of the RLA branch: 0 plain, 1 normalised (o_rla / D), 2 RMS-normalised")
     ap.add_argument("--prefill", type=int, default=0,
@@ -426,6 +433,7 @@ def main() -> int:
         layer = SplaLayer(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.top_k, mb,
                           kv_dtype=w.kv_dtype, device="cuda:0")
         layer.set_fused_select(args.fused_select)
+        layer.set_step_kernel(args.step_kernel)
         layer.set_rla_output(args.rla_form, gamma, RLA_EPS)
         return layer
 

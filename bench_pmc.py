@@ -42,7 +42,7 @@ import bench  # noqa: E402
 # kernel symbols of the decode path -> launch-plan names
 SYMBOLS = {"k_step_score": "step_score", "k_score": "score", "k_select_attend": "select_attend",
            "k_select": "select", "k_attend_mfma": "attend", "k_attend": "attend", "k_combine": "combine",
-           "k_append": "append", "k_state_add": "state_add"}
+           "k_append": "append", "k_state_add": "state_add", "k_step_fused": "step_fused"}
 COPY_MARK = "neg_kernel"
 
 

@@ -39,9 +39,11 @@ EXPORTED = [
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # spla_kernel ids (include/spla.h) -> kernel names
-KERNELS = {1: "score", 2: "step_score", 3: "select", 4: "attend", 5: "select_attend", 6: "combine"}
+KERNELS = {1: "score", 2: "step_score", 3: "select", 4: "attend", 5: "select_attend", 6: "combine",
+           7: "step_fused"}
 CALL_DECODE, CALL_DECODE_SEL_IN, CALL_DECODE_STEP = 0, 1, 2
 TUNE_FUSED_SELECT = 0
+TUNE_STEP_KERNEL = 1
 # output forms of the RLA branch (spla_rla_form)
 RLA_PLAIN, RLA_NORMALIZED, RLA_RMSNORM = 0, 1, 2
 # block scores the selection can rank (spla_score_form)
@@ -313,6 +315,11 @@ class SplaLayer:
     def set_fused_select(self, mode: int) -> None:
         """-1 automatic, 0 stand-alone selector, 1 fused select + attend where supported."""
         self.handle.set_tuning(TUNE_FUSED_SELECT, mode)
+
+    def set_step_kernel(self, mode: int) -> None:
+        """1: decode_step in one kernel (plus the combine) wherever the fused
+        select + attend runs; -1 automatic and 0: the separate kernels."""
+        self.handle.set_tuning(TUNE_STEP_KERNEL, mode)
 
     def set_rla_output(self, form: int = RLA_PLAIN, gamma=None, eps: float = 1e-6) -> None:
         """Output form of the RLA branch: RLA_PLAIN (o_rla), RLA_NORMALIZED

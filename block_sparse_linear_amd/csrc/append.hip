@@ -34,7 +34,8 @@ __global__ __launch_bounds__(kThreads) void k_append(const AppendArgs a) {
   if (item < a.stat_items) {
     const int e = find_entry(a.stat_prefix, a.n_entries, item);
     const int local = item - a.stat_prefix[e];
-    append_block_stats<BF16>(a.st, a.e[e], a.e[e].t0 / a.st.bk + local / a.st.G, local % a.st.G);
+    __shared__ BlockStatsLds<BF16> L;
+    append_block_stats<BF16>(a.st, a.e[e], a.e[e].t0 / a.st.bk + local / a.st.G, local % a.st.G, L);
   }
 }
 

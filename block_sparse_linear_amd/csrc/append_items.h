@@ -65,10 +65,15 @@ __device__ void append_page_row_head(const StateRefs& a, const AppendEntry& E, i
 // column of the row)), and held in registers for both passes; the per-column
 // sums meet in LDS.
 template <bool BF16>
-__device__ void append_block_stats(const StateRefs& a, const AppendEntry& E, int j, int g) {
+struct BlockStatsLds {
+  float red[kThreads * (BF16 ? 8 : 4)];  // per-column partial sums of every thread
+};
+
+template <bool BF16>
+__device__ void append_block_stats(const StateRefs& a, const AppendEntry& E, int j, int g, BlockStatsLds<BF16>& L) {
   constexpr int VE = BF16 ? 8 : 4;  // elements per 16-byte vector
   constexpr int MAXV = 16;          // vectors per thread (fp32 keys, d = 128, Bk = 128)
-  __shared__ float red[kThreads * VE];
+  float* red = L.red;
   const int d = a.d, bk = a.bk;
   const int vr = d / VE;            // vectors per token row
   const int tg = kThreads / vr;     // token groups

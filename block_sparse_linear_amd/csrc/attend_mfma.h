@@ -42,20 +42,32 @@ __device__ __forceinline__ void phi_bf16_split(const uint4& raw, uint4& hi, uint
 // first kernel of the decode wrote); other rows read row 0 and are masked
 // when the operands are formed
 template <int R, int D>
-__device__ __forceinline__ void load_q_mfma(const void* q, const uint16_t* phq, int H, int g, int b,
-                                            uint4 (&qraw)[D / 32], uint4 (&fh)[D / 32], uint4 (&fl)[D / 32]) {
-  constexpr int WB = R <= 4 ? 4 : 8;
+__device__ __forceinline__ void load_q_raw(const void* q, int H, int g, int b, uint4 (&qraw)[D / 32]) {
   const int lane = threadIdx.x % 64, m = lane % 16, lg4 = lane / 16;
   const int hq = m < R ? m : 0;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+    qraw[ks] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) +
+                                               ((size_t)b * H + g * R + hq) * D + 32 * ks + 8 * lg4);
+}
+template <int R, int D>
+__device__ __forceinline__ void load_phq(const uint16_t* phq, int H, int g, int b, uint4 (&fh)[D / 32],
+                                         uint4 (&fl)[D / 32]) {
+  constexpr int WB = R <= 4 ? 4 : 8;
+  const int lane = threadIdx.x % 64, m = lane % 16, lg4 = lane / 16;
   const int hw = (m >= WB && m < WB + R) ? m - WB : 0;
   const uint16_t* fq = phq + ((size_t)b * H + g * R + hw) * 2 * D;
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
-    qraw[ks] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) +
-                                               ((size_t)b * H + g * R + hq) * D + 32 * ks + 8 * lg4);
     fh[ks] = *reinterpret_cast<const uint4*>(fq + 32 * ks + 8 * lg4);
     fl[ks] = *reinterpret_cast<const uint4*>(fq + D + 32 * ks + 8 * lg4);
   }
+}
+template <int R, int D>
+__device__ __forceinline__ void load_q_mfma(const void* q, const uint16_t* phq, int H, int g, int b,
+                                            uint4 (&qraw)[D / 32], uint4 (&fh)[D / 32], uint4 (&fl)[D / 32]) {
+  load_q_raw<R, D>(q, H, g, b, qraw);
+  load_phq<R, D>(phq, H, g, b, fh, fl);
 }
 
 // Block j (page `page`) of (b, g), all R query heads, bf16 K/V; writes the

@@ -27,7 +27,6 @@ __global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, con
                                                              int32_t max_blocks, int32_t G, int32_t H,
                                                              const DecodeArgs a) {
   __shared__ SelectLds L;
-  __shared__ int s_j, s_page;
   const int slot = blockIdx.x >> 3;
   const int bgi = (blockIdx.y << 3) + (blockIdx.x & 7);
   const int b = bgi / G, g = bgi - b * G;
@@ -44,50 +43,7 @@ __global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, con
   const int nb = n_blocks(a, b);
   select_pages<KPT>(block_table, max_blocks, b, nb, k);
   int j, page;
-  const int kp = a.top_k - 2;
-  if (nb <= a.top_k) {
-    j = slot < nb ? slot : -1;
-    page = j >= 0 ? block_table[(size_t)b * max_blocks + j] : -1;
-  } else if (slot == 0) {  // the sink
-    j = 0;
-    page = k.pg_sink;
-  } else if (slot == kp + 1) {  // the current block
-    j = nb - 1;
-    page = k.pg_cur;
-  } else if (const int n = select_threshold_rank<KPT>(a, nb, k, L)) {
-    // every wavefront finds its slot on its own: passes of 64 listed
-    // candidates in candidate order, counting the chosen ones, until the
-    // pass holding the slot-th chosen candidate
-    const int lane = threadIdx.x & 63;
-    int base = 1, src = -1, m = 0;
-    for (; 64 * m < n; ++m) {
-      bool chosen;
-      const uint64_t mask = sel_chosen_pass(L, n, kp, m, chosen);
-      const int cnt = __popcll(mask);
-      if (slot < base + cnt) {
-        // the (slot - base)-th set bit of the mask
-        const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-        src = __ffsll((unsigned long long)__ballot(chosen && pos == slot)) - 1;
-        break;
-      }
-      base += cnt;
-    }
-    int i_, pg_;
-    sel_listed(L, min(64 * m + lane, n - 1), i_, pg_);
-    j = __builtin_amdgcn_readlane(i_ + 1, src);
-    page = __builtin_amdgcn_readlane(pg_, src);
-  } else {
-    select_bucket<KPT>(a, nb, k, L, [&](int pos, int id, int pg) {
-      if (pos == slot) {
-        s_j = id;
-        s_page = pg;
-      }
-    });
-    __syncthreads();
-    j = s_j;
-    page = s_page;
-  }
+  select_slot<KPT>(a, block_table, max_blocks, b, nb, slot, k, L, j, page);
   // the combine reads the selection to tell used slots from unused ones
   if (threadIdx.x == 0) a.sel[((size_t)b * a.G + g) * a.top_k + slot] = j;
   attend_block_mfma<R, D, 64>(a, slot, g, b, j, page, qraw, fh, fl);

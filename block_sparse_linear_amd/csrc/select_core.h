@@ -48,6 +48,7 @@ struct __attribute__((aligned(16))) SelectLds {
   float s_mn[4], s_mx[4];
   int s_cnt[4];
   int s_bt, s_above, s_cbt, s_nm;
+  int s_j, s_page;  // one slot's block and page (select_slot's bucket path)
 };
 
 // One thread's candidates: scores and page ids of candidates i = w * 64 KPT
@@ -84,6 +85,25 @@ __device__ __forceinline__ void select_load(const float* lg, const int32_t* bloc
     k.x[u] = row[i];
     k.pg[u] = btab[min(i + 1, max_blocks - 1)];
   }
+}
+
+// The two halves of select_load, for a kernel that has the page ids before
+// the scores exist: the candidates' page ids, then (later) their scores.
+template <int KPT>
+__device__ __forceinline__ void select_load_pages(const int32_t* block_table, int n_tiles, int max_blocks, int brow,
+                                                  SelectKeys<KPT>& k) {
+  const int cap = max(min(n_tiles * kTile, max_blocks) - 2, 0);
+  const int32_t* btab = block_table + (size_t)brow * max_blocks;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) k.pg[u] = btab[min(min(SelectKeys<KPT>::cand(u), cap) + 1, max_blocks - 1)];
+}
+template <int KPT>
+__device__ __forceinline__ void select_load_scores(const float* lg, int n_tiles, int max_blocks, int G, int g, int b,
+                                                   SelectKeys<KPT>& k) {
+  const int cap = max(min(n_tiles * kTile, max_blocks) - 2, 0);
+  const float* row = lg + ((size_t)b * G + g) * (size_t)(n_tiles * kTile) + 1;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) k.x[u] = row[min(SelectKeys<KPT>::cand(u), cap)];
 }
 
 // Pages of the sink and the current block.  They are read with vector
@@ -488,6 +508,61 @@ inline int max_candidates(const DecodeArgs& a) {
     if (nb > a.top_k) nc = nc > nb - 2 ? nc : nb - 2;
   }
   return nc;
+}
+
+// The block at position `slot` of the ascending selection of (b, g) and its
+// page (uniform over the workgroup), for a kernel whose workgroups each take
+// one slot: the sink and the current block directly; otherwise every
+// wavefront finds its slot in the threshold path's chosen list on its own
+// (passes of 64 listed candidates in candidate order, counting the chosen
+// ones, until the pass holding the slot-th chosen candidate), or the bucket
+// path hands it over in LDS.  Every thread of the workgroup must call it;
+// brow is b's block-table row.
+template <int KPT>
+__device__ __forceinline__ void select_slot(const DecodeArgs& a, const int32_t* block_table, int max_blocks, int brow,
+                                            int nb, int slot, const SelectKeys<KPT>& k, SelectLds& L, int& j,
+                                            int& page) {
+  const int kp = a.top_k - 2;
+  if (nb <= a.top_k) {
+    j = slot < nb ? slot : -1;
+    page = j >= 0 ? block_table[(size_t)brow * max_blocks + j] : -1;
+  } else if (slot == 0) {  // the sink
+    j = 0;
+    page = k.pg_sink;
+  } else if (slot == kp + 1) {  // the current block
+    j = nb - 1;
+    page = k.pg_cur;
+  } else if (const int n = select_threshold_rank<KPT>(a, nb, k, L)) {
+    const int lane = threadIdx.x & 63;
+    int base = 1, src = -1, m = 0;
+    for (; 64 * m < n; ++m) {
+      bool chosen;
+      const uint64_t mask = sel_chosen_pass(L, n, kp, m, chosen);
+      const int cnt = __popcll(mask);
+      if (slot < base + cnt) {
+        // the (slot - base)-th set bit of the mask
+        const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+        src = __ffsll((unsigned long long)__ballot(chosen && pos == slot)) - 1;
+        break;
+      }
+      base += cnt;
+    }
+    int i_, pg_;
+    sel_listed(L, min(64 * m + lane, n - 1), i_, pg_);
+    j = __builtin_amdgcn_readlane(i_ + 1, src);
+    page = __builtin_amdgcn_readlane(pg_, src);
+  } else {
+    select_bucket<KPT>(a, nb, k, L, [&](int pos, int id, int pg) {
+      if (pos == slot) {
+        L.s_j = id;
+        L.s_page = pg;
+      }
+    });
+    __syncthreads();
+    j = L.s_j;
+    page = L.s_page;
+  }
 }
 
 }  // namespace

@@ -28,6 +28,18 @@ constexpr int kRlaPlain = 0, kRlaNormalized = 1, kRlaRms = 2;
 // error word bits (workspace bytes [0, 4))
 constexpr uint32_t kErrPage = 1u;
 constexpr uint32_t kErrSel = 2u;
+// one-kernel step: a wait ran out (4), a producer count above its target at
+// a wait (8), more attend workgroups past their wait than slots (16), a
+// pair's producers not all on the attend workgroup's XCD (32)
+constexpr uint32_t kErrStepWait = 4u, kErrStepCount = 8u, kErrStepArrive = 16u, kErrStepXcd = 32u;
+
+// counters of the one-kernel decode step: one 128-byte line per (sequence,
+// KV head) pair (count of finished producer workgroups, count of attend
+// workgroups past their wait), at workspace bytes [256, 256 + 128 kStepPairs);
+// each call leaves them at zero
+constexpr int kStepPairs = 256;
+constexpr int kStepCtrStride = 32;  // int32 per pair
+constexpr size_t kStepCtrOffset = 256;
 
 struct AppendEntry {
   int32_t seq;  // sequence id
@@ -56,6 +68,7 @@ struct DecodeArgs {
   int32_t obar_one;  // 1: one o_bar / phi(q).z partial per head ([B][G][R][d], [B][G][R]) instead
   uint16_t* phq;     // workspace [B][H][2][d]: phi(q) as bf16 hi, then the bf16 rounding of the rest
   uint32_t* err;    // workspace error word
+  int32_t* step_ctr;  // workspace counters of the one-kernel step (kStepPairs lines)
   const int32_t* sel_in;
   int32_t* sel_out;
   float* lg_out;
@@ -176,8 +189,20 @@ hipError_t launch_block_mass(const DecodeArgs& a, bool bf16, float* lgx, int max
 // override and at most 16 * 256 candidates per sequence
 bool select_attend_supported(const DecodeArgs& a, bool bf16);
 hipError_t launch_select_attend(const DecodeArgs& a, const Launch& l);
+// one-kernel decode step (append + scores + o_bar partials, then select +
+// attend, with waits inside one XCD): where the fused select + attend is
+// supported, with the Taylor score and at most kStepPairs (b, g) pairs
+bool step_fused_supported(const DecodeArgs& a, bool bf16);
+hipError_t launch_step_fused(const StepArgs& a, const Launch& l);
 
 // ------------------------------------------------------------ device helpers
+// the XCD (accelerator complex die) the calling wavefront runs on
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(x));
+  return x;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // phi(x) = elu(x) + 1

@@ -65,8 +65,12 @@
  *   workspace         spla_workspace_bytes() bytes, zero-filled by the
  *                     caller once before the first call.  Bytes [0, 4) hold
  *                     a sticky uint32 error word (bit 0: out-of-range page
- *                     id, bit 1: a selected block id outside the sequence);
- *                     the rest is scratch that the library clears itself.
+ *                     id, bit 1: a selected block id outside the sequence,
+ *                     bits 2-4: a one-kernel step's counters out of step, see
+ *                     SPLA_TUNE_STEP_KERNEL); the rest is scratch: bytes
+ *                     [256, 33024) are the one-kernel step's counters, which
+ *                     every call leaves at zero, the rest the library clears
+ *                     itself.
  *                     A fresh state needs s_all, z_all zero-filled.
  */
 #ifndef SPLA_H
@@ -229,8 +233,18 @@ const char *spla_status_str(spla_status st);
  *   The fused kernel recomputes the selection of a (sequence, KV head) in
  *   every attend workgroup of that pair instead of handing it over through
  *   memory, which saves one launch per decode.
+ *   SPLA_TUNE_STEP_KERNEL: 1 = spla_decode_step runs its append, scores,
+ *   o_bar partials, selection and attend in one kernel wherever the fused
+ *   select + attend runs, the score form is the Taylor score and
+ *   B * n_kv_heads <= 256; -1 automatic (default) and 0 = the separate
+ *   kernels (automatic keeps them: they are as fast or faster).  The
+ *   one-kernel step hands each (sequence, KV head) pair's scores over to its
+ *   attend workgroups inside the kernel, through counters at workspace bytes
+ *   [256, 33024) that every call leaves at zero (the workspace starts
+ *   zero-filled); a wait that runs out sets bit 2 of the error word, a
+ *   counter found above its target bit 3, an attend count above top_k bit 4.
  * SPLA_ERR_INVALID_ARG for an unknown key or value. */
-typedef enum { SPLA_TUNE_FUSED_SELECT = 0 } spla_tune_key;
+typedef enum { SPLA_TUNE_FUSED_SELECT = 0, SPLA_TUNE_STEP_KERNEL = 1 } spla_tune_key;
 spla_status spla_set_tuning(spla_handle *h, int32_t key, int32_t value);
 
 /* Output form of the residual-linear-attention branch in o = o_sparse +
@@ -324,7 +338,8 @@ typedef enum {
     SPLA_KERNEL_SELECT = 3,        /* stand-alone top-k selector */
     SPLA_KERNEL_ATTEND = 4,        /* attend + correct over the selector's blocks */
     SPLA_KERNEL_SELECT_ATTEND = 5, /* fused select + attend + correct */
-    SPLA_KERNEL_COMBINE = 6        /* merge, o_bar, o_rla, D, gate */
+    SPLA_KERNEL_COMBINE = 6,       /* merge, o_bar, o_rla, D, gate */
+    SPLA_KERNEL_STEP_FUSED = 7     /* append + scores + o_bar partials + select + attend (spla_decode_step) */
 } spla_kernel;
 typedef enum {
     SPLA_CALL_DECODE = 0,          /* spla_decode without sel_in */

@@ -138,11 +138,12 @@ def test_sizes(lib):
     assert st == OK
     n_tiles = -(-130 // 64)
     assert lib.spla_stats_floats(h) == 3 * 2 * n_tiles * 64 * 64
-    # error word + scores + two index lists + per-head partials + the
-    # phi(q)^T S_all and phi(q).z partials of the d * d / 1024 row chunks +
-    # phi(q) as bf16 hi / lo, each part rounded up to 256 bytes
+    # error word + the one-kernel step's counters (256 lines of 128 bytes) +
+    # scores + two index lists + per-head partials + the phi(q)^T S_all and
+    # phi(q).z partials of the d * d / 1024 row chunks + phi(q) as bf16 hi /
+    # lo, each part rounded up to 256 bytes
     chunks = 64 * 64 // 1024
-    need = (256 + 3 * 2 * n_tiles * 64 * 4 + 2 * 3 * 2 * 20 * 4 + 3 * 8 * 20 * (2 * 64 + 4) * 4
+    need = (256 + 256 * 128 + 3 * 2 * n_tiles * 64 * 4 + 2 * 3 * 2 * 20 * 4 + 3 * 8 * 20 * (2 * 64 + 4) * 4
             + 3 * 8 * chunks * 64 * 4 + 3 * 8 * chunks * 4 + 3 * 8 * 2 * 64 * 2)
     ws = lib.spla_workspace_bytes(h)
     assert need <= ws <= need + 7 * 256 and ws % 256 == 0
@@ -288,12 +289,15 @@ def test_tuning_validation(lib):
     assert lib.spla_set_tuning(h, 0, 0) == OK
     assert lib.spla_set_tuning(h, 0, 1) == OK
     assert lib.spla_set_tuning(h, 0, 2) == INVALID
+    for v in (-1, 0, 1):
+        assert lib.spla_set_tuning(h, 1, v) == OK
+    assert lib.spla_set_tuning(h, 1, 2) == INVALID and lib.spla_set_tuning(h, 1, -2) == INVALID
     assert lib.spla_set_tuning(h, 7, 0) == INVALID
     assert lib.spla_set_tuning(None, 0, 0) == INVALID
     lib.spla_destroy(h)
 
 
-SCORE, STEP_SCORE, SELECT, ATTEND, SELECT_ATTEND, COMBINE = range(1, 7)
+SCORE, STEP_SCORE, SELECT, ATTEND, SELECT_ATTEND, COMBINE, STEP_FUSED = range(1, 8)
 
 
 def plan(lib, h, call):
@@ -305,15 +309,27 @@ def plan(lib, h, call):
 def test_launch_plan(lib):
     # bf16, Bk=64, top_k=16; lengths 100 (2 blocks) and 2000 (32 blocks > top_k)
     h, c = bound(lib)
-    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]  # automatic: 4 (b, g) pairs -> fused
+    # automatic: 4 (b, g) pairs -> fused select + attend, separate kernels
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
     assert plan(lib, h, 0) == [SCORE, SELECT_ATTEND, COMBINE]
     assert plan(lib, h, 1) == [SCORE, ATTEND, COMBINE]              # selection override
-    assert lib.spla_set_tuning(h, 0, 0) == OK
+    assert lib.spla_set_tuning(h, 1, 1) == OK                       # the step in one kernel
+    assert plan(lib, h, 2) == [STEP_FUSED, COMBINE]
+    assert plan(lib, h, 0) == [SCORE, SELECT_ATTEND, COMBINE]       # spla_decode: unchanged
+    assert lib.spla_set_tuning(h, 1, 0) == OK
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
+    assert lib.spla_set_tuning(h, 1, 1) == OK
+    assert lib.spla_set_tuning(h, 0, 0) == OK                       # the one-kernel step needs the fused selector
     assert plan(lib, h, 2) == [STEP_SCORE, SELECT, ATTEND, COMBINE]
     assert lib.spla_set_tuning(h, 0, 1) == OK
     assert plan(lib, h, 0) == [SCORE, SELECT_ATTEND, COMBINE]
     assert plan(lib, h, 3) == -1 and lib.spla_launch_plan(None, 0, None, 0) == -1
-    assert lib.spla_launch_plan(h, 2, None, 0) == 3                 # count only
+    assert lib.spla_launch_plan(h, 2, None, 0) == 2                 # count only
+    # the one-kernel step takes the Taylor score only
+    assert lib.spla_set_score_form(h, 1) == OK
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
+    assert lib.spla_set_score_form(h, 0) == OK
+    assert lib.spla_set_tuning(h, 1, -1) == OK
     assert lens_of(lib, h, 2) == [100, 2000]                       # the query changes nothing
     lib.spla_destroy(h)
     # every sequence short: the first kernel still runs (it forms the
@@ -321,6 +337,8 @@ def test_launch_plan(lib):
     h, c = bound(lib, lens=(5, 64 * 16))
     assert plan(lib, h, 0) == [SCORE, SELECT_ATTEND, COMBINE]
     assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
+    assert lib.spla_set_tuning(h, 1, 1) == OK
+    assert plan(lib, h, 2) == [STEP_FUSED, COMBINE]
     lib.spla_destroy(h)
     # the fused kernel needs bf16 and Bk = 64
     for kw in (dict(kv_dtype=0), dict(block_size=128)):
@@ -372,7 +390,10 @@ def test_score_form_and_block_mass_validation(lib):
     lib.spla_destroy(h)
     h, c = bound(lib, lens=(64, 128))
     assert lib.spla_block_mass(h, FAKE, FAKE, None) == OK
-    # the score form changes which score the selection ranks, not the kernels
+    # the score form changes which score the selection ranks; the one-kernel
+    # step takes the Taylor score only
+    assert lib.spla_set_tuning(h, 1, 1) == OK
+    assert plan(lib, h, 2) == [STEP_FUSED, COMBINE]
     assert lib.spla_set_score_form(h, 1) == OK
     assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
     lib.spla_destroy(h)

@@ -153,27 +153,54 @@ def test_step_matches_two_calls_bitwise():
 
 
 # ---- selector placement ---------------------------------------------------------
-def test_fused_select_matches_split_bitwise():
-    """The fused select + attend kernel and the stand-alone selector give the
-    same outputs and selections, bit for bit (both placements run the same
-    selection and the same attend arithmetic)."""
-    _needs_gpu()
+def _placements_bitwise(w, steps):
     import torch
     from tests.spla_parity import ParityRun
-    # ragged: one sequence with every block selected, others crossing block ends
-    w = small(name="fused_vs_split", batch=4, t0=(64 * 300 - 3, 64 * 5, 64 * 40 + 1, 3000), steps=6,
-              kind="outlier", n_outlier=8, top_k=12)
-    runs = [ParityRun(w, steps=6, prefill_chunk=1000, page_order="shuffled", fused_select=m) for m in (0, 1)]
+    print(f"[gpu-test] {w.name}: B={w.batch} G={w.n_kv_heads} k={w.top_k} t0={w.t0}", flush=True)
+    runs = [ParityRun(w, steps=steps, prefill_chunk=1000, page_order="shuffled", fused_select=m, step_kernel=sk)
+            for m, sk in ((0, -1), (1, -1), (1, 1))]
     assert runs[0].layer.launch_plan() == ["step_score", "select", "attend", "combine"]
     assert runs[1].layer.launch_plan() == ["step_score", "select_attend", "combine"]
+    assert runs[2].layer.launch_plan() == ["step_fused", "combine"]
     for r in runs:
         r.prefill()
-    for s in range(6):
+    for s in range(steps):
         st = w.step(s)
         res = [r.gpu_decode(st["q"], kv=(st["k"], st["v"])) for r in runs]
         for key in ("o", "sel_idx", "o_sparse", "o_rla", "d_rla", "lg"):
-            assert np.array_equal(res[0][key], res[1][key]), f"step {s}: {key}"
-    assert runs[0].layer.error_word() == 0 and runs[1].layer.error_word() == 0
+            for i in (1, 2):
+                assert np.array_equal(res[0][key], res[i][key]), f"step {s}: {key}, plan {i}"
+        print(f"[gpu-test] step {s}: lens {runs[2].layer.lens[:4]}, error words {[r.layer.error_word() for r in runs]}",
+              flush=True)
+    errs = [r.layer.error_word() for r in runs]
+    assert errs == [0, 0, 0]
+    for x, y in zip(runs[0].layer.state_tensors(), runs[2].layer.state_tensors()):
+        assert torch.equal(x, y)
+
+
+def test_fused_select_matches_split_bitwise():
+    """The stand-alone selector, the fused select + attend kernel and the
+    one-kernel step give the same outputs and selections, bit for bit (every
+    placement runs the same selection and the same attend arithmetic).  The
+    steps cross a block end, so the one-kernel step's append completes a
+    block whose statistics the next step scores."""
+    _needs_gpu()
+    # ragged: one sequence with every block selected, others crossing block ends
+    w = small(name="fused_vs_split", batch=4, t0=(64 * 300 - 3, 64 * 5, 64 * 40 + 1, 3000), steps=6,
+              kind="outlier", n_outlier=8, top_k=12)
+    _placements_bitwise(w, 6)
+
+
+def test_step_kernel_three_pairs_per_xcd_bitwise():
+    """The one-kernel step with 24 (sequence, KV head) pairs: three pairs on
+    each XCD, whose producers all come before any of their attend
+    workgroups; short sequences (every block selected) among long ones, a
+    block end crossed, d = 64 and four query heads per KV head."""
+    _needs_gpu()
+    w = Workload(name="step3pp", batch=6, n_q_heads=16, n_kv_heads=4, head_dim=64, block_size=64, top_k=16,
+                 kv_dtype="bf16", t0=(64 * 90 - 2, 100, 64 * 16, 5000, 64 * 33 + 7, 900), steps=5,
+                 kind="normal", seed=83)
+    _placements_bitwise(w, 5)
 
 
 # ---- ties: equal group scores go to the smaller block id -------------------------
