@@ -134,7 +134,7 @@ def kernel_bytes(name: str, w, lens, s_kv: int) -> int:
     d, G, H, bk, k = w.head_dim, w.n_kv_heads, w.n_q_heads, w.block_size, w.top_k
     r = H // G
     chunks = d * d // 1024
-    rec = (2 * d + 4) * 4  # one partial record: m, l, sum w, pad, acc[d], o_tilde[d]
+    rec = (2 * d + 4) * 4  # one partial record: acc[d], o_tilde[d] and its header m, l, sum w, pad
     lg = kv = recs = 0
     for T in lens:
         nb = -(-T // bk)

@@ -139,23 +139,20 @@ __global__ __launch_bounds__(kThreads) void k_attend(const DecodeArgs a) {
     }
   }
   __syncthreads();
-  const int rec = 2 * d + kPartHdr;
+  const int rec = 2 * d;
 #pragma unroll
   for (int k = 0; k < npair; ++k) {
     const int p = grp + k * ngrp;
     if (p < 2 * R) {
       const int h = p < R ? p : p - R;
-      float* dst = a.part + (((size_t)b * a.H + g * R + h) * a.top_k + slot) * rec + kPartHdr + (p < R ? 0 : d);
+      float* dst = a.part + (((size_t)b * a.H + g * R + h) * a.top_k + slot) * rec + (p < R ? 0 : d);
       dst[c] = acc[k];
     }
   }
   if (threadIdx.x < R) {
     const int h = threadIdx.x;
-    float* dst = a.part + (((size_t)b * a.H + g * R + h) * a.top_k + slot) * rec;
-    dst[0] = s_m[h];
-    dst[1] = s_l[h];
-    dst[2] = s_sw[h];
-    dst[3] = 0.f;
+    *reinterpret_cast<float4*>(a.part_hdr + (((size_t)b * a.H + g * R + h) * a.top_k + slot) * kPartHdr) =
+        make_float4(s_m[h], s_l[h], s_sw[h], 0.f);
   }
 }
 

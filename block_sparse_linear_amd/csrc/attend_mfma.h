@@ -260,7 +260,7 @@ __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot,
   }
   __syncthreads();
   // ---- product (2)
-  const int rec = 2 * D + kPartHdr;
+  const int rec = 2 * D;
   float* part0 = a.part + (((size_t)b * a.H + g * R) * a.top_k + slot) * rec;
 #pragma unroll
   for (int nt2 = 0; nt2 < NT2W; ++nt2) {
@@ -281,18 +281,17 @@ __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot,
         const int pi = 8 * mt + 2 * lg4 + e;
         if (pi < 2 * R) {
           const int kind = pi / R, h = pi % R;
-          part0[(size_t)h * a.top_k * rec + kPartHdr + (kind ? D : 0) + ch] = c[2 * e] + c[2 * e + 1];
+          part0[(size_t)h * a.top_k * rec + (kind ? D : 0) + ch] = c[2 * e] + c[2 * e + 1];
         }
       }
     }
   }
   if (threadIdx.x < R) {
     const int h = threadIdx.x;
-    float* dst = part0 + (size_t)h * a.top_k * rec;
-    dst[0] = fmaxf(fmaxf(s_max[0][h], s_max[1][h]), fmaxf(s_max[2][h], s_max[3][h])) ;
-    dst[1] = (s_l[0][h] + s_l[1][h]) + (s_l[2][h] + s_l[3][h]);
-    dst[2] = (s_sw[0][h] + s_sw[1][h]) + (s_sw[2][h] + s_sw[3][h]);
-    dst[3] = 0.f;
+    *reinterpret_cast<float4*>(a.part_hdr + ((((size_t)b * a.H + g * R + h) * a.top_k + slot) * kPartHdr)) =
+        make_float4(fmaxf(fmaxf(s_max[0][h], s_max[1][h]), fmaxf(s_max[2][h], s_max[3][h])),
+                    (s_l[0][h] + s_l[1][h]) + (s_l[2][h] + s_l[3][h]),
+                    (s_sw[0][h] + s_sw[1][h]) + (s_sw[2][h] + s_sw[3][h]), 0.f);
   }
 }
 

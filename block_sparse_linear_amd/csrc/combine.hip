@@ -24,9 +24,9 @@ namespace {
 // thousands of (token, head) pairs, so a workgroup then takes a whole head,
 // which spreads its merge-weight pass over four times the data.
 template <int R, int D, int FORM, bool ONE>
-__global__ __launch_bounds__(kThreads) void k_combine(const float* part, const float* obar_part, const float* dz_part,
-                                                       const int32_t* sel, int32_t G, int32_t H, int32_t top_k,
-                                                       const DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void k_combine(const float* part, const float* part_hdr, const float* obar_part,
+                                                       const float* dz_part, const int32_t* sel, int32_t G, int32_t H,
+                                                       int32_t top_k, const DecodeArgs a) {
   constexpr int CS = (FORM == kRlaRms || ONE) ? D : 32;  // channels per workgroup
   constexpr int NQ = CS / 4;                    // channel quartets
   constexpr int NIT = 2 * NQ;                   // float4 items (kind, quartet)
@@ -46,8 +46,9 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float* part, const f
   const int g = hq / R, h = hq % R;
   const size_t bg = (size_t)b * G + g;
   const int32_t* srow = sel + bg * top_k;
-  const int rec = 2 * D + kPartHdr;
+  const int rec = 2 * D;
   const float* P0 = part + ((size_t)b * H + hq) * top_k * (size_t)rec;
+  const float4* PH = reinterpret_cast<const float4*>(part_hdr) + ((size_t)b * H + hq) * top_k;  // this head's headers
   const int c0 = cc * CS;
   const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
   // ---- loads (slot indices clamped into range, masked afterwards)
@@ -57,14 +58,14 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float* part, const f
   for (int u = 0; u < SPL; ++u) {
     const int s = min(lane + 64 * u, top_k - 1);
     vs[u] = srow[s];
-    const float* P = P0 + (size_t)s * rec;
-    hm[u] = P[0];
-    hl[u] = P[1];
-    hs[u] = P[2];
+    const float4 hd = PH[s];
+    hm[u] = hd.x;
+    hl[u] = hd.y;
+    hs[u] = hd.z;
   }
   const int it = threadIdx.x % NIT, sg = threadIdx.x / NIT;
   const int kind = it / NQ, q4 = it % NQ;
-  const float* PD = P0 + kPartHdr + (kind ? D : 0) + c0 + 4 * q4;
+  const float* PD = P0 + (kind ? D : 0) + c0 + 4 * q4;
   float4 dv[SPT];
 #pragma unroll
   for (int u = 0; u < SPT; ++u)
@@ -202,10 +203,10 @@ hipError_t launch_combine_form(const DecodeArgs& a, const Launch& l) {
   const dim3 grid(a.d / cs, a.H, a.B);
   const int32_t* sel = a.sel_in ? a.sel_in : a.sel;
   if (a.obar_one)
-    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<RR, DD, FORM, true>, grid, l, a.part, a.obar_part, a.dz_part,
-                                             sel, a.G, a.H, a.top_k, a))
-  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<RR, DD, FORM, false>, grid, l, a.part, a.obar_part, a.dz_part,
-                                           sel, a.G, a.H, a.top_k, a))
+    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<RR, DD, FORM, true>, grid, l, a.part, a.part_hdr, a.obar_part,
+                                             a.dz_part, sel, a.G, a.H, a.top_k, a))
+  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<RR, DD, FORM, false>, grid, l, a.part, a.part_hdr, a.obar_part,
+                                           a.dz_part, sel, a.G, a.H, a.top_k, a))
 }
 
 }  // namespace

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
   __shared__ float s_max[4][16], s_l[4][16], s_sw[4][16];
   __shared__ int s_code[kPfQ];
   __shared__ int s_len[kPfQ];     // length of each query's sequence prefix (its causal limit)
-  __shared__ size_t s_dst[16];    // partial record (float index) of each A row of the current batch
+  __shared__ size_t s_dst[16];    // partial record index of each A row of the current batch
   // the item (the array holds max_items records, so any workgroup may read
   // its own) and the count, in one round trip
   const int4* itp = items + (size_t)blockIdx.x * kPfItemInts / 4;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
   const uint4 q7 = QPT > 7 ? piece(7, k7) : q0, q8 = QPT > 8 ? piece(8, k8) : q0, q9 = QPT > 9 ? piece(9, k9) : q0;
   const uint4 q10 = QPT > 10 ? piece(10, k10) : q0, q11 = QPT > 11 ? piece(11, k11) : q0;
   __builtin_amdgcn_sched_barrier(0);
-  SPLA_SCALARS_READY("s"(a.bk), "s"(a.top_k), "s"(a.part), "s"(a.inv_sqrt_d), "s"(a.H), "s"(a.B));
+  SPLA_SCALARS_READY("s"(a.bk), "s"(a.top_k), "s"(a.part), "s"(a.part_hdr), "s"(a.inv_sqrt_d), "s"(a.H), "s"(a.B));
   // rows of the tile past the group's last token: never attended, zeroed so
   // that 0 x (stale data) cannot make NaN
   const int nvalid = min(BK, a.lens[a.B - 1] - j * BK);
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
     for (int ks = 0; ks < NKS; ++ks) phi_bf16_split(kraw[nt][ks], fkh[nt][ks], fkl[nt][ks]);
   __syncthreads();
   const float inv_sqrt_d = a.inv_sqrt_d;
-  const int rec = 2 * D + kPartHdr;
+  const int rec = 2 * D;
   // batches of QB queries: row r = 4 lg4 + i of a result tile is (query
   // b0 + r / R, head r % R); the A operand row of this lane is l16
   const int eh = l16 % R, ee = l16 / R;
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
     if ((int)threadIdx.x < 16) {
       const int r = threadIdx.x, e = r / R, h = r % R;
       const int cd = s_code[min(b0 + e, n - 1)];
-      s_dst[r] = (((size_t)(cd >> 8) * a.H + g * R + h) * a.top_k + (cd & 255)) * rec;
+      s_dst[r] = ((size_t)(cd >> 8) * a.H + g * R + h) * a.top_k + (cd & 255);
     }
     // ---- product (1): logits s = q.k and linear weights w = phi(q).phi(k) of this wavefront's tokens
     f32x4_t cs[NT1W], cw[NT1W];
@@ -367,18 +367,17 @@ __global__ __launch_bounds__(kThreads) void k_pf_attend(const int4* items, const
         for (int e2 = 0; e2 < 2; ++e2) {
           const int pi = 8 * mt + 2 * lg4 + e2;
           const int kind = pi / 16, r = pi % 16;
-          if (r / R < nb) a.part[s_dst[r] + kPartHdr + (kind ? D : 0) + ch] = c[2 * e2] + c[2 * e2 + 1];
+          if (r / R < nb) a.part[s_dst[r] * rec + (kind ? D : 0) + ch] = c[2 * e2] + c[2 * e2 + 1];
         }
       }
     }
     if ((int)threadIdx.x < 16) {
       const int r = threadIdx.x;
       if (r / R < nb) {
-        float* dst = a.part + s_dst[r];
-        dst[0] = max_nn(max_nn(s_max[0][r], s_max[1][r]), max_nn(s_max[2][r], s_max[3][r]));
-        dst[1] = (s_l[0][r] + s_l[1][r]) + (s_l[2][r] + s_l[3][r]);
-        dst[2] = (s_sw[0][r] + s_sw[1][r]) + (s_sw[2][r] + s_sw[3][r]);
-        dst[3] = 0.f;
+        *reinterpret_cast<float4*>(a.part_hdr + s_dst[r] * kPartHdr) =
+            make_float4(max_nn(max_nn(s_max[0][r], s_max[1][r]), max_nn(s_max[2][r], s_max[3][r])),
+                        (s_l[0][r] + s_l[1][r]) + (s_l[2][r] + s_l[3][r]),
+                        (s_sw[0][r] + s_sw[1][r]) + (s_sw[2][r] + s_sw[3][r]), 0.f);
       }
     }
     __syncthreads();  // s_max / pw / s_l are rewritten by the next batch

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, con
   uint4 qraw[D / 32], fh[D / 32], fl[D / 32];
   load_q_mfma<R, D>(q, phq, H, g, b, qraw, fh, fl);
   SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.top_k), "s"(a.sel), "s"(a.k_pages), "s"(a.v_pages),
-                     "s"(a.part), "s"(a.num_pages), "s"(a.inv_sqrt_d));
+                     "s"(a.part), "s"(a.part_hdr), "s"(a.num_pages), "s"(a.inv_sqrt_d));
   const int nb = n_blocks(a, b);
   select_pages<KPT>(block_table, max_blocks, b, nb, k);
   int j, page;

@@ -27,7 +27,7 @@ struct spla_handle {
   float rla_eps = 0.f;
   int32_t score_form = SPLA_SCORE_TAYLOR;  // block score the selection ranks
   // workspace layout (bytes)
-  size_t off_lg = 0, off_sel = 0, off_page = 0, off_part = 0, off_obar = 0, off_dz = 0, off_phq = 0;
+  size_t off_lg = 0, off_sel = 0, off_page = 0, off_part = 0, off_phdr = 0, off_obar = 0, off_dz = 0, off_phq = 0;
   size_t ws_bytes = 0;
 };
 
@@ -35,7 +35,7 @@ struct spla_handle {
 // queries: the handle's own workspace (nq = batch) or a prefill workspace
 // (nq = virtual queries of one chunk)
 struct WsLayout {
-  size_t lg, sel, page, part, obar, dz, phq, bytes;
+  size_t lg, sel, page, part, phdr, obar, dz, phq, bytes;
 };
 
 namespace {
@@ -57,7 +57,9 @@ WsLayout ws_layout(const spla_config& c, int n_tiles, size_t nq) {
   w.page = off;
   off = align256(off + nq * G * k * sizeof(int32_t));
   w.part = off;
-  off = align256(off + nq * H * k * (2 * d + kPartHdr) * sizeof(float));
+  off = align256(off + nq * H * k * 2 * d * sizeof(float));
+  w.phdr = off;
+  off = align256(off + nq * H * k * kPartHdr * sizeof(float));
   const size_t chunks = d * d / 1024;  // S_all row chunks per (query, KV head)
   w.obar = off;
   off = align256(off + nq * G * chunks * (H / G) * d * sizeof(float));
@@ -102,6 +104,7 @@ void layout(spla_handle* h) {
   h->off_sel = w.sel;
   h->off_page = w.page;
   h->off_part = w.part;
+  h->off_phdr = w.phdr;
   h->off_obar = w.obar;
   h->off_dz = w.dz;
   h->off_phq = w.phq;
@@ -144,6 +147,7 @@ void fill_decode_args(const spla_handle* h, const void* q, const float* gate, fl
   a->sel = reinterpret_cast<int32_t*>(scratch_base + h->off_sel);
   a->sel_page = reinterpret_cast<int32_t*>(scratch_base + h->off_page);
   a->part = reinterpret_cast<float*>(scratch_base + h->off_part);
+  a->part_hdr = reinterpret_cast<float*>(scratch_base + h->off_phdr);
   a->obar_part = reinterpret_cast<float*>(scratch_base + h->off_obar);
   a->dz_part = reinterpret_cast<float*>(scratch_base + h->off_dz);
   a->phq = reinterpret_cast<uint16_t*>(scratch_base + h->off_phq);
@@ -696,6 +700,7 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
     a.sel = reinterpret_cast<int32_t*>(wsb + wl.sel);
     a.sel_page = reinterpret_cast<int32_t*>(wsb + wl.page);
     a.part = reinterpret_cast<float*>(wsb + wl.part);
+    a.part_hdr = reinterpret_cast<float*>(wsb + wl.phdr);
     a.obar_part = reinterpret_cast<float*>(wsb + wl.obar);
     a.dz_part = reinterpret_cast<float*>(wsb + wl.dz);
     a.phq = reinterpret_cast<uint16_t*>(wsb + wl.phq);

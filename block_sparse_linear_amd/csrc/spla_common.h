@@ -17,7 +17,7 @@ constexpr int kMaxBlocksPerSeq = 16386;  // the selector ranks at most 16384 can
 constexpr int kMaxAppendEntries = 64;  // entries per append launch (host splits larger calls)
 constexpr int kTile = 64;              // blocks per statistics tile (= wavefront width)
 constexpr int kThreads = 256;          // threads per workgroup of every kernel
-constexpr int kPartHdr = 4;            // m, l, sum_w, pad ahead of acc[d], o_tilde[d]
+constexpr int kPartHdr = 4;            // floats of a partial record's header: m, l, sum_w, pad
 
 // block score forms (spla_score_form)
 constexpr int kScoreTaylor = 0, kScoreMean = 1;
@@ -62,7 +62,8 @@ struct DecodeArgs {
   float* lg;        // workspace [B][G][NT*64]
   int32_t* sel;     // workspace [B][G][top_k] selected block ids
   int32_t* sel_page;  // workspace [B][G][top_k] their page ids
-  float* part;      // workspace [B][H][top_k][2d + kPartHdr]
+  float* part;      // workspace [B][H][top_k][2d]: a slot's partial acc[d], o_tilde[d] (line-aligned)
+  float* part_hdr;  // workspace [B][H][top_k][kPartHdr]: its m, l, sum_w, pad (a head's headers contiguous)
   float* obar_part;  // workspace [B][G][d * d / 1024][R][d]: phi(q)^T S_all over one chunk of S rows
   float* dz_part;    // workspace [B][G][d * d / 1024][R]: phi(q).z_all over the same rows
   int32_t obar_one;  // 1: one o_bar / phi(q).z partial per head ([B][G][R][d], [B][G][R]) instead

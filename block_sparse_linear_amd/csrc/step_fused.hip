@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void k_step_fused(const float* mean, cons
   uint4 qraw[D / 32], fh[D / 32], fl[D / 32];
   load_q_raw<R, D>(q, H, g, b, qraw);
   SPLA_SCALARS_READY("s"(dc.lens[b]), "s"(dc.bk), "s"(dc.top_k), "s"(dc.sel), "s"(dc.k_pages), "s"(dc.v_pages),
-                     "s"(dc.part), "s"(dc.num_pages), "s"(dc.inv_sqrt_d), "s"(dc.lg), "s"(dc.phq));
+                     "s"(dc.part), "s"(dc.part_hdr), "s"(dc.num_pages), "s"(dc.inv_sqrt_d), "s"(dc.lg), "s"(dc.phq));
   step_wait(ctr, np, dc.err);
   select_load_scores<KPT>(dc.lg, n_tiles, dc.max_blocks, G, g, b, k);
   load_phq<R, D>(dc.phq, H, g, b, fh, fl);
