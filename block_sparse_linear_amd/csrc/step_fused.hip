@@ -136,12 +136,15 @@ __global__ __launch_bounds__(kThreads) void k_step_fused(const float* mean, cons
   // on the pair's contended line; both are checked at the end.
   int arrived = 0, mask = 0;
   if (threadIdx.x == 0) {
-    arrived = __hip_atomic_fetch_add(ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + 1;
     if (slot == 0) {
       int zero;
       asm volatile("v_mov_b32 %0, 0" : "=v"(zero));  // an or of a known zero would become a load
       mask = __hip_atomic_fetch_or(ctr + 2, zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      // the mask has arrived before this workgroup counts itself in below:
+      // until then the pair's last attend workgroup cannot have cleared it
+      asm volatile("" ::"v"(mask));
     }
+    arrived = __hip_atomic_fetch_add(ctr + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) + 1;
   }
   const int nb = n_blocks(dc, b);
   select_pages<KPT>(dc.block_table, dc.max_blocks, b, nb, k);
