@@ -13,21 +13,24 @@ namespace spla {
 namespace {
 
 // grid (D / CS, H, B): one CS-channel slice of one query head (the whole head
-// for the RMS form, whose norm runs over all D channels).  Item = (kind,
+// for the RMS form, whose norm runs over all D channels, and with WHOLE).  Item = (kind,
 // channel quartet) with kind 0 the softmax numerators (weighted by
 // exp(m_s - m) / L) and kind 1 the linear-attention sums; the slots are split
 // over kThreads / (2 CS / 4) slot groups whose float4 sums meet in LDS.  Every
 // global load is issued before the first wait; the leading arguments address
 // all of them.
 // ONE: a single o_bar / phi(q).z partial per head (chunked prefill) instead
-// of the first kernel's D * D / 1024 row-chunk partials; a prefill group has
-// thousands of (token, head) pairs, so a workgroup then takes a whole head,
-// which spreads its merge-weight pass over four times the data.
-template <int R, int D, int FORM, bool ONE>
+// of the first kernel's D * D / 1024 row-chunk partials.
+// WHOLE: a workgroup takes a whole head (as ONE and the RMS form always do)
+// instead of a 32-channel slice: with many (b, h) pairs there are workgroups
+// enough, and each head's merge-weight pass and fixed costs are paid once
+// instead of D / 32 times (with 2048 pairs the combine takes 9.6 us instead of
+// 27 us); with few pairs the slices give the parallelism.
+template <int R, int D, int FORM, bool ONE, bool WHOLE>
 __global__ __launch_bounds__(kThreads) void k_combine(const float* part, const float* part_hdr, const float* obar_part,
                                                        const float* dz_part, const int32_t* sel, int32_t G, int32_t H,
                                                        int32_t top_k, const DecodeArgs a) {
-  constexpr int CS = (FORM == kRlaRms || ONE) ? D : 32;  // channels per workgroup
+  constexpr int CS = (FORM == kRlaRms || ONE || WHOLE) ? D : 32;  // channels per workgroup
   constexpr int NQ = CS / 4;                    // channel quartets
   constexpr int NIT = 2 * NQ;                   // float4 items (kind, quartet)
   constexpr int SG = kThreads / NIT;            // slot groups
@@ -197,16 +200,22 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float* part, const f
     for (int s = threadIdx.x; s < top_k; s += kThreads) a.sel_out[bg * top_k + s] = srow[s];
 }
 
+// (b, h) pairs from which a combine workgroup takes a whole head
+constexpr int kCombineWholeHeads = 256;
+
 template <int FORM>
 hipError_t launch_combine_form(const DecodeArgs& a, const Launch& l) {
-  const int cs = (FORM == kRlaRms || a.obar_one) ? a.d : 32;
-  const dim3 grid(a.d / cs, a.H, a.B);
+  const bool whole = FORM == kRlaRms || a.obar_one || a.B * a.H >= kCombineWholeHeads;
+  const dim3 grid(whole ? 1 : a.d / 32, a.H, a.B);
   const int32_t* sel = a.sel_in ? a.sel_in : a.sel;
   if (a.obar_one)
-    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<RR, DD, FORM, true>, grid, l, a.part, a.part_hdr, a.obar_part,
-                                             a.dz_part, sel, a.G, a.H, a.top_k, a))
-  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<RR, DD, FORM, false>, grid, l, a.part, a.part_hdr, a.obar_part,
-                                           a.dz_part, sel, a.G, a.H, a.top_k, a))
+    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<RR, DD, FORM, true, true>, grid, l, a.part, a.part_hdr,
+                                             a.obar_part, a.dz_part, sel, a.G, a.H, a.top_k, a))
+  if (whole)
+    SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<RR, DD, FORM, false, true>, grid, l, a.part, a.part_hdr,
+                                             a.obar_part, a.dz_part, sel, a.G, a.H, a.top_k, a))
+  SPLA_DISPATCH_RD(a.r, a.d, launch_kernel(k_combine<RR, DD, FORM, false, false>, grid, l, a.part, a.part_hdr,
+                                           a.obar_part, a.dz_part, sel, a.G, a.H, a.top_k, a))
 }
 
 }  // namespace
