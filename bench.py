@@ -126,11 +126,13 @@ def step_score_bytes(w, lens, s_kv: int) -> int:
     return tot
 
 
-def kernel_bytes(name: str, w, lens, s_kv: int) -> int:
+def kernel_bytes(name: str, w, lens, s_kv: int, merged: bool = False) -> int:
     """Algorithmic bytes of one launch of decode kernel ``name`` (a launch-plan
     name) for sequence lengths ``lens`` (after the step's append): what the
     method must move through that kernel, not its scratch traffic beyond the
-    partial records it hands to the next kernel."""
+    partial records it hands to the next kernel.  merged: the plan has no
+    combine kernel, so the fused select + attend also merges the records (it
+    reads the o_bar / phi(q).z partials and writes the outputs)."""
     d, G, H, bk, k = w.head_dim, w.n_kv_heads, w.n_q_heads, w.block_size, w.top_k
     r = H // G
     chunks = d * d // 1024
@@ -154,7 +156,8 @@ def kernel_bytes(name: str, w, lens, s_kv: int) -> int:
     if name == "attend":
         return kv + recs + B * H * d * s_kv
     if name == "select_attend":
-        return lg + kv + recs + B * H * d * s_kv
+        merge = B * G * chunks * r * (d + 1) * 4 + B * H * d * 4 + H * 4 if merged else 0
+        return lg + kv + recs + B * H * d * s_kv + merge
     if name == "combine":
         return recs + B * G * chunks * r * (d + 1) * 4 + B * H * d * 4 + H * 4
     if name == "step_fused":
@@ -363,6 +366,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-select", type=int, default=-1, choices=(-1, 0, 1),
                     help="selector placement: -1 automatic, 0 stand-alone kernel, 1 fused into attend")
+    ap.add_argument("--fused-merge", type=int, default=-1, choices=(-1, 0, 1),
+                    help="1: the fused select + attend merges the records; -1 automatic, 0: combine kernel")
     ap.add_argument("--step-kernel", type=int, default=-1, choices=(-1, 0, 1),
                     help="1: decode step in one kernel plus the combine; -1 automatic, 0: separate kernels")
     ap.add_argument("--rla-form", type=int, default=0, choices=sorted(RLA_FORMS),
@@ -434,6 +439,7 @@ def main() -> int:
                           kv_dtype=w.kv_dtype, device="cuda:0")
         layer.set_fused_select(args.fused_select)
         layer.set_step_kernel(args.step_kernel)
+        layer.set_fused_merge(args.fused_merge)
         layer.set_rla_output(args.rla_form, gamma, RLA_EPS)
         return layer
 
@@ -550,7 +556,7 @@ def main() -> int:
             for i, n in enumerate(names):
                 durs[n].append(evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e-3)
         for n in names:
-            launch_bytes[n].append(kernel_bytes(n, w, after[s], s_kv))
+            launch_bytes[n].append(kernel_bytes(n, w, after[s], s_kv, merged="combine" not in names))
     avg = {n: float(np.mean(v)) for n, v in durs.items()}
     nbytes = {n: float(np.mean(v)) for n, v in launch_bytes.items()}
 

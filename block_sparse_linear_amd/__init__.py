@@ -44,6 +44,7 @@ KERNELS = {1: "score", 2: "step_score", 3: "select", 4: "attend", 5: "select_att
 CALL_DECODE, CALL_DECODE_SEL_IN, CALL_DECODE_STEP = 0, 1, 2
 TUNE_FUSED_SELECT = 0
 TUNE_STEP_KERNEL = 1
+TUNE_FUSED_MERGE = 2
 # output forms of the RLA branch (spla_rla_form)
 RLA_PLAIN, RLA_NORMALIZED, RLA_RMSNORM = 0, 1, 2
 # block scores the selection can rank (spla_score_form)
@@ -315,6 +316,12 @@ class SplaLayer:
     def set_fused_select(self, mode: int) -> None:
         """-1 automatic, 0 stand-alone selector, 1 fused select + attend where supported."""
         self.handle.set_tuning(TUNE_FUSED_SELECT, mode)
+
+    def set_fused_merge(self, mode: int) -> None:
+        """1: the fused select + attend merges the records itself where it
+        supports the call (no combine kernel); -1 automatic and 0: the combine
+        kernel."""
+        self.handle.set_tuning(TUNE_FUSED_MERGE, mode)
 
     def set_step_kernel(self, mode: int) -> None:
         """1: decode_step in one kernel (plus the combine) wherever the fused

@@ -17,7 +17,10 @@ constexpr int kMaxBlocksPerSeq = 16386;  // the selector ranks at most 16384 can
 constexpr int kMaxAppendEntries = 64;  // entries per append launch (host splits larger calls)
 constexpr int kTile = 64;              // blocks per statistics tile (= wavefront width)
 constexpr int kThreads = 256;          // threads per workgroup of every kernel
-constexpr int kPartHdr = 4;            // floats of a partial record's header: m, l, sum_w, pad
+constexpr int kPartHdr = 4;
+// (b, h) pairs from which a combine workgroup takes a whole head (fewer: a
+// 32-channel slice each)
+constexpr int kCombineWholeHeads = 256;            // floats of a partial record's header: m, l, sum_w, pad
 
 // block score forms (spla_score_form)
 constexpr int kScoreTaylor = 0, kScoreMean = 1;
@@ -189,7 +192,11 @@ hipError_t launch_block_mass(const DecodeArgs& a, bool bf16, float* lgx, int max
 // fused select + attend: supported for bf16 K/V, block size 64, no selection
 // override and at most 16 * 256 candidates per sequence
 bool select_attend_supported(const DecodeArgs& a, bool bf16);
-hipError_t launch_select_attend(const DecodeArgs& a, const Launch& l);
+// merge: the fused kernel also merges each (b, g)'s records in place of the
+// combine kernel (plain and normalised RLA forms, B * H < kCombineWholeHeads,
+// B * G <= kStepPairs)
+bool select_attend_merge_supported(const DecodeArgs& a);
+hipError_t launch_select_attend(const DecodeArgs& a, const Launch& l, bool merge);
 // one-kernel decode step (append + scores + o_bar partials, then select +
 // attend, with waits inside one XCD): where the fused select + attend is
 // supported, with the Taylor score and at most kStepPairs (b, g) pairs

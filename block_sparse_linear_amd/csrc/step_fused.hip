@@ -27,49 +27,11 @@
 #include "attend_mfma.h"
 #include "score_parts.h"
 #include "select_core.h"
+#include "xcd_sync.h"
 
 namespace spla {
 
 namespace {
-
-constexpr int kSpinLimit = 1 << 20;
-constexpr int kPollSleep = 1;  // s_sleep units (64 clocks) between polls
-
-// producer: this workgroup's stores have reached the L2, then the count
-// (and the producers' XCD mask, which the attend workgroups check)
-__device__ __forceinline__ void step_signal(int32_t* ctr) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_or(ctr + 2, 1 << xcc_id(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  }
-}
-
-// attend: wait until the pair's producer count reaches `target`.  The poll
-// is an atomic (performed in the L2, where the producers' adds are); a load
-// would not do: even a load marked to skip the CU's L1 has been seen to
-// return a stale count from it for as long as the wait lasted.
-__device__ __forceinline__ void step_wait(int32_t* ctr, int target, uint32_t* err) {
-  if (threadIdx.x == 0) {
-    // an add of a zero the compiler cannot see as one (an add of a known zero
-    // would become a load)
-    int zero;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
-    int n = 0;
-    for (int spin = 0;; ++spin) {
-      n = __hip_atomic_fetch_add(ctr, zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      if (n >= target) break;
-      if (spin >= kSpinLimit) {
-        atomicOr(err, kErrStepWait);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(kPollSleep);
-    }
-    if (n > target) atomicOr(err, kErrStepCount);  // a count the previous call did not clear
-  }
-  __syncthreads();
-}
 
 template <int R, int D>
 union StepLds {

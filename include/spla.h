@@ -243,8 +243,16 @@ const char *spla_status_str(spla_status st);
  *   [256, 33024) that every call leaves at zero (the workspace starts
  *   zero-filled); a wait that runs out sets bit 2 of the error word, a
  *   counter found above its target bit 3, an attend count above top_k bit 4.
+ *   SPLA_TUNE_FUSED_MERGE: 1 = where the fused select + attend runs with the
+ *   plain or normalised RLA form and B * n_q_heads < 256, it also merges each
+ *   (sequence, KV head) pair's partial records into the outputs (the combine
+ *   kernel's workgroups for the pair's heads, in the same launch, waiting for
+ *   the pair's attend workgroups through the same workspace counters and
+ *   error bits as the one-kernel step) and no combine kernel runs; -1
+ *   automatic (default) and 0 = the combine kernel (automatic keeps it: it is
+ *   as fast or faster).
  * SPLA_ERR_INVALID_ARG for an unknown key or value. */
-typedef enum { SPLA_TUNE_FUSED_SELECT = 0, SPLA_TUNE_STEP_KERNEL = 1 } spla_tune_key;
+typedef enum { SPLA_TUNE_FUSED_SELECT = 0, SPLA_TUNE_STEP_KERNEL = 1, SPLA_TUNE_FUSED_MERGE = 2 } spla_tune_key;
 spla_status spla_set_tuning(spla_handle *h, int32_t key, int32_t value);
 
 /* Output form of the residual-linear-attention branch in o = o_sparse +
@@ -337,7 +345,7 @@ typedef enum {
     SPLA_KERNEL_STEP_SCORE = 2,    /* one-token append + block scorer (spla_decode_step) */
     SPLA_KERNEL_SELECT = 3,        /* stand-alone top-k selector */
     SPLA_KERNEL_ATTEND = 4,        /* attend + correct over the selector's blocks */
-    SPLA_KERNEL_SELECT_ATTEND = 5, /* fused select + attend + correct */
+    SPLA_KERNEL_SELECT_ATTEND = 5, /* fused select + attend + correct (+ the merge when no combine follows) */
     SPLA_KERNEL_COMBINE = 6,       /* merge, o_bar, o_rla, D, gate */
     SPLA_KERNEL_STEP_FUSED = 7     /* append + scores + o_bar partials + select + attend (spla_decode_step) */
 } spla_kernel;

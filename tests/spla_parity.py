@@ -95,7 +95,7 @@ class ParityRun:
                  device: str = "cuda", prefill_chunk: int = 4096, use_step: bool = False,
                  seqs: Optional[List[int]] = None, kv_heads: Optional[List[int]] = None,
                  fused_select: int = -1, rla_form: int = 0, rla_eps: float = 1e-6, score_form: int = 0,
-                 step_kernel: int = -1):
+                 step_kernel: int = -1, fused_merge: int = -1):
         import torch
         from block_sparse_linear_amd import SplaLayer
 
@@ -110,6 +110,7 @@ class ParityRun:
                                kv_dtype=w.kv_dtype, device=device, page_order=page_order, seed=w.seed)
         self.layer.set_fused_select(fused_select)
         self.layer.set_step_kernel(step_kernel)
+        self.layer.set_fused_merge(fused_merge)
         # sequences / KV heads the oracle checks (all by default)
         self.bs = list(range(w.batch)) if seqs is None else [int(b) for b in seqs]
         self.gs = list(range(w.n_kv_heads)) if kv_heads is None else [int(g) for g in kv_heads]

@@ -293,6 +293,9 @@ def test_tuning_validation(lib):
     for v in (-1, 0, 1):
         assert lib.spla_set_tuning(h, 1, v) == OK
     assert lib.spla_set_tuning(h, 1, 2) == INVALID and lib.spla_set_tuning(h, 1, -2) == INVALID
+    for v in (-1, 0, 1):
+        assert lib.spla_set_tuning(h, 2, v) == OK
+    assert lib.spla_set_tuning(h, 2, 2) == INVALID
     assert lib.spla_set_tuning(h, 7, 0) == INVALID
     assert lib.spla_set_tuning(None, 0, 0) == INVALID
     lib.spla_destroy(h)
@@ -310,10 +313,16 @@ def plan(lib, h, call):
 def test_launch_plan(lib):
     # bf16, Bk=64, top_k=16; lengths 100 (2 blocks) and 2000 (32 blocks > top_k)
     h, c = bound(lib)
-    # automatic: 4 (b, g) pairs -> fused select + attend, separate kernels
+    # automatic: 4 (b, g) pairs -> fused select + attend, then the combine
     assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
     assert plan(lib, h, 0) == [SCORE, SELECT_ATTEND, COMBINE]
     assert plan(lib, h, 1) == [SCORE, ATTEND, COMBINE]              # selection override
+    assert lib.spla_set_tuning(h, 2, 1) == OK                       # the fused kernel merges the records itself
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND]
+    assert plan(lib, h, 0) == [SCORE, SELECT_ATTEND]
+    assert plan(lib, h, 1) == [SCORE, ATTEND, COMBINE]
+    assert lib.spla_set_tuning(h, 2, 0) == OK
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
     assert lib.spla_set_tuning(h, 1, 1) == OK                       # the step in one kernel
     assert plan(lib, h, 2) == [STEP_FUSED, COMBINE]
     assert plan(lib, h, 0) == [SCORE, SELECT_ATTEND, COMBINE]       # spla_decode: unchanged
@@ -331,15 +340,26 @@ def test_launch_plan(lib):
     assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
     assert lib.spla_set_score_form(h, 0) == OK
     assert lib.spla_set_tuning(h, 1, -1) == OK
+    assert lib.spla_set_tuning(h, 2, -1) == OK
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
     assert lens_of(lib, h, 2) == [100, 2000]                       # the query changes nothing
     lib.spla_destroy(h)
     # every sequence short: the first kernel still runs (it forms the
-    # phi(q)^T S_all partials of the combine)
+    # phi(q)^T S_all partials of the merge)
     h, c = bound(lib, lens=(5, 64 * 16))
     assert plan(lib, h, 0) == [SCORE, SELECT_ATTEND, COMBINE]
     assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
+    assert lib.spla_set_tuning(h, 2, 1) == OK
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND]
     assert lib.spla_set_tuning(h, 1, 1) == OK
     assert plan(lib, h, 2) == [STEP_FUSED, COMBINE]
+    lib.spla_destroy(h)
+    # 256 (b, h) pairs or more: the combine kernel takes whole heads, and the
+    # fused kernel does not merge
+    h, c = bound(lib, lens=[100] * 64, batch=64, n_q_heads=4, n_kv_heads=2, max_blocks_per_seq=40, num_pages=64 * 40)
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT, ATTEND, COMBINE]  # 128 (b, g) pairs: split selector
+    assert lib.spla_set_tuning(h, 0, 1) == OK and lib.spla_set_tuning(h, 2, 1) == OK
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
     lib.spla_destroy(h)
     # the fused kernel needs bf16 and Bk = 64
     for kw in (dict(kv_dtype=0), dict(block_size=128)):
@@ -366,8 +386,12 @@ def test_rla_output_validation(lib):
     assert lib.spla_set_rla_output(h, 3, None, 0.0) == INVALID
     assert lib.spla_set_rla_output(h, -1, None, 0.0) == INVALID
     assert lib.spla_set_rla_output(None, 0, None, 0.0) == INVALID
-    # the form changes the combine's arithmetic, not the kernels a call launches
+    # with the merge asked for, the RMS form keeps the combine kernel; the
+    # plain and normalised forms merge inside the fused kernel
+    assert lib.spla_set_tuning(h, 2, 1) == OK
     assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
+    assert lib.spla_set_rla_output(h, 1, None, 0.0) == OK
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND]
     lib.spla_destroy(h)
 
 
@@ -393,6 +417,7 @@ def test_score_form_and_block_mass_validation(lib):
     assert lib.spla_block_mass(h, FAKE, FAKE, None) == OK
     # the score form changes which score the selection ranks; the one-kernel
     # step takes the Taylor score only
+    assert plan(lib, h, 2) == [STEP_SCORE, SELECT_ATTEND, COMBINE]
     assert lib.spla_set_tuning(h, 1, 1) == OK
     assert plan(lib, h, 2) == [STEP_FUSED, COMBINE]
     assert lib.spla_set_score_form(h, 1) == OK

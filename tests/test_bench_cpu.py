@@ -46,6 +46,10 @@ def test_kernel_bytes_partition(bench):
     assert fused == lg + s["kv"] + rec + 32 * 128 * 2
     assert split == fused + 8 * 32 * 4 * 2
     assert bench.kernel_bytes("step_score", w, lens, 2) == bench.step_score_bytes(w, lens, 2)
+    # a fused kernel that also merges the records moves the combine's
+    # o_bar / phi(q).z partials and outputs as well
+    merged = bench.kernel_bytes("select_attend", w, lens, 2, merged=True)
+    assert merged == fused + bench.kernel_bytes("combine", w, lens, 2) - rec
     # the combine reads every record once
     assert bench.kernel_bytes("combine", w, lens, 2) > rec
     with pytest.raises(ValueError):

@@ -157,31 +157,34 @@ def _placements_bitwise(w, steps):
     import torch
     from tests.spla_parity import ParityRun
     print(f"[gpu-test] {w.name}: B={w.batch} G={w.n_kv_heads} k={w.top_k} t0={w.t0}", flush=True)
-    runs = [ParityRun(w, steps=steps, prefill_chunk=1000, page_order="shuffled", fused_select=m, step_kernel=sk)
-            for m, sk in ((0, -1), (1, -1), (1, 1))]
+    runs = [ParityRun(w, steps=steps, prefill_chunk=1000, page_order="shuffled", fused_select=m, step_kernel=sk,
+                      fused_merge=fm)
+            for m, sk, fm in ((0, -1, -1), (1, -1, -1), (1, 1, -1), (1, -1, 1))]
     assert runs[0].layer.launch_plan() == ["step_score", "select", "attend", "combine"]
     assert runs[1].layer.launch_plan() == ["step_score", "select_attend", "combine"]
     assert runs[2].layer.launch_plan() == ["step_fused", "combine"]
+    assert runs[3].layer.launch_plan() == ["step_score", "select_attend"]  # merges the records itself
     for r in runs:
         r.prefill()
     for s in range(steps):
         st = w.step(s)
         res = [r.gpu_decode(st["q"], kv=(st["k"], st["v"])) for r in runs]
         for key in ("o", "sel_idx", "o_sparse", "o_rla", "d_rla", "lg"):
-            for i in (1, 2):
+            for i in (1, 2, 3):
                 assert np.array_equal(res[0][key], res[i][key]), f"step {s}: {key}, plan {i}"
         print(f"[gpu-test] step {s}: lens {runs[2].layer.lens[:4]}, error words {[r.layer.error_word() for r in runs]}",
               flush=True)
     errs = [r.layer.error_word() for r in runs]
-    assert errs == [0, 0, 0]
+    assert errs == [0, 0, 0, 0]
     for x, y in zip(runs[0].layer.state_tensors(), runs[2].layer.state_tensors()):
         assert torch.equal(x, y)
 
 
 def test_fused_select_matches_split_bitwise():
-    """The stand-alone selector, the fused select + attend kernel and the
-    one-kernel step give the same outputs and selections, bit for bit (every
-    placement runs the same selection and the same attend arithmetic).  The
+    """The stand-alone selector, the fused select + attend kernel (with the
+    combine kernel, and merging the records itself) and the one-kernel step
+    give the same outputs and selections, bit for bit (every placement runs
+    the same selection, attend and merge arithmetic).  The
     steps cross a block end, so the one-kernel step's append completes a
     block whose statistics the next step scores."""
     _needs_gpu()
