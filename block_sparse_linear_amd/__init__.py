@@ -133,7 +133,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.spla_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.spla_prefill.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                 ctypes.c_size_t, ctypes.c_void_p]
+                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.spla_prefill.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -212,11 +212,11 @@ class SplaHandle:
         return int(self.lib.spla_prefill_workspace_bytes(self.h, chunk))
 
     def prefill_raw(self, seq: int, n: int, k_ptr: int, v_ptr: int, q_ptr: int, gate_ptr: int, out_ptr: int,
-                    sel_ptr: int, ws_ptr: int, ws_bytes: int, stream: int) -> int:
+                    sel_ptr: int, lg_ptr: int, ws_ptr: int, ws_bytes: int, stream: int) -> int:
         return self.lib.spla_prefill(self.h, seq, n, ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr),
                                      ctypes.c_void_p(q_ptr), ctypes.c_void_p(gate_ptr), ctypes.c_void_p(out_ptr),
-                                     ctypes.c_void_p(sel_ptr or None), ctypes.c_void_p(ws_ptr), ws_bytes,
-                                     ctypes.c_void_p(stream))
+                                     ctypes.c_void_p(sel_ptr or None), ctypes.c_void_p(lg_ptr or None),
+                                     ctypes.c_void_p(ws_ptr), ws_bytes, ctypes.c_void_p(stream))
 
     def block_mass_raw(self, q_ptr: int, lgx_ptr: int, stream: int) -> int:
         return self.lib.spla_block_mass(self.h, ctypes.c_void_p(q_ptr), ctypes.c_void_p(lgx_ptr),
@@ -349,12 +349,15 @@ class SplaLayer:
         """Block score the selection ranks: SCORE_TAYLOR or SCORE_MEAN."""
         self.handle.set_score_form(form)
 
-    def prefill(self, seq: int, k_new, v_new, q, gate, out=None, chunk: int = 256, workspace=None, sel_idx=None):
+    def prefill(self, seq: int, k_new, v_new, q, gate, out=None, chunk: int = 256, workspace=None, sel_idx=None,
+                lg=None):
         """Chunked prefill of sequence seq: append k_new / v_new ([n][G][d]) and
         return out [n][H][d] float32, the decode output of every new token's
         query q ([n][H][d]) at its own position.  chunk: tokens per group of
         launches (the prefill workspace is sized for it unless given).
-        sel_idx: optional int32 [n][G][top_k] receiving the selections."""
+        sel_idx: optional int32 [n][G][top_k] receiving the selections; lg:
+        optional float32 [n][G][MB] receiving the group log scores of every
+        token's candidate blocks (other entries untouched)."""
         t = self.torch
         n = int(k_new.shape[0])
         self._check_kv(k_new, v_new, n)
@@ -370,8 +373,12 @@ class SplaLayer:
         if sel_idx is not None and (sel_idx.dtype != t.int32 or tuple(sel_idx.shape) != (n, self.G, self.top_k)
                                     or not sel_idx.is_contiguous()):
             raise ValueError(f"sel_idx must be a contiguous int32 [{n}][{self.G}][{self.top_k}] tensor")
+        if lg is not None and (lg.dtype != t.float32 or tuple(lg.shape) != (n, self.G, self.mb)
+                               or not lg.is_contiguous()):
+            raise ValueError(f"lg must be a contiguous float32 [{n}][{self.G}][{self.mb}] tensor")
         st = self.handle.prefill_raw(seq, n, k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), gate.data_ptr(),
                                      out.data_ptr(), 0 if sel_idx is None else sel_idx.data_ptr(),
+                                     0 if lg is None else lg.data_ptr(),
                                      workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                      self._stream())
         _check(st, "spla_prefill", self.handle.lib, self.handle.h)

@@ -648,7 +648,8 @@ size_t spla_prefill_workspace_bytes(const spla_handle* h, int32_t chunk) {
 }
 
 spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_new, const void* v_new, const void* q,
-                         const float* gate, float* out, int32_t* sel_idx, void* workspace, size_t workspace_bytes,
+                         const float* gate, float* out, int32_t* sel_idx, float* lg, void* workspace,
+                         size_t workspace_bytes,
                          void* stream) {
   if (!h) return SPLA_ERR_INVALID_ARG;
   if (!h->bound) return SPLA_ERR_STATE;
@@ -659,7 +660,7 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
   const void* ptrs[] = {k_new, v_new, q, gate, out, workspace};
   for (const void* p : ptrs)
     if (!aligned16(p)) return SPLA_ERR_ALIGNMENT;
-  if (sel_idx && !aligned16(sel_idx)) return SPLA_ERR_ALIGNMENT;
+  if ((sel_idx && !aligned16(sel_idx)) || (lg && !aligned16(lg))) return SPLA_ERR_ALIGNMENT;
   if ((int64_t)h->lens[seq] + n > (int64_t)c.max_blocks_per_seq * c.block_size) return SPLA_ERR_CAPACITY;
   if ((int64_t)n > (int64_t)INT32_MAX / (c.n_q_heads * c.head_dim)) return SPLA_ERR_INVALID_ARG;
   int chunk = kMaxBatch;  // virtual queries per launch: the most the workspace holds
@@ -709,6 +710,7 @@ spla_status spla_prefill(spla_handle* h, int32_t seq, int32_t n, const void* k_n
     a.B = m;
     a.virtual_queries = 1;
     a.sel_out = sel_idx ? sel_idx + (size_t)c0 * G * c.top_k : nullptr;
+    a.lg_out = lg ? lg + (size_t)c0 * G * c.max_blocks_per_seq : nullptr;
     a.block_table = h->buf.block_table + (size_t)seq * c.max_blocks_per_seq;
     a.blk_mean = h->buf.blk_mean + (size_t)seq * stats_row;
     a.blk_var = h->buf.blk_var + (size_t)seq * stats_row;

@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define SPLA_ABI_VERSION 1
+#define SPLA_ABI_VERSION 2
 
 typedef enum {
     SPLA_OK = 0,
@@ -290,7 +290,10 @@ spla_status spla_set_rla_output(spla_handle *h, int32_t form, const float *gamma
  * attends to itself and to every earlier token, causally inside its own
  * block).  Other sequences are untouched.  The handle's output form and
  * score form apply.  sel_idx (optional, device [n][G][top_k] int32) receives
- * every token's selected block ids, ascending, -1 padded.
+ * every token's selected block ids, ascending, -1 padded; lg (optional,
+ * device [n][G][max_blocks_per_seq] float32, 16-byte aligned) every token's
+ * group log score of each of its candidate blocks 1 .. nb-2 (the other
+ * entries untouched), as spla_decode_aux.lg does for a decode.
  * workspace: device scratch of workspace_bytes >= spla_prefill_workspace_bytes
  * (h, 1), caller-owned; the call processes up to 256 tokens per group of
  * launches, as many as the workspace holds (spla_prefill_workspace_bytes(h,
@@ -307,8 +310,8 @@ spla_status spla_set_rla_output(spla_handle *h, int32_t form, const float *gamma
  * undefined (part of the tokens may be in it). */
 size_t spla_prefill_workspace_bytes(const spla_handle *h, int32_t chunk);
 spla_status spla_prefill(spla_handle *h, int32_t seq, int32_t n, const void *k_new, const void *v_new,
-                         const void *q, const float *gate, float *out, int32_t *sel_idx, void *workspace,
-                         size_t workspace_bytes, void *stream);
+                         const void *q, const float *gate, float *out, int32_t *sel_idx, float *lg,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Block score the selection ranks (per handle, host only; from the next
  * decode on).

@@ -432,14 +432,14 @@ def test_prefill_workspace_and_validation(lib):
     assert lib.spla_prefill_workspace_bytes(h, 0) == 0 and lib.spla_prefill_workspace_bytes(h, 257) == 0
     assert lib.spla_prefill_workspace_bytes(None, 1) == 0
     big = lib.spla_prefill_workspace_bytes(h, 256)
-    args = (FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, FAKE + 16384, None, FAKE + (1 << 31))
+    args = (FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, FAKE + 16384, None, None, FAKE + (1 << 31))
     assert lib.spla_prefill(h, 0, 4, *args, big, None) == STATE    # before spla_bind
     lib.spla_destroy(h)
     h, c = bound(lib, lens=(100, 2000))
     for seq, n, want in ((-1, 4, INVALID), (2, 4, INVALID), (0, -1, INVALID), (0, 0, OK)):
         assert lib.spla_prefill(h, seq, n, *args, big, None) == want, (seq, n)
     assert lib.spla_prefill(h, 0, 4, *args, one - 1, None) == INVALID   # workspace below one token
-    for i in (0, 1, 2, 3, 4, 6):
+    for i in (0, 1, 2, 3, 4, 7):
         bad = list(args)
         bad[i] = None
         assert lib.spla_prefill(h, 0, 4, *bad, big, None) == INVALID, i
@@ -447,6 +447,9 @@ def test_prefill_workspace_and_validation(lib):
         assert lib.spla_prefill(h, 0, 4, *bad, big, None) == ALIGN, i
     bad = list(args)
     bad[5] = FAKE + 20484                                          # misaligned sel_idx
+    assert lib.spla_prefill(h, 0, 4, *bad, big, None) == ALIGN
+    bad = list(args)
+    bad[6] = FAKE + 24580                                          # misaligned lg
     assert lib.spla_prefill(h, 0, 4, *bad, big, None) == ALIGN
     cap = c.max_blocks_per_seq * c.block_size
     assert lib.spla_prefill(h, 1, cap - 2000 + 1, *args, big, None) == CAPACITY

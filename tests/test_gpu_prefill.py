@@ -11,7 +11,7 @@ sequences must stay untouched, and 128K of prefix with 512 prefilled tokens."""
 import numpy as np
 import pytest
 
-from tests.spla_parity import OUT_REL, S_REL, STAT_REL, check_selection, rel_err
+from tests.spla_parity import LG_ABS, OUT_REL, S_REL, STAT_REL, check_selection, rel_err
 from tests.test_gpu_parity import _needs_gpu, small
 from workloads import make_workload
 
@@ -59,23 +59,37 @@ def _prefill_case(w, seq, split, chunk=256, kv_heads=None, rla_form=0, score_for
     gate_np = w.gate()
     ws = torch.empty(L.handle.prefill_workspace_bytes(chunk) // 4 + 64, dtype=torch.int32, device=dev)
     sel = torch.full((n, w.n_kv_heads, w.top_k), -7, dtype=torch.int32, device=dev)
+    lg = torch.zeros((n, w.n_kv_heads, L.mb), dtype=torch.float32, device=dev)
     out = L.prefill(seq, dv(K[split:]), dv(V[split:]), dv(Q), torch.from_numpy(gate_np).to(dev), workspace=ws,
-                    sel_idx=sel)
+                    sel_idx=sel, lg=lg)
     torch.cuda.synchronize()
     assert L.lens[seq] == t0 and all(L.lens[b] == w.t0[b] for b in range(w.batch))
     got = out.cpu().numpy()[:, hs]
     sel_g = sel.cpu().numpy()[:, gs]
+    lg_g = lg.cpu().numpy()[:, gs]
     form = dict(rla_mode=rla_form, eps=eps, score_form=score_form,
                 gamma=None if gamma is None else w.rla_gamma()[hs])
     snap = (o.K[0].copy(), o.V[0].copy(), o.mean.copy(), o.var.copy(), o.S.copy(), o.z.copy(), o.lens.copy())
     ref = o.prefill_sequence(0, K[split:][:, gs], V[split:][:, gs], Q[:, hs], gate_np[hs], **form)
     failures, ties = [], 0
+    lg_worst = 0.0
     for t in range(n):
         nb = -(-(split + t + 1) // w.block_size)
         for gg in range(len(gs)):
             msg = check_selection(sel_g[t, gg], ref["lg"][t][gg], nb, w.top_k)
             if msg:
                 failures.append(f"token {t} g {gs[gg]}: {msg}")
+            # group log scores of the candidate blocks: absolute in the log
+            # domain, relative past |LG| = 1 (the decode's bar)
+            if nb > w.top_k:
+                js = np.arange(1, nb - 1)
+                lg_ref = np.array([ref["lg"][t][gg][int(j)] for j in js])
+                dlg = np.abs(lg_g[t, gg, js].astype(np.float64) - lg_ref) / np.maximum(1.0, np.abs(lg_ref))
+                lg_worst = max(lg_worst, float(dlg.max()))
+                if dlg.max() > LG_ABS:
+                    i = int(np.argmax(dlg))
+                    failures.append(f"token {t} g {gs[gg]}: group log score of block {int(js[i])} off by "
+                                    f"{dlg[i]:.3g} (oracle {lg_ref[i]:.6g})")
             if not np.array_equal(sel_g[t, gg], ref["sel"][t, gg]):
                 ties += 1
     if ties:
@@ -106,7 +120,8 @@ def _prefill_case(w, seq, split, chunk=256, kv_heads=None, rla_form=0, score_for
             failures.append(f"sequence {b} changed")
     if L.error_word():
         failures.append(f"error word {L.error_word():#x}")
-    print(f"[prefill] {w.name} n={n} worst o rel err {worst:.3g} near-tie tokens {ties}", flush=True)
+    print(f"[prefill] {w.name} n={n} worst o rel err {worst:.3g} worst lg err {lg_worst:.3g} near-tie tokens {ties}",
+          flush=True)
     assert not failures, "\n".join(failures[:20])
 
 
