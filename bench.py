@@ -57,9 +57,9 @@ KERNEL_SOURCES = {
     "step_score": ["score.hip", "score_parts.h"],
     "select": ["select.hip", "select_core.h"],
     "attend": ["attend.hip", "attend_mfma.h"],
-    "select_attend": ["select_attend.hip", "select_core.h", "attend_mfma.h"],
-    "combine": ["combine.hip"],
-    "step_fused": ["step_fused.hip", "score_parts.h", "select_core.h", "attend_mfma.h"],
+    "select_attend": ["select_attend.hip", "select_core.h", "attend_mfma.h", "combine_body.h", "xcd_sync.h"],
+    "combine": ["combine.hip", "combine_body.h", "xcd_sync.h"],
+    "step_fused": ["step_fused.hip", "score_parts.h", "select_core.h", "attend_mfma.h", "xcd_sync.h"],
 }
 PMC_SUMMARY = "profiles/decode_{workload}_pmc.txt"
 # plain copy of known size run by every bench (outside the timed region) so the
