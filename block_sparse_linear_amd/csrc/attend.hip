@@ -174,7 +174,9 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(const DecodeArgs a) {
     j = a.sel[srow];
     page = a.sel_page[srow];
   }
-  attend_block_mfma<R, D, BK>(a, slot, g, b, j, page, qraw, fh, fl);
+  // many workgroups per CU here: V straight into LDS (fewer registers, more
+  // workgroups resident)
+  attend_block_mfma<R, D, BK, true>(a, slot, g, b, j, page, qraw, fh, fl);
 }
 
 }  // namespace

@@ -37,6 +37,35 @@ __device__ __forceinline__ void phi_bf16_split(const uint4& raw, uint4& hi, uint
   lo = make_uint4(ol[0], ol[1], ol[2], ol[3]);
 }
 
+// V tiles in LDS are row-major (token rows of D bf16), each row's 16-byte
+// chunks permuted by the row: chunk c of token row t sits at chunk position
+// c ^ vswz(t).  The transposing reads of product (2) take 8 bytes from each of
+// 16 rows (4 rows 8 apart per 16-lane group); the permutation spreads those
+// rows over the LDS banks so that every bank serves two of the 64 reads, the
+// fewest 512 bytes allow.
+template <int D>
+__device__ __forceinline__ int vswz(int t) {
+  return (2 * (((t >> 3) & 3) | ((t & 1) << 2))) & (D / 8 - 1);
+}
+
+typedef __bf16 bf16x4v_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
+
+// 16-lane groups of a transposing LDS read (gfx950): source lane 4 e + q of
+// the group gives the address of 4 consecutive bf16 (positions 0..3); lane i
+// of the group receives position i % 4 of source lanes i / 4, 4 + i / 4,
+// 8 + i / 4, 12 + i / 4, in that order
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const auto lp = (__attribute__((address_space(3))) bf16x4v_t*)(p);
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
+}
+
+// 16 bytes from global memory into LDS, lane i of the wavefront to
+// lds_block + 16 i (lds_block uniform over the wavefront), no registers
+__device__ __forceinline__ void load_to_lds16(const void* src, uint16_t* lds_block) {
+  __builtin_amdgcn_global_load_lds(const_cast<void*>(src), (__attribute__((address_space(3))) void*)(lds_block), 16, 0,
+                                   0);
+}
+
 // A operands of product (1) for this lane: row m = lane % 16 holds query m
 // (m < R), or bf16 hi / lo of phi(query m - WB) (from the phi(q) array the
 // first kernel of the decode wrote); other rows read row 0 and are masked
@@ -78,12 +107,18 @@ __device__ __forceinline__ void load_q_mfma(const void* q, const uint16_t* phq, 
 //       page plus phi(K) hi/lo computed in registers; wavefront w takes 16
 //       (Bk = 64) or 32 (Bk = 128) tokens;
 //   (2) sum_t p_t v_t and sum_t w_t v_t: rows of A are p and w (hi/lo split,
-//       from LDS), B is the V tile staged transposed in LDS; wavefront w
-//       takes a quarter of the value channels.
+//       from LDS), B is the V tile in LDS; wavefront w takes a quarter of the
+//       value channels.  VLDS: the V tile goes from the page straight into
+//       LDS (row-major, chunks permuted by vswz), with no registers and whole
+//       1 KB runs per load instruction, and B is read with transposing LDS
+//       reads; the compiler then waits for V as well as K before product
+//       (1).  Otherwise V is loaded into registers with K and written
+//       transposed into LDS after product (1), so product (1) waits for K
+//       only: the form for a kernel bound by one workgroup's latency.
 // Softmax max / sums cross the wavefronts through LDS (two barriers).
 // j < 0 (an unused slot) returns at once; j and page must be uniform over
 // the workgroup.
-template <int R, int D, int BK>
+template <int R, int D, int BK, bool VLDS = false>
 __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot, int g, int b, int j, int page,
                                                   const uint4 (&qraw)[D / 32], const uint4 (&fh)[D / 32],
                                                   const uint4 (&fl)[D / 32]) {
@@ -93,10 +128,15 @@ __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot,
   constexpr int NT2W = D / 64;             // 16-channel tiles per wavefront
   constexpr int MT2 = (4 * R + 15) / 16;   // row tiles of product (2): hi/lo rows of p and w
   constexpr int KS2 = BK / 32;             // token k-steps of product (2)
-  constexpr int VS = BK + 8;               // row stride (elements) of the transposed V tile
   constexpr int PS = BK + 8;               // row stride of the p / w rows
+  // VLDS: row-major V tile
+  constexpr int NC = D / 8;                // 16-byte chunks of a V row
+  constexpr int RPI = 64 * 16 / (2 * D);   // V rows per 1 KB load instruction of a wavefront
+  constexpr int NVI = BK * D * 2 / (kThreads * 16);  // V load instructions per wavefront
+  // otherwise: V tile transposed (channel rows)
+  constexpr int VS = BK + 8;               // row stride (elements) of the transposed V tile
   constexpr int NV = BK * D / (16 * kThreads);  // token-pair x 8-channel pieces per thread
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[VLDS ? BK * D : D * VS];
   __shared__ __attribute__((aligned(16))) uint16_t pw[MT2 * 16 * PS];
   __shared__ float s_max[4][R], s_l[4][R], s_sw[4][R];
 
@@ -118,7 +158,7 @@ __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot,
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k_pages) + ((size_t)page * a.G + g) * BK * D;
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v_pages) + ((size_t)page * a.G + g) * BK * D;
 
-  // ---- issue every global load first: K operands, V pieces, queries
+  // ---- issue every global load first: K operands, V, queries
   uint4 kraw[NT1W][NKS];
 #pragma unroll
   for (int nt = 0; nt < NT1W; ++nt) {
@@ -127,13 +167,28 @@ __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot,
     for (int ks = 0; ks < NKS; ++ks)
       kraw[nt][ks] = *reinterpret_cast<const uint4*>(kp + (size_t)tok * D + 32 * ks + 8 * lg4);
   }
-  uint4 vr[NV][2];
+  uint4 vr[VLDS ? 1 : NV][2];
+  if constexpr (VLDS) {
+    // 1 KB block bl = NVI w + i of the tile per instruction, lane -> token
+    // row bl RPI + lane / NC, chunk position lane % NC (holding chunk
+    // (lane % NC) ^ vswz(row) of the row).  Rows past the block's end take
+    // token 0's data instead: their p and w are exactly zero in product (2),
+    // so finite values there add exactly zero, and no page row past the last
+    // written token is read.
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = threadIdx.x + kThreads * i;
-    const int tp = idx % (BK / 2), cg = idx / (BK / 2);
-    vr[i][0] = *reinterpret_cast<const uint4*>(vp + (size_t)(2 * tp) * D + 8 * cg);
-    vr[i][1] = *reinterpret_cast<const uint4*>(vp + (size_t)(2 * tp + 1) * D + 8 * cg);
+    for (int i = 0; i < NVI; ++i) {
+      const int bl = NVI * w + i;
+      const int t = bl * RPI + lane / NC, cp = lane % NC;
+      load_to_lds16(vp + (size_t)(t < ntok ? t : 0) * D + 8 * (cp ^ vswz<D>(t)), vs + bl * 512);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int idx = threadIdx.x + kThreads * i;
+      const int tp = idx % (BK / 2), cg = idx / (BK / 2);
+      vr[i][0] = *reinterpret_cast<const uint4*>(vp + (size_t)(2 * tp) * D + 8 * cg);
+      vr[i][1] = *reinterpret_cast<const uint4*>(vp + (size_t)(2 * tp + 1) * D + 8 * cg);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (R < 4) {
@@ -242,20 +297,26 @@ __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot,
       if (row >= WB && row < WB + R) s_sw[w][row - WB] = wsum[i];
     }
   }
-  // ---- V tile, transposed into LDS (rows past the block's end are zero)
+  if constexpr (VLDS) {
+    // this wavefront's V rows are in LDS once its loads are done (the barrier
+    // then shows every wavefront's rows to all)
+    __builtin_amdgcn_s_waitcnt(0);
+  } else {
+    // ---- V tile, transposed into LDS (rows past the block's end are zero)
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int idx = threadIdx.x + kThreads * i;
-    const int tp = idx % (BK / 2), cg = idx / (BK / 2);
-    const bool v0 = 2 * tp < ntok, v1 = 2 * tp + 1 < ntok;
-    const uint32_t r0[4] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w};
-    const uint32_t r1[4] = {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
-    uint32_t* dst = reinterpret_cast<uint32_t*>(vt) + (size_t)(8 * cg) * (VS / 2) + tp;
+    for (int i = 0; i < NV; ++i) {
+      const int idx = threadIdx.x + kThreads * i;
+      const int tp = idx % (BK / 2), cg = idx / (BK / 2);
+      const bool v0 = 2 * tp < ntok, v1 = 2 * tp + 1 < ntok;
+      const uint32_t r0[4] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w};
+      const uint32_t r1[4] = {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
+      uint32_t* dst = reinterpret_cast<uint32_t*>(vs) + (size_t)(8 * cg) * (VS / 2) + tp;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t a0 = v0 ? r0[k] : 0u, a1 = v1 ? r1[k] : 0u;
-      dst[(2 * k) * (VS / 2)] = (a0 & 0xffffu) | (a1 << 16);
-      dst[(2 * k + 1) * (VS / 2)] = (a0 >> 16) | (a1 & 0xffff0000u);
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t a0 = v0 ? r0[k] : 0u, a1 = v1 ? r1[k] : 0u;
+        dst[(2 * k) * (VS / 2)] = (a0 & 0xffffu) | (a1 << 16);
+        dst[(2 * k + 1) * (VS / 2)] = (a0 >> 16) | (a1 & 0xffff0000u);
+      }
     }
   }
   __syncthreads();
@@ -265,14 +326,33 @@ __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot,
 #pragma unroll
   for (int nt2 = 0; nt2 < NT2W; ++nt2) {
     const int ch = (w * NT2W + nt2) * 16 + l16;
+    // B operands: lane (lg4, n = l16) holds tokens 32 ks + 8 lg4 + 0..7 of
+    // channel ch
+    uint4 bvs[KS2];
+#pragma unroll
+    for (int ks = 0; ks < KS2; ++ks) {
+      if constexpr (VLDS) {
+        // two transposing reads; as a source this lane addresses token
+        // 32 ks + 8 lg4 + 4 h + l16 / 4, channels ch0 + 4 (l16 % 4) .. + 3
+        const int chs = (w * NT2W + nt2) * 16 + 4 * (l16 % 4);
+        uint2 hv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int t = 32 * ks + 8 * lg4 + 4 * h + l16 / 4;
+          hv[h] = lds_read_tr16(&vs[t * D + 8 * ((chs / 8) ^ vswz<D>(t)) + chs % 8]);
+        }
+        bvs[ks] = make_uint4(hv[0].x, hv[0].y, hv[1].x, hv[1].y);
+      } else {
+        bvs[ks] = *reinterpret_cast<const uint4*>(&vs[ch * VS + 32 * ks + 8 * lg4]);
+      }
+    }
 #pragma unroll
     for (int mt = 0; mt < MT2; ++mt) {
       f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS2; ++ks) {
         const uint4 av = *reinterpret_cast<const uint4*>(&pw[(mt * 16 + l16) * PS + 32 * ks + 8 * lg4]);
-        const uint4 bv = *reinterpret_cast<const uint4*>(&vt[ch * VS + 32 * ks + 8 * lg4]);
-        c = mfma_bf16(av, bv, c);
+        c = mfma_bf16(av, bvs[ks], c);
       }
       // lane group lg4 holds rows 4 lg4 .. 4 lg4 + 3 of tile mt: pairs
       // pi0 = 8 mt + 2 lg4 (hi + lo in c[0], c[1]) and pi0 + 1 (c[2], c[3])
