@@ -27,18 +27,19 @@ __global__ __launch_bounds__(kThreads) void k_score(const float* mean, const flo
   state_rows<BF16, R, D, false>(a.dec, a.st, b, g, x - score_tiles, L);
 }
 
-// Fused decode step, first launch, grid (score_tiles + D * D / 1024 + 1, G,
-// B): for each (b, g), the scorer's tiles, then the S_all / z_all update of
-// this step's token in row chunks (with their o_bar partials), then the
-// token's page row and the statistics of the block it completes.  The two
+// Fused decode step, first launch, grid (score_tiles + D * D / (1024 CPW) +
+// 1, G, B): for each (b, g), the scorer's tiles, then the S_all / z_all
+// update of this step's token in row chunks, CPW chunks a workgroup (with
+// their o_bar partials), then the token's page row and the statistics of the
+// block it completes.  The two
 // parts are independent: the scorer reads statistics of candidate blocks
 // 1..nb-2 only, all completed by earlier appends, and neither pages nor
 // S_all.
-template <bool BF16, int R, int D, bool TAYLOR>
+template <bool BF16, int R, int D, bool TAYLOR, int CPW>
 __global__ __launch_bounds__(kThreads) void k_step_score(const float* mean, const float* var, const void* q,
                                                           int32_t n_tiles, int32_t G, int32_t H, int32_t tiles_all,
                                                           int32_t score_tiles, const StepArgs a) {
-  constexpr int kChunks = D / (1024 / D);  // S_all row chunks per (b, g)
+  constexpr int kGroups = D / (1024 / D) / CPW;  // S_all row-chunk workgroups per (b, g)
   __shared__ ProducerLds<BF16, R, D> L;
   const DecodeArgs& dc = a.dec;
   const int x = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -50,8 +51,8 @@ __global__ __launch_bounds__(kThreads) void k_step_score(const float* mean, cons
   SPLA_SCALARS_READY("s"(dc.bk), "s"(a.st.k_new), "s"(a.st.v_new), "s"(a.st.s_all), "s"(a.st.z_all),
                      "s"(dc.obar_part), "s"(dc.dz_part), "s"(a.st.block_table), "s"(a.st.k_pages),
                      "s"(a.st.v_pages));
-  if (x < score_tiles + kChunks) {
-    state_rows<BF16, R, D, true>(dc, a.st, b, g, x - score_tiles, L.state);
+  if (x < score_tiles + kGroups) {
+    state_rows<BF16, R, D, true, CPW>(dc, a.st, b, g, (x - score_tiles) * CPW, L.state);
     return;
   }
   const int T = dc.lens[b];  // after the append
@@ -72,16 +73,26 @@ hipError_t launch_score_form(const StepArgs& a, bool bf16, const Launch& l) {
                                            d.q, d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
 }
 
-template <bool TAYLOR>
-hipError_t launch_step_score_form(const StepArgs& a, bool bf16, const Launch& l) {
-  const int chunks = a.dec.d / (1024 / a.dec.d);
-  const dim3 grid(a.dec.score_tiles + chunks + 1, a.dec.G, a.dec.B);
+template <bool TAYLOR, int CPW>
+hipError_t launch_step_score_cpw(const StepArgs& a, bool bf16, const Launch& l) {
+  const int groups = a.dec.d / (1024 / a.dec.d) / CPW;
+  const dim3 grid(a.dec.score_tiles + groups + 1, a.dec.G, a.dec.B);
   const DecodeArgs& d = a.dec;
   if (bf16)
-    SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<true, RR, DD, TAYLOR>, grid, l, d.blk_mean, d.blk_var,
-                                             d.q, d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
-  SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<false, RR, DD, TAYLOR>, grid, l, d.blk_mean, d.blk_var,
-                                           d.q, d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
+    SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<true, RR, DD, TAYLOR, CPW>, grid, l, d.blk_mean,
+                                             d.blk_var, d.q, d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
+  SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<false, RR, DD, TAYLOR, CPW>, grid, l, d.blk_mean,
+                                           d.blk_var, d.q, d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
+}
+
+// the S_all row chunks four to a workgroup from kStateGroupPairs (b, g)
+// pairs on: at 64 sequences x 8 KV heads the first kernel takes 56 us
+// instead of 63 us that way, while at 128 pairs and fewer the single-chunk
+// workgroups are faster (the longer state workgroups end the kernel)
+template <bool TAYLOR>
+hipError_t launch_step_score_form(const StepArgs& a, bool bf16, const Launch& l) {
+  if (a.dec.B * a.dec.G >= kStateGroupPairs) return launch_step_score_cpw<TAYLOR, 4>(a, bf16, l);
+  return launch_step_score_cpw<TAYLOR, 1>(a, bf16, l);
 }
 
 }  // namespace

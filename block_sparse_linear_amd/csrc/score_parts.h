@@ -158,68 +158,83 @@ __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const 
 //            every query head h of the group, from the rows just read or
 //            updated (so the token attends to itself): the combine sums the
 //            D * D / 1024 chunks and never reads S_all.
+// CPW > 1: one workgroup takes CPW consecutive chunks (for batches with so
+// many (b, g) pairs that a workgroup per chunk costs more in workgroup
+// overhead than it gains in spread).
 template <int R, int D>
 struct StateRowsLds {
   float4 red[R][1024 / D][D / 4];
   float zred[R][1024 / D];
 };
 
-template <bool BF16, int R, int D, bool UPDATE>
-__device__ void state_rows(const DecodeArgs& dc, const StateRefs& st, int b, int g, int rc, StateRowsLds<R, D>& L) {
+template <bool BF16, int R, int D, bool UPDATE, int CPW = 1>
+__device__ void state_rows(const DecodeArgs& dc, const StateRefs& st, int b, int g, int rc0, StateRowsLds<R, D>& L) {
   constexpr int ROWS = 1024 / D, C4N = D / 4, CHUNKS = D / ROWS;
   auto& red = L.red;
   auto& zred = L.zred;
   const int xr = threadIdx.x / C4N, c4 = threadIdx.x % C4N;
-  const int x = rc * ROWS + xr;
   const size_t bg = (size_t)b * dc.G + g;
-  float4* S = reinterpret_cast<float4*>(st.s_all) + (bg * D + x) * C4N + c4;
-  float* z = st.z_all + bg * D + x;
-  float4 s = *S;
-  float zx = *z;
-  float qx[R];
+  // CPW consecutive chunks rc0 .. rc0 + CPW - 1: every load first, then one
+  // chunk after the other through the same LDS (each chunk's arithmetic and
+  // partials as when it has a workgroup of its own)
+  float4 s[CPW];
+  float zx[CPW], qx[CPW][R], kx[CPW];
 #pragma unroll
-  for (int h = 0; h < R; ++h) qx[h] = load_elem<BF16>(dc.q, ((size_t)b * dc.H + g * R + h) * D + x);
-  if constexpr (UPDATE) {
-    const float f = phi_f(load_elem<BF16>(st.k_new, bg * D + x));
-    const float4 v = load4<BF16>(st.v_new, bg * D + c4 * 4);
-    s = make_float4(s.x + fmaf(f, v.x, 0.f), s.y + fmaf(f, v.y, 0.f), s.z + fmaf(f, v.z, 0.f),
-                    s.w + fmaf(f, v.w, 0.f));
-    zx = zx + (0.f + f);
-    *S = s;
-    if (c4 == 0) *z = zx;
+  for (int c = 0; c < CPW; ++c) {
+    const int x = (rc0 + c) * ROWS + xr;
+    s[c] = reinterpret_cast<const float4*>(st.s_all)[(bg * D + x) * C4N + c4];
+    zx[c] = st.z_all[bg * D + x];
+#pragma unroll
+    for (int h = 0; h < R; ++h) qx[c][h] = load_elem<BF16>(dc.q, ((size_t)b * dc.H + g * R + h) * D + x);
+    if constexpr (UPDATE) kx[c] = load_elem<BF16>(st.k_new, bg * D + x);
   }
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (UPDATE) v = load4<BF16>(st.v_new, bg * D + c4 * 4);
 #pragma unroll
-  for (int h = 0; h < R; ++h) {
-    const float fq = phi_f(qx[h]);
-    red[h][xr][c4] = make_float4(fq * s.x, fq * s.y, fq * s.z, fq * s.w);
-    if (c4 == 0) {
-      zred[h][xr] = fq * zx;
-      // phi(q) of row x as bf16 hi + lo for the attend kernel's matrix-core
-      // operands (hi + lo carries phi to ~2^-16 relative)
-      const uint32_t hi = pack_bf16(fq, 0.f) & 0xffffu;
-      const uint32_t lo = pack_bf16(fq - bf16_lo_f(hi), 0.f) & 0xffffu;
-      uint16_t* dst = dc.phq + ((size_t)b * dc.H + g * R + h) * 2 * D + x;
-      dst[0] = (uint16_t)hi;
-      dst[D] = (uint16_t)lo;
+  for (int c = 0; c < CPW; ++c) {
+    const int rc = rc0 + c, x = rc * ROWS + xr;
+    if (c > 0) __syncthreads();  // the previous chunk's partials are read out of LDS
+    if constexpr (UPDATE) {
+      const float f = phi_f(kx[c]);
+      s[c] = make_float4(s[c].x + fmaf(f, v.x, 0.f), s[c].y + fmaf(f, v.y, 0.f), s[c].z + fmaf(f, v.z, 0.f),
+                         s[c].w + fmaf(f, v.w, 0.f));
+      zx[c] = zx[c] + (0.f + f);
+      reinterpret_cast<float4*>(st.s_all)[(bg * D + x) * C4N + c4] = s[c];
+      if (c4 == 0) st.z_all[bg * D + x] = zx[c];
     }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < R * C4N; i += kThreads) {
-    const int h = i / C4N, c = i % C4N;
-    float4 acc = red[h][0][c];
 #pragma unroll
-    for (int r = 1; r < ROWS; ++r) {
-      const float4 t = red[h][r][c];
-      acc = make_float4(acc.x + t.x, acc.y + t.y, acc.z + t.z, acc.w + t.w);
+    for (int h = 0; h < R; ++h) {
+      const float fq = phi_f(qx[c][h]);
+      red[h][xr][c4] = make_float4(fq * s[c].x, fq * s[c].y, fq * s[c].z, fq * s[c].w);
+      if (c4 == 0) {
+        zred[h][xr] = fq * zx[c];
+        // phi(q) of row x as bf16 hi + lo for the attend kernel's matrix-core
+        // operands (hi + lo carries phi to ~2^-16 relative)
+        const uint32_t hi = pack_bf16(fq, 0.f) & 0xffffu;
+        const uint32_t lo = pack_bf16(fq - bf16_lo_f(hi), 0.f) & 0xffffu;
+        uint16_t* dst = dc.phq + ((size_t)b * dc.H + g * R + h) * 2 * D + x;
+        dst[0] = (uint16_t)hi;
+        dst[D] = (uint16_t)lo;
+      }
     }
-    reinterpret_cast<float4*>(dc.obar_part)[((bg * CHUNKS + rc) * R + h) * C4N + c] = acc;
-  }
-  if ((int)threadIdx.x < R) {
-    const int h = threadIdx.x;
-    float acc = zred[h][0];
+    __syncthreads();
+    for (int i = threadIdx.x; i < R * C4N; i += kThreads) {
+      const int h = i / C4N, cc = i % C4N;
+      float4 acc = red[h][0][cc];
 #pragma unroll
-    for (int r = 1; r < ROWS; ++r) acc += zred[h][r];
-    dc.dz_part[(bg * CHUNKS + rc) * R + h] = acc;
+      for (int r = 1; r < ROWS; ++r) {
+        const float4 t = red[h][r][cc];
+        acc = make_float4(acc.x + t.x, acc.y + t.y, acc.z + t.z, acc.w + t.w);
+      }
+      reinterpret_cast<float4*>(dc.obar_part)[((bg * CHUNKS + rc) * R + h) * C4N + cc] = acc;
+    }
+    if ((int)threadIdx.x < R) {
+      const int h = threadIdx.x;
+      float acc = zred[h][0];
+#pragma unroll
+      for (int r = 1; r < ROWS; ++r) acc += zred[h][r];
+      dc.dz_part[(bg * CHUNKS + rc) * R + h] = acc;
+    }
   }
 }
 

@@ -17,10 +17,13 @@ constexpr int kMaxBlocksPerSeq = 16386;  // the selector ranks at most 16384 can
 constexpr int kMaxAppendEntries = 64;  // entries per append launch (host splits larger calls)
 constexpr int kTile = 64;              // blocks per statistics tile (= wavefront width)
 constexpr int kThreads = 256;          // threads per workgroup of every kernel
-constexpr int kPartHdr = 4;
+constexpr int kPartHdr = 4;  // floats of a partial record's header: m, l, sum_w, pad
 // (b, h) pairs from which a combine workgroup takes a whole head (fewer: a
 // 32-channel slice each)
-constexpr int kCombineWholeHeads = 256;            // floats of a partial record's header: m, l, sum_w, pad
+constexpr int kCombineWholeHeads = 256;
+// (b, g) pairs from which the first kernel of a decode step takes four S_all
+// row chunks per workgroup instead of one
+constexpr int kStateGroupPairs = 512;
 
 // block score forms (spla_score_form)
 constexpr int kScoreTaylor = 0, kScoreMean = 1;

@@ -124,6 +124,28 @@ def test_step_ragged_batch_with_chunks():
     _run(w, page_order="shuffled", use_step=True)
 
 
+@pytest.mark.parametrize("d, G", [(128, 8), (64, 4)])
+def test_step_many_pairs_state_groups(d, G):
+    # at least 512 (sequence, KV head) pairs: the first kernel updates S_all
+    # four row chunks per workgroup (d = 64: all four chunks of a pair in one);
+    # ragged lengths, block ends crossed, sampled pairs against the oracle
+    _needs_gpu()
+    from tests.spla_parity import ParityRun
+    B = 512 // G
+    rng = np.random.default_rng(5)
+    t0 = tuple(int(x) for x in rng.integers(1, 64 * 12, size=B))
+    t0 = (64 * 20 - 2, 63, 64) + t0[3:]
+    w = Workload(name=f"pairs{B}x{G}", batch=B, n_q_heads=2 * G, n_kv_heads=G, head_dim=d, block_size=64, top_k=6,
+                 kv_dtype="bf16", t0=t0, steps=3, kind="normal", seed=57)
+    seqs = [0, 1, 2, 5, B // 2, B - 1]
+    print(f"[case] {w.name} d={d} seqs={seqs}", flush=True)
+    run = ParityRun(w, steps=3, page_order="shuffled", prefill_chunk=1000, use_step=True, seqs=seqs,
+                    kv_heads=[0, G - 1])
+    failures = run.run(verbose=True)
+    assert not failures, "\n".join(failures[:20])
+    assert run.layer.error_word() == 0
+
+
 def test_step_fp32_and_block128():
     _run(make_workload("tiny_fp32", steps=4), use_step=True)
     _run(small(name="step_bk128", head_dim=64, block_size=128, t0=(128 * 40 + 126,), top_k=12, steps=4),
