@@ -10,7 +10,7 @@
 // The two kinds touch disjoint memory: statistics read tokens older than the
 // append from the pages (written by earlier launches) and the new tokens from
 // k_new, never the page rows this launch writes.
-#include "append_items.h"
+#include "decode_common.h"
 
 namespace spla {
 
@@ -22,7 +22,7 @@ __device__ __forceinline__ int find_entry(const int32_t* prefix, int n, int item
   return e;
 }
 
-template <bool BF16>
+template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void k_append(const AppendArgs a) {
   int item = blockIdx.x;
   if (item < a.page_items) {
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kThreads) void k_append(const AppendArgs a) {
     const int e = find_entry(a.stat_prefix, a.n_entries, item);
     const int local = item - a.stat_prefix[e];
     __shared__ BlockStatsLds<BF16> L;
-    append_block_stats<BF16>(a.st, a.e[e], a.e[e].t0 / a.st.bk + local / a.st.G, local % a.st.G, L);
+    append_block_stats<BF16, D>(a.st, a.e[e], a.e[e].t0 / a.st.bk + local / a.st.G, local % a.st.G, L);
   }
 }
 
@@ -44,7 +44,8 @@ __global__ __launch_bounds__(kThreads) void k_append(const AppendArgs a) {
 hipError_t launch_append(const AppendArgs& a, bool bf16, const Launch& l) {
   const int n = a.page_items + a.stat_items;
   if (n == 0) return hipSuccess;
-  return bf16 ? launch_kernel(k_append<true>, dim3(n), l, a) : launch_kernel(k_append<false>, dim3(n), l, a);
+  if (bf16) SPLA_DISPATCH_D(a.st.d, launch_kernel(k_append<true, DD>, dim3(n), l, a))
+  SPLA_DISPATCH_D(a.st.d, launch_kernel(k_append<false, DD>, dim3(n), l, a))
 }
 
 }  // namespace spla

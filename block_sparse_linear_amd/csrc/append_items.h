@@ -69,14 +69,15 @@ struct BlockStatsLds {
   float red[kThreads * (BF16 ? 8 : 4)];  // per-column partial sums of every thread
 };
 
-template <bool BF16>
+template <bool BF16, int D>
 __device__ void append_block_stats(const StateRefs& a, const AppendEntry& E, int j, int g, BlockStatsLds<BF16>& L) {
   constexpr int VE = BF16 ? 8 : 4;  // elements per 16-byte vector
-  constexpr int MAXV = 16;          // vectors per thread (fp32 keys, d = 128, Bk = 128)
+  constexpr int d = D;
+  constexpr int vr = d / VE;        // vectors per token row
+  constexpr int tg = kThreads / vr;  // token groups
+  constexpr int MAXV = 128 / tg;    // vectors (tokens) per thread at Bk = 128
   float* red = L.red;
-  const int d = a.d, bk = a.bk;
-  const int vr = d / VE;            // vectors per token row
-  const int tg = kThreads / vr;     // token groups
+  const int bk = a.bk;
   const int nv = bk / tg;           // vectors (tokens) per thread
   const int col = threadIdx.x % vr, t0 = threadIdx.x / vr;
   const int page = a.block_table[(size_t)E.seq * a.max_blocks + j];
@@ -96,7 +97,7 @@ __device__ void append_block_stats(const StateRefs& a, const AppendEntry& E, int
                         : kn[((size_t)(E.row + p - E.t0) * a.G + g) * vr + col];
     }
   }
-  auto elem = [&](const uint4& v, int e) -> float {
+  auto elem = [](uint4 v, int e) -> float {
     const uint32_t w = e < 2 * (VE / 4) ? (e < VE / 4 ? v.x : v.y) : (e < 3 * (VE / 4) ? v.z : v.w);
     if constexpr (BF16) return (e & 1) ? bf16_hi_f(w) : bf16_lo_f(w);
     return __uint_as_float(w);

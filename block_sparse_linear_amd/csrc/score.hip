@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void k_step_score(const float* mean, cons
   const int T = dc.lens[b];  // after the append
   const AppendEntry E{b, 1, T - 1, b};
   append_page_row_head<BF16>(a.st, E, g);
-  if (T % dc.bk == 0) append_block_stats<BF16>(a.st, E, T / dc.bk - 1, g, L.stats);
+  if (T % dc.bk == 0) append_block_stats<BF16, D>(a.st, E, T / dc.bk - 1, g, L.stats);
 }
 
 template <bool TAYLOR>

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void k_step_fused(const float* mean, cons
       const int T = dc.lens[b];  // after the append
       const AppendEntry E{b, 1, T - 1, b};
       append_page_row_head<true>(a.st, E, g);
-      if (T % dc.bk == 0) append_block_stats<true>(a.st, E, T / dc.bk - 1, g, L.prod.stats);
+      if (T % dc.bk == 0) append_block_stats<true, D>(a.st, E, T / dc.bk - 1, g, L.prod.stats);
     }
     step_signal(dc.step_ctr + (size_t)bgi * kStepCtrStride);
     return;
