@@ -163,8 +163,8 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(const DecodeArgs a) {
   const int slot = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.top_k), "s"(a.sel_in), "s"(a.sel), "s"(a.sel_page),
                      "s"(a.G), "s"(a.q), "s"(a.H), "s"(a.k_pages), "s"(a.v_pages));
-  uint4 qraw[D / 32], fh[D / 32], fl[D / 32];
-  load_q_mfma<R, D>(a.q, a.phq, a.H, g, b, qraw, fh, fl);  // independent of the selection: issued first
+  QOps<R, D> qo;
+  load_qops<R, D>(a.q, a.phq, a.H, g, b, qo);  // independent of the selection: issued first
   const size_t srow = ((size_t)b * a.G + g) * a.top_k + slot;
   int j, page;
   if (a.sel_in) {
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(const DecodeArgs a) {
   }
   // many workgroups per CU here: V straight into LDS (fewer registers, more
   // workgroups resident)
-  attend_block_mfma<R, D, BK, true>(a, slot, g, b, j, page, qraw, fh, fl);
+  attend_block_mfma<R, D, BK, true>(a, slot, g, b, j, page, qo);
 }
 
 }  // namespace

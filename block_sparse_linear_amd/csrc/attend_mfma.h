@@ -66,46 +66,100 @@ __device__ __forceinline__ void load_to_lds16(const void* src, uint16_t* lds_blo
                                    0);
 }
 
-// A operands of product (1) for this lane: row m = lane % 16 holds query m
-// (m < R), or bf16 hi / lo of phi(query m - WB) (from the phi(q) array the
-// first kernel of the decode wrote); other rows read row 0 and are masked
-// when the operands are formed
+// A operands of product (1), loaded before the block is known.  A row of a
+// matrix product depends on that row of A alone, so rows that hold nothing
+// useful read any valid data and their results are never used.
+//  - Packed (R <= 4): one row set per k-step.  Row m < R holds query m, row
+//    4 + h the bf16 hi part of phi(query h), row 8 + h its lo part (from the
+//    phi(q) array the first kernel of the decode wrote).  Three products per
+//    k-step, against K, phi(K) hi and phi(K) lo, give q.k in rows < R of one
+//    accumulator and the hi and lo halves of phi(q).phi(k) in rows 4 + h and
+//    8 + h of another.
+//  - Otherwise (R = 8): q in rows m < R, phi(q) hi and lo in rows 8 + h of two
+//    more row sets, masked to zero elsewhere, all in one accumulator.
 template <int R, int D>
-__device__ __forceinline__ void load_q_raw(const void* q, int H, int g, int b, uint4 (&qraw)[D / 32]) {
-  const int lane = threadIdx.x % 64, m = lane % 16, lg4 = lane / 16;
-  const int hq = m < R ? m : 0;
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-    qraw[ks] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) +
-                                               ((size_t)b * H + g * R + hq) * D + 32 * ks + 8 * lg4);
+struct QOps {
+  static constexpr bool kPacked = R <= 4;
+  static constexpr int kRows = kPacked ? 1 : 3;
+  uint4 a[kRows][D / 32];
+};
+
+// this lane's A-row pointer of the packed form: q rows, phi(q) hi / lo rows,
+// or query 0 for the unused rows
+template <int R, int D>
+__device__ __forceinline__ const uint16_t* packed_row(const void* q, const uint16_t* phq, int H, int g, int b,
+                                                      bool with_phi) {
+  const int m = (threadIdx.x % 64) % 16;
+  const uint16_t* qp = reinterpret_cast<const uint16_t*>(q) + ((size_t)b * H + g * R) * D;
+  const uint16_t* fp = phq + ((size_t)b * H + g * R) * 2 * D;
+  if (m < R) return qp + (size_t)m * D;
+  if (with_phi && m >= 4 && m < 4 + R) return fp + (size_t)(m - 4) * 2 * D;
+  if (with_phi && m >= 8 && m < 8 + R) return fp + (size_t)(m - 8) * 2 * D + D;
+  return qp;
 }
+
+// the rows that come from q (the packed form's phi rows get query 0 for now)
 template <int R, int D>
-__device__ __forceinline__ void load_phq(const uint16_t* phq, int H, int g, int b, uint4 (&fh)[D / 32],
-                                         uint4 (&fl)[D / 32]) {
-  constexpr int WB = R <= 4 ? 4 : 8;
+__device__ __forceinline__ void load_qops_q(const void* q, int H, int g, int b, QOps<R, D>& o) {
   const int lane = threadIdx.x % 64, m = lane % 16, lg4 = lane / 16;
-  const int hw = (m >= WB && m < WB + R) ? m - WB : 0;
-  const uint16_t* fq = phq + ((size_t)b * H + g * R + hw) * 2 * D;
+  if constexpr (QOps<R, D>::kPacked) {
+    const uint16_t* p = packed_row<R, D>(q, nullptr, H, g, b, false);
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    fh[ks] = *reinterpret_cast<const uint4*>(fq + 32 * ks + 8 * lg4);
-    fl[ks] = *reinterpret_cast<const uint4*>(fq + D + 32 * ks + 8 * lg4);
+    for (int ks = 0; ks < D / 32; ++ks) o.a[0][ks] = *reinterpret_cast<const uint4*>(p + 32 * ks + 8 * lg4);
+  } else {
+    const int hq = m < R ? m : 0;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      o.a[0][ks] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) +
+                                                   ((size_t)b * H + g * R + hq) * D + 32 * ks + 8 * lg4);
   }
 }
+
+// the rows that come from phi(q) (after load_qops_q)
 template <int R, int D>
-__device__ __forceinline__ void load_q_mfma(const void* q, const uint16_t* phq, int H, int g, int b,
-                                            uint4 (&qraw)[D / 32], uint4 (&fh)[D / 32], uint4 (&fl)[D / 32]) {
-  load_q_raw<R, D>(q, H, g, b, qraw);
-  load_phq<R, D>(phq, H, g, b, fh, fl);
+__device__ __forceinline__ void load_qops_phi(const uint16_t* phq, int H, int g, int b, QOps<R, D>& o) {
+  const int lane = threadIdx.x % 64, m = lane % 16, lg4 = lane / 16;
+  if constexpr (QOps<R, D>::kPacked) {
+    const bool hi = m >= 4 && m < 4 + R, lo = m >= 8 && m < 8 + R;
+    const uint16_t* fq = phq + ((size_t)b * H + g * R + (hi ? m - 4 : (lo ? m - 8 : 0))) * 2 * D + (lo ? D : 0);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const uint4 v = *reinterpret_cast<const uint4*>(fq + 32 * ks + 8 * lg4);
+      if (hi || lo) o.a[0][ks] = v;
+    }
+  } else {
+    constexpr int WB = 8;
+    const int hw = (m >= WB && m < WB + R) ? m - WB : 0;
+    const uint16_t* fq = phq + ((size_t)b * H + g * R + hw) * 2 * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      o.a[1][ks] = *reinterpret_cast<const uint4*>(fq + 32 * ks + 8 * lg4);
+      o.a[2][ks] = *reinterpret_cast<const uint4*>(fq + D + 32 * ks + 8 * lg4);
+    }
+  }
+}
+
+// both: one load per k-step in the packed form
+template <int R, int D>
+__device__ __forceinline__ void load_qops(const void* q, const uint16_t* phq, int H, int g, int b, QOps<R, D>& o) {
+  if constexpr (QOps<R, D>::kPacked) {
+    const int lg4 = (threadIdx.x % 64) / 16;
+    const uint16_t* p = packed_row<R, D>(q, phq, H, g, b, true);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) o.a[0][ks] = *reinterpret_cast<const uint4*>(p + 32 * ks + 8 * lg4);
+  } else {
+    load_qops_q<R, D>(q, H, g, b, o);
+    load_qops_phi<R, D>(phq, H, g, b, o);
+  }
 }
 
 // Block j (page `page`) of (b, g), all R query heads, bf16 K/V; writes the
 // partial record of `slot`.  Matrix cores do both contractions:
 //   (1) logits s = q.k and linear weights w = phi(q).phi(k) of the block's
 //       tokens: rows of the 16-row A operand are the R queries and the R
-//       phi(q) (bf16 hi/lo split), B is the K tile read straight from the
-//       page plus phi(K) hi/lo computed in registers; wavefront w takes 16
-//       (Bk = 64) or 32 (Bk = 128) tokens;
+//       phi(q) (bf16 hi/lo split; layouts at QOps), B is the K tile read
+//       straight from the page plus phi(K) hi/lo computed in registers;
+//       wavefront w takes 16 (Bk = 64) or 32 (Bk = 128) tokens;
 //   (2) sum_t p_t v_t and sum_t w_t v_t: rows of A are p and w (hi/lo split,
 //       from LDS), B is the V tile in LDS; wavefront w takes a quarter of the
 //       value channels.  VLDS: the V tile goes from the page straight into
@@ -120,8 +174,7 @@ __device__ __forceinline__ void load_q_mfma(const void* q, const uint16_t* phq, 
 // the workgroup.
 template <int R, int D, int BK, bool VLDS = false>
 __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot, int g, int b, int j, int page,
-                                                  const uint4 (&qraw)[D / 32], const uint4 (&fh)[D / 32],
-                                                  const uint4 (&fl)[D / 32]) {
+                                                  const QOps<R, D>& qo) {
   constexpr int NKS = D / 32;              // k-steps per channel block
   constexpr int NT1W = BK / 64;            // 16-token tiles per wavefront
   constexpr int WB = R <= 4 ? 4 : 8;       // first linear-weight row of product (1)
@@ -195,40 +248,63 @@ __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot,
     for (int i = threadIdx.x; i < MT2 * 16 * PS / 2; i += kThreads) reinterpret_cast<uint32_t*>(pw)[i] = 0u;
   }
 
-  // ---- A operands of product (1)
-  const bool is_q = m < R, is_w = m >= WB && m < WB + R;
-  // rows that are not queries / phi(q) rows are zero (bit masks keep this
-  // plain VALU work)
-  const uint32_t mq = is_q ? 0xffffffffu : 0u, mw = is_w ? 0xffffffffu : 0u;
-  uint4 aq[NKS], afh[NKS], afl[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    aq[ks] = make_uint4(qraw[ks].x & mq, qraw[ks].y & mq, qraw[ks].z & mq, qraw[ks].w & mq);
-    afh[ks] = make_uint4(fh[ks].x & mw, fh[ks].y & mw, fh[ks].z & mw, fh[ks].w & mw);
-    afl[ks] = make_uint4(fl[ks].x & mw, fl[ks].y & mw, fl[ks].z & mw, fl[ks].w & mw);
-  }
-
-  // ---- product (1): logits and linear weights of this wavefront's tokens
+  // ---- product (1): logits and linear weights of this wavefront's tokens.
+  // w = phi(q).phi(k) from bf16 hi / lo pairs of both: a single bf16 phi(k)
+  // would leave ~1e-4 relative error in sum w, which the subtraction
+  // D = phi(q).z_all - sum w magnifies when few tokens are unselected.
+  // c1: lane (lg4, reg i) holds row 4 lg4 + i of the 16 x 16 result for
+  // token l16, with rows < R the logits and rows WB + h the linear weights
   f32x4_t c1[NT1W];
+  if constexpr (QOps<R, D>::kPacked) {
 #pragma unroll
-  for (int nt = 0; nt < NT1W; ++nt) {
-    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT1W; ++nt) {
+      f32x4_t cs = {0.f, 0.f, 0.f, 0.f}, cw = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        uint4 fkh, fkl;
+        phi_bf16_split(kraw[nt][ks], fkh, fkl);
+        cs = mfma_bf16(qo.a[0][ks], kraw[nt][ks], cs);
+        cw = mfma_bf16(qo.a[0][ks], fkh, cw);
+        cw = mfma_bf16(qo.a[0][ks], fkl, cw);
+      }
+      // rows 4 + h (lane group 1) hold phi_hi(q_h).phi(k), rows 8 + h (lane
+      // group 2, 16 lanes up) phi_lo(q_h).phi(k): their sum is w
+      const int src = ((lane + 16) & 63) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float up = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(cw[i])));
+        c1[nt][i] = lg4 == 1 ? cw[i] + up : cs[i];
+      }
+    }
+  } else {
+    // q rows and phi(q) rows in one accumulator: rows that are not queries /
+    // phi(q) rows of each operand are zero (bit masks keep this plain VALU
+    // work); the lo x lo product (~2^-18 relative) is left out
+    const bool is_q = m < R, is_w = m >= WB && m < WB + R;
+    const uint32_t mq = is_q ? 0xffffffffu : 0u, mw = is_w ? 0xffffffffu : 0u;
+    uint4 aq[NKS], afh[NKS], afl[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      // w = phi(q).phi(k) from hi / lo pairs of both (the lo x lo product,
-      // ~2^-18 relative, is left out).  A single bf16 phi(k) would leave
-      // ~1e-4 relative error in sum w, which the subtraction
-      // D = phi(q).z_all - sum w magnifies when few tokens are unselected.
-      uint4 fkh, fkl;
-      phi_bf16_split(kraw[nt][ks], fkh, fkl);
-      c = mfma_bf16(aq[ks], kraw[nt][ks], c);
-      c = mfma_bf16(afh[ks], fkh, c);
-      c = mfma_bf16(afl[ks], fkh, c);
-      c = mfma_bf16(afh[ks], fkl, c);
+      const uint4 q0 = qo.a[0][ks], f0 = qo.a[1 % QOps<R, D>::kRows][ks], f1 = qo.a[2 % QOps<R, D>::kRows][ks];
+      aq[ks] = make_uint4(q0.x & mq, q0.y & mq, q0.z & mq, q0.w & mq);
+      afh[ks] = make_uint4(f0.x & mw, f0.y & mw, f0.z & mw, f0.w & mw);
+      afl[ks] = make_uint4(f1.x & mw, f1.y & mw, f1.z & mw, f1.w & mw);
     }
-    c1[nt] = c;
+#pragma unroll
+    for (int nt = 0; nt < NT1W; ++nt) {
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        uint4 fkh, fkl;
+        phi_bf16_split(kraw[nt][ks], fkh, fkl);
+        c = mfma_bf16(aq[ks], kraw[nt][ks], c);
+        c = mfma_bf16(afh[ks], fkh, c);
+        c = mfma_bf16(afl[ks], fkh, c);
+        c = mfma_bf16(afh[ks], fkl, c);
+      }
+      c1[nt] = c;
+    }
   }
-  // lane (lg4, reg i) holds row 4*lg4 + i of the 16 x 16 result, token l16
   const float inv_sqrt_d = a.inv_sqrt_d;
   float mloc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll

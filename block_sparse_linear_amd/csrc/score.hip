@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kThreads) void k_score(const float* mean, const flo
 // 1..nb-2 only, all completed by earlier appends, and neither pages nor
 // S_all.
 template <bool BF16, int R, int D, bool TAYLOR, int CPW>
-__global__ __launch_bounds__(kThreads) void k_step_score(const float* mean, const float* var, const void* q,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_step_score(const float* mean, const float* var, const void* q,
                                                           int32_t n_tiles, int32_t G, int32_t H, int32_t tiles_all,
                                                           int32_t score_tiles, const StepArgs a) {
   constexpr int kGroups = D / (1024 / D) / CPW;  // S_all row-chunk workgroups per (b, g)

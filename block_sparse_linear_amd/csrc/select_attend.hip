@@ -71,8 +71,8 @@ __global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, con
   // the queries
   SelectKeys<KPT> k;
   select_load<KPT>(lg, block_table, n_tiles, max_blocks, G, g, b, b, k);
-  uint4 qraw[D / 32], fh[D / 32], fl[D / 32];
-  load_q_mfma<R, D>(q, phq, H, g, b, qraw, fh, fl);
+  QOps<R, D> qo;
+  load_qops<R, D>(q, phq, H, g, b, qo);
   SPLA_SCALARS_READY("s"(a.lens[b]), "s"(a.bk), "s"(a.top_k), "s"(a.sel), "s"(a.k_pages), "s"(a.v_pages),
                      "s"(a.part), "s"(a.part_hdr), "s"(a.num_pages), "s"(a.inv_sqrt_d));
   const int nb = n_blocks(a, b);
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void k_select_attend(const float* lg, con
   select_slot<KPT>(a, block_table, max_blocks, b, nb, slot, k, U.sel, j, page);
   // the combine reads the selection to tell used slots from unused ones
   if (threadIdx.x == 0) a.sel[((size_t)b * a.G + g) * a.top_k + slot] = j;
-  attend_block_mfma<R, D, 64>(a, slot, g, b, j, page, qraw, fh, fl);
+  attend_block_mfma<R, D, 64>(a, slot, g, b, j, page, qo);
   // the record and the selection are in the L2: the pair's merge workgroups
   // may read them
   if constexpr (MERGE) step_signal(a.step_ctr + (size_t)bgi * kStepCtrStride);

@@ -84,13 +84,13 @@ __global__ __launch_bounds__(kThreads) void k_step_fused(const float* mean, cons
   // queries
   SelectKeys<KPT> k;
   select_load_pages<KPT>(dc.block_table, n_tiles, dc.max_blocks, b, k);
-  uint4 qraw[D / 32], fh[D / 32], fl[D / 32];
-  load_q_raw<R, D>(q, H, g, b, qraw);
+  QOps<R, D> qo;
+  load_qops_q<R, D>(q, H, g, b, qo);
   SPLA_SCALARS_READY("s"(dc.lens[b]), "s"(dc.bk), "s"(dc.top_k), "s"(dc.sel), "s"(dc.k_pages), "s"(dc.v_pages),
                      "s"(dc.part), "s"(dc.part_hdr), "s"(dc.num_pages), "s"(dc.inv_sqrt_d), "s"(dc.lg), "s"(dc.phq));
   step_wait(ctr, np, dc.err);
   select_load_scores<KPT>(dc.lg, n_tiles, dc.max_blocks, G, g, b, k);
-  load_phq<R, D>(dc.phq, H, g, b, fh, fl);
+  load_qops_phi<R, D>(dc.phq, H, g, b, qo);
   // the pair's attend count, and (slot 0) the producers' XCD mask: every
   // producer counted here must have run on this XCD, else its stores may
   // sit in another XCD's L2.  Issued after the loads above, so that their
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void k_step_fused(const float* mean, cons
   select_slot<KPT>(dc, dc.block_table, dc.max_blocks, b, nb, slot, k, L.sel, j, page);
   // the combine reads the selection to tell used slots from unused ones
   if (threadIdx.x == 0) dc.sel[((size_t)b * G + g) * dc.top_k + slot] = j;
-  attend_block_mfma<R, D, 64>(dc, slot, g, b, j, page, qraw, fh, fl);
+  attend_block_mfma<R, D, 64>(dc, slot, g, b, j, page, qo);
   if (threadIdx.x == 0) {
     if (arrived > dc.top_k) atomicOr(dc.err, kErrStepArrive);
     if (slot == 0 && mask != (1 << xcc_id())) atomicOr(dc.err, kErrStepXcd);
