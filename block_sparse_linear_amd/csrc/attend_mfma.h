@@ -20,6 +20,13 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32
                                                   c, 0, 0, 0);
 }
 
+// 16 bytes of a K/V tile: read once per call, streamed past the caches
+__device__ __forceinline__ uint4 load_stream_u4(const uint16_t* p) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u x = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 __device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
 // phi of 8 packed bf16 values as bf16 hi + lo pairs (hi = phi rounded to
@@ -218,7 +225,7 @@ __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot,
     const int tok = (w * NT1W + nt) * 16 + l16;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      kraw[nt][ks] = *reinterpret_cast<const uint4*>(kp + (size_t)tok * D + 32 * ks + 8 * lg4);
+      kraw[nt][ks] = load_stream_u4(kp + (size_t)tok * D + 32 * ks + 8 * lg4);
   }
   uint4 vr[VLDS ? 1 : NV][2];
   if constexpr (VLDS) {
@@ -239,8 +246,8 @@ __device__ __forceinline__ void attend_block_mfma(const DecodeArgs& a, int slot,
     for (int i = 0; i < NV; ++i) {
       const int idx = threadIdx.x + kThreads * i;
       const int tp = idx % (BK / 2), cg = idx / (BK / 2);
-      vr[i][0] = *reinterpret_cast<const uint4*>(vp + (size_t)(2 * tp) * D + 8 * cg);
-      vr[i][1] = *reinterpret_cast<const uint4*>(vp + (size_t)(2 * tp + 1) * D + 8 * cg);
+      vr[i][0] = load_stream_u4(vp + (size_t)(2 * tp) * D + 8 * cg);
+      vr[i][1] = load_stream_u4(vp + (size_t)(2 * tp + 1) * D + 8 * cg);
     }
   }
   __builtin_amdgcn_sched_barrier(0);

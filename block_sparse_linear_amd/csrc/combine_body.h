@@ -64,6 +64,21 @@ __device__ __forceinline__ void combine_wait(const CombineWait& wt, uint32_t* er
   }
 }
 
+// 16 bytes of a partial record, read once per call: past the caches
+// (non-temporal) for the whole-head decode combine of many (b, h) pairs
+// (with 16 x 32 and 64 x 32 heads the combine took 5.1 and 9.6 us that way
+// against 5.2 and 9.9 us)
+template <bool STREAM>
+__device__ __forceinline__ float4 load_rec4(const float* p) {
+  if constexpr (STREAM) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const v4f x = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+    return make_float4(x[0], x[1], x[2], x[3]);
+  } else {
+    return *reinterpret_cast<const float4*>(p);
+  }
+}
+
 template <int R, int D, int FORM, bool ONE, bool WHOLE>
 __device__ __forceinline__ void combine_slice(const float* part, const float* part_hdr, const float* obar_part,
                                               const float* dz_part, const int32_t* sel, int32_t G, int32_t H,
@@ -117,7 +132,7 @@ __device__ __forceinline__ void combine_slice(const float* part, const float* pa
   float4 dv[SPT];
 #pragma unroll
   for (int u = 0; u < SPT; ++u)
-    dv[u] = *reinterpret_cast<const float4*>(PD + (size_t)min(sg + SG * u, top_k - 1) * rec);
+    dv[u] = load_rec4<WHOLE && !ONE>(PD + (size_t)min(sg + SG * u, top_k - 1) * rec);
   __builtin_amdgcn_sched_barrier(0);
   // the rest of the arguments, while the loads are in flight
   float4 gm = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -172,7 +187,7 @@ __device__ __forceinline__ void combine_slice(const float* part, const float* pa
     if (u0 > 0) {
 #pragma unroll
       for (int u = 0; u < SPT; ++u)
-        dv[u] = *reinterpret_cast<const float4*>(PD + (size_t)min(sg + SG * (u0 + u), top_k - 1) * rec);
+        dv[u] = load_rec4<WHOLE && !ONE>(PD + (size_t)min(sg + SG * (u0 + u), top_k - 1) * rec);
     }
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {

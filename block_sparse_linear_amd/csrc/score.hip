@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kThreads) void k_score(const float* mean, const flo
 // parts are independent: the scorer reads statistics of candidate blocks
 // 1..nb-2 only, all completed by earlier appends, and neither pages nor
 // S_all.
-template <bool BF16, int R, int D, bool TAYLOR, int CPW>
+template <bool BF16, int R, int D, bool TAYLOR, int CPW, bool STREAM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_step_score(const float* mean, const float* var, const void* q,
                                                           int32_t n_tiles, int32_t G, int32_t H, int32_t tiles_all,
                                                           int32_t score_tiles, const StepArgs a) {
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                      "s"(dc.obar_part), "s"(dc.dz_part), "s"(a.st.block_table), "s"(a.st.k_pages),
                      "s"(a.st.v_pages));
   if (x < score_tiles + kGroups) {
-    state_rows<BF16, R, D, true, CPW>(dc, a.st, b, g, (x - score_tiles) * CPW, L.state);
+    state_rows<BF16, R, D, true, CPW, STREAM>(dc, a.st, b, g, (x - score_tiles) * CPW, L.state);
     return;
   }
   const int T = dc.lens[b];  // after the append
@@ -73,17 +73,23 @@ hipError_t launch_score_form(const StepArgs& a, bool bf16, const Launch& l) {
                                            d.q, d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
 }
 
-template <bool TAYLOR, int CPW>
+template <bool TAYLOR, int CPW, bool STREAM>
 hipError_t launch_step_score_cpw(const StepArgs& a, bool bf16, const Launch& l) {
   const int groups = a.dec.d / (1024 / a.dec.d) / CPW;
   const dim3 grid(a.dec.score_tiles + groups + 1, a.dec.G, a.dec.B);
   const DecodeArgs& d = a.dec;
   if (bf16)
-    SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<true, RR, DD, TAYLOR, CPW>, grid, l, d.blk_mean,
+    SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<true, RR, DD, TAYLOR, CPW, STREAM>, grid, l, d.blk_mean,
                                              d.blk_var, d.q, d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
-  SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<false, RR, DD, TAYLOR, CPW>, grid, l, d.blk_mean,
+  SPLA_DISPATCH_RD(d.r, d.d, launch_kernel(k_step_score<false, RR, DD, TAYLOR, CPW, STREAM>, grid, l, d.blk_mean,
                                            d.blk_var, d.q, d.n_tiles, d.G, d.H, d.tiles_all, d.score_tiles, a))
 }
+
+// (b, g) pairs from which the S_all rows are read and written past the
+// caches (non-temporal): at 16 x 8 and 64 x 8 pairs the decode step took 62.5
+// and 165 us that way against 64.8 and 173 us, at 8 pairs (B = 1) 19.5
+// against 19.4 us
+constexpr int kStreamStatePairs = 128;
 
 // the S_all row chunks four to a workgroup from kStateGroupPairs (b, g)
 // pairs on: at 64 sequences x 8 KV heads the first kernel takes 56 us
@@ -91,8 +97,10 @@ hipError_t launch_step_score_cpw(const StepArgs& a, bool bf16, const Launch& l) 
 // workgroups are faster (the longer state workgroups end the kernel)
 template <bool TAYLOR>
 hipError_t launch_step_score_form(const StepArgs& a, bool bf16, const Launch& l) {
-  if (a.dec.B * a.dec.G >= kStateGroupPairs) return launch_step_score_cpw<TAYLOR, 4>(a, bf16, l);
-  return launch_step_score_cpw<TAYLOR, 1>(a, bf16, l);
+  const int pairs = a.dec.B * a.dec.G;
+  if (pairs >= kStateGroupPairs) return launch_step_score_cpw<TAYLOR, 4, true>(a, bf16, l);
+  if (pairs >= kStreamStatePairs) return launch_step_score_cpw<TAYLOR, 1, true>(a, bf16, l);
+  return launch_step_score_cpw<TAYLOR, 1, false>(a, bf16, l);
 }
 
 }  // namespace

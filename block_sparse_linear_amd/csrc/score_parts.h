@@ -35,6 +35,19 @@ struct ScoreTileLds {
   float red[4][2 * R][kTile];
 };
 
+// a float4 that is read (or written) once per call, streamed past the caches
+__device__ __forceinline__ float4 load_stream4(const float4* p) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const v4f x = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+  return make_float4(x[0], x[1], x[2], x[3]);
+}
+
+__device__ __forceinline__ void store_stream4(float4* p, const float4& v) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  v4f x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<v4f*>(p));
+}
+
 template <bool BF16, int R, int D, bool TAYLOR>
 __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const int b, const ScorePre& p,
                            ScoreTileLds<R, D>& L) {
@@ -68,9 +81,10 @@ __device__ void score_tile(const DecodeArgs& a, const int t, const int g, const 
                       (size_t)(w * NC4) * kTile + lane;
   float4 m[NC4], v[NC4];
 #pragma unroll
-  for (int i = 0; i < NC4; ++i) m[i] = mean4[base + (size_t)i * kTile];
+  for (int i = 0; i < NC4; ++i) m[i] = load_stream4(&mean4[base + (size_t)i * kTile]);
 #pragma unroll
-  for (int i = 0; i < NC4; ++i) v[i] = TAYLOR ? var4[base + (size_t)i * kTile] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < NC4; ++i)
+    v[i] = TAYLOR ? load_stream4(&var4[base + (size_t)i * kTile]) : make_float4(0.f, 0.f, 0.f, 0.f);
   // keep every load above this point: the whole tile is in flight before the
   // first use
   __builtin_amdgcn_sched_barrier(0);
@@ -167,7 +181,7 @@ struct StateRowsLds {
   float zred[R][1024 / D];
 };
 
-template <bool BF16, int R, int D, bool UPDATE, int CPW = 1>
+template <bool BF16, int R, int D, bool UPDATE, int CPW = 1, bool STREAM = false>
 __device__ void state_rows(const DecodeArgs& dc, const StateRefs& st, int b, int g, int rc0, StateRowsLds<R, D>& L) {
   constexpr int ROWS = 1024 / D, C4N = D / 4, CHUNKS = D / ROWS;
   auto& red = L.red;
@@ -182,7 +196,8 @@ __device__ void state_rows(const DecodeArgs& dc, const StateRefs& st, int b, int
 #pragma unroll
   for (int c = 0; c < CPW; ++c) {
     const int x = (rc0 + c) * ROWS + xr;
-    s[c] = reinterpret_cast<const float4*>(st.s_all)[(bg * D + x) * C4N + c4];
+    const float4* sp = reinterpret_cast<const float4*>(st.s_all) + (bg * D + x) * C4N + c4;
+    s[c] = STREAM ? load_stream4(sp) : *sp;
     zx[c] = st.z_all[bg * D + x];
 #pragma unroll
     for (int h = 0; h < R; ++h) qx[c][h] = load_elem<BF16>(dc.q, ((size_t)b * dc.H + g * R + h) * D + x);
@@ -199,7 +214,12 @@ __device__ void state_rows(const DecodeArgs& dc, const StateRefs& st, int b, int
       s[c] = make_float4(s[c].x + fmaf(f, v.x, 0.f), s[c].y + fmaf(f, v.y, 0.f), s[c].z + fmaf(f, v.z, 0.f),
                          s[c].w + fmaf(f, v.w, 0.f));
       zx[c] = zx[c] + (0.f + f);
-      reinterpret_cast<float4*>(st.s_all)[(bg * D + x) * C4N + c4] = s[c];
+      float4* sp = reinterpret_cast<float4*>(st.s_all) + (bg * D + x) * C4N + c4;
+      if constexpr (STREAM) {
+        store_stream4(sp, s[c]);
+      } else {
+        *sp = s[c];
+      }
       if (c4 == 0) st.z_all[bg * D + x] = zx[c];
     }
 #pragma unroll
