@@ -110,7 +110,7 @@ template <int R, int D>
 __device__ __forceinline__ void load_qops_q(const void* q, int H, int g, int b, QOps<R, D>& o) {
   const int lane = threadIdx.x % 64, m = lane % 16, lg4 = lane / 16;
   if constexpr (QOps<R, D>::kPacked) {
-    const uint16_t* p = packed_row<R, D>(q, nullptr, H, g, b, false);
+    const uint16_t* p = packed_row<R, D>(q, reinterpret_cast<const uint16_t*>(q), H, g, b, false);  // no phi rows
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) o.a[0][ks] = *reinterpret_cast<const uint4*>(p + 32 * ks + 8 * lg4);
   } else {
